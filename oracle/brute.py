@@ -1,0 +1,58 @@
+"""Independent NumPy brute force of the LLA codec and decode attention, for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY.  Written separately from lla_oracle.c (whole-tensor reshapes and
+einsum instead of explicit loops) so the two can pin each other.  Latents here are in logical
+order [B][N][G][r] (no paging); lengths mask the tail.
+
+Follows the pages on Looped Latent Attention (arXiv 2607.15456): pith.science paper page,
+"What carries the argument" (encode c = (x - mu) W_down, reconstruct x_hat_t = c W_up,t + mu_t,
+attention unchanged) and the abstract (per-head default, LLA-2D folds the heads).
+"""
+import numpy as np
+
+
+def stack(mode, x):
+    """Staging [B][T][H][d] -> stacked, un-centred vectors [B][G][X] ((t, h, i) order for 2D)."""
+    B, T, H, d = x.shape
+    if mode == 1:
+        return x.reshape(B, 1, T * H * d)
+    return np.transpose(x, (0, 2, 1, 3)).reshape(B, H, T * d)
+
+
+def encode(mode, W_down, mu, x):
+    xs = stack(mode, np.asarray(x, dtype=np.float64))
+    return np.einsum("bgx,gxr->bgr", xs - mu[None], W_down)
+
+
+def reconstruct(t, c, W_up, mu, T):
+    """c [B][N][G][r], W_up [T][G][r][Dg], mu [G][X] -> [B][N][G][Dg] for loop t."""
+    Dg = W_up.shape[-1]
+    mu_t = mu.reshape(mu.shape[0], T, Dg)[:, t, :]
+    return np.einsum("bngr,grk->bngk", c, W_up[t]) + mu_t[None, None]
+
+
+def attention(q, K, V, lens, k_self=None, v_self=None, scale=None):
+    """q [B][H][d]; K, V [B][N][H][d]; positions j >= lens[b] are masked out."""
+    B, N, H, d = K.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    s = scale * np.einsum("bhd,bnhd->bhn", q, K)
+    mask = np.arange(N)[None, :] < np.asarray(lens)[:, None]  # [B][N]
+    s = np.where(mask[:, None, :], s, -np.inf)
+    if k_self is not None:
+        s = np.concatenate([s, scale * np.einsum("bhd,bhd->bh", q, k_self)[..., None]], axis=-1)
+        V = np.concatenate([V, v_self[:, None]], axis=1)
+    m = np.max(s, axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(s - m)
+    Z = w.sum(-1, keepdims=True)
+    p = w / np.where(Z > 0, Z, 1.0)
+    return np.einsum("bhn,bnhd->bhd", p, V)
+
+
+def decode(mode, T, H, d, t, W_up_k, W_up_v, mu_k, mu_v, ck, cv, lens, q, k_self=None,
+           v_self=None, scale=None):
+    B, N = ck.shape[:2]
+    K = reconstruct(t, ck, W_up_k, mu_k, T).reshape(B, N, H, d)
+    V = reconstruct(t, cv, W_up_v, mu_v, T).reshape(B, N, H, d)
+    return attention(q, K, V, lens, k_self, v_self, scale)
