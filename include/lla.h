@@ -1,0 +1,177 @@
+/*
+ * lla.h -- C ABI of liblla.so, the MI355X (gfx950) Looped Latent Attention decode hot path.
+ *
+ * Method: "Looped Latent Attention: Cross-Loop KV Compression for Looped Transformers"
+ * (O'Neill & Reid, arXiv 2607.15456).  For each layer, head and axis (K or V) the T per-loop
+ * vectors of a token are stacked and centred and stored as a latent c = (x - mu) W_down of rank
+ * r; loop t reads it back as x_hat_t = c W_up,t + mu_t, and attention itself is unchanged
+ * (pith.science paper page, "What carries the argument").  Loop-specific K/V are rebuilt only when
+ * attention reads them; the default codec is per head, LLA-2D folds all heads of a layer into one
+ * latent per axis (abstract).  Compression rho = 2 T d_head / (r_k + r_v) (Eq. 4).
+ *
+ * Conventions shared by every entry point
+ *   - Plain C: every pointer is a raw device pointer unless it says "host".  No torch types.
+ *   - Ownership: the caller allocates and owns every buffer; the library allocates nothing, keeps
+ *     no global mutable state and never frees anything.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *     call returns without synchronising.
+ *   - Errors: arguments are validated on the host before anything is enqueued; on a validation
+ *     error the call returns the status and enqueues nothing.  LLA_ERR_HIP reports a failed launch.
+ *     No C++ exception crosses the ABI.  Calls on disjoint buffers are thread-safe.
+ *   - Loop index t is 0-based (the pages count loops 1..T).
+ *   - Shapes.  H = n_heads, d = d_head, T = loops.  Per-head mode: G = H latent groups, D_g = d.
+ *     LLA-2D mode: G = 1, D_g = H*d.  X = T*D_g is the stacked length.  Element type is
+ *     codec->dtype (bf16 or fp32) for every floating buffer except the optional fp32 encode copies.
+ *   - Stacking order of x (a reading: the pages say only "stacked"): per-head x[t*d + i] for head
+ *     h; LLA-2D x[(t*H + h)*d + i].  mu_t is block t of mu (length D_g).
+ *   - Out-of-range page ids in a block table make the affected outputs NaN (never a fault).
+ *     Lengths are clamped to [0, max_seq_len].
+ */
+#ifndef LLA_H
+#define LLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LLA_OK = 0,
+    LLA_ERR_NULL = 1,        /* a required pointer is NULL (or only one of k_self / v_self given) */
+    LLA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    LLA_ERR_DTYPE = 3,       /* unknown dtype */
+    LLA_ERR_ALIGN = 4,       /* a buffer is not 16-byte aligned */
+    LLA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the size query returned */
+    LLA_ERR_UNSUPPORTED = 6, /* valid, but no kernel is built for this shape */
+    LLA_ERR_HIP = 7          /* a kernel launch failed */
+} lla_status;
+
+typedef enum { LLA_F32 = 0, LLA_BF16 = 1 } lla_dtype;
+typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_mode;
+
+/* Codec shape (host struct).  Supported: d_head in {64, 128}; 1 <= T <= 64; 1 <= r <= X.
+ * bf16 decode: (r_k, r_v) in {(16,16), (16,32), (32,32), (32,64), (64,64), (64,128), (96,160)}.
+ * fp32 decode: any r_k, r_v with (r_k + r_v) * d_head <= 16384.  Encode: any r. */
+typedef struct {
+    int32_t mode;      /* lla_mode */
+    int32_t T;         /* loops per token */
+    int32_t n_heads;   /* H (query heads = key/value heads) */
+    int32_t d_head;    /* d */
+    int32_t r_k, r_v;  /* latent ranks of the K and V codecs */
+    int32_t dtype;     /* lla_dtype of every floating buffer */
+} lla_codec;
+
+/* Codec parameters of one layer (host struct of device pointers, row-major):
+ *   W_down_{k,v} [G][X][r]           encode projection (encode only; may be NULL for decode)
+ *   W_up_{k,v}   [T][G][r][D_g]      per-loop up-projection W_up,t
+ *   mu_{k,v}     [G][X]              centring mean; mu_t = mu[g][t*D_g : (t+1)*D_g]           */
+typedef struct {
+    const void *W_down_k, *W_down_v;
+    const void *W_up_k, *W_up_v;
+    const void *mu_k, *mu_v;
+} lla_params;
+
+/* Paged cache of one layer (host struct of device pointers).
+ *   latent pools: k_pool [n_pages][G][P][r_k], v_pool [n_pages][G][P][r_v]
+ *   flat pools (lla_ref_attn):  [n_pages][H][P][d] each, one loop's uncompressed K / V
+ *   block_table [batch][max_pages] int32: token j of sequence b is at page block_table[b][j/P],
+ *   slot j%P.  seq_lens [batch] int32: cached tokens per sequence (never modified here; the
+ *   caller increments it after lla_encode_append).  max_seq_len bounds every seq_lens entry and
+ *   must satisfy max_seq_len <= max_pages * P; it sizes the split plan.
+ *   page_size P: a multiple of 32 for the bf16 decode path.                                  */
+typedef struct {
+    void *k_pool, *v_pool;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int32_t batch, page_size, max_pages, n_pages, max_seq_len;
+} lla_cache;
+
+/* How a decode call is split across the GPU (reported for tests and benchmarks). */
+typedef struct {
+    int32_t kernel;           /* 1 bf16 MFMA latent kernel, 2 fp32 latent kernel, 3 flat kernel */
+    int32_t splits;           /* context splits per (sequence, head) */
+    int32_t tokens_per_split;
+    int32_t waves_per_block;
+    size_t workspace_bytes;   /* what the call needs (0 if none) */
+} lla_plan;
+
+/* Eq. 4 (pith.science paper page, "What carries the argument"): rho = 2 T d / (r_k + r_v) per
+ * head and layer; for LLA-2D the latent covers all heads, rho = 2 T H d / (r_k + r_v).
+ * Returns 0.0 for a NULL or invalid codec. */
+double lla_compression_ratio(const lla_codec *codec);
+
+/* Bytes one cached token occupies per layer: G * (r_k + r_v) * sizeof(dtype) (0 if invalid). */
+size_t lla_latent_bytes_per_token(const lla_codec *codec);
+
+/* Bytes the uncompressed loop-indexed cache would take per token and layer:
+ * 2 * T * H * d * sizeof(dtype) (Figure 1: every loop keeps its own K_t, V_t). */
+size_t lla_flat_bytes_per_token(const lla_codec *codec);
+
+/* Split plan and workspace size of lla_decode_attn for this codec and cache (host call). */
+lla_status lla_decode_plan(const lla_codec *codec, const lla_cache *cache, lla_plan *plan);
+
+/*
+ * Decode attention of loop t for every sequence and head of one layer, reading the latent cache
+ * (arXiv abstract: K/V are reconstructed only when attention reads them; pith.science paper
+ * page, "What carries the argument": x_hat_t = c W_up,t + mu_t, attention unchanged).
+ * For each sequence b and head h:
+ *   s_j  = scale * <q[b][h], K_hat_t(j)[h]>   for every cached token j < seq_lens[b]
+ *   plus, when k_self/v_self are given, the current token's own loop-t key/value (a reading:
+ *   the token attends to itself, as in a causal decoder);
+ *   out[b][h] = sum_j softmax(s)_j V_hat_t(j)[h].
+ * An empty context without a self term gives out = 0.
+ *   q, out           [B][H][d]   (dtype)
+ *   k_self, v_self   rows at k_self + b*self_stride + h*d (dtype); both NULL or both set;
+ *                    self_stride in elements, 0 means H*d
+ *   workspace        device, >= plan.workspace_bytes (may be NULL if that is 0)
+ * Reads W_up_{k,v} and mu_{k,v} of `params` only.
+ */
+lla_status lla_decode_attn(const lla_codec *codec, const lla_params *params,
+                           const lla_cache *cache, int32_t t, const void *q, const void *k_self,
+                           const void *v_self, int64_t self_stride, float scale, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Encode and append (pith.science paper page, "What carries the argument": the T per-loop vectors
+ * are stacked and centred, c = (x - mu) W_down).  For every sequence b, group g and axis:
+ *   c = (stack_g(x[b]) - mu[g]) W_down[g],  accumulated in fp32,
+ *   written (rounded to the pool dtype, bf16 round-to-nearest-even) to the pool slot of logical
+ *   position write_pos[b] (page block_table[b][pos/P], slot pos%P).
+ *   x_k, x_v        staging [B][T][H][d] (dtype): the token's K / V at every loop
+ *   write_pos       device int32 [B]; positions >= max_pages*P or < 0 are skipped
+ *   c_k_out/c_v_out optional device fp32 [B][G][r] copies of c before rounding (NULL = none)
+ * Reads W_down_{k,v} and mu_{k,v} of `params`.  seq_lens is not read or modified.
+ */
+lla_status lla_encode_append(const lla_codec *codec, const lla_params *params,
+                             const lla_cache *cache, const void *x_k, const void *x_v,
+                             const int32_t *write_pos, float *c_k_out, float *c_v_out,
+                             void *stream);
+
+/* Split plan and workspace size of lla_ref_attn. */
+lla_status lla_ref_plan(int32_t n_heads, int32_t d_head, int32_t dtype, const lla_cache *flat,
+                        lla_plan *plan);
+
+/*
+ * Flat comparator: the same decode attention over an uncompressed loop-t cache (Figure 1 caption:
+ * each recurrent step t contributes its own (K_t, V_t)).  `flat` describes pools
+ * [n_pages][H][P][d] of loop t's keys and values; q, k_self, v_self, self_stride, scale, out and
+ * the workspace are as in lla_decode_attn.  d_head in {64, 128}.
+ */
+lla_status lla_ref_attn(int32_t n_heads, int32_t d_head, int32_t dtype, const lla_cache *flat,
+                        const void *q, const void *k_self, const void *v_self,
+                        int64_t self_stride, float scale, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *lla_status_str(lla_status status);
+
+/* Library version, "major.minor.patch". */
+const char *lla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H */

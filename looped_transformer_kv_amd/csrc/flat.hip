@@ -1,0 +1,150 @@
+// flat.hip -- decode attention over an uncompressed, paged loop-t K/V cache (the comparator).
+//
+// The loop-indexed cache the latent store replaces (Figure 1 caption of "Looped Latent
+// Attention": each recurrent step t contributes its own (K_t, V_t), so loop t's attention reads
+// exactly those).  Pure HBM streaming at about one flop per byte, so this is a VALU kernel laid
+// out for coalescing: a token's d-vector is read by D/8 (bf16) or D/4 (fp32) lanes with 16-byte
+// loads, every lane group keeps its own online-softmax state (no cross-group traffic in the loop),
+// and U steps are unrolled so each lane keeps 2U loads in flight.
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+template <int D, typename TS, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void flat_kernel(DecodeArgs a) {
+    constexpr int EPL = 16 / sizeof(TS);    // elements per lane per 16-byte load
+    constexpr int LPT = D / EPL;            // lanes per token
+    constexpr int TPW = 64 / LPT;           // tokens per wave step
+    static_assert(LPT >= 1 && LPT <= 64 && 64 % LPT == 0, "lane layout");
+
+    __shared__ __align__(16) float sO[WAVES][D];
+    __shared__ float sM[WAVES], sL[WAVES];
+
+    const int S = a.S;
+    const int id = blockIdx.x;
+    const int s = id % S;
+    const int h = (id / S) % a.H;
+    const int b = id / (S * a.H);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane / LPT, sub = lane % LPT;
+
+    const TS *qp = static_cast<const TS *>(a.q) + ((size_t)b * a.H + h) * D + sub * EPL;
+    float qv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = ld_elt<TS>(qp + e) * a.scale_log2;
+
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    const int j_begin = s * a.tokens_per_split;
+    const int j_end = min(j_begin + a.tokens_per_split, len);
+    const TS *kpool = static_cast<const TS *>(a.k_pool);
+    const TS *vpool = static_cast<const TS *>(a.v_pool);
+    const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+
+    float m = -INFINITY, l = 0.f, o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+
+    for (int j0 = j_begin + wave * TPW * U; j0 < j_end; j0 += WAVES * TPW * U) {
+        uint4 kr[U], vr[U];
+        bool ok[U], bad[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * TPW + grp;
+            ok[u] = j < j_end;
+            bad[u] = false;
+            kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
+            if (ok[u]) {
+                int page = bt[j / a.P];
+                bad[u] = (unsigned)page >= (unsigned)a.n_pages;
+                page = bad[u] ? 0 : page;
+                const size_t off = (((size_t)page * a.H + h) * a.P + j % a.P) * D + sub * EPL;
+                kr[u] = *reinterpret_cast<const uint4 *>(kpool + off);
+                vr[u] = *reinterpret_cast<const uint4 *>(vpool + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const TS *kk = reinterpret_cast<const TS *>(&kr[u]);
+            const TS *vv = reinterpret_cast<const TS *>(&vr[u]);
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dot += qv[e] * ld_elt<TS>(kk + e);
+#pragma unroll
+            for (int off = LPT / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+            float sc = ok[u] ? dot : -INFINITY;
+            if (bad[u]) sc = __builtin_nanf("");
+            const float m_new = fmaxf(m, sc);
+            const float alpha = (m == m_new) ? 1.f : exp2_(m - m_new);
+            const float p = (sc == -INFINITY) ? 0.f : exp2_(sc - m_new);
+            l = l * alpha + p;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = o[e] * alpha + p * ld_elt<TS>(vv + e);
+            m = m_new;
+        }
+    }
+
+    // merge the lane groups of the wave (lanes that differ in the group bits)
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m, off, 64);
+        const float l2 = __shfl_xor(l, off, 64);
+        const float M = fmaxf(m, m2);
+        const float e1 = (m == -INFINITY) ? 0.f : exp2_(m - M);
+        const float e2 = (m2 == -INFINITY) ? 0.f : exp2_(m2 - M);
+        l = l * e1 + l2 * e2;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float o2 = __shfl_xor(o[e], off, 64);
+            o[e] = o[e] * e1 + o2 * e2;
+        }
+        m = M;
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sO[wave][sub * EPL + e] = o[e];
+        if (sub == 0) {
+            sM[wave] = m;
+            sL[wave] = l;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < D; i += 64 * WAVES) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sM[w]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const float e = exp2_(sM[w] - M);
+                L += sL[w] * e;
+                O += sO[w][i] * e;
+            }
+        }
+        float *rec = a.ws + (((size_t)b * a.H + h) * S + s) * (D + kPartialPad);
+        rec[i] = O;
+        if (i == 0) {
+            rec[D] = M;
+            rec[D + 1] = L;
+        }
+    }
+}
+
+template <int D, typename TS>
+hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
+    const unsigned blocks = (unsigned)a.B * a.H * a.S;
+    hipLaunchKernelGGL((flat_kernel<D, TS, 4, 4>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t st) {
+    if (d == 128) return bf16 ? launch_t<128, uint16_t>(a, st) : launch_t<128, float>(a, st);
+    if (d == 64) return bf16 ? launch_t<64, uint16_t>(a, st) : launch_t<64, float>(a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lla

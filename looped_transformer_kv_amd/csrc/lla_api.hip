@@ -1,0 +1,311 @@
+// lla_api.hip -- the C ABI of liblla.so (declared in include/lla.h): argument validation, split
+// planning and kernel launches.  No allocation, no global mutable state, no host synchronisation.
+#include <cstdint>
+#include <cstdlib>
+
+#include "lla_internal.h"
+
+namespace lla {
+size_t decode_f32_lds_bytes(int d, int r_k, int r_v);
+}
+
+using namespace lla;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr size_t kMaxDynLds = 64 * 1024;
+
+struct Shape {
+    int G, Dg;
+    long X;
+};
+
+Shape shape_of(const lla_codec *c) {
+    Shape s;
+    s.G = c->mode == LLA_2D ? 1 : c->n_heads;
+    s.Dg = c->mode == LLA_2D ? c->n_heads * c->d_head : c->d_head;
+    s.X = (long)c->T * s.Dg;
+    return s;
+}
+
+size_t elt_size(int dtype) { return dtype == LLA_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lla_status check_codec(const lla_codec *c) {
+    if (!c) return LLA_ERR_NULL;
+    if (c->dtype != LLA_F32 && c->dtype != LLA_BF16) return LLA_ERR_DTYPE;
+    if (c->mode != LLA_PER_HEAD && c->mode != LLA_2D) return LLA_ERR_SHAPE;
+    if (c->T < 1 || c->T > 64 || c->n_heads < 1 || c->n_heads > 4096) return LLA_ERR_SHAPE;
+    if (c->d_head != 64 && c->d_head != 128) return LLA_ERR_SHAPE;
+    const long X = shape_of(c).X;
+    if (c->r_k < 1 || c->r_v < 1 || c->r_k > X || c->r_v > X) return LLA_ERR_SHAPE;
+    return LLA_OK;
+}
+
+// Pools, block table and sizes of a paged cache.  seq_lens is required only for decode.
+lla_status check_cache(const lla_cache *k, bool need_lens) {
+    if (!k) return LLA_ERR_NULL;
+    if (!k->k_pool || !k->v_pool || !k->block_table || (need_lens && !k->seq_lens))
+        return LLA_ERR_NULL;
+    if (k->batch < 0 || k->page_size < 1 || k->max_pages < 1 || k->n_pages < 1 ||
+        k->max_seq_len < 0 || (long)k->max_seq_len > (long)k->max_pages * k->page_size)
+        return LLA_ERR_SHAPE;
+    if (!aligned16(k->k_pool) || !aligned16(k->v_pool)) return LLA_ERR_ALIGN;
+    return LLA_OK;
+}
+
+int target_blocks() {
+    // Workgroups a decode call aims for (context splits are added until B*H*S reaches it).
+    // LLA_TARGET_BLOCKS overrides the default for tuning sweeps.
+    static const int v = [] {
+        const char *e = std::getenv("LLA_TARGET_BLOCKS");
+        const int x = e ? std::atoi(e) : 0;
+        return x > 0 ? x : 1024;
+    }();
+    return v;
+}
+
+// Context splits: enough workgroups to fill the chip, each covering a multiple of `unit`
+// tokens and at most `max_tps` tokens.
+void split_plan(int rows, int max_len, int unit, int max_tps, lla_plan *p) {
+    const int chunks = (max_len + unit - 1) / unit;
+    int S = (target_blocks() + rows - 1) / (rows > 0 ? rows : 1);
+    const int S_min = (max_len + max_tps - 1) / max_tps;
+    if (S > chunks) S = chunks;
+    if (S < S_min) S = S_min;
+    if (S < 1) S = 1;
+    int tps = (max_len + S - 1) / S;
+    tps = ((tps + unit - 1) / unit) * unit;
+    if (tps < unit) tps = unit;
+    S = (max_len + tps - 1) / tps;
+    if (S < 1) S = 1;
+    p->splits = S;
+    p->tokens_per_split = tps;
+}
+
+lla_status decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
+    const bool bf16 = c->dtype == LLA_BF16;
+    p->kernel = bf16 ? 1 : 2;
+    p->waves_per_block = 4;
+    split_plan(k->batch * c->n_heads, k->max_seq_len, bf16 ? 32 * 4 : 256,
+               bf16 ? 32 * kMaxChunksPerSplit : (1 << 30), p);
+    p->workspace_bytes = (size_t)k->batch * c->n_heads * p->splits *
+                         (c->d_head + kPartialPad) * sizeof(float);
+    return LLA_OK;
+}
+
+lla_status ref_plan(int H, int d, int dtype, const lla_cache *k, lla_plan *p) {
+    const int epl = dtype == LLA_BF16 ? 8 : 4;
+    const int tpw = 64 / (d / epl);
+    p->kernel = 3;
+    p->waves_per_block = 4;
+    split_plan(k->batch * H, k->max_seq_len, tpw * 4 * 4, 1 << 30, p);
+    p->workspace_bytes = (size_t)k->batch * H * p->splits * (d + kPartialPad) * sizeof(float);
+    return LLA_OK;
+}
+
+lla_status check_workspace(const lla_plan &p, void *ws, size_t bytes) {
+    if (p.workspace_bytes == 0) return LLA_OK;
+    if (!ws || bytes < p.workspace_bytes) return LLA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return LLA_ERR_ALIGN;
+    return LLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+double lla_compression_ratio(const lla_codec *c) {
+    if (check_codec(c) != LLA_OK) return 0.0;
+    const double flat = 2.0 * c->T * c->d_head * (c->mode == LLA_2D ? c->n_heads : 1);
+    return flat / (double)(c->r_k + c->r_v);
+}
+
+size_t lla_latent_bytes_per_token(const lla_codec *c) {
+    if (check_codec(c) != LLA_OK) return 0;
+    return (size_t)shape_of(c).G * (c->r_k + c->r_v) * elt_size(c->dtype);
+}
+
+size_t lla_flat_bytes_per_token(const lla_codec *c) {
+    if (check_codec(c) != LLA_OK) return 0;
+    return (size_t)2 * c->T * c->n_heads * c->d_head * elt_size(c->dtype);
+}
+
+lla_status lla_decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
+    lla_status st = check_codec(c);
+    if (st != LLA_OK) return st;
+    if (!k || !p) return LLA_ERR_NULL;
+    if (k->batch < 0 || k->max_seq_len < 0) return LLA_ERR_SHAPE;
+    return decode_plan(c, k, p);
+}
+
+lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                           int32_t t, const void *q, const void *k_self, const void *v_self,
+                           int64_t self_stride, float scale, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    lla_status st = check_codec(c);
+    if (st != LLA_OK) return st;
+    if (!prm || !prm->W_up_k || !prm->W_up_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
+    if ((st = check_cache(k, true)) != LLA_OK) return st;
+    if (!q || !out || (k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_NULL;
+    if (t < 0 || t >= c->T || self_stride < 0) return LLA_ERR_SHAPE;
+    const bool bf16 = c->dtype == LLA_BF16;
+    if (bf16) {
+        if (!decode_bf16_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
+        if (k->page_size % 32 != 0) return LLA_ERR_SHAPE;
+    } else if (decode_f32_lds_bytes(c->d_head, c->r_k, c->r_v) > kMaxDynLds) {
+        return LLA_ERR_UNSUPPORTED;
+    }
+    lla_plan plan;
+    decode_plan(c, k, &plan);
+    if ((st = check_workspace(plan, workspace, workspace_bytes)) != LLA_OK) return st;
+    if (k->batch == 0) return LLA_OK;
+
+    const Shape sh = shape_of(c);
+    DecodeArgs a{};
+    a.k_pool = k->k_pool;
+    a.v_pool = k->v_pool;
+    a.block_table = k->block_table;
+    a.seq_lens = k->seq_lens;
+    a.W_up_k = prm->W_up_k;
+    a.W_up_v = prm->W_up_v;
+    a.mu_k = prm->mu_k;
+    a.mu_v = prm->mu_v;
+    a.q = q;
+    a.k_self = k_self;
+    a.v_self = v_self;
+    a.self_stride = self_stride ? self_stride : (int64_t)c->n_heads * c->d_head;
+    a.out = out;
+    a.ws = static_cast<float *>(workspace);
+    a.B = k->batch;
+    a.H = c->n_heads;
+    a.G = sh.G;
+    a.Dg = sh.Dg;
+    a.T = c->T;
+    a.t = t;
+    a.r_k = c->r_k;
+    a.r_v = c->r_v;
+    a.P = k->page_size;
+    a.max_pages = k->max_pages;
+    a.n_pages = k->n_pages;
+    a.max_seq_len = k->max_seq_len;
+    a.S = plan.splits;
+    a.tokens_per_split = plan.tokens_per_split;
+    a.mode = c->mode;
+    a.scale_log2 = scale * kLog2e;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = bf16 ? launch_decode_bf16(a, plan.waves_per_block, s) : launch_decode_f32(a, s);
+    if (e != hipSuccess) return LLA_ERR_HIP;
+    e = launch_combine(a, c->d_head, bf16, true, s);
+    return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                             const void *x_k, const void *x_v, const int32_t *write_pos,
+                             float *c_k_out, float *c_v_out, void *stream) {
+    lla_status st = check_codec(c);
+    if (st != LLA_OK) return st;
+    if (!prm || !prm->W_down_k || !prm->W_down_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
+    if ((st = check_cache(k, false)) != LLA_OK) return st;
+    if (!x_k || !x_v || !write_pos) return LLA_ERR_NULL;
+    if (k->batch == 0) return LLA_OK;
+    const Shape sh = shape_of(c);
+    const bool bf16 = c->dtype == LLA_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int axis = 0; axis < 2; ++axis) {
+        EncodeArgs a{};
+        a.x = axis ? x_v : x_k;
+        a.W_down = axis ? prm->W_down_v : prm->W_down_k;
+        a.mu = axis ? prm->mu_v : prm->mu_k;
+        a.pool = axis ? k->v_pool : k->k_pool;
+        a.block_table = k->block_table;
+        a.write_pos = write_pos;
+        a.c_out = axis ? c_v_out : c_k_out;
+        a.B = k->batch;
+        a.H = c->n_heads;
+        a.G = sh.G;
+        a.Dg = sh.Dg;
+        a.T = c->T;
+        a.d = c->d_head;
+        a.r = axis ? c->r_v : c->r_k;
+        a.P = k->page_size;
+        a.max_pages = k->max_pages;
+        a.n_pages = k->n_pages;
+        a.mode = c->mode;
+        if (launch_encode(a, bf16, s) != hipSuccess) return LLA_ERR_HIP;
+    }
+    return LLA_OK;
+}
+
+lla_status lla_ref_plan(int32_t H, int32_t d, int32_t dtype, const lla_cache *k, lla_plan *p) {
+    if (!k || !p) return LLA_ERR_NULL;
+    if (dtype != LLA_F32 && dtype != LLA_BF16) return LLA_ERR_DTYPE;
+    if (H < 1 || (d != 64 && d != 128) || k->batch < 0 || k->max_seq_len < 0)
+        return LLA_ERR_SHAPE;
+    return ref_plan(H, d, dtype, k, p);
+}
+
+lla_status lla_ref_attn(int32_t H, int32_t d, int32_t dtype, const lla_cache *k, const void *q,
+                        const void *k_self, const void *v_self, int64_t self_stride, float scale,
+                        void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (dtype != LLA_F32 && dtype != LLA_BF16) return LLA_ERR_DTYPE;
+    if (H < 1 || H > 4096 || (d != 64 && d != 128)) return LLA_ERR_SHAPE;
+    lla_status st = check_cache(k, true);
+    if (st != LLA_OK) return st;
+    if (!q || !out || (k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_NULL;
+    if (self_stride < 0) return LLA_ERR_SHAPE;
+    lla_plan plan;
+    ref_plan(H, d, dtype, k, &plan);
+    if ((st = check_workspace(plan, workspace, workspace_bytes)) != LLA_OK) return st;
+    if (k->batch == 0) return LLA_OK;
+    DecodeArgs a{};
+    a.k_pool = k->k_pool;
+    a.v_pool = k->v_pool;
+    a.block_table = k->block_table;
+    a.seq_lens = k->seq_lens;
+    a.q = q;
+    a.k_self = k_self;
+    a.v_self = v_self;
+    a.self_stride = self_stride ? self_stride : (int64_t)H * d;
+    a.out = out;
+    a.ws = static_cast<float *>(workspace);
+    a.B = k->batch;
+    a.H = H;
+    a.G = H;
+    a.Dg = d;
+    a.T = 1;
+    a.t = 0;
+    a.P = k->page_size;
+    a.max_pages = k->max_pages;
+    a.n_pages = k->n_pages;
+    a.max_seq_len = k->max_seq_len;
+    a.S = plan.splits;
+    a.tokens_per_split = plan.tokens_per_split;
+    a.mode = 0;
+    a.scale_log2 = scale * kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == LLA_BF16;
+    if (launch_flat(a, d, bf16, s) != hipSuccess) return LLA_ERR_HIP;
+    return launch_combine(a, d, bf16, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+const char *lla_status_str(lla_status s) {
+    switch (s) {
+        case LLA_OK: return "ok";
+        case LLA_ERR_NULL: return "null pointer";
+        case LLA_ERR_SHAPE: return "invalid shape or size";
+        case LLA_ERR_DTYPE: return "invalid dtype";
+        case LLA_ERR_ALIGN: return "buffer not 16-byte aligned";
+        case LLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case LLA_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
+        case LLA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+const char *lla_version(void) { return "0.1.0"; }
+
+}  // extern "C"

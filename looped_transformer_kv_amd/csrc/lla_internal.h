@@ -1,0 +1,120 @@
+// lla_internal.h -- shared internals of liblla.so: kernel argument blocks, launchers and small
+// device helpers for gfx950 (CDNA4, 64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lla.h"
+
+namespace lla {
+
+// ---------------------------------------------------------------- kernel argument blocks
+
+// One decode call (latent or flat).  Pointers are device pointers; element type is bf16
+// (stored as uint16_t) or fp32 according to the kernel instantiation.
+struct DecodeArgs {
+    const void *k_pool, *v_pool;     // latent: [n_pages][G][P][r]; flat: [n_pages][H][P][d]
+    const int32_t *block_table;      // [B][max_pages]
+    const int32_t *seq_lens;         // [B]
+    const void *W_up_k, *W_up_v;     // [T][G][r][Dg]   (latent only)
+    const void *mu_k, *mu_v;         // [G][X]          (latent only)
+    const void *q;                   // [B][H][d]
+    const void *k_self, *v_self;     // rows at + b*self_stride + h*d, or null
+    int64_t self_stride;
+    void *out;                       // [B][H][d]
+    float *ws;                       // partials [B][H][S][d + 4]: o[d], m, l, -, -
+    int B, H, G, Dg, T, t, r_k, r_v, P, max_pages, n_pages, max_seq_len;
+    int S, tokens_per_split;
+    int mode;                        // 0 per-head, 1 LLA-2D
+    float scale_log2;                // softmax scale * log2(e): scores live in the log2 domain
+};
+
+// One encode+append call.
+struct EncodeArgs {
+    const void *x;                   // staging [B][T][H][d]
+    const void *W_down;              // [G][X][r]
+    const void *mu;                  // [G][X]
+    void *pool;                      // [n_pages][G][P][r]
+    const int32_t *block_table;      // [B][max_pages]
+    const int32_t *write_pos;        // [B]
+    float *c_out;                    // optional [B][G][r]
+    int B, H, G, Dg, T, d, r, P, max_pages, n_pages, mode;
+};
+
+// ---------------------------------------------------------------- launchers (host)
+// Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
+hipError_t launch_decode_bf16(const DecodeArgs &a, int waves, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &a, bool bf16, hipStream_t s);
+bool decode_bf16_supported(int d, int r_k, int r_v);
+
+constexpr int kPartialPad = 4;   // partial record = d + 4 floats (16-byte aligned records)
+constexpr int kMaxChunksPerSplit = 512;   // 32-token chunks one latent-decode workgroup covers
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf2f(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename TS> __device__ __forceinline__ float ld_elt(const TS *p);
+template <> __device__ __forceinline__ float ld_elt<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float ld_elt<uint16_t>(const uint16_t *p) { return bf2f(*p); }
+
+template <typename TS> __device__ __forceinline__ void st_elt(TS *p, float v);
+template <> __device__ __forceinline__ void st_elt<float>(float *p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st_elt<uint16_t>(uint16_t *p, float v) { *p = f2bf(v); }
+
+// Butterfly reductions over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// 2^x with 2^(-inf) = 0.
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane permutations inside 16-lane rows (gfx9 encodings).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8-lane half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over each 16-lane row, result in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    return v;
+}
+
+// x[l] + x[l ^ 32] in every lane (v_permlane32_swap).
+__device__ __forceinline__ float add_swap32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace lla

@@ -1,0 +1,65 @@
+"""Uploads a tinycase.Problem to the GPU and wraps it in a runtime.LatentLayer."""
+import numpy as np
+import torch
+
+from looped_transformer_kv_amd import lla, synth
+from looped_transformer_kv_amd.runtime import LatentLayer
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+CODE_DT = {"bf16": lla.LLA_BF16, "f32": lla.LLA_F32}
+
+
+def tol(dtype):
+    """Parity bar: bf16 max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3; fp32 <= 1e-4 max|oracle|."""
+    if dtype == "bf16":
+        return lambda ref: 2e-2 * np.max(np.abs(ref)) + 1e-3
+    return lambda ref: 1e-4 * np.max(np.abs(ref))
+
+
+def assert_close(gpu, ref, dtype, what=""):
+    err = np.max(np.abs(gpu - ref)) if ref.size else 0.0
+    bound = tol(dtype)(ref) if ref.size else 0.0
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    assert err <= bound, f"{what}: max|gpu-oracle| = {err:.3e} > {bound:.3e}"
+    return err, bound
+
+
+class DeviceProblem:
+    def __init__(self, p, device="cuda"):
+        c = p.cfg
+        self.p = p
+        up = lambda a: synth.to_device(a, c.dtype, device)
+        self.codec = lla.make_codec(c.mode, c.T, c.H, c.d, c.r_k, c.r_v, CODE_DT[c.dtype])
+        self.k_pool = up(p.k_pool)
+        self.v_pool = up(p.v_pool)
+        self.block_table = torch.from_numpy(p.block_table).to(device)
+        self.seq_lens = torch.from_numpy(p.seq_lens).to(device)
+        self.x_k = up(p.x_k)
+        self.x_v = up(p.x_v)
+        self.q = {t: up(p.q[t]) for t in p.q}
+        self.layer = LatentLayer(self.codec, up(p.W_down_k), up(p.W_down_v), up(p.W_up_k),
+                                 up(p.W_up_v), up(p.mu_k), up(p.mu_v), self.k_pool, self.v_pool,
+                                 self.block_table, self.seq_lens, c.page, p.max_seq_len)
+        self.device = device
+
+    def decode(self, t, with_self=True, q=None):
+        c = self.p.cfg
+        q = self.q[t] if q is None else q
+        out = torch.full((self.p.B, c.H, c.d), float("nan"), dtype=TORCH_DT[c.dtype],
+                         device=self.device)
+        ws = self.layer.workspace(self.device)
+        ks = self.x_k[:, t] if with_self else None
+        vs = self.x_v[:, t] if with_self else None
+        stride = c.T * c.H * c.d if with_self else 0
+        self.layer.decode(t, q, out, ws, ks, vs, stride)
+        torch.cuda.synchronize()
+        return synth.from_device(out)
+
+    def oracle_decode(self, t, with_self=True, k_pool=None, v_pool=None, seq_lens=None):
+        from oracle import oracle as O
+        p, c = self.p, self.p.cfg
+        ks, vs = p.self_kv(t) if with_self else (None, None)
+        return O.decode(c.mode, c.T, c.H, c.d, c.r_k, c.r_v, t, p.W_up_k, p.W_up_v, p.mu_k,
+                        p.mu_v, p.k_pool if k_pool is None else k_pool,
+                        p.v_pool if v_pool is None else v_pool, p.block_table,
+                        p.seq_lens if seq_lens is None else seq_lens, c.page, p.q[t], ks, vs)

@@ -1,0 +1,115 @@
+"""The C ABI on the CPU: liblla.so loads, exports every function include/lla.h declares, and its
+host-only helpers and argument validation behave (nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+from fractions import Fraction
+
+import pytest
+
+from looped_transformer_kv_amd import lla, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("lla_decode_attn", "lla_encode_append", "lla_ref_attn"):
+        assert must in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(name):
+    L = lla.lib()
+    assert hasattr(L, name), f"liblla.so does not export {name}"
+
+
+def test_package_has_no_fallback():
+    # the binding refuses to run without the library rather than computing anywhere else
+    assert os.path.exists(lla.LIB_PATH)
+    src = open(os.path.join(ROOT, "looped_transformer_kv_amd", "lla.py")).read()
+    assert "oracle" not in src.replace("no fallback", "")
+
+
+def _codec(c):
+    return lla.make_codec(c.mode, c.T, c.H, c.d, c.r_k, c.r_v,
+                          lla.LLA_F32 if c.dtype == "f32" else lla.LLA_BF16)
+
+
+@pytest.mark.parametrize("name", sorted(synth.CONFIGS))
+def test_ratio_and_byte_accounting(name):
+    c = synth.CONFIGS[name]
+    codec = _codec(c)
+    rho = lla.lla_compression_ratio(codec)
+    exact = Fraction(2 * c.T * c.d * (c.H if c.mode else 1), c.r_k + c.r_v)
+    assert rho == float(exact)
+    elt = 4 if c.dtype == "f32" else 2
+    lat = lla.lla_latent_bytes_per_token(codec)
+    flat = lla.lla_flat_bytes_per_token(codec)
+    assert lat == c.G * (c.r_k + c.r_v) * elt
+    assert flat == 2 * c.T * c.H * c.d * elt
+    assert Fraction(flat, lat) == exact      # the reduction is exact
+
+
+def test_ratio_rejects_invalid_codec():
+    assert lla.lla_compression_ratio(lla.make_codec(0, 4, 16, 96, 16, 32, 1)) == 0.0
+    assert lla.lla_latent_bytes_per_token(lla.make_codec(0, 0, 16, 128, 16, 32, 1)) == 0
+
+
+def test_decode_plan_covers_the_context():
+    c = synth.CONFIGS["ouro14_21x"]
+    cache = lla.lla_cache(None, None, None, None, c.B, c.page, c.max_pages, c.B * c.max_pages,
+                          c.N)
+    plan = lla.lla_decode_plan(_codec(c), cache)
+    assert plan.kernel == 1
+    assert plan.splits * plan.tokens_per_split >= c.N
+    assert (plan.splits - 1) * plan.tokens_per_split < c.N
+    assert plan.tokens_per_split % 128 == 0
+    assert plan.workspace_bytes == c.B * c.H * plan.splits * (c.d + 4) * 4
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def _status(**kw):
+    c = synth.CONFIGS["ouro14_21x"]
+    codec = kw.get("codec", _codec(c))
+    params = lla.lla_params(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = kw.get("cache", lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 2, 64, 2, 4, 128))
+    L = lla.lib()
+    return L.lla_decode_attn(ctypes.byref(codec) if codec is not None else None,
+                             ctypes.byref(params), ctypes.byref(cache), kw.get("t", 0),
+                             kw.get("q", FAKE), kw.get("ks", None), kw.get("vs", None), 0, 0.1,
+                             FAKE, kw.get("ws", None), kw.get("wsb", 0), None)
+
+
+def test_validation_codes_without_launch():
+    c = synth.CONFIGS["ouro14_21x"]
+    assert _status(codec=None) == lla.LLA_ERR_NULL
+    assert _status(t=4) == lla.LLA_ERR_SHAPE
+    assert _status(q=None) == lla.LLA_ERR_NULL
+    assert _status(ks=FAKE) == lla.LLA_ERR_NULL                     # k_self without v_self
+    assert _status(codec=lla.make_codec(0, 4, 16, 128, 16, 32, 5)) == lla.LLA_ERR_DTYPE
+    assert _status(codec=lla.make_codec(0, 4, 16, 128, 8, 32, 1)) == lla.LLA_ERR_UNSUPPORTED
+    assert _status(codec=lla.make_codec(0, 4, 16, 128, 600, 32, 1)) == lla.LLA_ERR_SHAPE
+    assert _status(cache=lla.lla_cache(FAKE + 2, FAKE, FAKE, FAKE, 2, 64, 2, 4, 128)) == \
+        lla.LLA_ERR_ALIGN
+    assert _status(cache=lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 2, 64, 2, 4, 129)) == \
+        lla.LLA_ERR_SHAPE                                                # max_seq_len > pages*P
+    assert _status(cache=lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 2, 48, 3, 6, 128)) == \
+        lla.LLA_ERR_SHAPE                                                # P not a multiple of 32
+    assert _status() == lla.LLA_ERR_WORKSPACE                            # no workspace
+    assert _status(ws=FAKE + 4, wsb=1 << 20) == lla.LLA_ERR_ALIGN
+
+
+def test_status_strings():
+    for s in range(8):
+        assert lla.lla_status_str(s)
+    assert lla.lla_version().count(".") == 2

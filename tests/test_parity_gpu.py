@@ -1,0 +1,293 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on seeded inputs.
+
+Bar: bf16 max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3; fp32 <= 1e-4 max|oracle|.
+Small cases span several 32-token chunks, several context splits and a ragged tail; full-size
+cases run the exact launch configuration of the benchmark and check sampled sequences.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from looped_transformer_kv_amd import lla, synth
+from looped_transformer_kv_amd.runtime import LatentLayer
+from oracle import brute
+from oracle import oracle as O
+import gpucase
+import tinycase
+from gpucase import assert_close
+
+pytestmark = pytest.mark.gpu
+
+BF16_CFGS = ["ouro14_21x", "ouro14_4x", "ouro26_2d_64x", "huginn_32x"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ tiny fp32 configuration
+def test_tiny_f32_four_loops_encode_append_and_readback(gpu):
+    """All T loops over 256 cached tokens, then encode+append of the new token, then a decode at
+    length N+1 that must see the appended latent."""
+    cfg = synth.CONFIGS["tiny_f32"]
+    p = tinycase.make(cfg)
+    dp = gpucase.DeviceProblem(p)
+    for t in range(cfg.T):
+        say(f"tiny_f32 decode t={t}")
+        assert_close(dp.decode(t), dp.oracle_decode(t), "f32", f"tiny_f32 t={t}")
+    B, N = p.B, cfg.N
+    pos = torch.full((B,), N, dtype=torch.int32, device=gpu)
+    ck = torch.empty((B, cfg.G, cfg.r_k), dtype=torch.float32, device=gpu)
+    cv = torch.empty((B, cfg.G, cfg.r_v), dtype=torch.float32, device=gpu)
+    kb, vb = synth.from_device(dp.k_pool), synth.from_device(dp.v_pool)
+    say("tiny_f32 encode_append")
+    dp.layer.encode_append(dp.x_k, dp.x_v, pos, ck, cv)
+    torch.cuda.synchronize()
+    for axis, cgpu, W, mu, r, before, pool in (
+            (0, ck, p.W_down_k, p.mu_k, cfg.r_k, kb, dp.k_pool),
+            (1, cv, p.W_down_v, p.mu_v, cfg.r_v, vb, dp.v_pool)):
+        ref = O.encode(cfg.mode, cfg.T, cfg.H, cfg.d, r, W, mu, p.x_v if axis else p.x_k)
+        c = cgpu.double().cpu().numpy()
+        assert_close(c, ref, "f32", f"encode axis {axis}")
+        after = synth.from_device(pool)
+        expect = O.append(c, np.full(B, N, np.int32), p.block_table, cfg.page, before)
+        assert np.array_equal(after, expect)   # fp32 pool: the slot holds c exactly
+    dp.seq_lens += 1
+    p.seq_lens = p.seq_lens + 1
+    dp.layer.set_max_seq_len(N + 1)
+    kp, vp = synth.from_device(dp.k_pool), synth.from_device(dp.v_pool)
+    for t in (0, cfg.T - 1):
+        say(f"tiny_f32 decode after append t={t}")
+        ref = dp.oracle_decode(t, k_pool=kp, v_pool=vp)
+        assert_close(dp.decode(t), ref, "f32", f"tiny_f32 post-append t={t}")
+
+
+# ------------------------------------------------------------------ bf16, reduced sizes
+def _small(name):
+    cfg = synth.CONFIGS[name]
+    B = 2 if cfg.mode == 1 else 3
+    return cfg, B, 300
+
+
+@pytest.mark.parametrize("variant", ["plain", "ragged", "peaked", "noself"])
+@pytest.mark.parametrize("name", BF16_CFGS)
+def test_bf16_decode_small(gpu, name, variant):
+    cfg, B, N = _small(name)
+    lens = None
+    if variant == "ragged":
+        lens = synth.seq_lens(cfg, B, N, ragged=True, salt=3)
+        lens[0], lens[1] = 0, 1   # empty context and a single token
+    p = tinycase.make(cfg, B=B, N=N, lens=lens, q_gain=8.0 if variant == "peaked" else 1.0,
+                      loud_tokens=3 if variant == "peaked" else 0)
+    dp = gpucase.DeviceProblem(p)
+    with_self = variant != "noself"
+    for t in sorted({0, 1, cfg.T - 1}):
+        say(f"{name}/{variant} B={B} lens={list(p.seq_lens)} t={t}")
+        gpu_out = dp.decode(t, with_self)
+        ref = dp.oracle_decode(t, with_self)
+        assert_close(gpu_out, ref, "bf16", f"{name}/{variant} t={t}")
+
+
+@pytest.mark.parametrize("name", BF16_CFGS)
+def test_bf16_empty_context(gpu, name):
+    cfg = synth.CONFIGS[name]
+    p = tinycase.make(cfg, B=2, N=64, lens=np.zeros(2, np.int32))
+    dp = gpucase.DeviceProblem(p)
+    say(f"{name} empty context")
+    assert np.all(dp.decode(0, with_self=False) == 0.0)
+    out = dp.decode(0, with_self=True)
+    assert np.array_equal(out, p.x_v[:, 0])   # softmax over the self term alone
+
+
+@pytest.mark.parametrize("name", BF16_CFGS + ["tiny_f32"])
+def test_encode_append(gpu, name):
+    cfg = synth.CONFIGS[name]
+    B = 70 if cfg.mode == 0 else 5    # > 64 rows exercises the batch tiling
+    N = 100
+    p = tinycase.make(cfg, B=B, N=N)
+    dp = gpucase.DeviceProblem(p)
+    pos_h = np.full(B, N, dtype=np.int32)
+    pos_h[1] = 3                       # overwrite an existing slot
+    pos_h[2] = -1                      # skipped
+    pos = torch.from_numpy(pos_h).to(gpu)
+    ck = torch.zeros((B, cfg.G, cfg.r_k), dtype=torch.float32, device=gpu)
+    cv = torch.zeros((B, cfg.G, cfg.r_v), dtype=torch.float32, device=gpu)
+    kb, vb = synth.from_device(dp.k_pool), synth.from_device(dp.v_pool)
+    say(f"{name} encode_append B={B}")
+    dp.layer.encode_append(dp.x_k, dp.x_v, pos, ck, cv)
+    torch.cuda.synchronize()
+    for axis, cgpu, W, mu, r, before, pool in (
+            (0, ck, p.W_down_k, p.mu_k, cfg.r_k, kb, dp.k_pool),
+            (1, cv, p.W_down_v, p.mu_v, cfg.r_v, vb, dp.v_pool)):
+        ref = O.encode(cfg.mode, cfg.T, cfg.H, cfg.d, r, W, mu, p.x_v if axis else p.x_k)
+        c = cgpu.double().cpu().numpy()
+        assert_close(c, ref, "bf16" if cfg.dtype == "bf16" else "f32", f"{name} c axis {axis}")
+        # the pool holds c rounded once to the storage dtype, at the written slots only
+        stored = synth.quantize(c, cfg.dtype)
+        keep = pos_h >= 0
+        expect = O.append(stored[keep], pos_h[keep], p.block_table[keep], cfg.page, before)
+        after = synth.from_device(pool)
+        assert np.array_equal(after, expect), f"{name} axis {axis}: pool differs"
+
+
+# ------------------------------------------------------------------ flat comparator
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_flat_ref_attn_vs_oracle(gpu, dtype):
+    cfg = synth.scaled(synth.CONFIGS["ouro14_21x"], dtype=dtype)
+    B, N, H, d, P = 4, 333, cfg.H, cfg.d, cfg.page
+    g = np.random.default_rng(11)
+    max_pages = (N + P - 1) // P
+    n_pages = B * max_pages
+    kf = synth.quantize(0.3 * g.standard_normal((n_pages, H, P, d)), dtype)
+    vf = synth.quantize(0.3 * g.standard_normal((n_pages, H, P, d)), dtype)
+    bt = synth.block_table(cfg, B, max_pages, salt=9)
+    lens = np.array([N, 1, 0, 200], dtype=np.int32)
+    q = synth.quantize(g.standard_normal((B, H, d)), dtype)
+    ks = synth.quantize(0.3 * g.standard_normal((B, H, d)), dtype)
+    vs = synth.quantize(0.3 * g.standard_normal((B, H, d)), dtype)
+    up = lambda a: synth.to_device(a, dtype)
+    kd, vd, btd, ld = up(kf), up(vf), torch.from_numpy(bt).to(gpu), torch.from_numpy(lens).to(gpu)
+    flat = lla.make_cache(kd, vd, btd, ld, P, int(lens.max()))
+    code = gpucase.CODE_DT[dtype]
+    plan = lla.lla_ref_plan(H, d, code, flat)
+    ws = torch.empty(max(4, plan.workspace_bytes // 4), dtype=torch.float32, device=gpu)
+    for with_self in (False, True):
+        out = torch.full((B, H, d), float("nan"), dtype=gpucase.TORCH_DT[dtype], device=gpu)
+        say(f"flat {dtype} self={with_self}")
+        lla.lla_ref_attn(H, d, code, flat, up(q), up(ks) if with_self else None,
+                         up(vs) if with_self else None, 0, 1.0 / np.sqrt(d), out, ws)
+        torch.cuda.synchronize()
+        ref = O.flat_attn(H, d, kf, vf, bt, lens, P, q, ks if with_self else None,
+                          vs if with_self else None)
+        assert_close(synth.from_device(out), ref, dtype, f"flat {dtype} self={with_self}")
+
+
+def test_flat_equals_latent_on_materialised_reconstructions_f32(gpu):
+    """lla_ref_attn over explicitly reconstructed (fp32) K/V equals lla_decode_attn."""
+    cfg = synth.CONFIGS["tiny_f32"]
+    p = tinycase.make(cfg, B=2, N=200, ragged=True)
+    dp = gpucase.DeviceProblem(p)
+    t = 2
+    ck = tinycase.logical_latents(p.k_pool, p.block_table, p.seq_lens, cfg.page)
+    cv = tinycase.logical_latents(p.v_pool, p.block_table, p.seq_lens, cfg.page)
+    Nmax = ck.shape[1]
+    K = brute.reconstruct(t, ck, p.W_up_k, p.mu_k, cfg.T).reshape(p.B, Nmax, cfg.H, cfg.d)
+    V = brute.reconstruct(t, cv, p.W_up_v, p.mu_v, cfg.T).reshape(p.B, Nmax, cfg.H, cfg.d)
+    fk = np.zeros((p.n_pages, cfg.H, cfg.page, cfg.d))
+    fv = np.zeros_like(fk)
+    for b in range(p.B):
+        for j in range(int(p.seq_lens[b])):
+            fk[p.block_table[b, j // cfg.page], :, j % cfg.page] = K[b, j]
+            fv[p.block_table[b, j // cfg.page], :, j % cfg.page] = V[b, j]
+    # keep the pool tensors alive: the cache struct holds raw device pointers only
+    fkd, fvd = synth.to_device(fk, "f32"), synth.to_device(fv, "f32")
+    flat = lla.make_cache(fkd, fvd, dp.block_table, dp.seq_lens, cfg.page, p.max_seq_len)
+    plan = lla.lla_ref_plan(cfg.H, cfg.d, lla.LLA_F32, flat)
+    ws = torch.empty(max(4, plan.workspace_bytes // 4), dtype=torch.float32, device=gpu)
+    out = torch.empty((p.B, cfg.H, cfg.d), dtype=torch.float32, device=gpu)
+    lla.lla_ref_attn(cfg.H, cfg.d, lla.LLA_F32, flat, dp.q[t], dp.x_k[:, t], dp.x_v[:, t],
+                     cfg.T * cfg.H * cfg.d, 1.0 / np.sqrt(cfg.d), out, ws)
+    torch.cuda.synchronize()
+    lat = dp.decode(t)
+    assert_close(out.double().cpu().numpy(), lat, "f32", "flat vs latent")
+
+
+# ------------------------------------------------------------------ determinism, error paths
+def test_decode_is_deterministic(gpu):
+    cfg = synth.CONFIGS["ouro14_21x"]
+    p = tinycase.make(cfg, B=4, N=1000, ragged=True)
+    dp = gpucase.DeviceProblem(p)
+    a, b = dp.decode(1), dp.decode(1)
+    assert np.array_equal(a, b)
+
+
+def test_invalid_arguments_enqueue_nothing(gpu):
+    cfg = synth.CONFIGS["ouro14_21x"]
+    p = tinycase.make(cfg, B=2, N=64)
+    dp = gpucase.DeviceProblem(p)
+    L = dp.layer
+    out = torch.full((2, cfg.H, cfg.d), 7.0, dtype=torch.bfloat16, device=gpu)
+    ws = L.workspace(gpu)
+    q = dp.q[0]
+    call = lambda **kw: lla.lla_decode_attn(
+        kw.get("codec", L.codec), L.params, kw.get("cache", L.cache), kw.get("t", 0), q,
+        kw.get("ks", None), kw.get("vs", None), 0, 0.1, out, kw.get("ws", ws),
+        kw.get("wsb", None), check=False)
+    assert call(t=cfg.T) == lla.LLA_ERR_SHAPE
+    assert call(t=-1) == lla.LLA_ERR_SHAPE
+    assert call(ks=dp.x_k) == lla.LLA_ERR_NULL
+    assert call(ws=None, wsb=0) == lla.LLA_ERR_WORKSPACE
+    assert call(wsb=8) == lla.LLA_ERR_WORKSPACE
+    bad = lla.make_codec(0, cfg.T, cfg.H, cfg.d, 8, 16, lla.LLA_BF16)
+    assert call(codec=bad) == lla.LLA_ERR_UNSUPPORTED
+    bad = lla.make_codec(0, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, 9)
+    assert call(codec=bad) == lla.LLA_ERR_DTYPE
+    c2 = lla.make_cache(dp.k_pool, dp.v_pool, dp.block_table, dp.seq_lens, 48, 64)
+    assert call(cache=c2) == lla.LLA_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 7.0)
+
+
+# ------------------------------------------------------------------ full sizes, sampled outputs
+FULL = ["ouro14_21x", "ouro14_4x", "huginn_32x", "ouro26_2d_64x", "ouro14_21x_cap"]
+
+
+def _full_layer(cfg, gpu):
+    """One layer of a configuration at its full batch and context, pools drawn on the device."""
+    B, N = cfg.B, cfg.N
+    max_pages = cfg.max_pages
+    n_pages = B * max_pages
+    Wdk, Wuk, muk = synth.codec(cfg, 0, synth.AX_K)
+    Wdv, Wuv, muv = synth.codec(cfg, 0, synth.AX_V)
+    kpool = synth.device_latent_pool(cfg, 0, synth.AX_K, n_pages, gpu)
+    vpool = synth.device_latent_pool(cfg, 0, synth.AX_V, n_pages, gpu)
+    bt = synth.block_table(cfg, B, max_pages)
+    lens = synth.seq_lens(cfg, B, N)
+    up = lambda a: synth.to_device(a, cfg.dtype, gpu)
+    codec = lla.make_codec(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
+    layer = LatentLayer(codec, up(Wdk), up(Wdv), up(Wuk), up(Wuv), up(muk), up(muv), kpool, vpool,
+                        torch.from_numpy(bt).to(gpu), torch.from_numpy(lens).to(gpu), cfg.page,
+                        N)
+    host = dict(Wuk=Wuk, Wuv=Wuv, muk=muk, muv=muv, bt=bt, lens=lens)
+    return layer, host
+
+
+def _sampled_oracle(cfg, layer, host, sel, t, q, ks, vs):
+    """Oracle on the sequences in `sel`, from a read-back of exactly their pages."""
+    bt = host["bt"][sel]
+    pages = np.unique(bt)
+    remap = {int(pg): i for i, pg in enumerate(pages)}
+    bt2 = np.vectorize(lambda x: remap[int(x)])(bt).astype(np.int32)
+    idx = torch.from_numpy(pages.astype(np.int64)).to(layer.tensors["k_pool"].device)
+    kp = synth.from_device(layer.tensors["k_pool"].index_select(0, idx))
+    vp = synth.from_device(layer.tensors["v_pool"].index_select(0, idx))
+    return O.decode(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, host["Wuk"], host["Wuv"],
+                    host["muk"], host["muv"], kp, vp, bt2, host["lens"][sel], cfg.page, q[sel],
+                    ks[sel], vs[sel])
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(gpu, name):
+    cfg = synth.CONFIGS[name]
+    say(f"{name}: full size B={cfg.B} N={cfg.N} (one layer)")
+    layer, host = _full_layer(cfg, gpu)
+    sel = [cfg.B - 1] if cfg.mode == 1 else [0, cfg.B // 2, cfg.B - 1]
+    xk = synth.staging(cfg, 0, synth.AX_K, cfg.B)
+    xv = synth.staging(cfg, 0, synth.AX_V, cfg.B)
+    xkd, xvd = synth.to_device(xk, "bf16", gpu), synth.to_device(xv, "bf16", gpu)
+    ws = layer.workspace(gpu)
+    for t in sorted({0, cfg.T - 1}):
+        q = synth.queries(cfg, 0, t, cfg.B)
+        out = torch.empty((cfg.B, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
+        say(f"{name}: decode t={t} splits={layer.plan.splits}")
+        layer.decode(t, synth.to_device(q, "bf16", gpu), out, ws, xkd[:, t], xvd[:, t],
+                     cfg.T * cfg.H * cfg.d)
+        torch.cuda.synchronize()
+        got = synth.from_device(out)
+        assert np.all(np.isfinite(got))
+        say(f"{name}: oracle on sequences {sel}")
+        ref = _sampled_oracle(cfg, layer, host, sel, t, q, xk[:, t], xv[:, t])
+        assert_close(got[sel], ref, "bf16", f"{name} t={t}")
