@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the LLA decode hot path on one MI355X.
+
+One step = one decode step of a weight-tied looped model on the Ouro-1.4B-like 21.3x workload:
+24 layers, 16 heads, d_head 128, T = 4 loops, per-head codec r_k = 16 / r_v = 32, bf16 latents,
+batch 32, 4096 cached tokens per sequence.  In loop-major order (loop t outer, layer inner) every
+(layer, loop) runs lla_decode_attn over that layer's whole latent cache (96 calls, each on a
+distinct 201 MB layer cache, so the 256 MB Infinity Cache cannot serve repeats), then every layer
+runs lla_encode_append for the new token (24 calls).  Each step decodes against the same 4096
+cached tokens and appends at slot 4096, so every timed step does identical work.
+
+value      cached token-loops per second for the whole step (B * N * T * L per step)
+roofline   the decode kernel: latent bytes per launch / its average launch time (HIP events
+           around the decode segment of every timed step), against MI355X's 8 TB/s
+cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the same step
+flat_ref   the uncompressed loop-t comparator (lla_ref_attn) at batch 32 on the same GPU
+Inputs are synthetic (seeded) and resident in HBM before timing starts.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LLA decode-attn latent HBM GB/s (% of peak) + cached token·loops/s at 1 GPU"
+UNIT = "cached token·loops/s"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "ouro14_21x"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_ouro14_21x_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "looped_transformer_kv_amd", "csrc", f)
+                  for f in ("decode_bf16.hip", "lla_internal.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None when it
+    is missing or was taken on a different version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_layers(cfg, dev):
+    import torch
+    from looped_transformer_kv_amd import lla, synth
+    from looped_transformer_kv_amd.runtime import LatentLayer
+
+    B, N = cfg.B, cfg.N
+    n_pages = B * cfg.max_pages
+    bt = torch.from_numpy(synth.block_table(cfg, B, cfg.max_pages)).to(dev)
+    lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+    codec = lla.make_codec(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
+    layers, host = [], []
+    for l in range(cfg.L):
+        Wdk, Wuk, muk = synth.codec(cfg, l, synth.AX_K)
+        Wdv, Wuv, muv = synth.codec(cfg, l, synth.AX_V)
+        up = lambda a: synth.to_device(a, "bf16", dev)
+        kp = synth.device_latent_pool(cfg, l, synth.AX_K, n_pages, dev)
+        vp = synth.device_latent_pool(cfg, l, synth.AX_V, n_pages, dev)
+        layers.append(LatentLayer(codec, up(Wdk), up(Wdv), up(Wuk), up(Wuv), up(muk), up(muv),
+                                  kp, vp, bt, lens, cfg.page, N))
+        host.append(dict(Wdk=Wdk, Wdv=Wdv, Wuk=Wuk, Wuv=Wuv, muk=muk, muv=muv))
+    return layers, host, bt, lens
+
+
+def cpu_baseline(cfg, layers, host, bt, q, xk, xv, budget_s):
+    """The fp64 oracle, timed on this host's cores, on whole layers of one step (all T decode
+    calls at the full batch, then the layer's encode+append) until `budget_s` of CPU time."""
+    import numpy as np
+    from looped_transformer_kv_amd import synth
+    from oracle import oracle as O
+
+    B, N, T = cfg.B, cfg.N, cfg.T
+    bt_h = bt.cpu().numpy()
+    lens = np.full(B, N, dtype=np.int32)
+    pos = np.full(B, N, dtype=np.int32)
+    spent, done_layers, token_loops = 0.0, 0, 0
+    for l in range(cfg.L):
+        kp = synth.from_device(layers[l].tensors["k_pool"])
+        vp = synth.from_device(layers[l].tensors["v_pool"])
+        xk_h, xv_h = synth.from_device(xk[l]), synth.from_device(xv[l])
+        q_h = [synth.from_device(q[t][l]) for t in range(T)]
+        hd = host[l]
+        t0 = time.perf_counter()
+        for t in range(T):
+            O.decode(cfg.mode, T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, hd["Wuk"], hd["Wuv"],
+                     hd["muk"], hd["muv"], kp, vp, bt_h, lens, cfg.page, q_h[t], xk_h[:, t],
+                     xv_h[:, t])
+        ck = O.encode(cfg.mode, T, cfg.H, cfg.d, cfg.r_k, hd["Wdk"], hd["muk"], xk_h)
+        cv = O.encode(cfg.mode, T, cfg.H, cfg.d, cfg.r_v, hd["Wdv"], hd["muv"], xv_h)
+        O.append(ck, pos, bt_h, cfg.page, kp)
+        O.append(cv, pos, bt_h, cfg.page, vp)
+        spent += time.perf_counter() - t0
+        done_layers += 1
+        token_loops += B * N * T
+        log(f"cpu_baseline: layer {l} done, {spent:.1f} s of oracle time")
+        if spent >= budget_s:
+            break
+    return {"value": token_loops / spent, "unit": UNIT, "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done_layers} of {cfg.L} layers of one decode step: all {T} loops of "
+                      f"decode attention at batch {B} x {N} cached tokens, then encode+append; "
+                      f"fp64, {spent:.1f} s"}
+
+
+def flat_comparator(cfg, dev, steps, bt, lens):
+    """lla_ref_attn over uncompressed loop-t K/V slices at batch 32, rotating over 4 distinct
+    slices (4.3 GB) so the Infinity Cache cannot serve repeats."""
+    import torch
+    from looped_transformer_kv_amd import lla
+
+    B, N, H, d = cfg.B, cfg.N, cfg.H, cfg.d
+    n_pages = B * cfg.max_pages
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    slices = []
+    for _ in range(4):
+        kf = (0.12 * torch.randn((n_pages, H, cfg.page, d), generator=gen, device=dev)).to(
+            torch.bfloat16)
+        vf = (0.12 * torch.randn((n_pages, H, cfg.page, d), generator=gen, device=dev)).to(
+            torch.bfloat16)
+        slices.append((kf, vf, lla.make_cache(kf, vf, bt, lens, cfg.page, N)))
+    plan = lla.lla_ref_plan(H, d, lla.LLA_BF16, slices[0][2])
+    ws = torch.empty(max(4, plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
+    q = torch.randn((B, H, d), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(d)
+    for i in range(4):
+        lla.lla_ref_attn(H, d, lla.LLA_BF16, slices[i][2], q, None, None, 0, scale, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls = 4 * steps
+    e0.record()
+    for i in range(calls):
+        lla.lla_ref_attn(H, d, lla.LLA_BF16, slices[i % 4][2], q, None, None, 0, scale, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    flat_bytes = B * N * H * d * 2 * 2
+    gbs = flat_bytes / (us * 1e-6) / 1e9
+    del slices
+    torch.cuda.empty_cache()
+    return {"kernel": "lla_ref_attn (flat loop-t cache)", "batch": B, "context": N,
+            "us_per_call": round(us, 2), "bytes_per_call": flat_bytes,
+            "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "splits": plan.splits}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time budget for the CPU baseline (0 disables it)")
+    ap.add_argument("--no-flat", action="store_true", help="skip the flat comparator")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written":
+                          dst.numel() * 4, "launches": 3}), flush=True)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the LLA decode path is measured on a single MI355X and has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from looped_transformer_kv_amd import lla, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    lla.lib()
+    cfg = synth.CONFIGS[WORKLOAD]
+    B, N, L, T, H, d = cfg.B, cfg.N, cfg.L, cfg.T, cfg.H, cfg.d
+
+    log(f"building {L} layers of {cfg.name} (batch {B}, context {N}) on {dev}")
+    layers, host, bt, lens = build_layers(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.ROOT_SEED)
+    q = [[torch.randn((B, H, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(L)]
+         for _ in range(T)]
+    xs = math.sqrt(sum(cfg.decay ** i for i in range(cfg.r_k)) / cfg.X + 0.01)
+    xk = [(xs * torch.randn((B, T, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+          for _ in range(L)]
+    xv = [(xs * torch.randn((B, T, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+          for _ in range(L)]
+    write_pos = torch.full((B,), N, dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    plan = layers[0].plan
+    ws = layers[0].workspace(dev)
+    stride = T * H * d
+
+    def decode_all():
+        for t in range(T):
+            for l in range(L):
+                layers[l].decode(t, q[t][l], out, ws, xk[l][:, t], xv[l][:, t], stride)
+
+    def encode_all():
+        for l in range(L):
+            layers[l].encode_append(xk[l], xv[l], write_pos)
+
+    decode_all()
+    encode_all()
+    torch.cuda.synchronize()
+    launch = "eager"
+    if not args.eager:
+        try:
+            g_dec, g_enc = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_dec):
+                decode_all()
+            with torch.cuda.graph(g_enc):
+                encode_all()
+            run_dec, run_enc, launch = g_dec.replay, g_enc.replay, "hip_graph"
+        except Exception as e:  # capture unsupported: fall back to eager launches
+            log(f"graph capture failed ({e}); timing eager launches")
+    if launch == "eager":
+        run_dec, run_enc = decode_all, encode_all
+
+    for _ in range(args.warmup):
+        run_dec()
+        run_enc()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(K):
+        ev[k][0].record()
+        run_dec()
+        ev[k][1].record()
+        run_enc()
+    end.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / K
+    dec_us = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / (K * T * L)
+    enc_us = (step_ms * 1e3 - dec_us * T * L) / L
+
+    latent_bytes = B * N * cfg.G * (cfg.r_k + cfg.r_v) * 2
+    achieved = latent_bytes / (dec_us * 1e-6) / 1e9
+    token_loops = B * N * T * L
+    result = {
+        "metric": METRIC,
+        "value": token_loops / (step_ms * 1e-3),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: Ouro-1.4B-like looped decode step, {L} layers x {T} loops "
+                        f"of LLA decode attention + {L} encode/append calls",
+            "layers": L, "heads": H, "d_head": d, "loops": T, "r_k": cfg.r_k, "r_v": cfg.r_v,
+            "compression": round(lla.lla_compression_ratio(layers[0].codec), 3),
+            "global_batch": B, "seq_len": N, "page_size": cfg.page,
+            "splits": plan.splits, "launch": launch, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(),
+        },
+        "decode_us_per_call": round(dec_us, 3),
+        "decode_latent_bytes_per_call": latent_bytes,
+        "decode_token_loops_per_s_per_call": round(B * N / (dec_us * 1e-6), 1),
+        "encode_us_per_call": round(enc_us, 3),
+    }
+    if not args.no_flat:
+        log("timing the flat comparator")
+        result["flat_ref"] = flat_comparator(cfg, dev, max(5, K), bt, lens)
+    if args.cpu_seconds > 0:
+        log("timing the oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline(cfg, layers, host, bt, q, xk, xv, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -122,7 +122,7 @@ lla_status lla_decode_plan(const lla_codec *codec, const lla_cache *cache, lla_p
  *   the token attends to itself, as in a causal decoder);
  *   out[b][h] = sum_j softmax(s)_j V_hat_t(j)[h].
  * An empty context without a self term gives out = 0.
- *   q, out           [B][H][d]   (dtype)
+ *   q, out           [B][H][d]   (dtype; q 16-byte aligned for bf16)
  *   k_self, v_self   rows at k_self + b*self_stride + h*d (dtype); both NULL or both set;
  *                    self_stride in elements, 0 means H*d
  *   workspace        device, >= plan.workspace_bytes (may be NULL if that is 0)
@@ -139,7 +139,8 @@ lla_status lla_decode_attn(const lla_codec *codec, const lla_params *params,
  *   c = (stack_g(x[b]) - mu[g]) W_down[g],  accumulated in fp32,
  *   written (rounded to the pool dtype, bf16 round-to-nearest-even) to the pool slot of logical
  *   position write_pos[b] (page block_table[b][pos/P], slot pos%P).
- *   x_k, x_v        staging [B][T][H][d] (dtype): the token's K / V at every loop
+ *   x_k, x_v        staging [B][T][H][d] (dtype, 16-byte aligned; mu_k / mu_v too): the
+ *                   token's K / V at every loop
  *   write_pos       device int32 [B]; positions >= max_pages*P or < 0 are skipped
  *   c_k_out/c_v_out optional device fp32 [B][G][r] copies of c before rounding (NULL = none)
  * Reads W_down_{k,v} and mu_{k,v} of `params`.  seq_lens is not read or modified.

@@ -22,6 +22,8 @@
 //           at the end.
 // Online softmax in the log2 domain with one wave-wide max per chunk; the waves of a workgroup
 // merge through LDS and write one (o, m, l) partial per split, finished by combine.hip.
+#include <cstdlib>
+
 #include "lla_internal.h"
 
 namespace lla {
@@ -41,11 +43,26 @@ struct Chunk {
     uint4 k[KK], v[KV];
 };
 
-template <int D, int RK, int RV, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(DecodeArgs a) {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight fp32 values -> eight bf16 (round to nearest even, v_cvt_pk_bf16_f32) in one uint4.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ uint4 pack8(const f32x16 &a, int base) {
+    return make_uint4(pk_bf16(a[base + 0], a[base + 1]), pk_bf16(a[base + 2], a[base + 3]),
+                      pk_bf16(a[base + 4], a[base + 5]), pk_bf16(a[base + 6], a[base + 7]));
+}
+
+template <int D, int RK, int RV, int WAVES, bool SMFMA>
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(SMFMA && RK + RV <= 64 ? 3 : 1)))
+void decode_bf16_kernel(DecodeArgs a) {
     constexpr int MT = D / 32;                  // 32-column tiles over the head dim
     constexpr int KK = RK / 16, KV = RV / 16;   // MFMA k-steps over the latent ranks
-    constexpr bool WREG = (KK + KV) * MT <= 16; // W_up operands kept in registers
+    constexpr bool OCC3 = SMFMA && RK + RV <= 64;  // sized for 3 waves per SIMD
+    constexpr bool WREG = !OCC3 && (KK + KV) * MT <= 16; // W_up operands kept in registers
     constexpr int RKP = RK + 8, RVP = RV + 8;   // padded LDS rows (keeps 16-byte alignment)
 
     __shared__ __align__(16) uint16_t sWk[D * RKP];   // W_up,t^K transposed: [i][k]
@@ -101,12 +118,27 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(DecodeArgs a) {
 
     // ---- query in the K-tile row layout, pre-scaled by scale*log2(e); <q, mu_t^K>
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h) * D;
-    float qs[MT][16];
+    // VALU scores: q rows 32M + 8bb + 4h2 + 0..3 of the K tile, fp32, pre-scaled.
+    // MFMA scores: q as the A operand of S = q . K_hat^T, the same bf16 in every row m; k-slot
+    // kk of lane half h2 in step (M, half) is d-row 32M + 16half + 8(kk/4) + 4h2 + kk%4, the
+    // row the K_hat tile holds in element 8half + kk of that lane.
+    float qs[SMFMA ? 1 : MT][16];
+    uint4 qop[SMFMA ? MT : 1][2];
 #pragma unroll
     for (int M = 0; M < MT; ++M)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            qs[M][v] = bf2f(qp[32 * M + 8 * (v >> 2) + 4 * h2 + (v & 3)]) * a.scale_log2;
+        for (int bb = 0; bb < 4; ++bb) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(qp + 32 * M + 8 * bb + 4 * h2);
+            if constexpr (SMFMA) {
+                if (bb & 1) { qop[M][bb >> 1].z = u.x; qop[M][bb >> 1].w = u.y; }
+                else        { qop[M][bb >> 1].x = u.x; qop[M][bb >> 1].y = u.y; }
+            } else {
+                qs[M][4 * bb + 0] = __uint_as_float(u.x << 16) * a.scale_log2;
+                qs[M][4 * bb + 1] = __uint_as_float(u.x & 0xffff0000u) * a.scale_log2;
+                qs[M][4 * bb + 2] = __uint_as_float(u.y << 16) * a.scale_log2;
+                qs[M][4 * bb + 3] = __uint_as_float(u.y & 0xffff0000u) * a.scale_log2;
+            }
+        }
     float qm;
     {
         const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) +
@@ -176,26 +208,61 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(DecodeArgs a) {
             for (int ks = 0; ks < KK; ++ks)
                 acc[M] = mfma32x32x16(WREG ? wkr[M * KK + ks] : wk_op(M, ks), x.k[ks], acc[M]);
         }
-        float sp = 0.f;
+        float sc;                                   // token l32's score, in both lane halves
+        if constexpr (SMFMA) {
+            // K_hat (rounded to bf16) contracted with q on the matrix pipe: every row of the
+            // result holds the 32 scores of the chunk, so no cross-lane step is needed.
+            f32x16 sacc = {};
 #pragma unroll
-        for (int M = 0; M < MT; ++M)
+            for (int M = 0; M < MT; ++M) {
+                sacc = mfma32x32x16(qop[M][0], pack8(acc[M], 0), sacc);
+                sacc = mfma32x32x16(qop[M][1], pack8(acc[M], 8), sacc);
+            }
+            sc = sacc[0] * a.scale_log2 + qm;
+        } else {
+            float sp[MT];                           // independent chains, one per tile
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sp += qs[M][v] * acc[M][v];
-        float sc = add_swap32(sp) + qm;            // token l32's score, in both lane halves
+            for (int M = 0; M < MT; ++M) {
+                sp[M] = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sp[M] += qs[M][v] * acc[M][v];
+            }
+            float tot = sp[0];
+#pragma unroll
+            for (int M = 1; M < MT; ++M) tot += sp[M];
+            sc = add_swap32(tot) + qm;
+        }
         if (valid < 32 && l32 >= valid) sc = -INFINITY;
         if (sSlot[c] < 0) sc = __builtin_nanf("");
 
-        // online softmax (log2 domain); the two 16-lane rows of a half hold all 32 scores
-        const float r = row16_max(sc);
-        const float cmax = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)),
-                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16)));
-        const float m_new = fmaxf(m_run, cmax);
-        const float alpha = exp2_(m_run - m_new);
-        const float p = exp2_(sc - m_new);
-        l_lane = l_lane * alpha + (h2 == 0 ? p : 0.f);
+        // V_hat tiles (32 token rows x d columns); independent of the softmax below, so the
+        // matrix pipe works on them while the max / exp / p exchange runs
+        f32x16 vacc[MT];
 #pragma unroll
-        for (int N = 0; N < MT; ++N) o[N] *= alpha;
-        m_run = m_new;
+        for (int N = 0; N < MT; ++N) {
+            vacc[N] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks)
+                vacc[N] = mfma32x32x16(x.v[ks], WREG ? wvr[N * KV + ks] : wv_op(N, ks), vacc[N]);
+        }
+
+        // online softmax (log2 domain).  The running max only moves when some score of the
+        // chunk exceeds it; otherwise the rescale factor is exactly 1 and the wave-wide max, the
+        // exp of the old max and the rescale are skipped (a wave-uniform branch).
+        if (__builtin_amdgcn_ballot_w64(sc > m_run) != 0) {
+            // the two 16-lane rows of a lane half hold all 32 scores
+            const float r = row16_max(sc);
+            const float cmax = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)),
+                                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16)));
+            const float m_new = fmaxf(m_run, cmax);
+            const float alpha = exp2_(m_run - m_new);
+            l_lane *= alpha;
+#pragma unroll
+            for (int N = 0; N < MT; ++N) o[N] *= alpha;
+            m_run = m_new;
+        }
+        const float p = exp2_(sc - m_run);
+        l_lane += (h2 == 0 ? p : 0.f);
 
         // p of tokens 8*(v/4) + 4*h2 + (v%4): the V tile's row layout
         if (h2 == 0) sP[wave][l32] = p;
@@ -208,36 +275,41 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(DecodeArgs a) {
             pr[4 * bb + 2] = t4.z; pr[4 * bb + 3] = t4.w;
         }
 
-        // V_hat tiles (32 token rows x d columns), p-weighted into o
+        // p-weighted V_hat into o
 #pragma unroll
-        for (int N = 0; N < MT; ++N) {
-            f32x16 vacc = {};
+        for (int N = 0; N < MT; ++N)
 #pragma unroll
-            for (int ks = 0; ks < KV; ++ks)
-                vacc = mfma32x32x16(x.v[ks], WREG ? wvr[N * KV + ks] : wv_op(N, ks), vacc);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[v];
-        }
+            for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[N][v];
         __builtin_amdgcn_wave_barrier();
     };
 
     // ---- main loop: chunks wave, wave + WAVES, ...; the next chunk's latents are in flight
     // while the current one is computed.  Prefetch indices are clamped, so the instruction
     // stream has no data-dependent branches around the loads.
-    if (wave < nchunks) {
-        Chunk<KK, KV> A, Bq;
-        int c = wave;
-        load(c, A);
-        load(min(c + WAVES, nchunks - 1), Bq);
-        while (true) {
+    if constexpr (KK + KV <= 4) {
+        // small ranks: 3 KB per wave-chunk, so keep a second chunk in flight
+        if (wave < nchunks) {
+            Chunk<KK, KV> A, Bq;
+            int c = wave;
+            load(c, A);
+            load(min(c + WAVES, nchunks - 1), Bq);
+            while (true) {
+                compute(c, A);
+                load(min(c + 2 * WAVES, nchunks - 1), A);
+                c += WAVES;
+                if (c >= nchunks) break;
+                compute(c, Bq);
+                load(min(c + 2 * WAVES, nchunks - 1), Bq);
+                c += WAVES;
+                if (c >= nchunks) break;
+            }
+        }
+    } else {
+        // large ranks: one chunk is already KK+KV 1-KB loads per wave; registers go to occupancy
+        for (int c = wave; c < nchunks; c += WAVES) {
+            Chunk<KK, KV> A;
+            load(c, A);
             compute(c, A);
-            load(min(c + 2 * WAVES, nchunks - 1), A);
-            c += WAVES;
-            if (c >= nchunks) break;
-            compute(c, Bq);
-            load(min(c + 2 * WAVES, nchunks - 1), Bq);
-            c += WAVES;
-            if (c >= nchunks) break;
         }
     }
 
@@ -253,11 +325,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(DecodeArgs a) {
         sM[wave] = m_run;
         sL[wave] = l_w;
     }
+    // a single split finishes the output here (same arithmetic as combine.hip): the current
+    // token's own loop-t key/value joins the softmax and (sum of cached weights) mu_t^V is added
+    float s_self = -INFINITY;
+    const bool has_self = a.k_self != nullptr;
+    if (S == 1 && has_self) {
+        const uint16_t *ks = static_cast<const uint16_t *>(a.k_self) + (size_t)b * a.self_stride +
+                             (size_t)h * D;
+        float acc = 0.f;
+        for (int i = lane; i < D; i += 64) acc += bf2f(qp[i]) * bf2f(ks[i]);
+        s_self = wave_sum(acc) * a.scale_log2;
+    }
     __syncthreads();
     if (tid < D) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sM[w]);
+        if (S == 1) M = fmaxf(M, s_self);
         float L = 0.f, O = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
@@ -267,20 +351,49 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(DecodeArgs a) {
                 O += sO[w][tid] * e;
             }
         }
-        float *rec = a.ws + (((size_t)b * a.H + h) * S + s) * (D + kPartialPad);
-        rec[tid] = O;
-        if (tid == 0) {
-            rec[D] = M;
-            rec[D + 1] = L;
+        if (S == 1) {
+            float res = 0.f;
+            if (M != -INFINITY) {
+                const uint16_t *muv = static_cast<const uint16_t *>(a.mu_v) +
+                                      (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
+                float w_self = 0.f, v_self = 0.f;
+                if (has_self) {
+                    w_self = exp2_(s_self - M);
+                    v_self = bf2f(static_cast<const uint16_t *>(a.v_self)[
+                        (size_t)b * a.self_stride + (size_t)h * D + tid]);
+                }
+                res = (O + L * bf2f(muv[tid]) + w_self * v_self) / (L + w_self);
+            }
+            static_cast<uint16_t *>(a.out)[((size_t)b * a.H + h) * D + tid] = f2bf(res);
+        } else {
+            float *rec = a.ws + (((size_t)b * a.H + h) * S + s) * (D + kPartialPad);
+            rec[tid] = O;
+            if (tid == 0) {
+                rec[D] = M;
+                rec[D + 1] = L;
+            }
         }
     }
+}
+
+// Scores on the vector ALU (fp32 FMAs, default) or on the matrix pipe (LLA_SCORE_MFMA=1).
+bool score_on_valu() {
+    static const bool v = [] {
+        const char *e = std::getenv("LLA_SCORE_MFMA");
+        return !(e && e[0] == '1');
+    }();
+    return v;
 }
 
 template <int D, int RK, int RV, int WAVES>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.S;
-    hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, WAVES>), dim3(blocks), dim3(64 * WAVES), 0,
-                       st, a);
+    if (score_on_valu())
+        hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, WAVES, false>), dim3(blocks),
+                           dim3(64 * WAVES), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, WAVES, true>), dim3(blocks),
+                           dim3(64 * WAVES), 0, st, a);
     return hipGetLastError();
 }
 

@@ -71,8 +71,7 @@ __global__ __launch_bounds__(64 * WAVES) void flat_kernel(DecodeArgs a) {
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) dot += qv[e] * ld_elt<TS>(kk + e);
-#pragma unroll
-            for (int off = LPT / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+            dot = group_sum<LPT>(dot);
             float sc = ok[u] ? dot : -INFINITY;
             if (bad[u]) sc = __builtin_nanf("");
             const float m_new = fmaxf(m, sc);
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(64 * WAVES) void flat_kernel(DecodeArgs a) {
 template <int D, typename TS>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.S;
-    hipLaunchKernelGGL((flat_kernel<D, TS, 4, 4>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((flat_kernel<D, TS, 4, kFlatUnroll>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

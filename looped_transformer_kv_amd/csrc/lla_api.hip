@@ -62,7 +62,7 @@ int target_blocks() {
     static const int v = [] {
         const char *e = std::getenv("LLA_TARGET_BLOCKS");
         const int x = e ? std::atoi(e) : 0;
-        return x > 0 ? x : 1024;
+        return x > 0 ? x : 512;
     }();
     return v;
 }
@@ -91,8 +91,10 @@ lla_status decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
     p->waves_per_block = 4;
     split_plan(k->batch * c->n_heads, k->max_seq_len, bf16 ? 32 * 4 : 256,
                bf16 ? 32 * kMaxChunksPerSplit : (1 << 30), p);
-    p->workspace_bytes = (size_t)k->batch * c->n_heads * p->splits *
-                         (c->d_head + kPartialPad) * sizeof(float);
+    // a single-split bf16 plan finishes in the latent kernel and needs no partials
+    const bool direct = bf16 && p->splits == 1;
+    p->workspace_bytes = direct ? 0 : (size_t)k->batch * c->n_heads * p->splits *
+                                          (c->d_head + kPartialPad) * sizeof(float);
     return LLA_OK;
 }
 
@@ -101,7 +103,7 @@ lla_status ref_plan(int H, int d, int dtype, const lla_cache *k, lla_plan *p) {
     const int tpw = 64 / (d / epl);
     p->kernel = 3;
     p->waves_per_block = 4;
-    split_plan(k->batch * H, k->max_seq_len, tpw * 4 * 4, 1 << 30, p);
+    split_plan(k->batch * H, k->max_seq_len, tpw * 4 * kFlatUnroll, 1 << 30, p);
     p->workspace_bytes = (size_t)k->batch * H * p->splits * (d + kPartialPad) * sizeof(float);
     return LLA_OK;
 }
@@ -155,6 +157,7 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     if (bf16) {
         if (!decode_bf16_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
         if (k->page_size % 32 != 0) return LLA_ERR_SHAPE;
+        if (!aligned16(q)) return LLA_ERR_ALIGN;
     } else if (decode_f32_lds_bytes(c->d_head, c->r_k, c->r_v) > kMaxDynLds) {
         return LLA_ERR_UNSUPPORTED;
     }
@@ -199,6 +202,7 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = bf16 ? launch_decode_bf16(a, plan.waves_per_block, s) : launch_decode_f32(a, s);
     if (e != hipSuccess) return LLA_ERR_HIP;
+    if (bf16 && plan.splits == 1) return LLA_OK;   // the latent kernel finished the output itself
     e = launch_combine(a, c->d_head, bf16, true, s);
     return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
@@ -211,12 +215,16 @@ lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const ll
     if (!prm || !prm->W_down_k || !prm->W_down_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
     if ((st = check_cache(k, false)) != LLA_OK) return st;
     if (!x_k || !x_v || !write_pos) return LLA_ERR_NULL;
+    if (!aligned16(x_k) || !aligned16(x_v) || !aligned16(prm->mu_k) || !aligned16(prm->mu_v))
+        return LLA_ERR_ALIGN;
     if (k->batch == 0) return LLA_OK;
     const Shape sh = shape_of(c);
     const bool bf16 = c->dtype == LLA_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    EncodeArgs ax[2];
     for (int axis = 0; axis < 2; ++axis) {
-        EncodeArgs a{};
+        EncodeArgs &a = ax[axis];
+        a = EncodeArgs{};
         a.x = axis ? x_v : x_k;
         a.W_down = axis ? prm->W_down_v : prm->W_down_k;
         a.mu = axis ? prm->mu_v : prm->mu_k;
@@ -235,9 +243,8 @@ lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const ll
         a.max_pages = k->max_pages;
         a.n_pages = k->n_pages;
         a.mode = c->mode;
-        if (launch_encode(a, bf16, s) != hipSuccess) return LLA_ERR_HIP;
     }
-    return LLA_OK;
+    return launch_encode(ax[0], ax[1], bf16, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
 lla_status lla_ref_plan(int32_t H, int32_t d, int32_t dtype, const lla_cache *k, lla_plan *p) {

@@ -48,11 +48,13 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int waves, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, hipStream_t s);
-hipError_t launch_encode(const EncodeArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
+                         hipStream_t s);
 bool decode_bf16_supported(int d, int r_k, int r_v);
 
 constexpr int kPartialPad = 4;   // partial record = d + 4 floats (16-byte aligned records)
 constexpr int kMaxChunksPerSplit = 512;   // 32-token chunks one latent-decode workgroup covers
+constexpr int kFlatUnroll = 8;            // token steps per flat-kernel load batch
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf2f(uint16_t u) {
@@ -98,7 +100,7 @@ constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each row
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Max over each 16-lane row, result in every lane of the row.
@@ -107,6 +109,18 @@ __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp<kDppXor2>(v));
     v = fmaxf(v, dpp<kDppHalfMirror>(v));
     v = fmaxf(v, dpp<kDppMirror>(v));
+    return v;
+}
+
+// Sum over aligned groups of G lanes (G = 8, 16 or 32), result in every lane of the group.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 8 || G == 16 || G == 32, "group size");
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (G == 32) v += __shfl_xor(v, 16, 64);
     return v;
 }
 

@@ -206,10 +206,11 @@ def test_decode_is_deterministic(gpu):
 
 def test_invalid_arguments_enqueue_nothing(gpu):
     cfg = synth.CONFIGS["ouro14_21x"]
-    p = tinycase.make(cfg, B=2, N=64)
+    p = tinycase.make(cfg, B=1, N=1024)   # one sequence: the context is split, partials needed
     dp = gpucase.DeviceProblem(p)
     L = dp.layer
-    out = torch.full((2, cfg.H, cfg.d), 7.0, dtype=torch.bfloat16, device=gpu)
+    assert L.plan.splits > 1 and L.plan.workspace_bytes > 0
+    out = torch.full((1, cfg.H, cfg.d), 7.0, dtype=torch.bfloat16, device=gpu)
     ws = L.workspace(gpu)
     q = dp.q[0]
     call = lambda **kw: lla.lla_decode_attn(
@@ -225,7 +226,7 @@ def test_invalid_arguments_enqueue_nothing(gpu):
     assert call(codec=bad) == lla.LLA_ERR_UNSUPPORTED
     bad = lla.make_codec(0, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, 9)
     assert call(codec=bad) == lla.LLA_ERR_DTYPE
-    c2 = lla.make_cache(dp.k_pool, dp.v_pool, dp.block_table, dp.seq_lens, 48, 64)
+    c2 = lla.make_cache(dp.k_pool, dp.v_pool, dp.block_table, dp.seq_lens, 48, 1024)
     assert call(cache=c2) == lla.LLA_ERR_SHAPE
     torch.cuda.synchronize()
     assert torch.all(out.float() == 7.0)
