@@ -6,33 +6,38 @@
 // stacking order used here is (t, h, i), a reading, which makes the LLA-2D stacked vector of a
 // token simply its contiguous [T][H][d] staging row.
 //
-// One launch covers both axes.  A workgroup of 256 threads owns (axis, group g, 32 latent
-// columns, 8 sequences): thread (row, col) accumulates c[b0 + row][k0 + col].  The stacked axis
-// is walked in stages of XC elements: the 8 centred stacked rows (x - mu, fp32) and the
-// XC x 32 tile of W_down are staged through LDS with 16-byte coalesced loads, then each thread
-// runs XC fp32 FMAs from LDS.  Accumulation order is fixed (increasing stacked index).  The result
-// is rounded once to the pool dtype (bf16 round-to-nearest-even) and written to the slot of
-// logical position write_pos[b]; the optional fp32 copy keeps the value before rounding.
+// One launch covers both axes.  bf16 caches use the matrix-core kernel below; fp32 caches use
+// this vector kernel: a workgroup of 256 threads owns (axis, group g, 32 latent
+// columns, 32 sequences); thread (row group rg, column col) accumulates the four outputs
+// c[b0 + rg + 8i][k0 + col], i = 0..3, in four independent fp32 chains.  The stacked axis is
+// walked in stages of XC elements: the centred stacked rows (x - mu, fp32) and the XC x 32 tile
+// of W_down (storage dtype) are staged through LDS with 16-byte loads, and the next stage's loads
+// are in flight while the current stage is multiplied.  Every output is summed in increasing
+// stacked index.  The result is rounded once to the pool dtype (bf16 round-to-nearest-even) and
+// written to the slot of logical position write_pos[b]; the optional fp32 copy keeps the value
+// before rounding.
 #include "lla_internal.h"
 
 namespace lla {
 namespace {
 
 constexpr int KC = 32;    // latent columns per workgroup
-constexpr int BR = 8;     // sequences per workgroup
-constexpr int XC = 256;   // stacked elements per LDS stage
-constexpr int NT = KC * BR;
+constexpr int RG = 8;     // row groups
+constexpr int RPT = 4;    // rows per thread
+constexpr int BR = RG * RPT;   // sequences per workgroup
+constexpr int NT = KC * RG;
 
 struct EncodePair {
     EncodeArgs ax[2];
     int blocks_k;         // workgroups of the K axis (the V axis follows)
 };
 
-template <typename TS>
-__device__ __forceinline__ void load8(const TS *p, float *v);
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float *v) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+template <typename TS> struct Cfg;
+template <> struct Cfg<uint16_t> { static constexpr int XC = 256; };   // 32 KB + 17 KB of LDS
+template <> struct Cfg<float> { static constexpr int XC = 128; };      // 16 KB + 17 KB of LDS
+
+// 16 bytes of storage -> float values
+__device__ __forceinline__ void unpack(const uint4 u, float *v, uint16_t) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -40,18 +45,20 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float *v) {
         v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 }
-template <>
-__device__ __forceinline__ void load8<float>(const float *p, float *v) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+__device__ __forceinline__ void unpack(const uint4 u, float *v, float) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
 }
 
 template <typename TS>
 __global__ __launch_bounds__(NT) void encode_kernel(EncodePair pr) {
-    __shared__ __align__(16) float sX[BR][XC];        // centred stacked rows
-    __shared__ __align__(16) float sW[XC][KC + 1];    // W_down tile (fp32), padded rows
+    constexpr int XC = Cfg<TS>::XC;
+    constexpr int EPV = 16 / sizeof(TS);                 // elements per 16-byte load
+    constexpr int XL = BR * XC / EPV / NT;               // x loads per thread per stage
+    constexpr int WL = XC * KC / EPV / NT;               // W loads per thread per stage
+    constexpr int WROW = KC + 2 * EPV;                   // padded LDS row (keeps 16 B alignment)
+    __shared__ __align__(16) float sX[BR][XC];
+    __shared__ __align__(16) TS sW[XC][WROW];
 
     int blk = blockIdx.x;
     const int axis = blk < pr.blocks_k ? 0 : 1;
@@ -65,64 +72,256 @@ __global__ __launch_bounds__(NT) void encode_kernel(EncodePair pr) {
     const int k0 = kt * KC, b0 = bt_ * BR;
 
     const int tid = threadIdx.x;
-    const int col = tid % KC, row = tid / KC;
-    const size_t X = (size_t)a.T * a.Dg;
+    const int col = tid % KC, rg = tid / KC;
+    const int X = a.T * a.Dg;
     const TS *x = static_cast<const TS *>(a.x);
     const TS *W = static_cast<const TS *>(a.W_down) + (size_t)g * X * a.r;
     const TS *mu = static_cast<const TS *>(a.mu) + (size_t)g * X;
+    // W rows start 16-byte aligned when r is a multiple of the vector width
+    const bool wvec = (a.r % EPV) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
 
-    float acc = 0.f;
-    for (size_t x0 = 0; x0 < X; x0 += XC) {
-        const int nx = (int)((X - x0) < (size_t)XC ? (X - x0) : (size_t)XC);   // multiple of 8
-        __syncthreads();
-        // centred rows: 8 consecutive stacked elements per thread-step (never crossing a d-row)
-        for (int e = tid; e < BR * (XC / 8); e += NT) {
-            const int br = e / (XC / 8), xx = (e % (XC / 8)) * 8;
-            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint4 xr[XL], mr[XL], wr[WL];
+    // issue the global loads of the stage starting at x0 (zeros outside the problem)
+    auto fetch = [&](int x0) {
+#pragma unroll
+        for (int u = 0; u < XL; ++u) {
+            const int e = tid + u * NT;
+            const int br = e / (XC / EPV), xx = (e % (XC / EPV)) * EPV;
             const int b = b0 + br;
-            if (b < a.B && xx < nx) {
-                const size_t xi = x0 + xx;
+            xr[u] = mr[u] = make_uint4(0, 0, 0, 0);
+            if (b < a.B && x0 + xx < X) {
+                const int xi = x0 + xx;
                 size_t off;
                 if (a.mode) {
-                    off = (size_t)b * X + xi;                      // (t, h, i) order
+                    off = (size_t)b * X + xi;                               // (t, h, i) order
                 } else {
-                    const size_t t = xi / a.d, i = xi % a.d;       // (t, i) of head g
+                    const int t = xi / a.d, i = xi - t * a.d;               // (t, i) of head g
                     off = (((size_t)b * a.T + t) * a.H + g) * a.d + i;
                 }
-                float m[8];
-                load8<TS>(x + off, v);
-                load8<TS>(mu + xi, m);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] -= m[q];
+                xr[u] = *reinterpret_cast<const uint4 *>(x + off);
+                mr[u] = *reinterpret_cast<const uint4 *>(mu + xi);
             }
+        }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sX[br][xx + q] = v[q];
+        for (int u = 0; u < WL; ++u) {
+            const int e = tid + u * NT;
+            const int xx = e / (KC / EPV), kk = (e % (KC / EPV)) * EPV;
+            wr[u] = make_uint4(0, 0, 0, 0);
+            const int xi = x0 + xx, k = k0 + kk;
+            if (xi < X && k < a.r) {
+                const TS *src = W + (size_t)xi * a.r + k;
+                if (wvec && k + EPV <= a.r) {
+                    wr[u] = *reinterpret_cast<const uint4 *>(src);
+                } else {
+                    TS tmp[EPV];
+#pragma unroll
+                    for (int q = 0; q < EPV; ++q) tmp[q] = (k + q < a.r) ? src[q] : TS(0);
+                    wr[u] = *reinterpret_cast<const uint4 *>(tmp);
+                }
+            }
         }
-        // W_down rows x0 .. x0+nx-1, columns k0 .. k0+31
-        for (int e = tid; e < XC * KC; e += NT) {
-            const int xx = e / KC, kk = e % KC;
-            float w = 0.f;
-            if (xx < nx && k0 + kk < a.r) w = ld_elt<TS>(W + (x0 + xx) * a.r + k0 + kk);
-            sW[xx][kk] = w;
+    };
+    // write the fetched stage into LDS (x centred in fp32, W in its storage type)
+    auto stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < XL; ++u) {
+            const int e = tid + u * NT;
+            const int br = e / (XC / EPV), xx = (e % (XC / EPV)) * EPV;
+            float v[8], m[8];
+            unpack(xr[u], v, TS(0));
+            unpack(mr[u], m, TS(0));
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) sX[br][xx + q] = v[q] - m[q];
         }
+#pragma unroll
+        for (int u = 0; u < WL; ++u) {
+            const int e = tid + u * NT;
+            const int xx = e / (KC / EPV), kk = (e % (KC / EPV)) * EPV;
+            *reinterpret_cast<uint4 *>(&sW[xx][kk]) = wr[u];
+        }
+    };
+
+    float acc[RPT] = {0.f, 0.f, 0.f, 0.f};
+    fetch(0);
+    for (int x0 = 0; x0 < X; x0 += XC) {
+        __syncthreads();                 // previous stage fully consumed
+        stage();
         __syncthreads();
-#pragma unroll 8
-        for (int xx = 0; xx < nx; ++xx) acc += sX[row][xx] * sW[xx][col];
+        if (x0 + XC < X) fetch(x0 + XC); // next stage in flight during the FMAs below
+        const int nx = min(XC, X - x0);
+        for (int xx = 0; xx < nx; xx += 4) {
+            float w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = ld_elt<TS>(&sW[xx + q][col]);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float4 xv = *reinterpret_cast<const float4 *>(&sX[rg + RG * i][xx]);
+                acc[i] += xv.x * w[0];
+                acc[i] += xv.y * w[1];
+                acc[i] += xv.z * w[2];
+                acc[i] += xv.w * w[3];
+            }
+        }
     }
 
-    const int b = b0 + row, k = k0 + col;
-    if (b >= a.B || k >= a.r) return;
-    if (a.c_out) a.c_out[((size_t)b * a.G + g) * a.r + k] = acc;
-    const int pos = a.write_pos[b];
-    if (pos < 0 || pos >= a.max_pages * a.P) return;
-    const int page = a.block_table[(size_t)b * a.max_pages + pos / a.P];
-    if ((unsigned)page >= (unsigned)a.n_pages) return;
-    st_elt<TS>(static_cast<TS *>(a.pool) + (((size_t)page * a.G + g) * a.P + pos % a.P) * a.r + k,
-               acc);
+    const int k = k0 + col;
+    if (k >= a.r) return;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int b = b0 + rg + RG * i;
+        if (b >= a.B) continue;
+        if (a.c_out) a.c_out[((size_t)b * a.G + g) * a.r + k] = acc[i];
+        const int pos = a.write_pos[b];
+        if (pos < 0 || pos >= a.max_pages * a.P) continue;
+        const int page = a.block_table[(size_t)b * a.max_pages + pos / a.P];
+        if ((unsigned)page >= (unsigned)a.n_pages) continue;
+        st_elt<TS>(static_cast<TS *>(a.pool) + (((size_t)page * a.G + g) * a.P + pos % a.P) * a.r +
+                       k,
+                   acc[i]);
+    }
 }
 
 int blocks_of(const EncodeArgs &a) {
     return a.G * ((a.r + KC - 1) / KC) * ((a.B + BR - 1) / BR);
+}
+
+// ---------------------------------------------------------------- bf16: matrix cores
+// C = X W - 1 (mu W) per (axis, group): a dense contraction over the stacked axis, run on
+// v_mfma_f32_32x32x16_bf16.  A workgroup owns one 32 x 32 output tile (32 sequences x 32 latent
+// columns); its four waves split the stacked axis of every 512-element chunk into contiguous
+// quarters.  A operands are the staging rows (16 bytes per lane straight from HBM) and the mean
+// mu (the same in every row); the B operand is the W_down tile, staged row-major in LDS.  Both
+// inputs stay exact bf16; x W and mu W accumulate in separate fp32 chains and are subtracted at
+// the end.  The four waves' partial tiles are summed in a fixed order through LDS.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int MXC = 512;             // stacked elements per chunk
+constexpr int MKS = MXC / 16;        // MFMA k-steps per chunk
+constexpr int MKW = MKS / 4;         // k-steps per wave per chunk
+constexpr int MWROW = 32 + 8;        // LDS row of the W tile (80 bytes)
+
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void encode_mfma_kernel(EncodePair pr) {
+    __shared__ __align__(16) uint16_t sW[MXC][MWROW];
+    __shared__ float sAcc[4][32][33];
+
+    int blk = blockIdx.x;
+    const int axis = blk < pr.blocks_k ? 0 : 1;
+    if (axis) blk -= pr.blocks_k;
+    const EncodeArgs a = axis ? pr.ax[1] : pr.ax[0];
+    const int ctiles = (a.r + 31) / 32;
+    const int rtiles = (a.B + 31) / 32;
+    const int ct = blk % ctiles;
+    const int rt = (blk / ctiles) % rtiles;
+    const int g = blk / (ctiles * rtiles);
+    const int c0 = ct * 32, b0 = rt * 32;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int X = a.T * a.Dg;
+    const uint16_t *x = static_cast<const uint16_t *>(a.x);
+    const uint16_t *W = static_cast<const uint16_t *>(a.W_down) + (size_t)g * X * a.r;
+    const uint16_t *mu = static_cast<const uint16_t *>(a.mu) + (size_t)g * X;
+    const bool wvec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+    const int b = b0 + l32;                       // this lane's A-operand row
+
+    f32x16 acc = {}, accmu = {};
+    for (int x0 = 0; x0 < X; x0 += MXC) {
+        const int nks = min(MXC, X - x0) / 16;
+        // this wave's A operands (staging rows and mu) for its quarter of the chunk
+        uint4 ax[MKW], am[MKW];
+#pragma unroll
+        for (int j = 0; j < MKW; ++j) {
+            const int ks = wave * MKW + j;
+            ax[j] = am[j] = make_uint4(0, 0, 0, 0);
+            if (ks < nks) {
+                const int xi = x0 + 16 * ks + 8 * h2;
+                am[j] = *reinterpret_cast<const uint4 *>(mu + xi);
+                if (b < a.B) {
+                    size_t off;
+                    if (a.mode) {
+                        off = (size_t)b * X + xi;                           // (t, h, i) order
+                    } else {
+                        const int t = xi / a.d, i = xi - t * a.d;           // (t, i) of head g
+                        off = (((size_t)b * a.T + t) * a.H + g) * a.d + i;
+                    }
+                    ax[j] = *reinterpret_cast<const uint4 *>(x + off);
+                }
+            }
+        }
+        // W_down rows x0 .. x0+511, columns c0 .. c0+31 (4 x 16 bytes per row)
+        uint4 wr[MXC * 4 / 256];
+#pragma unroll
+        for (int u = 0; u < MXC * 4 / 256; ++u) {
+            const int e = tid + 256 * u;
+            const int row = e >> 2, k = c0 + 8 * (e & 3);
+            const int xi = x0 + row;
+            wr[u] = make_uint4(0, 0, 0, 0);
+            if (xi < X && k < a.r) {
+                const uint16_t *src = W + (size_t)xi * a.r + k;
+                if (wvec && k + 8 <= a.r) {
+                    wr[u] = *reinterpret_cast<const uint4 *>(src);
+                } else {
+                    uint16_t tmp[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) tmp[q] = (k + q < a.r) ? src[q] : 0;
+                    wr[u] = *reinterpret_cast<const uint4 *>(tmp);
+                }
+            }
+        }
+        __syncthreads();                          // previous chunk's tile fully read
+#pragma unroll
+        for (int u = 0; u < MXC * 4 / 256; ++u) {
+            const int e = tid + 256 * u;
+            *reinterpret_cast<uint4 *>(&sW[e >> 2][8 * (e & 3)]) = wr[u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < MKW; ++j) {
+            const int ks = wave * MKW + j;
+            if (ks < nks) {
+                // B operand: W rows 16ks + 8h2 + 0..7 of column l32
+                const uint16_t *p = &sW[16 * ks + 8 * h2][l32];
+                uint4 bw;
+                bw.x = (uint32_t)p[0 * MWROW] | ((uint32_t)p[1 * MWROW] << 16);
+                bw.y = (uint32_t)p[2 * MWROW] | ((uint32_t)p[3 * MWROW] << 16);
+                bw.z = (uint32_t)p[4 * MWROW] | ((uint32_t)p[5 * MWROW] << 16);
+                bw.w = (uint32_t)p[6 * MWROW] | ((uint32_t)p[7 * MWROW] << 16);
+                acc = mfma32(ax[j], bw, acc);
+                accmu = mfma32(am[j], bw, accmu);
+            }
+        }
+    }
+    // partial tile: rows 8(v/4) + 4h2 + v%4, column l32
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sAcc[wave][8 * (v >> 2) + 4 * h2 + (v & 3)][l32] = acc[v] - accmu[v];
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        const int idx = tid + 256 * o;
+        const int row = idx >> 5, col = idx & 31;
+        const int bb = b0 + row, k = c0 + col;
+        if (bb >= a.B || k >= a.r) continue;
+        const float c = ((sAcc[0][row][col] + sAcc[1][row][col]) + sAcc[2][row][col]) +
+                        sAcc[3][row][col];
+        if (a.c_out) a.c_out[((size_t)bb * a.G + g) * a.r + k] = c;
+        const int pos = a.write_pos[bb];
+        if (pos < 0 || pos >= a.max_pages * a.P) continue;
+        const int page = a.block_table[(size_t)bb * a.max_pages + pos / a.P];
+        if ((unsigned)page >= (unsigned)a.n_pages) continue;
+        static_cast<uint16_t *>(a.pool)[(((size_t)page * a.G + g) * a.P + pos % a.P) * a.r + k] =
+            f2bf(c);
+    }
+}
+
+int mfma_blocks_of(const EncodeArgs &a) {
+    return a.G * ((a.r + 31) / 32) * ((a.B + 31) / 32);
 }
 
 }  // namespace
@@ -132,12 +331,15 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
     EncodePair pr;
     pr.ax[0] = k_axis;
     pr.ax[1] = v_axis;
-    pr.blocks_k = blocks_of(k_axis);
-    const unsigned blocks = (unsigned)(pr.blocks_k + blocks_of(v_axis));
-    if (bf16)
-        hipLaunchKernelGGL(encode_kernel<uint16_t>, dim3(blocks), dim3(NT), 0, st, pr);
-    else
+    if (bf16) {
+        pr.blocks_k = mfma_blocks_of(k_axis);
+        const unsigned blocks = (unsigned)(pr.blocks_k + mfma_blocks_of(v_axis));
+        hipLaunchKernelGGL(encode_mfma_kernel, dim3(blocks), dim3(256), 0, st, pr);
+    } else {
+        pr.blocks_k = blocks_of(k_axis);
+        const unsigned blocks = (unsigned)(pr.blocks_k + blocks_of(v_axis));
         hipLaunchKernelGGL(encode_kernel<float>, dim3(blocks), dim3(NT), 0, st, pr);
+    }
     return hipGetLastError();
 }
 

@@ -99,11 +99,11 @@ lla_status decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
 }
 
 lla_status ref_plan(int H, int d, int dtype, const lla_cache *k, lla_plan *p) {
-    const int epl = dtype == LLA_BF16 ? 8 : 4;
-    const int tpw = 64 / (d / epl);
+    (void)d;
+    (void)dtype;
     p->kernel = 3;
     p->waves_per_block = 4;
-    split_plan(k->batch * H, k->max_seq_len, tpw * 4 * kFlatUnroll, 1 << 30, p);
+    split_plan(k->batch * H, k->max_seq_len, 32 * 4, 32 * kMaxChunksPerSplit, p);
     p->workspace_bytes = (size_t)k->batch * H * p->splits * (d + kPartialPad) * sizeof(float);
     return LLA_OK;
 }
@@ -263,7 +263,7 @@ lla_status lla_ref_attn(int32_t H, int32_t d, int32_t dtype, const lla_cache *k,
     lla_status st = check_cache(k, true);
     if (st != LLA_OK) return st;
     if (!q || !out || (k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_NULL;
-    if (self_stride < 0) return LLA_ERR_SHAPE;
+    if (self_stride < 0 || k->page_size % 32 != 0) return LLA_ERR_SHAPE;
     lla_plan plan;
     ref_plan(H, d, dtype, k, &plan);
     if ((st = check_workspace(plan, workspace, workspace_bytes)) != LLA_OK) return st;

@@ -54,7 +54,6 @@ bool decode_bf16_supported(int d, int r_k, int r_v);
 
 constexpr int kPartialPad = 4;   // partial record = d + 4 floats (16-byte aligned records)
 constexpr int kMaxChunksPerSplit = 512;   // 32-token chunks one latent-decode workgroup covers
-constexpr int kFlatUnroll = 8;            // token steps per flat-kernel load batch
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf2f(uint16_t u) {
