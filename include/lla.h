@@ -80,7 +80,7 @@ typedef struct {
  *   slot j%P.  seq_lens [batch] int32: cached tokens per sequence (never modified here; the
  *   caller increments it after lla_encode_append).  max_seq_len bounds every seq_lens entry and
  *   must satisfy max_seq_len <= max_pages * P; it sizes the split plan.
- *   page_size P: a multiple of 32 for the bf16 decode path.                                  */
+ *   page_size P: a multiple of 32 for the bf16 latent decode and for the flat comparator.    */
 typedef struct {
     void *k_pool, *v_pool;
     const int32_t *block_table;

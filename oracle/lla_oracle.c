@@ -71,10 +71,11 @@ static const double *latent_at(const double *pool, const int32_t *block_table, i
  * out has D_g entries. */
 static void reconstruct(const double *c, int r, const double *W_up_tg, const double *mu_t,
                         int Dg, double *out) {
-    for (int i = 0; i < Dg; ++i) {
-        double acc = mu_t[i];
-        for (int k = 0; k < r; ++k) acc += c[k] * W_up_tg[(size_t)k * Dg + i];
-        out[i] = acc;
+    /* out[i] = mu_t[i] + c[0] W[0][i] + c[1] W[1][i] + ... (summed in that order for every i) */
+    for (int i = 0; i < Dg; ++i) out[i] = mu_t[i];
+    for (int k = 0; k < r; ++k) {
+        const double *row = W_up_tg + (size_t)k * Dg;
+        for (int i = 0; i < Dg; ++i) out[i] += c[k] * row[i];
     }
 }
 
