@@ -122,7 +122,7 @@ lla_status lla_decode_plan(const lla_codec *codec, const lla_cache *cache, lla_p
  *   the token attends to itself, as in a causal decoder);
  *   out[b][h] = sum_j softmax(s)_j V_hat_t(j)[h].
  * An empty context without a self term gives out = 0.
- *   q, out           [B][H][d]   (dtype; q 16-byte aligned for bf16)
+ *   q, out           [B][H][d]   (dtype; for bf16, q and W_up_{k,v} must be 16-byte aligned)
  *   k_self, v_self   rows at k_self + b*self_stride + h*d (dtype); both NULL or both set;
  *                    self_stride in elements, 0 means H*d
  *   workspace        device, >= plan.workspace_bytes (may be NULL if that is 0)

@@ -3,38 +3,65 @@
 // Computes, for loop t, sequence b, head h (pith.science paper page for "Looped Latent Attention",
 // section "What carries the argument": x_hat_t = c W_up,t + mu_t, attention unchanged; abstract:
 // K/V rebuilt only when attention reads them):
-//   K_hat(j) = c_k(j) W_up,t^K (+ mu_t^K),  s_j = scale <q, K_hat(j)>
-//   V_hat(j) = c_v(j) W_up,t^V (+ mu_t^V),  out = sum_j softmax(s)_j V_hat(j)
-// Both reconstructions are real dense contractions over the latent rank, run on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  mu_t enters exactly, as constants: <q, mu_t^K>
-// is added to every cached score, and (sum_j p_j) mu_t^V is added by the combine kernel, so the
-// MFMA tiles hold c W_up,t and the full K_hat / V_hat are never written anywhere.
+//   K_hat(j) = c_k(j) W_up,t^K + mu_t^K,  s_j = scale <q, K_hat(j)>
+//   V_hat(j) = c_v(j) W_up,t^V + mu_t^V,  out = sum_j softmax(s)_j V_hat(j)
+// Both reconstructions are dense contractions over the latent rank, run per cached token on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the full K_hat / V_hat never leave registers.
+// mu_t enters exactly, as constants: <q, mu_t^K> is added to every cached score and
+// (sum_j p_j) mu_t^V to the output.
 //
-// Work decomposition: one workgroup per (sequence b, head h, context split s); each of its waves
-// takes 32-token chunks round-robin.  Per chunk and lane, latents are loaded straight from HBM
-// into MFMA operand registers (16 bytes per lane, one contiguous span per chunk), so no LDS round
-// trip is needed for the stream.
-//   K side: A = W_up,t^K transposed (d x r_k), B = chunk latents (r_k x 32 tokens); the 32x32
-//           result tile has tokens as columns, so <q, K_hat> is a 16-term in-lane dot product
-//           plus one exchange between lane l and l^32.
-//   V side: A = chunk latents (32 tokens x r_v), B = W_up,t^V (r_v x d); the tile has tokens as
-//           rows, so p-weighted accumulation into o is in-lane; lanes l and l^32 are summed once
+// Work decomposition: one workgroup per (sequence b, head h, context split s); its waves take
+// 32-token chunks round-robin, each wave keeping the next chunks' latents in flight.  Latents go
+// straight from HBM into MFMA operand registers (16 bytes per lane per 16 ranks; a chunk is one
+// contiguous run per axis).  The split's page table and W_up,t are staged in LDS once.
+//
+// Small ranks (r_k, r_v <= 32): the attention weights ride on the expansion operands.
+//   Scores: A = W_up,t^K transposed (d x r_k) with lane (l32, .)'s column i = 32M + l32 scaled by
+//           q_i * scale * log2(e) and rounded to bf16, B = chunk latents (r_k x 32 tokens).  The
+//           tiles of all 32-row groups of the head dim accumulate into one 32x32 tile whose row r
+//           holds sum over M of q_i K_hat_i(j), i = 32M + r: 16 in-lane adds and one exchange
+//           between lanes l and l^32 give token l32's score.
+//   Values: A = chunk latents (32 tokens x r_v) with token j's row scaled by its softmax weight
+//           p_j and rounded to bf16, B = W_up,t^V (r_v x d).  The p-weighted V_hat tiles add into
+//           four persistent 32x32 accumulators across chunks; their 32 token rows are summed once
 //           at the end.
-// Online softmax in the log2 domain with one wave-wide max per chunk; the waves of a workgroup
-// merge through LDS and write one (o, m, l) partial per split, finished by combine.hip.
-#include <cstdlib>
-
+//   Every cached token still gets its full d x r expansion on the matrix cores; the query and
+//   the weights enter as operand scalings.  Rounding q_i W and p_j c_j to bf16 is the same
+//   precision class as a bf16 K cache and bf16 softmax weights in a flat attention kernel.
+// Larger ranks: explicit K_hat / V_hat tiles per chunk; scores are in-lane dot products with q
+//   held in fp32, and p_j V_hat(j) accumulates into o with fp32 FMAs (p reaches the V tile's row
+//   layout through 128 B of LDS).
+// Online softmax in the log2 domain; the waves of a workgroup merge through LDS.  A single-split
+// plan finishes the output here (self term and mu_t^V included); otherwise one (o, m, l) partial
+// per split goes to combine.hip.
 #include "lla_internal.h"
 
 namespace lla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// 8 bf16 times s, rounded back to bf16
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 w, float s) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = pk_bf16(__uint_as_float(in[i] << 16) * s, __uint_as_float(in[i] & 0xffff0000u) * s);
+    return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // Latent registers of one 32-token chunk (this lane's 16-byte slices).
@@ -43,26 +70,28 @@ struct Chunk {
     uint4 k[KK], v[KV];
 };
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int D, int RK, int RV>
+struct Shape {
+    static constexpr int MT = D / 32;                  // 32-column tiles over the head dim
+    static constexpr int KK = RK / 16, KV = RV / 16;   // MFMA k-steps over the latent ranks
+    // small ranks: the attention weights ride on the expansion operands (query on W_up^K, softmax
+    // weight on the value latents) and V_hat accumulates in the matrix-core accumulators across
+    // chunks; W_up operands live in registers.  Larger ranks: W_up operands from LDS, explicit
+    // per-chunk V_hat tiles, query and output in VALU registers.
+    static constexpr bool FUSED = KK <= 2 && KV <= 2;
+    static constexpr int WAVES = 4;
+    static constexpr int DEPTH = KK + KV <= 3 ? 3 : (KK + KV <= 4 ? 2 : 1);   // chunks in flight per wave
+};
 
-// Eight fp32 values -> eight bf16 (round to nearest even, v_cvt_pk_bf16_f32) in one uint4.
-__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-__device__ __forceinline__ uint4 pack8(const f32x16 &a, int base) {
-    return make_uint4(pk_bf16(a[base + 0], a[base + 1]), pk_bf16(a[base + 2], a[base + 3]),
-                      pk_bf16(a[base + 4], a[base + 5]), pk_bf16(a[base + 6], a[base + 7]));
-}
+template <int D, int RK, int RV>
+constexpr int kThreads = 64 * Shape<D, RK, RV>::WAVES;
 
-template <int D, int RK, int RV, int WAVES, bool SMFMA>
-__global__ __launch_bounds__(64 * WAVES)
-__attribute__((amdgpu_waves_per_eu(SMFMA && RK + RV <= 64 ? 3 : 1)))
+template <int D, int RK, int RV>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, kThreads<D, RK, RV>)))
 void decode_bf16_kernel(DecodeArgs a) {
-    constexpr int MT = D / 32;                  // 32-column tiles over the head dim
-    constexpr int KK = RK / 16, KV = RV / 16;   // MFMA k-steps over the latent ranks
-    constexpr bool OCC3 = SMFMA && RK + RV <= 64;  // sized for 3 waves per SIMD
-    constexpr bool WREG = !OCC3 && (KK + KV) * MT <= 16; // W_up operands kept in registers
+    using SH = Shape<D, RK, RV>;
+    constexpr int MT = SH::MT, KK = SH::KK, KV = SH::KV, WAVES = SH::WAVES;
+    constexpr bool FUSED = SH::FUSED;
     constexpr int RKP = RK + 8, RVP = RV + 8;   // padded LDS rows (keeps 16-byte alignment)
 
     __shared__ __align__(16) uint16_t sWk[D * RKP];   // W_up,t^K transposed: [i][k]
@@ -89,63 +118,183 @@ void decode_bf16_kernel(DecodeArgs a) {
     const int j_begin = s * a.tokens_per_split;
     const int j_end = min(j_begin + a.tokens_per_split, len);
     const int nchunks = j_end > j_begin ? (j_end - j_begin + 31) >> 5 : 0;
-    {
-        const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
-        for (int c = tid; c < nchunks; c += 64 * WAVES) {
-            const int j = j_begin + 32 * c;
-            const int page = bt[j / a.P];
-            const bool bad = (unsigned)page >= (unsigned)a.n_pages;
-            const int row = ((bad ? 0 : page) * a.G + g) * a.P + j % a.P;
-            sSlot[c] = bad ? -row - 1 : row;   // negative marks an invalid page id
-        }
-    }
+    const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+    // chunk c -> first token row of its page slot; negative marks an invalid page id.  The
+    // table read is clamped, so any c >= 0 reads in bounds (callers use c < nchunks).
+    auto slot_of = [&](int c) {
+        const int j = j_begin + 32 * c;
+        const int page = bt[min(j / a.P, a.max_pages - 1)];
+        const bool bad = (unsigned)page >= (unsigned)a.n_pages;
+        const int row = ((bad ? 0 : page) * a.G + g) * a.P + j % a.P;
+        return bad ? -row - 1 : row;
+    };
 
-    // ---- stage W_up,t for this head's D columns, transposed, into LDS
+    const uint16_t *kpool = static_cast<const uint16_t *>(a.k_pool);
+    const uint16_t *vpool = static_cast<const uint16_t *>(a.v_pool);
+    const int lane_k = l32 * RK + 8 * h2, lane_v = l32 * RV + 8 * h2;
+
+    // chunk c at pool row `slot` (as from slot_of): token row (slot + l32), latent entries
+    // 16ks + 8h2 .. +7.  Lanes past the sequence end read the chunk's last valid token instead
+    // (its weight is zero), so within a chunk no slot beyond the sequence is read; a chunk past
+    // the end (only ever prefetched, never used) reads its page slot's first row.
+    auto load_slot = [&](int c, int slot, Chunk<KK, KV> &x) {
+        const int row = __builtin_amdgcn_readfirstlane(slot < 0 ? -slot - 1 : slot);
+        const int valid = j_end - (j_begin + 32 * c);
+        const int tok = min(l32, max(valid - 1, 0));
+        const uint16_t *kb = kpool + (size_t)row * RK;
+        const uint16_t *vb = vpool + (size_t)row * RV;
+        const int dk = lane_k + (tok - l32) * RK, dv = lane_v + (tok - l32) * RV;
+#pragma unroll
+        for (int ks = 0; ks < KK; ++ks)
+            x.k[ks] = *reinterpret_cast<const uint4 *>(kb + dk + 16 * ks);
+#pragma unroll
+        for (int ks = 0; ks < KV; ++ks)
+            x.v[ks] = *reinterpret_cast<const uint4 *>(vb + dv + 16 * ks);
+    };
+    auto load = [&](int c, Chunk<KK, KV> &x) { load_slot(c, sSlot[c], x); };
+
+    // ---- prologue.  A wave's vector loads complete in order, so the order of issue matters:
+    // (1) page-table entries of this wave's first chunks, (2) every small set-up operand, raw
+    // into registers, (3) the first latent chunks, and only then (4) the reductions and LDS
+    // stores that wait on (2).  HBM streaming thus starts one page-table round trip after entry.
+    constexpr int DEPTH = SH::DEPTH;
+    constexpr int NT = 64 * WAVES;
+    // Every load here is unconditional, at a clamped in-bounds index, so no branch separates
+    // them (a load under a branch costs a full wait at the join).
+    const int c_last = max(nchunks - 1, 0);
+    int first[DEPTH];   // not clamped to the sequence: these reads need not wait for its length
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) first[i] = slot_of(wave + i * WAVES);
+
+    // (2) W_up,t rows of this head's D columns as 16-byte pieces: piece e is row e / (D/8),
+    // columns 8 (e % (D/8)) .. +7
+    constexpr int PK = RK * D / 8, PV = RV * D / 8;                 // pieces per matrix
+    constexpr int UK = (PK + NT - 1) / NT, UV = (PV + NT - 1) / NT;  // pieces per thread
+    uint4 wpk[UK], wpv[UV];
     {
         const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
                              ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
         const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
                              ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
-        for (int e = tid; e < RK * D; e += 64 * WAVES) {
-            const int k = e / D, i = e - k * D;
-            sWk[i * RKP + k] = Wk[(size_t)k * a.Dg + i];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int e = min(tid + u * NT, PK - 1);
+            wpk[u] = *reinterpret_cast<const uint4 *>(Wk + (size_t)(e / (D / 8)) * a.Dg +
+                                                      8 * (e % (D / 8)));
         }
-        for (int e = tid; e < RV * D; e += 64 * WAVES) {
-            const int k = e / D, i = e - k * D;
-            sWv[i * RVP + k] = Wv[(size_t)k * a.Dg + i];
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int e = min(tid + u * NT, PV - 1);
+            wpv[u] = *reinterpret_cast<const uint4 *>(Wv + (size_t)(e / (D / 8)) * a.Dg +
+                                                      8 * (e % (D / 8)));
+        }
+    }
+    constexpr int US = (kMaxChunksPerSplit + NT - 1) / NT;   // page-table entries per thread
+    int slot_reg[US];
+#pragma unroll
+    for (int u = 0; u < US; ++u) slot_reg[u] = slot_of(min(tid + u * NT, c_last));
+    // query, mu_t^K, and the current token's own loop-t key / value (single-split plans finish
+    // the output here): element i = lane + 64 u of the head's d
+    constexpr int UD = D / 64;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h) * D;
+    const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) +
+                          (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
+    const bool has_self = a.k_self != nullptr;
+    const bool self_here = S == 1 && has_self;
+    const uint16_t *muvp = static_cast<const uint16_t *>(a.mu_v) +
+                           (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
+    // without a self term these read q / mu_v instead and the values are dropped
+    const uint16_t *ksp = self_here ? static_cast<const uint16_t *>(a.k_self) +
+                                          (size_t)b * a.self_stride + (size_t)h * D
+                                    : qp;
+    const uint16_t *vsp = self_here ? static_cast<const uint16_t *>(a.v_self) +
+                                          (size_t)b * a.self_stride + (size_t)h * D
+                                    : muvp;
+    uint16_t qv[UD], mkv[UD], ksv[UD];
+#pragma unroll
+    for (int u = 0; u < UD; ++u) {
+        const int i = lane + 64 * u;
+        qv[u] = qp[i];
+        mkv[u] = muk[i];
+        ksv[u] = ksp[i];
+    }
+    // element tid of the output (threads tid < D use them)
+    const uint16_t vs_raw = vsp[tid % D], muv_raw = muvp[tid % D];
+    // fused path: q_i for this lane's columns i = 32M + l32; explicit path: q rows
+    // 32M + 8bb + 4h2 + 0..3 of the K tile
+    uint16_t qcol[FUSED ? MT : 1];
+    uint2 qrow[FUSED ? 1 : MT][4];
+#pragma unroll
+    for (int M = 0; M < MT; ++M) {
+        if constexpr (FUSED) {
+            qcol[M] = qp[32 * M + l32];
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                qrow[M][bb] = *reinterpret_cast<const uint2 *>(qp + 32 * M + 8 * bb + 4 * h2);
         }
     }
 
-    // ---- query in the K-tile row layout, pre-scaled by scale*log2(e); <q, mu_t^K>
-    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h) * D;
-    // VALU scores: q rows 32M + 8bb + 4h2 + 0..3 of the K tile, fp32, pre-scaled.
-    // MFMA scores: q as the A operand of S = q . K_hat^T, the same bf16 in every row m; k-slot
-    // kk of lane half h2 in step (M, half) is d-row 32M + 16half + 8(kk/4) + 4h2 + kk%4, the
-    // row the K_hat tile holds in element 8half + kk of that lane.
-    float qs[SMFMA ? 1 : MT][16];
-    uint4 qop[SMFMA ? MT : 1][2];
+    // (3) the first latent chunks of this wave
+    Chunk<KK, KV> buf[DEPTH];
 #pragma unroll
-    for (int M = 0; M < MT; ++M)
+    for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
+
+    // (4) page table and W_up,t (transposed: [column][rank]) into LDS; <q, mu_t^K>, <q, k_self>
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(qp + 32 * M + 8 * bb + 4 * h2);
-            if constexpr (SMFMA) {
-                if (bb & 1) { qop[M][bb >> 1].z = u.x; qop[M][bb >> 1].w = u.y; }
-                else        { qop[M][bb >> 1].x = u.x; qop[M][bb >> 1].y = u.y; }
-            } else {
+    for (int u = 0; u < US; ++u) {
+        const int c = tid + u * NT;
+        if (c < nchunks) sSlot[c] = slot_reg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+        const int e = tid + u * NT;
+        if (e < PK) {
+            const int k = e / (D / 8), i0 = 8 * (e % (D / 8));
+            const uint32_t w[4] = {wpk[u].x, wpk[u].y, wpk[u].z, wpk[u].w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                sWk[(i0 + 2 * x) * RKP + k] = (uint16_t)(w[x] & 0xffffu);
+                sWk[(i0 + 2 * x + 1) * RKP + k] = (uint16_t)(w[x] >> 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+        const int e = tid + u * NT;
+        if (e < PV) {
+            const int k = e / (D / 8), i0 = 8 * (e % (D / 8));
+            const uint32_t w[4] = {wpv[u].x, wpv[u].y, wpv[u].z, wpv[u].w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                sWv[(i0 + 2 * x) * RVP + k] = (uint16_t)(w[x] & 0xffffu);
+                sWv[(i0 + 2 * x + 1) * RVP + k] = (uint16_t)(w[x] >> 16);
+            }
+        }
+    }
+    float qm, s_self = -INFINITY;   // log2-scaled
+    {
+        float am = 0.f, as = 0.f;
+#pragma unroll
+        for (int u = 0; u < UD; ++u) {
+            am += bf2f(qv[u]) * bf2f(mkv[u]);
+            as += bf2f(qv[u]) * bf2f(ksv[u]);
+        }
+        qm = wave_sum(am) * a.scale_log2;
+        if (self_here) s_self = wave_sum(as) * a.scale_log2;
+    }
+    float qs[FUSED ? 1 : MT][16];
+    if constexpr (!FUSED) {
+#pragma unroll
+        for (int M = 0; M < MT; ++M)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const uint2 u = qrow[M][bb];
                 qs[M][4 * bb + 0] = __uint_as_float(u.x << 16) * a.scale_log2;
                 qs[M][4 * bb + 1] = __uint_as_float(u.x & 0xffff0000u) * a.scale_log2;
                 qs[M][4 * bb + 2] = __uint_as_float(u.y << 16) * a.scale_log2;
                 qs[M][4 * bb + 3] = __uint_as_float(u.y & 0xffff0000u) * a.scale_log2;
             }
-        }
-    float qm;
-    {
-        const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) +
-                              (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
-        float acc = 0.f;
-        for (int i = lane; i < D; i += 64) acc += bf2f(qp[i]) * bf2f(muk[i]);
-        qm = wave_sum(acc) * a.scale_log2;
     }
     __syncthreads();
 
@@ -157,169 +306,209 @@ void decode_bf16_kernel(DecodeArgs a) {
     auto wv_op = [&](int N, int ks) {
         return *reinterpret_cast<const uint4 *>(&sWv[(32 * N + l32) * RVP + 16 * ks + 8 * h2]);
     };
-    uint4 wkr[WREG ? MT * KK : 1], wvr[WREG ? MT * KV : 1];
-    if constexpr (WREG) {
+    // fused path: this lane's column i = 32M + l32 of W_up,t^K scaled by q_i (log2-scaled)
+    uint4 wkq[FUSED ? MT * KK : 1], wvr[FUSED ? MT * KV : 1];
+    if constexpr (FUSED) {
 #pragma unroll
-        for (int M = 0; M < MT; ++M)
+        for (int M = 0; M < MT; ++M) {
+            const float qi = bf2f(qcol[M]) * a.scale_log2;
 #pragma unroll
-            for (int ks = 0; ks < KK; ++ks) wkr[M * KK + ks] = wk_op(M, ks);
+            for (int ks = 0; ks < KK; ++ks) wkq[M * KK + ks] = scale_bf16x8(wk_op(M, ks), qi);
+        }
 #pragma unroll
         for (int N = 0; N < MT; ++N)
 #pragma unroll
             for (int ks = 0; ks < KV; ++ks) wvr[N * KV + ks] = wv_op(N, ks);
     }
 
-    const uint16_t *kpool = static_cast<const uint16_t *>(a.k_pool);
-    const uint16_t *vpool = static_cast<const uint16_t *>(a.v_pool);
-
-    // 16-byte slices of chunk c: token row (slot + l32), latent entries 16ks + 8h2 .. +7
-    auto load = [&](int c, Chunk<KK, KV> &x) {
-        int row = sSlot[c];
-        row = row < 0 ? -row - 1 : row;
-        const uint16_t *ck = kpool + ((size_t)row + l32) * RK + 8 * h2;
-        const uint16_t *cv = vpool + ((size_t)row + l32) * RV + 8 * h2;
-#pragma unroll
-        for (int ks = 0; ks < KK; ++ks) x.k[ks] = *reinterpret_cast<const uint4 *>(ck + 16 * ks);
-#pragma unroll
-        for (int ks = 0; ks < KV; ++ks) x.v[ks] = *reinterpret_cast<const uint4 *>(cv + 16 * ks);
-    };
-
     float m_run = -INFINITY, l_lane = 0.f;
-    float o[MT];
+    float o[FUSED ? 1 : MT];                  // explicit path: p-weighted V_hat, column 32N + l32
+    f32x16 ov[FUSED ? MT : 1];                // fused path: sum over chunks of p-weighted V_hat
 #pragma unroll
-    for (int N = 0; N < MT; ++N) o[N] = 0.f;
+    for (int N = 0; N < (FUSED ? 1 : MT); ++N) o[N] = 0.f;
+#pragma unroll
+    for (int N = 0; N < (FUSED ? MT : 1); ++N) ov[N] = f32x16{};
 
-    auto compute = [&](int c, Chunk<KK, KV> &x) {
-        const int valid = j_end - (j_begin + 32 * c);   // >= 1, wave-uniform
-        if (valid < 32) {
-            // slots past the sequence end may hold anything (even NaN bit patterns)
-            const bool keep = l32 < valid;
-#pragma unroll
-            for (int ks = 0; ks < KK; ++ks) x.k[ks] = keep ? x.k[ks] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int ks = 0; ks < KV; ++ks) x.v[ks] = keep ? x.v[ks] : make_uint4(0, 0, 0, 0);
-        }
-        // K_hat tiles (d rows x 32 token columns) and the scores of this chunk
-        f32x16 acc[MT];
-#pragma unroll
-        for (int M = 0; M < MT; ++M) {
-            acc[M] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KK; ++ks)
-                acc[M] = mfma32x32x16(WREG ? wkr[M * KK + ks] : wk_op(M, ks), x.k[ks], acc[M]);
-        }
-        float sc;                                   // token l32's score, in both lane halves
-        if constexpr (SMFMA) {
-            // K_hat (rounded to bf16) contracted with q on the matrix pipe: every row of the
-            // result holds the 32 scores of the chunk, so no cross-lane step is needed.
-            f32x16 sacc = {};
-#pragma unroll
-            for (int M = 0; M < MT; ++M) {
-                sacc = mfma32x32x16(qop[M][0], pack8(acc[M], 0), sacc);
-                sacc = mfma32x32x16(qop[M][1], pack8(acc[M], 8), sacc);
-            }
-            sc = sacc[0] * a.scale_log2 + qm;
-        } else {
-            float sp[MT];                           // independent chains, one per tile
-#pragma unroll
-            for (int M = 0; M < MT; ++M) {
-                sp[M] = 0.f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sp[M] += qs[M][v] * acc[M][v];
-            }
-            float tot = sp[0];
-#pragma unroll
-            for (int M = 1; M < MT; ++M) tot += sp[M];
-            sc = add_swap32(tot) + qm;
-        }
-        if (valid < 32 && l32 >= valid) sc = -INFINITY;
-        if (sSlot[c] < 0) sc = __builtin_nanf("");
-
-        // V_hat tiles (32 token rows x d columns); independent of the softmax below, so the
-        // matrix pipe works on them while the max / exp / p exchange runs
-        f32x16 vacc[MT];
-#pragma unroll
-        for (int N = 0; N < MT; ++N) {
-            vacc[N] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KV; ++ks)
-                vacc[N] = mfma32x32x16(x.v[ks], WREG ? wvr[N * KV + ks] : wv_op(N, ks), vacc[N]);
-        }
-
-        // online softmax (log2 domain).  The running max only moves when some score of the
-        // chunk exceeds it; otherwise the rescale factor is exactly 1 and the wave-wide max, the
-        // exp of the old max and the rescale are skipped (a wave-uniform branch).
+    // online softmax (log2 domain) for this chunk's scores: returns token l32's weight.  The
+    // running max only moves when some score of the chunk exceeds it; otherwise the rescale
+    // factor is exactly 1 and the wave-wide max, the exp of the old max and the rescale are
+    // skipped (a wave-uniform branch).
+    auto softmax_step = [&](float sc) {
         if (__builtin_amdgcn_ballot_w64(sc > m_run) != 0) {
-            // the two 16-lane rows of a lane half hold all 32 scores
-            const float r = row16_max(sc);
+            const float r = row16_max(sc);   // the two 16-lane rows of a half hold all 32 scores
             const float cmax = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)),
                                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16)));
             const float m_new = fmaxf(m_run, cmax);
             const float alpha = exp2_(m_run - m_new);
             l_lane *= alpha;
+            if constexpr (FUSED) {
 #pragma unroll
-            for (int N = 0; N < MT; ++N) o[N] *= alpha;
+                for (int N = 0; N < MT; ++N)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) ov[N][v] *= alpha;
+            } else {
+#pragma unroll
+                for (int N = 0; N < MT; ++N) o[N] *= alpha;
+            }
             m_run = m_new;
         }
         const float p = exp2_(sc - m_run);
         l_lane += (h2 == 0 ? p : 0.f);
-
-        // p of tokens 8*(v/4) + 4*h2 + (v%4): the V tile's row layout
-        if (h2 == 0) sP[wave][l32] = p;
-        __builtin_amdgcn_wave_barrier();
-        float pr[16];
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const float4 t4 = *reinterpret_cast<const float4 *>(&sP[wave][8 * bb + 4 * h2]);
-            pr[4 * bb + 0] = t4.x; pr[4 * bb + 1] = t4.y;
-            pr[4 * bb + 2] = t4.z; pr[4 * bb + 3] = t4.w;
-        }
-
-        // p-weighted V_hat into o
-#pragma unroll
-        for (int N = 0; N < MT; ++N)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[N][v];
-        __builtin_amdgcn_wave_barrier();
+        return p;
     };
 
-    // ---- main loop: chunks wave, wave + WAVES, ...; the next chunk's latents are in flight
-    // while the current one is computed.  Prefetch indices are clamped, so the instruction
-    // stream has no data-dependent branches around the loads.
-    if constexpr (KK + KV <= 4) {
-        // small ranks: 3 KB per wave-chunk, so keep a second chunk in flight
-        if (wave < nchunks) {
-            Chunk<KK, KV> A, Bq;
-            int c = wave;
-            load(c, A);
-            load(min(c + WAVES, nchunks - 1), Bq);
-            while (true) {
-                compute(c, A);
-                load(min(c + 2 * WAVES, nchunks - 1), A);
-                c += WAVES;
-                if (c >= nchunks) break;
-                compute(c, Bq);
-                load(min(c + 2 * WAVES, nchunks - 1), Bq);
-                c += WAVES;
-                if (c >= nchunks) break;
-            }
+    // ---- fused path, in two stages so that the matrix core can work on the next chunk's scores
+    // while the vector ALUs finish the current one.
+    // Scores: A = q-scaled W_up^K transposed (d x r_k), B = chunk latents (r_k x 32 tokens); the
+    // tiles of all 32-row groups of the head dim add into one accumulator, whose row r holds the
+    // sum over M of q_i K_hat_i(j), i = 32M + r.
+    auto kscore = [&](const Chunk<KK, KV> &x) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int M = 0; M < MT; ++M)
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) acc = mfma32x32x16(wkq[M * KK + ks], x.k[ks], acc);
+        return acc;
+    };
+    // Rest of chunk c: finish the dot, softmax, then the values.  A = chunk latents with token
+    // l32's row scaled by its weight p (rounded to bf16), B = W_up^V (r_v x d): V_hat tiles of 32
+    // token rows, already p-weighted, add into ov across chunks; the rows are summed at the end.
+    auto finish = [&](int c, const f32x16 &acc, const Chunk<KK, KV> &x) {
+        const int valid = j_end - (j_begin + 32 * c);   // >= 1, wave-uniform
+        float t8[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) t8[v] = acc[v] + acc[v + 8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) t8[v] += t8[v + 4];
+        float sc = add_swap32((t8[0] + t8[2]) + (t8[1] + t8[3])) + qm;
+        if (l32 >= valid) sc = -INFINITY;
+        if (sSlot[c] < 0) sc = __builtin_nanf("");
+        const float p = softmax_step(sc);   // token l32's weight, in both lane halves
+#pragma unroll
+        for (int ks = 0; ks < KV; ++ks) {
+            const uint4 xs = scale_bf16x8(x.v[ks], p);
+#pragma unroll
+            for (int N = 0; N < MT; ++N) ov[N] = mfma32x32x16(xs, wvr[N * KV + ks], ov[N]);
         }
-    } else {
-        // large ranks: one chunk is already KK+KV 1-KB loads per wave; registers go to occupancy
-        for (int c = wave; c < nchunks; c += WAVES) {
-            Chunk<KK, KV> A;
-            load(c, A);
-            compute(c, A);
+    };
+
+    // explicit path (larger ranks): one chunk, start to end
+    auto compute = [&](int c, const Chunk<KK, KV> &x) {
+        const int valid = j_end - (j_begin + 32 * c);   // >= 1, wave-uniform
+        {
+            // ---- scores: K_hat tiles (d rows x 32 token columns) dotted with q per lane
+            float sp[MT];                           // independent chains, one per tile
+#pragma unroll
+            for (int M = 0; M < MT; ++M) {
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < KK; ++ks) acc = mfma32x32x16(wk_op(M, ks), x.k[ks], acc);
+                sp[M] = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sp[M] += qs[M][v] * acc[v];
+            }
+            float tot = sp[0];
+#pragma unroll
+            for (int M = 1; M < MT; ++M) tot += sp[M];
+            float sc = add_swap32(tot) + qm;        // token l32's score, in both lane halves
+            if (l32 >= valid) sc = -INFINITY;
+            if (sSlot[c] < 0) sc = __builtin_nanf("");
+
+            // ---- V_hat tiles (32 token rows x d columns), issued before the softmax chain
+            f32x16 vacc[MT];
+#pragma unroll
+            for (int N = 0; N < MT; ++N) {
+                vacc[N] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < KV; ++ks)
+                    vacc[N] = mfma32x32x16(x.v[ks], wv_op(N, ks), vacc[N]);
+            }
+            const float p = softmax_step(sc);
+
+            // ---- p of tokens 8*(v/4) + 4*h2 + (v%4): the V tile's row layout, via LDS
+            if (h2 == 0) sP[wave][l32] = p;
+            __builtin_amdgcn_wave_barrier();
+            float pr[16];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const float4 t4 = *reinterpret_cast<const float4 *>(&sP[wave][8 * bb + 4 * h2]);
+                pr[4 * bb + 0] = t4.x; pr[4 * bb + 1] = t4.y;
+                pr[4 * bb + 2] = t4.z; pr[4 * bb + 3] = t4.w;
+            }
+#pragma unroll
+            for (int N = 0; N < MT; ++N)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[N][v];
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+
+    // ---- main loop: chunks wave, wave + WAVES, ...  DEPTH chunks per wave are in flight: a
+    // buffer is refilled with the chunk DEPTH rounds ahead as soon as it has been consumed.
+    // Prefetch indices are clamped to the last chunk, so no load sits behind a data-dependent
+    // branch and the wait counts stay exact.
+    if (wave < nchunks) {
+        const int rounds = (nchunks - wave + WAVES - 1) / WAVES;   // chunks of this wave, >= 1
+        int c = wave, r = 0;
+        if constexpr (FUSED) {
+            // the next chunk's scores go to the matrix core before this chunk's vector work
+            f32x16 kacc = kscore(buf[0]);
+            for (; r + DEPTH <= rounds; r += DEPTH) {
+#pragma unroll
+                for (int i = 0; i < DEPTH; ++i) {
+                    const f32x16 knext = kscore(buf[(i + 1) % DEPTH]);
+                    finish(c, kacc, buf[i]);
+                    load(min(c + DEPTH * WAVES, nchunks - 1), buf[i]);
+                    kacc = knext;
+                    c += WAVES;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i + 1 < DEPTH; ++i) {
+                if (r + i < rounds) {
+                    const f32x16 knext = kscore(buf[(i + 1) % DEPTH]);
+                    finish(c, kacc, buf[i]);
+                    kacc = knext;
+                    c += WAVES;
+                }
+            }
+        } else {
+            for (; r + DEPTH <= rounds; r += DEPTH) {
+#pragma unroll
+                for (int i = 0; i < DEPTH; ++i) {
+                    compute(c, buf[i]);
+                    load(min(c + DEPTH * WAVES, nchunks - 1), buf[i]);
+                    c += WAVES;
+                }
+            }
+            // the last rounds % DEPTH chunks are already in their buffers
+#pragma unroll
+            for (int i = 0; i + 1 < DEPTH; ++i) {
+                if (r + i < rounds) {
+                    compute(c, buf[i]);
+                    c += WAVES;
+                }
+            }
         }
     }
 
-    // ---- merge lanes, then waves, into this split's partial
+    // ---- merge lanes, then waves, into this split's result
     const float l_w = wave_sum(l_lane);
+    float of[MT];                              // column 32N + l32 of this wave's p-weighted sum
 #pragma unroll
-    for (int N = 0; N < MT; ++N) o[N] = add_swap32(o[N]);
+    for (int N = 0; N < MT; ++N) {
+        if constexpr (FUSED) {
+            float t = 0.f;                     // the 16 token rows this lane holds, then l ^ 32
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t += ov[N][v];
+            of[N] = add_swap32(t);
+        } else {
+            of[N] = add_swap32(o[N]);
+        }
+    }
     if (h2 == 0) {
 #pragma unroll
-        for (int N = 0; N < MT; ++N) sO[wave][32 * N + l32] = o[N];
+        for (int N = 0; N < MT; ++N) sO[wave][32 * N + l32] = of[N];
     }
     if (lane == 0) {
         sM[wave] = m_run;
@@ -327,15 +516,6 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
     // a single split finishes the output here (same arithmetic as combine.hip): the current
     // token's own loop-t key/value joins the softmax and (sum of cached weights) mu_t^V is added
-    float s_self = -INFINITY;
-    const bool has_self = a.k_self != nullptr;
-    if (S == 1 && has_self) {
-        const uint16_t *ks = static_cast<const uint16_t *>(a.k_self) + (size_t)b * a.self_stride +
-                             (size_t)h * D;
-        float acc = 0.f;
-        for (int i = lane; i < D; i += 64) acc += bf2f(qp[i]) * bf2f(ks[i]);
-        s_self = wave_sum(acc) * a.scale_log2;
-    }
     __syncthreads();
     if (tid < D) {
         float M = -INFINITY;
@@ -354,15 +534,9 @@ void decode_bf16_kernel(DecodeArgs a) {
         if (S == 1) {
             float res = 0.f;
             if (M != -INFINITY) {
-                const uint16_t *muv = static_cast<const uint16_t *>(a.mu_v) +
-                                      (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
-                float w_self = 0.f, v_self = 0.f;
-                if (has_self) {
-                    w_self = exp2_(s_self - M);
-                    v_self = bf2f(static_cast<const uint16_t *>(a.v_self)[
-                        (size_t)b * a.self_stride + (size_t)h * D + tid]);
-                }
-                res = (O + L * bf2f(muv[tid]) + w_self * v_self) / (L + w_self);
+                const float w_self = self_here ? exp2_(s_self - M) : 0.f;
+                const float v_self = self_here ? bf2f(vs_raw) : 0.f;
+                res = (O + L * bf2f(muv_raw) + w_self * v_self) / (L + w_self);
             }
             static_cast<uint16_t *>(a.out)[((size_t)b * a.H + h) * D + tid] = f2bf(res);
         } else {
@@ -376,31 +550,18 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
 }
 
-// Scores on the vector ALU (fp32 FMAs, default) or on the matrix pipe (LLA_SCORE_MFMA=1).
-bool score_on_valu() {
-    static const bool v = [] {
-        const char *e = std::getenv("LLA_SCORE_MFMA");
-        return !(e && e[0] == '1');
-    }();
-    return v;
-}
-
-template <int D, int RK, int RV, int WAVES>
+template <int D, int RK, int RV>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.S;
-    if (score_on_valu())
-        hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, WAVES, false>), dim3(blocks),
-                           dim3(64 * WAVES), 0, st, a);
-    else
-        hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, WAVES, true>), dim3(blocks),
-                           dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV>), dim3(blocks),
+                       dim3(64 * Shape<D, RK, RV>::WAVES), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t st) {
 #define LLA_CASE(RK, RV) \
-    if (a.r_k == RK && a.r_v == RV) return launch_t<D, RK, RV, 4>(a, st);
+    if (a.r_k == RK && a.r_v == RV) return launch_t<D, RK, RV>(a, st);
     LLA_CASE(16, 16)
     LLA_CASE(16, 32)
     LLA_CASE(32, 32)

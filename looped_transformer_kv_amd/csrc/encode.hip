@@ -32,27 +32,16 @@ struct EncodePair {
     int blocks_k;         // workgroups of the K axis (the V axis follows)
 };
 
-template <typename TS> struct Cfg;
-template <> struct Cfg<uint16_t> { static constexpr int XC = 256; };   // 32 KB + 17 KB of LDS
-template <> struct Cfg<float> { static constexpr int XC = 128; };      // 16 KB + 17 KB of LDS
-
-// 16 bytes of storage -> float values
-__device__ __forceinline__ void unpack(const uint4 u, float *v, uint16_t) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void unpack(const uint4 u, float *v, float) {
+// 16 bytes of fp32 storage -> float values
+__device__ __forceinline__ void unpack(const uint4 u, float *v) {
     v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
     v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
 }
 
-template <typename TS>
+// fp32 codecs (bf16 ones take encode_mfma_kernel below)
 __global__ __launch_bounds__(NT) void encode_kernel(EncodePair pr) {
-    constexpr int XC = Cfg<TS>::XC;
+    using TS = float;
+    constexpr int XC = 128;                              // 16 KB + 17 KB of LDS
     constexpr int EPV = 16 / sizeof(TS);                 // elements per 16-byte load
     constexpr int XL = BR * XC / EPV / NT;               // x loads per thread per stage
     constexpr int WL = XC * KC / EPV / NT;               // W loads per thread per stage
@@ -128,8 +117,8 @@ __global__ __launch_bounds__(NT) void encode_kernel(EncodePair pr) {
             const int e = tid + u * NT;
             const int br = e / (XC / EPV), xx = (e % (XC / EPV)) * EPV;
             float v[8], m[8];
-            unpack(xr[u], v, TS(0));
-            unpack(mr[u], m, TS(0));
+            unpack(xr[u], v);
+            unpack(mr[u], m);
 #pragma unroll
             for (int q = 0; q < EPV; ++q) sX[br][xx + q] = v[q] - m[q];
         }
@@ -338,7 +327,7 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
     } else {
         pr.blocks_k = blocks_of(k_axis);
         const unsigned blocks = (unsigned)(pr.blocks_k + blocks_of(v_axis));
-        hipLaunchKernelGGL(encode_kernel<float>, dim3(blocks), dim3(NT), 0, st, pr);
+        hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(NT), 0, st, pr);
     }
     return hipGetLastError();
 }

@@ -157,7 +157,8 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     if (bf16) {
         if (!decode_bf16_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
         if (k->page_size % 32 != 0) return LLA_ERR_SHAPE;
-        if (!aligned16(q)) return LLA_ERR_ALIGN;
+        if (!aligned16(q) || !aligned16(prm->W_up_k) || !aligned16(prm->W_up_v))
+            return LLA_ERR_ALIGN;
     } else if (decode_f32_lds_bytes(c->d_head, c->r_k, c->r_v) > kMaxDynLds) {
         return LLA_ERR_UNSUPPORTED;
     }
