@@ -102,7 +102,7 @@ void decode_bf16_kernel(DecodeArgs a) {
     __shared__ int sSlot[kMaxChunksPerSplit];         // chunk -> first token row in the pool
 
     const int S = a.S;
-    const int id = blockIdx.x;
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int s = id % S;
     const int h = (id / S) % a.H;
     const int b = id / (S * a.H);
@@ -166,16 +166,36 @@ void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) first[i] = slot_of(wave + i * WAVES);
 
-    // (2) W_up,t rows of this head's D columns as 16-byte pieces: piece e is row e / (D/8),
-    // columns 8 (e % (D/8)) .. +7
+    // (2) W_up,t of this head's D columns.  Fused path: each lane loads its own MFMA operands
+    // (rows 16ks + 8h2 + e, e = 0..7, of column 32 tile + l32) straight from memory, so no
+    // workgroup-wide staging or barrier is needed.  Explicit path: 16-byte row pieces for the
+    // transposed LDS copy (piece e is row e / (D/8), columns 8 (e % (D/8)) .. +7).
+    const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
+                         ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
+    const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
+                         ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
+    uint16_t wkraw[FUSED ? MT * KK : 1][8], wvraw[FUSED ? MT * KV : 1][8];
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int M = 0; M < MT; ++M)
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wkraw[M * KK + ks][e] = Wk[(size_t)(16 * ks + 8 * h2 + e) * a.Dg + 32 * M + l32];
+#pragma unroll
+        for (int N = 0; N < MT; ++N)
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wvraw[N * KV + ks][e] = Wv[(size_t)(16 * ks + 8 * h2 + e) * a.Dg + 32 * N + l32];
+    }
     constexpr int PK = RK * D / 8, PV = RV * D / 8;                 // pieces per matrix
-    constexpr int UK = (PK + NT - 1) / NT, UV = (PV + NT - 1) / NT;  // pieces per thread
+    constexpr int UK = FUSED ? 1 : (PK + NT - 1) / NT;               // pieces per thread
+    constexpr int UV = FUSED ? 1 : (PV + NT - 1) / NT;
     uint4 wpk[UK], wpv[UV];
-    {
-        const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
-                             ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
-        const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
-                             ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
+    if constexpr (!FUSED) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int e = min(tid + u * NT, PK - 1);
@@ -189,10 +209,14 @@ void decode_bf16_kernel(DecodeArgs a) {
                                                       8 * (e % (D / 8)));
         }
     }
-    constexpr int US = (kMaxChunksPerSplit + NT - 1) / NT;   // page-table entries per thread
+    // page table.  Fused path: this wave's own chunks c = wave + WAVES (lane + 64 u) only, as
+    // only this wave reads them; explicit path: the whole split, block-wide.
+    constexpr int US = FUSED ? (kMaxChunksPerSplit / WAVES + 63) / 64
+                             : (kMaxChunksPerSplit + NT - 1) / NT;   // entries per thread
     int slot_reg[US];
 #pragma unroll
-    for (int u = 0; u < US; ++u) slot_reg[u] = slot_of(min(tid + u * NT, c_last));
+    for (int u = 0; u < US; ++u)
+        slot_reg[u] = slot_of(min(FUSED ? wave + WAVES * (lane + 64 * u) : tid + u * NT, c_last));
     // query, mu_t^K, and the current token's own loop-t key / value (single-split plans finish
     // the output here): element i = lane + 64 u of the head's d
     constexpr int UD = D / 64;
@@ -240,14 +264,15 @@ void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
 
-    // (4) page table and W_up,t (transposed: [column][rank]) into LDS; <q, mu_t^K>, <q, k_self>
+    // (4) page table (and, explicit path, W_up,t transposed: [column][rank]) into LDS;
+    // <q, mu_t^K>, <q, k_self>
 #pragma unroll
     for (int u = 0; u < US; ++u) {
-        const int c = tid + u * NT;
+        const int c = FUSED ? wave + WAVES * (lane + 64 * u) : tid + u * NT;
         if (c < nchunks) sSlot[c] = slot_reg[u];
     }
 #pragma unroll
-    for (int u = 0; u < UK; ++u) {
+    for (int u = 0; u < (FUSED ? 0 : UK); ++u) {
         const int e = tid + u * NT;
         if (e < PK) {
             const int k = e / (D / 8), i0 = 8 * (e % (D / 8));
@@ -260,7 +285,7 @@ void decode_bf16_kernel(DecodeArgs a) {
         }
     }
 #pragma unroll
-    for (int u = 0; u < UV; ++u) {
+    for (int u = 0; u < (FUSED ? 0 : UV); ++u) {
         const int e = tid + u * NT;
         if (e < PV) {
             const int k = e / (D / 8), i0 = 8 * (e % (D / 8));
@@ -295,8 +320,8 @@ void decode_bf16_kernel(DecodeArgs a) {
                 qs[M][4 * bb + 2] = __uint_as_float(u.y << 16) * a.scale_log2;
                 qs[M][4 * bb + 3] = __uint_as_float(u.y & 0xffff0000u) * a.scale_log2;
             }
+        __syncthreads();   // W_up and the page table are shared by the workgroup
     }
-    __syncthreads();
 
     // W_up operands: K tile M / V tile N, k-step ks; lane (l32, h2) holds rows 16ks+8h2 .. +7
     // of column 32*tile + l32.
@@ -309,16 +334,21 @@ void decode_bf16_kernel(DecodeArgs a) {
     // fused path: this lane's column i = 32M + l32 of W_up,t^K scaled by q_i (log2-scaled)
     uint4 wkq[FUSED ? MT * KK : 1], wvr[FUSED ? MT * KV : 1];
     if constexpr (FUSED) {
+        auto pack8 = [](const uint16_t *v) {
+            return make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                              v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+        };
 #pragma unroll
         for (int M = 0; M < MT; ++M) {
             const float qi = bf2f(qcol[M]) * a.scale_log2;
 #pragma unroll
-            for (int ks = 0; ks < KK; ++ks) wkq[M * KK + ks] = scale_bf16x8(wk_op(M, ks), qi);
+            for (int ks = 0; ks < KK; ++ks)
+                wkq[M * KK + ks] = scale_bf16x8(pack8(wkraw[M * KK + ks]), qi);
         }
 #pragma unroll
         for (int N = 0; N < MT; ++N)
 #pragma unroll
-            for (int ks = 0; ks < KV; ++ks) wvr[N * KV + ks] = wv_op(N, ks);
+            for (int ks = 0; ks < KV; ++ks) wvr[N * KV + ks] = pack8(wvraw[N * KV + ks]);
     }
 
     float m_run = -INFINITY, l_lane = 0.f;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
     float *red = sO + kThreads;      // [8] reduction scratch
 
     const int S = a.S;
-    const int id = blockIdx.x;
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int s = id % S;
     const int h = (id / S) % a.H;
     const int b = id / (S * a.H);

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(64 * WAVES) void flat_kernel(DecodeArgs a) {
     __shared__ int sRow[kMaxChunksPerSplit];   // chunk -> first token row of its page slot
 
     const int S = a.S;
-    const int id = blockIdx.x;
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int s = id % S;
     const int h = (id / S) % a.H;
     const int b = id / (S * a.H);

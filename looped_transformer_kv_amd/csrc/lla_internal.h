@@ -9,6 +9,16 @@
 
 namespace lla {
 
+// Workgroup index -> work item, XCD-aware.  Consecutive workgroup ids are dispatched round-robin
+// over the 8 XCDs of the chip, so id % 8 names the XCD.  With the plain order every XCD would
+// serve a fixed subset of heads (head h sits at the same offset in every page, so each XCD's
+// requests would hit a fixed subset of memory channels).  Transposing gives XCD x the
+// contiguous work range [x n/8, (x+1) n/8): whole sequences, all heads.  Identity when n % 8 != 0.
+__device__ __forceinline__ int xcd_work_item(int id, int n) {
+    return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
+}
+
+
 // ---------------------------------------------------------------- kernel argument blocks
 
 // One decode call (latent or flat).  Pointers are device pointers; element type is bf16
