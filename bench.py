@@ -11,10 +11,15 @@ cached tokens and appends at slot 4096, so every timed step does identical work.
 
 value      cached token-loops per second for the whole step (B * N * T * L per step)
 roofline   the decode kernel: latent bytes per launch / its average launch time (HIP events
-           around the decode segment of every timed step), against MI355X's 8 TB/s
+           around the decode segment of every timed step), against MI355X's 8 TB/s; for the
+           LLA-2D workload (matrix-core bound) the literal reconstruct-path flops against the
+           2.5 PFLOP/s dense bf16 peak, with the latent bandwidth alongside
+read_ceiling  a plain streaming read (lla_stream_read) of 2 GiB on the same run: the achievable
+           HBM read bandwidth, against which the latent bandwidth is also given
 cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the same step
-flat_ref   the uncompressed loop-t comparator (lla_ref_attn) at batch 32 on the same GPU
-Inputs are synthetic (seeded) and resident in HBM before timing starts.
+flat_ref   the uncompressed loop-t comparator (lla_ref_attn) at batch <= 32 on the same GPU
+Inputs are synthetic (seeded) and resident in HBM before timing starts.  --workload selects
+another of the configured shapes (the default is the one the metric is quoted on).
 """
 import argparse
 import hashlib
@@ -31,7 +36,18 @@ if ROOT not in sys.path:
 METRIC = "LLA decode-attn latent HBM GB/s (% of peak) + cached token·loops/s at 1 GPU"
 UNIT = "cached token·loops/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "ouro14_21x"
+DESCRIBE = {
+    "ouro14_21x": "Ouro-1.4B-like looped decode step at 21.3x",
+    "ouro14_21x_cap": "Ouro-1.4B-like 21.3x capacity point (batch 768)",
+    "ouro14_4x": "Ouro-1.4B-like looped decode step, 4x codec",
+    "ouro26_2d_64x": "Ouro-2.6B-like LLA-2D decode step at 64x",
+    "huginn_32x": "Huginn-like 32-loop decode step at 32x",
+}
+# oracle sample (sequences) per workload: about 10-30 s of fp64 work per (layer, loop) call
+CPU_SAMPLE_SEQS = {"ouro14_21x": 32, "ouro14_21x_cap": 32, "ouro14_4x": 8,
+                   "ouro26_2d_64x": 1, "huginn_32x": 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_ouro14_21x_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "looped_transformer_kv_amd", "csrc", f)
                   for f in ("decode_bf16.hip", "lla_internal.h")]
@@ -68,7 +84,7 @@ def recorded_traffic():
         return None
 
 
-def build_layers(cfg, dev):
+def build_layers(cfg, dev, n_layers):
     import torch
     from looped_transformer_kv_amd import lla, synth
     from looped_transformer_kv_amd.runtime import LatentLayer
@@ -79,7 +95,7 @@ def build_layers(cfg, dev):
     lens = torch.full((B,), N, dtype=torch.int32, device=dev)
     codec = lla.make_codec(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
     layers, host = [], []
-    for l in range(cfg.L):
+    for l in range(n_layers):
         Wdk, Wuk, muk = synth.codec(cfg, l, synth.AX_K)
         Wdv, Wuv, muv = synth.codec(cfg, l, synth.AX_V)
         up = lambda a: synth.to_device(a, "bf16", dev)
@@ -92,22 +108,27 @@ def build_layers(cfg, dev):
 
 
 def cpu_baseline(cfg, layers, host, bt, q, xk, xv, budget_s):
-    """The fp64 oracle, timed on this host's cores, on whole layers of one step (all T decode
-    calls at the full batch, then the layer's encode+append) until `budget_s` of CPU time."""
+    """The fp64 oracle, timed on this host's cores, on a sample of the step: whole layers (all T
+    decode calls, then the layer's encode+append) over the first CPU_SAMPLE_SEQS sequences (all
+    of them for the default workload), until `budget_s` of oracle time."""
     import numpy as np
+    import torch
     from looped_transformer_kv_amd import synth
     from oracle import oracle as O
 
     B, N, T = cfg.B, cfg.N, cfg.T
-    bt_h = bt.cpu().numpy()
-    lens = np.full(B, N, dtype=np.int32)
-    pos = np.full(B, N, dtype=np.int32)
+    nb = min(B, CPU_SAMPLE_SEQS.get(cfg.name, B))
+    # the sampled sequences' pages only, renumbered
+    pages = bt[:nb].reshape(-1)
+    bt_h = np.arange(pages.numel(), dtype=np.int32).reshape(nb, -1)
+    lens = np.full(nb, N, dtype=np.int32)
+    pos = np.full(nb, N, dtype=np.int32)
     spent, done_layers, token_loops = 0.0, 0, 0
-    for l in range(cfg.L):
-        kp = synth.from_device(layers[l].tensors["k_pool"])
-        vp = synth.from_device(layers[l].tensors["v_pool"])
-        xk_h, xv_h = synth.from_device(xk[l]), synth.from_device(xv[l])
-        q_h = [synth.from_device(q[t][l]) for t in range(T)]
+    for l in range(len(layers)):
+        kp = synth.from_device(torch.index_select(layers[l].tensors["k_pool"], 0, pages))
+        vp = synth.from_device(torch.index_select(layers[l].tensors["v_pool"], 0, pages))
+        xk_h, xv_h = synth.from_device(xk[l][:nb]), synth.from_device(xv[l][:nb])
+        q_h = [synth.from_device(q[t][l][:nb]) for t in range(T)]
         hd = host[l]
         t0 = time.perf_counter()
         for t in range(T):
@@ -120,25 +141,53 @@ def cpu_baseline(cfg, layers, host, bt, q, xk, xv, budget_s):
         O.append(cv, pos, bt_h, cfg.page, vp)
         spent += time.perf_counter() - t0
         done_layers += 1
-        token_loops += B * N * T
+        token_loops += nb * N * T
         log(f"cpu_baseline: layer {l} done, {spent:.1f} s of oracle time")
         if spent >= budget_s:
             break
     return {"value": token_loops / spent, "unit": UNIT, "cores": O.num_threads(),
             "kind": "oracle",
             "sample": f"{done_layers} of {cfg.L} layers of one decode step: all {T} loops of "
-                      f"decode attention at batch {B} x {N} cached tokens, then encode+append; "
-                      f"fp64, {spent:.1f} s"}
+                      f"decode attention over {nb} of {B} sequences x {N} cached tokens, then "
+                      f"encode+append; fp64, {spent:.1f} s"}
 
 
-def flat_comparator(cfg, dev, steps, bt, lens):
-    """lla_ref_attn over uncompressed loop-t K/V slices at batch 32, rotating over 4 distinct
-    slices (4.3 GB) so the Infinity Cache cannot serve repeats."""
+def read_ceiling(dev, reps=5):
+    """Achievable HBM read bandwidth on this run: lla_stream_read over 2 GiB, best of `reps`."""
     import torch
     from looped_transformer_kv_amd import lla
 
-    B, N, H, d = cfg.B, cfg.N, cfg.H, cfg.d
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    lla.lla_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lla.lla_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del buf
+    torch.cuda.empty_cache()
+    gbs = nbytes / best / 1e9
+    return {"kernel": "lla_stream_read", "bytes": nbytes, "GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def flat_comparator(cfg, dev, steps):
+    """lla_ref_attn over uncompressed loop-t K/V slices at batch min(B, 32), rotating over 4
+    distinct slices (4.3 GB at the default shape) so the Infinity Cache cannot serve repeats."""
+    import torch
+    from looped_transformer_kv_amd import lla, synth
+
+    B, N, H, d = min(cfg.B, 32), cfg.N, cfg.H, cfg.d
     n_pages = B * cfg.max_pages
+    bt = torch.from_numpy(synth.block_table(cfg, B, cfg.max_pages)).to(dev)
+    lens = torch.full((B,), N, dtype=torch.int32, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(77)
     slices = []
@@ -183,6 +232,11 @@ def main():
                     help="oracle time budget for the CPU baseline (0 disables it)")
     ap.add_argument("--no-flat", action="store_true", help="skip the flat comparator")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(DESCRIBE),
+                    help="shape to time (default: the one the metric is quoted on)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="build only this many layers (0: all; the step then covers them)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -211,11 +265,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     lla.lib()
-    cfg = synth.CONFIGS[WORKLOAD]
-    B, N, L, T, H, d = cfg.B, cfg.N, cfg.L, cfg.T, cfg.H, cfg.d
+    cfg = synth.CONFIGS[args.workload]
+    B, N, T, H, d = cfg.B, cfg.N, cfg.T, cfg.H, cfg.d
+    L = min(cfg.L, args.layers) if args.layers > 0 else cfg.L
 
+    ceiling = None
+    if not args.no_ceiling:
+        log("measuring the read ceiling")
+        ceiling = read_ceiling(dev)
     log(f"building {L} layers of {cfg.name} (batch {B}, context {N}) on {dev}")
-    layers, host, bt, lens = build_layers(cfg, dev)
+    layers, host, bt, lens = build_layers(cfg, dev, L)
     gen = torch.Generator(device=dev)
     gen.manual_seed(synth.ROOT_SEED)
     q = [[torch.randn((B, H, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(L)]
@@ -281,7 +340,21 @@ def main():
 
     latent_bytes = B * N * cfg.G * (cfg.r_k + cfg.r_v) * 2
     achieved = latent_bytes / (dec_us * 1e-6) / 1e9
+    # literal reconstruct path per call: every cached token expanded for K and V, plus attention
+    flops = B * N * (cfg.G * 2 * (cfg.r_k + cfg.r_v) * cfg.Dg + 4 * H * d)
+    tflops = flops / (dec_us * 1e-6) / 1e12
     token_loops = B * N * T * L
+    # encode: staging rows, W_down and mu read, latents written, both axes
+    enc_bytes = sum(B * T * H * d * 2 + cfg.G * cfg.X * r * 2 + cfg.G * cfg.X * 2 + B * cfg.G * r * 2
+                    for r in (cfg.r_k, cfg.r_v))
+    if cfg.mode == 1:   # matrix-core bound: the roofline is the expansion's flops
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic() if cfg.name == WORKLOAD else None}
     result = {
         "metric": METRIC,
         "value": token_loops / (step_ms * 1e-3),
@@ -296,29 +369,31 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: Ouro-1.4B-like looped decode step, {L} layers x {T} loops "
+            "workload": f"{cfg.name}: {DESCRIBE[cfg.name]}, {L} layers x {T} loops "
                         f"of LLA decode attention + {L} encode/append calls",
+            "mode": "lla_2d" if cfg.mode == 1 else "per_head",
             "layers": L, "heads": H, "d_head": d, "loops": T, "r_k": cfg.r_k, "r_v": cfg.r_v,
             "compression": round(lla.lla_compression_ratio(layers[0].codec), 3),
             "global_batch": B, "seq_len": N, "page_size": cfg.page,
             "splits": plan.splits, "launch": launch, "parallelism": "none (1 GPU)",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(),
-        },
+        "roofline": roofline,
+        "read_ceiling": ceiling,
         "decode_us_per_call": round(dec_us, 3),
         "decode_latent_bytes_per_call": latent_bytes,
+        "decode_latent_GBps": round(achieved, 1),
+        "decode_frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
+        "decode_frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4) if ceiling else None,
+        "decode_flops_per_call": flops,
+        "decode_TFLOPs": round(tflops, 2),
         "decode_token_loops_per_s_per_call": round(B * N / (dec_us * 1e-6), 1),
         "encode_us_per_call": round(enc_us, 3),
+        "encode_bytes_per_call": enc_bytes,
+        "encode_GBps": round(enc_bytes / (enc_us * 1e-6) / 1e9, 1),
     }
     if not args.no_flat:
         log("timing the flat comparator")
-        result["flat_ref"] = flat_comparator(cfg, dev, max(5, K), bt, lens)
+        result["flat_ref"] = flat_comparator(cfg, dev, max(5, K))
     if args.cpu_seconds > 0:
         log("timing the oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(cfg, layers, host, bt, q, xk, xv, args.cpu_seconds)

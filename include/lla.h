@@ -165,6 +165,14 @@ lla_status lla_ref_attn(int32_t n_heads, int32_t d_head, int32_t dtype, const ll
                         int64_t self_stride, float scale, void *out, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement helper (not an LLA operation): streams `bytes` of `buf` once from device memory
+ * and XORs every 32-bit word into sink[0] (the caller zeroes it first if it wants the checksum).
+ * Its time gives the achievable HBM read bandwidth, the practical ceiling for the latent stream.
+ * buf: device, 16-byte aligned, bytes a multiple of 16 (0 enqueues nothing); sink: device uint32.
+ */
+lla_status lla_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Static description of a status code. */
 const char *lla_status_str(lla_status status);
 

@@ -177,27 +177,32 @@ int blocks_of(const EncodeArgs &a) {
 // ---------------------------------------------------------------- bf16: matrix cores
 // C = X W - 1 (mu W) per (axis, group): a dense contraction over the stacked axis, run on
 // v_mfma_f32_32x32x16_bf16.  A workgroup owns one 32 x 32 output tile (32 sequences x 32 latent
-// columns); its four waves split the stacked axis of every 512-element chunk into contiguous
-// quarters.  A operands are the staging rows (16 bytes per lane straight from HBM) and the mean
-// mu (the same in every row); the B operand is the W_down tile, staged row-major in LDS.  Both
-// inputs stay exact bf16; x W and mu W accumulate in separate fp32 chains and are subtracted at
-// the end.  The four waves' partial tiles are summed in a fixed order through LDS.
+// columns); its EWAVES waves split the stacked axis into contiguous ranges of 16-element k-steps.
+// Every lane loads its own operands straight from memory: A = staging rows (16 bytes per lane
+// per k-step) and the mean mu (the same in every row), B = W_down rows 16ks + 8h2 + 0..7 of
+// column c0 + l32 (eight 2-byte loads; a wave's loads cover whole 64-byte row segments).  Groups
+// of EGRP k-steps are double-buffered.  Inputs stay exact bf16; x W and mu W accumulate in
+// separate fp32 chains and are subtracted at the end; the waves' partial tiles are summed in a
+// fixed order through LDS.  The append slots (write_pos, then the page table) are fetched at the
+// start so that the stores at the end wait on nothing.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int MXC = 512;             // stacked elements per chunk
-constexpr int MKS = MXC / 16;        // MFMA k-steps per chunk
-constexpr int MKW = MKS / 4;         // k-steps per wave per chunk
-constexpr int MWROW = 32 + 8;        // LDS row of the W tile (80 bytes)
+constexpr int EWAVES = 8;            // waves per workgroup
+constexpr int EGRP = 4;              // k-steps per load group
 
 __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void encode_mfma_kernel(EncodePair pr) {
-    __shared__ __align__(16) uint16_t sW[MXC][MWROW];
-    __shared__ float sAcc[4][32][33];
+struct EncOps {
+    uint4 x[EGRP], m[EGRP];
+    uint16_t w[EGRP][8];
+};
+
+__global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr) {
+    __shared__ float sAcc[EWAVES][32][33];
 
     int blk = blockIdx.x;
     const int axis = blk < pr.blocks_k ? 0 : 1;
@@ -214,98 +219,93 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodePair pr) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h2 = lane >> 5;
     const int X = a.T * a.Dg;
+    const int nks = X / 16;                              // X is a multiple of 64
+    const int per = (nks + EWAVES - 1) / EWAVES;
+    const int ks0 = min(wave * per, nks), ks1 = min(ks0 + per, nks);
+
+    // ---- append slots of this thread's outputs (rows tid / 32 and tid / 32 + 16 of the tile),
+    // fetched first; the page-table reads wait only for the write positions
+    constexpr int OUTS = 32 * 32 / (64 * EWAVES);        // outputs per thread
+    int wpos[OUTS], page[OUTS];
+#pragma unroll
+    for (int o = 0; o < OUTS; ++o) wpos[o] = a.write_pos[min(b0 + (tid + 64 * EWAVES * o) / 32, a.B - 1)];
+
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
     const uint16_t *W = static_cast<const uint16_t *>(a.W_down) + (size_t)g * X * a.r;
     const uint16_t *mu = static_cast<const uint16_t *>(a.mu) + (size_t)g * X;
-    const bool wvec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
-    const int b = b0 + l32;                       // this lane's A-operand row
+    const int brow = min(b0 + l32, a.B - 1);             // this lane's A-operand row (clamped)
+    const int wcol = min(c0 + l32, a.r - 1);             // this lane's B-operand column (clamped)
 
+    // k-steps kg .. kg + EGRP - 1 of this wave; steps past its range load in bounds and are zeroed
+    auto load_grp = [&](int kg, EncOps &op) {
+#pragma unroll
+        for (int j = 0; j < EGRP; ++j) {
+            const int ks = min(kg + j, max(ks1 - 1, 0));
+            const int xi = 16 * ks + 8 * h2;
+            size_t off;
+            if (a.mode) {
+                off = (size_t)brow * X + xi;                           // (t, h, i) order
+            } else {
+                const int t = xi / a.d, i = xi - t * a.d;              // (t, i) of head g
+                off = (((size_t)brow * a.T + t) * a.H + g) * a.d + i;
+            }
+            op.x[j] = *reinterpret_cast<const uint4 *>(x + off);
+            op.m[j] = *reinterpret_cast<const uint4 *>(mu + xi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) op.w[j][e] = W[(size_t)(xi + e) * a.r + wcol];
+        }
+    };
     f32x16 acc = {}, accmu = {};
-    for (int x0 = 0; x0 < X; x0 += MXC) {
-        const int nks = min(MXC, X - x0) / 16;
-        // this wave's A operands (staging rows and mu) for its quarter of the chunk
-        uint4 ax[MKW], am[MKW];
+    auto compute = [&](int kg, const EncOps &op) {
 #pragma unroll
-        for (int j = 0; j < MKW; ++j) {
-            const int ks = wave * MKW + j;
-            ax[j] = am[j] = make_uint4(0, 0, 0, 0);
-            if (ks < nks) {
-                const int xi = x0 + 16 * ks + 8 * h2;
-                am[j] = *reinterpret_cast<const uint4 *>(mu + xi);
-                if (b < a.B) {
-                    size_t off;
-                    if (a.mode) {
-                        off = (size_t)b * X + xi;                           // (t, h, i) order
-                    } else {
-                        const int t = xi / a.d, i = xi - t * a.d;           // (t, i) of head g
-                        off = (((size_t)b * a.T + t) * a.H + g) * a.d + i;
-                    }
-                    ax[j] = *reinterpret_cast<const uint4 *>(x + off);
-                }
-            }
+        for (int j = 0; j < EGRP; ++j) {
+            const bool live = kg + j < ks1;
+            const uint4 ax = live ? op.x[j] : make_uint4(0, 0, 0, 0);
+            const uint4 am = live ? op.m[j] : make_uint4(0, 0, 0, 0);
+            const uint16_t *w = op.w[j];
+            const uint4 bw = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
+                                        w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
+            acc = mfma32(ax, bw, acc);
+            accmu = mfma32(am, bw, accmu);
         }
-        // W_down rows x0 .. x0+511, columns c0 .. c0+31 (4 x 16 bytes per row)
-        uint4 wr[MXC * 4 / 256];
+    };
+
+    EncOps A, Bq;
+    load_grp(ks0, A);
 #pragma unroll
-        for (int u = 0; u < MXC * 4 / 256; ++u) {
-            const int e = tid + 256 * u;
-            const int row = e >> 2, k = c0 + 8 * (e & 3);
-            const int xi = x0 + row;
-            wr[u] = make_uint4(0, 0, 0, 0);
-            if (xi < X && k < a.r) {
-                const uint16_t *src = W + (size_t)xi * a.r + k;
-                if (wvec && k + 8 <= a.r) {
-                    wr[u] = *reinterpret_cast<const uint4 *>(src);
-                } else {
-                    uint16_t tmp[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) tmp[q] = (k + q < a.r) ? src[q] : 0;
-                    wr[u] = *reinterpret_cast<const uint4 *>(tmp);
-                }
-            }
-        }
-        __syncthreads();                          // previous chunk's tile fully read
-#pragma unroll
-        for (int u = 0; u < MXC * 4 / 256; ++u) {
-            const int e = tid + 256 * u;
-            *reinterpret_cast<uint4 *>(&sW[e >> 2][8 * (e & 3)]) = wr[u];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < MKW; ++j) {
-            const int ks = wave * MKW + j;
-            if (ks < nks) {
-                // B operand: W rows 16ks + 8h2 + 0..7 of column l32
-                const uint16_t *p = &sW[16 * ks + 8 * h2][l32];
-                uint4 bw;
-                bw.x = (uint32_t)p[0 * MWROW] | ((uint32_t)p[1 * MWROW] << 16);
-                bw.y = (uint32_t)p[2 * MWROW] | ((uint32_t)p[3 * MWROW] << 16);
-                bw.z = (uint32_t)p[4 * MWROW] | ((uint32_t)p[5 * MWROW] << 16);
-                bw.w = (uint32_t)p[6 * MWROW] | ((uint32_t)p[7 * MWROW] << 16);
-                acc = mfma32(ax[j], bw, acc);
-                accmu = mfma32(am[j], bw, accmu);
-            }
-        }
+    for (int o = 0; o < OUTS; ++o) {
+        const int pos = wpos[o];
+        const int pi = min(max(pos, 0) / a.P, a.max_pages - 1);
+        page[o] = a.block_table[(size_t)min(b0 + (tid + 64 * EWAVES * o) / 32, a.B - 1) *
+                                a.max_pages + pi];
     }
-    // partial tile: rows 8(v/4) + 4h2 + v%4, column l32
+    for (int kg = ks0; kg < ks1; kg += 2 * EGRP) {
+        load_grp(kg + EGRP, Bq);
+        compute(kg, A);
+        if (kg + EGRP >= ks1) break;
+        load_grp(kg + 2 * EGRP, A);
+        compute(kg + EGRP, Bq);
+    }
+
+    // ---- partial tile (rows 8(v/4) + 4h2 + v%4, column l32) -> fixed-order sum over waves
 #pragma unroll
     for (int v = 0; v < 16; ++v) sAcc[wave][8 * (v >> 2) + 4 * h2 + (v & 3)][l32] = acc[v] - accmu[v];
     __syncthreads();
 #pragma unroll
-    for (int o = 0; o < 4; ++o) {
-        const int idx = tid + 256 * o;
+    for (int o = 0; o < OUTS; ++o) {
+        const int idx = tid + 64 * EWAVES * o;
         const int row = idx >> 5, col = idx & 31;
         const int bb = b0 + row, k = c0 + col;
         if (bb >= a.B || k >= a.r) continue;
-        const float c = ((sAcc[0][row][col] + sAcc[1][row][col]) + sAcc[2][row][col]) +
-                        sAcc[3][row][col];
+        float c = 0.f;
+#pragma unroll
+        for (int w = 0; w < EWAVES; ++w) c += sAcc[w][row][col];
         if (a.c_out) a.c_out[((size_t)bb * a.G + g) * a.r + k] = c;
-        const int pos = a.write_pos[bb];
+        const int pos = wpos[o];
         if (pos < 0 || pos >= a.max_pages * a.P) continue;
-        const int page = a.block_table[(size_t)bb * a.max_pages + pos / a.P];
-        if ((unsigned)page >= (unsigned)a.n_pages) continue;
-        static_cast<uint16_t *>(a.pool)[(((size_t)page * a.G + g) * a.P + pos % a.P) * a.r + k] =
-            f2bf(c);
+        if ((unsigned)page[o] >= (unsigned)a.n_pages) continue;
+        static_cast<uint16_t *>(a.pool)[(((size_t)page[o] * a.G + g) * a.P + pos % a.P) * a.r +
+                                        k] = f2bf(c);
     }
 }
 
@@ -323,7 +323,7 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
     if (bf16) {
         pr.blocks_k = mfma_blocks_of(k_axis);
         const unsigned blocks = (unsigned)(pr.blocks_k + mfma_blocks_of(v_axis));
-        hipLaunchKernelGGL(encode_mfma_kernel, dim3(blocks), dim3(256), 0, st, pr);
+        hipLaunchKernelGGL(encode_mfma_kernel, dim3(blocks), dim3(64 * EWAVES), 0, st, pr);
     } else {
         pr.blocks_k = blocks_of(k_axis);
         const unsigned blocks = (unsigned)(pr.blocks_k + blocks_of(v_axis));

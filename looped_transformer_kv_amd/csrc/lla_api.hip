@@ -300,6 +300,16 @@ lla_status lla_ref_attn(int32_t H, int32_t d, int32_t dtype, const lla_cache *k,
     return launch_combine(a, d, bf16, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
+lla_status lla_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink) return LLA_ERR_NULL;
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return LLA_ERR_ALIGN;
+    if (bytes % 16 != 0) return LLA_ERR_SHAPE;
+    if (bytes == 0) return LLA_OK;
+    return launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LLA_OK
+               : LLA_ERR_HIP;
+}
+
 const char *lla_status_str(lla_status s) {
     switch (s) {
         case LLA_OK: return "ok";

@@ -81,6 +81,8 @@ def lib():
         L.lla_ref_attn.restype = i32
         L.lla_ref_attn.argtypes = [i32, i32, i32, P(lla_cache), vp, vp, vp, i64, f32, vp, vp, sz,
                                    vp]
+        L.lla_stream_read.restype = i32
+        L.lla_stream_read.argtypes = [vp, sz, vp, vp]
         L.lla_status_str.restype = ctypes.c_char_p
         L.lla_status_str.argtypes = [i32]
         L.lla_version.restype = ctypes.c_char_p
@@ -191,6 +193,15 @@ def lla_ref_attn(n_heads, d_head, dtype, flat, q, k_self, v_self, self_stride, s
                             _ptr(v_self), int(self_stride), float(scale), _ptr(out),
                             _ptr(workspace), int(workspace_bytes), _stream(stream))
     return _check("lla_ref_attn", st, check)
+
+
+def lla_stream_read(buf, sink, nbytes=None, stream=None, check=True) -> int:
+    """Stream `nbytes` (default: all) of the device tensor `buf` once; XOR its 32-bit words
+    into the int32 device tensor `sink[0]` (a read-bandwidth probe)."""
+    if nbytes is None:
+        nbytes = buf.numel() * buf.element_size()
+    st = lib().lla_stream_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream))
+    return _check("lla_stream_read", st, check)
 
 
 def lla_status_str(status: int) -> str:

@@ -129,3 +129,14 @@ def test_status_strings():
     for s in range(8):
         assert lla.lla_status_str(s)
     assert lla.lla_version().count(".") == 2
+
+
+def test_stream_read_validation_without_launch():
+    _no_gpu()
+    L = lla.lib()
+    assert L.lla_stream_read(None, 16, FAKE, None) == lla.LLA_ERR_NULL
+    assert L.lla_stream_read(FAKE, 16, None, None) == lla.LLA_ERR_NULL
+    assert L.lla_stream_read(FAKE + 8, 16, FAKE, None) == lla.LLA_ERR_ALIGN
+    assert L.lla_stream_read(FAKE, 16, FAKE + 2, None) == lla.LLA_ERR_ALIGN
+    assert L.lla_stream_read(FAKE, 24, FAKE, None) == lla.LLA_ERR_SHAPE
+    assert L.lla_stream_read(FAKE, 0, FAKE, None) == lla.LLA_OK        # nothing to read

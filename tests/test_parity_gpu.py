@@ -292,3 +292,18 @@ def test_full_size_sampled(gpu, name):
         say(f"{name}: oracle on sequences {sel}")
         ref = _sampled_oracle(cfg, layer, host, sel, t, q, xk[:, t], xv[:, t])
         assert_close(got[sel], ref, "bf16", f"{name} t={t}")
+
+
+# ------------------------------------------------------------------ read-bandwidth probe
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 7])
+def test_stream_read_reads_every_word(gpu, nbytes):
+    """The probe behind the read ceiling: its checksum equals the XOR of every 32-bit word."""
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(gpu)
+    sink = torch.zeros(1, dtype=torch.int32, device=gpu)
+    say(f"stream_read {nbytes} bytes")
+    lla.lla_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    expect = np.bitwise_xor.reduce(host)
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(expect)
