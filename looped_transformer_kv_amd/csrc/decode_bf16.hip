@@ -477,6 +477,15 @@ void decode_bf16_kernel(DecodeArgs a) {
     // buffer is refilled with the chunk DEPTH rounds ahead as soon as it has been consumed.
     // Prefetch indices are clamped to the last chunk, so no load sits behind a data-dependent
     // branch and the wait counts stay exact.
+    // Two workgroups share each CU and the SIMD issues from the older wave first, so left alone
+    // the older workgroup runs ahead and the younger one finishes alone.  A wave's issue priority
+    // therefore rises with the work it has left (in chunks), which keeps the pair in step.
+    auto fair_prio = [](int left) {
+        if (left > 12) __builtin_amdgcn_s_setprio(3);
+        else if (left > 6) __builtin_amdgcn_s_setprio(2);
+        else if (left > 3) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+    };
     if (wave < nchunks) {
         const int rounds = (nchunks - wave + WAVES - 1) / WAVES;   // chunks of this wave, >= 1
         int c = wave, r = 0;
@@ -484,6 +493,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             // the next chunk's scores go to the matrix core before this chunk's vector work
             f32x16 kacc = kscore(buf[0]);
             for (; r + DEPTH <= rounds; r += DEPTH) {
+                fair_prio(rounds - r);
 #pragma unroll
                 for (int i = 0; i < DEPTH; ++i) {
                     const f32x16 knext = kscore(buf[(i + 1) % DEPTH]);
@@ -504,6 +514,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             }
         } else {
             for (; r + DEPTH <= rounds; r += DEPTH) {
+                fair_prio(rounds - r);
 #pragma unroll
                 for (int i = 0; i < DEPTH; ++i) {
                     compute(c, buf[i]);
