@@ -134,6 +134,22 @@ lla_status lla_decode_attn(const lla_codec *codec, const lla_params *params,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Absorbed-attention decode (the form the editorial letter on the pith.science paper page for
+ * "Looped Latent Attention" discusses): the same result as lla_decode_attn up to rounding, computed
+ * in the latent space.  q~ = W_up,t^K q once per sequence and head; s_j = scale (<q~, c_k(j)> +
+ * <q, mu_t^K>); c~ = sum_j softmax(s)_j c_v(j); out = c~ W_up,t^V + mu_t^V (plus the self term).
+ * It is exact only while nothing acts between expansion and attention (no rotation); the per-token
+ * work is r_k + r_v multiply-adds per head instead of the d x (r_k + r_v) of the expansion.
+ * Arguments, layouts, plan and workspace (lla_decode_plan) are those of lla_decode_attn; bf16
+ * codecs only (LLA_ERR_DTYPE otherwise), with the same supported (d_head, r_k, r_v).
+ */
+lla_status lla_decode_attn_absorbed(const lla_codec *codec, const lla_params *params,
+                                    const lla_cache *cache, int32_t t, const void *q,
+                                    const void *k_self, const void *v_self, int64_t self_stride,
+                                    float scale, void *out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
  * Encode and append (pith.science paper page, "What carries the argument": the T per-loop vectors
  * are stacked and centred, c = (x - mu) W_down).  For every sequence b, group g and axis:
  *   c = (stack_g(x[b]) - mu[g]) W_down[g],  accumulated in fp32,

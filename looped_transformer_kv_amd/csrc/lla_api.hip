@@ -143,10 +143,17 @@ lla_status lla_decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) 
     return decode_plan(c, k, p);
 }
 
-lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_cache *k,
-                           int32_t t, const void *q, const void *k_self, const void *v_self,
-                           int64_t self_stride, float scale, void *out, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel arguments shared by the two latent decode entry points.  `absorbed`
+// restricts to bf16 (the absorbed kernel has no fp32 variant).
+lla_status prepare_decode(const lla_codec *c, const lla_params *prm, const lla_cache *k, int32_t t,
+                          const void *q, const void *k_self, const void *v_self,
+                          int64_t self_stride, float scale, void *out, void *workspace,
+                          size_t workspace_bytes, bool absorbed, DecodeArgs *args,
+                          lla_plan *plan) {
     lla_status st = check_codec(c);
     if (st != LLA_OK) return st;
     if (!prm || !prm->W_up_k || !prm->W_up_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
@@ -154,6 +161,7 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     if (!q || !out || (k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_NULL;
     if (t < 0 || t >= c->T || self_stride < 0) return LLA_ERR_SHAPE;
     const bool bf16 = c->dtype == LLA_BF16;
+    if (absorbed && !bf16) return LLA_ERR_DTYPE;
     if (bf16) {
         if (!decode_bf16_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
         if (k->page_size % 32 != 0) return LLA_ERR_SHAPE;
@@ -162,13 +170,12 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     } else if (decode_f32_lds_bytes(c->d_head, c->r_k, c->r_v) > kMaxDynLds) {
         return LLA_ERR_UNSUPPORTED;
     }
-    lla_plan plan;
-    decode_plan(c, k, &plan);
-    if ((st = check_workspace(plan, workspace, workspace_bytes)) != LLA_OK) return st;
-    if (k->batch == 0) return LLA_OK;
+    decode_plan(c, k, plan);
+    if ((st = check_workspace(*plan, workspace, workspace_bytes)) != LLA_OK) return st;
 
     const Shape sh = shape_of(c);
-    DecodeArgs a{};
+    DecodeArgs &a = *args;
+    a = DecodeArgs{};
     a.k_pool = k->k_pool;
     a.v_pool = k->v_pool;
     a.block_table = k->block_table;
@@ -195,17 +202,51 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     a.max_pages = k->max_pages;
     a.n_pages = k->n_pages;
     a.max_seq_len = k->max_seq_len;
-    a.S = plan.splits;
-    a.tokens_per_split = plan.tokens_per_split;
+    a.S = plan->splits;
+    a.tokens_per_split = plan->tokens_per_split;
     a.mode = c->mode;
     a.scale_log2 = scale * kLog2e;
+    return LLA_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                           int32_t t, const void *q, const void *k_self, const void *v_self,
+                           int64_t self_stride, float scale, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    DecodeArgs a;
+    lla_plan plan;
+    lla_status st = prepare_decode(c, prm, k, t, q, k_self, v_self, self_stride, scale, out,
+                                   workspace, workspace_bytes, false, &a, &plan);
+    if (st != LLA_OK) return st;
+    if (k->batch == 0) return LLA_OK;
+    const bool bf16 = c->dtype == LLA_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = bf16 ? launch_decode_bf16(a, plan.waves_per_block, s) : launch_decode_f32(a, s);
     if (e != hipSuccess) return LLA_ERR_HIP;
     if (bf16 && plan.splits == 1) return LLA_OK;   // the latent kernel finished the output itself
     e = launch_combine(a, c->d_head, bf16, true, s);
     return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+lla_status lla_decode_attn_absorbed(const lla_codec *c, const lla_params *prm,
+                                    const lla_cache *k, int32_t t, const void *q,
+                                    const void *k_self, const void *v_self, int64_t self_stride,
+                                    float scale, void *out, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    DecodeArgs a;
+    lla_plan plan;
+    lla_status st = prepare_decode(c, prm, k, t, q, k_self, v_self, self_stride, scale, out,
+                                   workspace, workspace_bytes, true, &a, &plan);
+    if (st != LLA_OK) return st;
+    if (k->batch == 0) return LLA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_decode_absorbed(a, s) != hipSuccess) return LLA_ERR_HIP;
+    if (plan.splits == 1) return LLA_OK;
+    return launch_combine(a, c->d_head, true, true, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
 lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const lla_cache *k,

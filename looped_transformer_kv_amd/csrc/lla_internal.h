@@ -56,6 +56,7 @@ struct EncodeArgs {
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
 hipError_t launch_decode_bf16(const DecodeArgs &a, int waves, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_absorbed(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t s);
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, hipStream_t s);

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4 *__re
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st) {
     const size_t n = bytes / 16;
     const size_t tiles = (n + (size_t)kThreads * kUnroll - 1) / ((size_t)kThreads * kUnroll);
-    const unsigned blocks = (unsigned)(tiles < 2048 ? (tiles ? tiles : 1) : 2048);
+    const unsigned blocks = (unsigned)(tiles < 512 ? (tiles ? tiles : 1) : 512);   // 2 per CU
     hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kThreads), 0, st,
                        static_cast<const uint4 *>(buf), n, sink);
     return hipGetLastError();

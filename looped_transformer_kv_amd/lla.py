@@ -73,6 +73,9 @@ def lib():
         L.lla_decode_attn.restype = i32
         L.lla_decode_attn.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp, vp, vp,
                                       i64, f32, vp, vp, sz, vp]
+        L.lla_decode_attn_absorbed.restype = i32
+        L.lla_decode_attn_absorbed.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp,
+                                               vp, vp, i64, f32, vp, vp, sz, vp]
         L.lla_encode_append.restype = i32
         L.lla_encode_append.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), vp, vp, vp, vp,
                                         vp, vp]
@@ -168,6 +171,17 @@ def lla_decode_attn(codec, params, cache, t, q, k_self, v_self, self_stride, sca
                                float(scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
                                _stream(stream))
     return _check("lla_decode_attn", st, check)
+
+
+def lla_decode_attn_absorbed(codec, params, cache, t, q, k_self, v_self, self_stride, scale, out,
+                             workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lla_decode_attn_absorbed(ctypes.byref(codec), ctypes.byref(params),
+                                        ctypes.byref(cache), int(t), _ptr(q), _ptr(k_self),
+                                        _ptr(v_self), int(self_stride), float(scale), _ptr(out),
+                                        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _check("lla_decode_attn_absorbed", st, check)
 
 
 def lla_encode_append(codec, params, cache, x_k, x_v, write_pos, c_k_out=None, c_v_out=None,

@@ -50,6 +50,15 @@ class LatentLayer:
         return lla.lla_decode_attn(self.codec, self.params, self.cache, t, q, k_self, v_self,
                                    self_stride, scale, out, workspace, stream=stream, check=check)
 
+    def decode_absorbed(self, t, q, out, workspace, k_self=None, v_self=None, self_stride=0,
+                        scale=None, stream=None, check=True):
+        """The same attention in the latent space (lla_decode_attn_absorbed); same workspace."""
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.codec.d_head)
+        return lla.lla_decode_attn_absorbed(self.codec, self.params, self.cache, t, q, k_self,
+                                            v_self, self_stride, scale, out, workspace,
+                                            stream=stream, check=check)
+
     def encode_append(self, x_k, x_v, write_pos, c_k_out=None, c_v_out=None, stream=None,
                       check=True):
         return lla.lla_encode_append(self.codec, self.params, self.cache, x_k, x_v, write_pos,

@@ -42,7 +42,7 @@ class DeviceProblem:
                                  self.block_table, self.seq_lens, c.page, p.max_seq_len)
         self.device = device
 
-    def decode(self, t, with_self=True, q=None):
+    def decode(self, t, with_self=True, q=None, absorbed=False):
         c = self.p.cfg
         q = self.q[t] if q is None else q
         out = torch.full((self.p.B, c.H, c.d), float("nan"), dtype=TORCH_DT[c.dtype],
@@ -51,7 +51,8 @@ class DeviceProblem:
         ks = self.x_k[:, t] if with_self else None
         vs = self.x_v[:, t] if with_self else None
         stride = c.T * c.H * c.d if with_self else 0
-        self.layer.decode(t, q, out, ws, ks, vs, stride)
+        run = self.layer.decode_absorbed if absorbed else self.layer.decode
+        run(t, q, out, ws, ks, vs, stride)
         torch.cuda.synchronize()
         return synth.from_device(out)
 

@@ -140,3 +140,20 @@ def test_stream_read_validation_without_launch():
     assert L.lla_stream_read(FAKE, 16, FAKE + 2, None) == lla.LLA_ERR_ALIGN
     assert L.lla_stream_read(FAKE, 24, FAKE, None) == lla.LLA_ERR_SHAPE
     assert L.lla_stream_read(FAKE, 0, FAKE, None) == lla.LLA_OK        # nothing to read
+
+
+def test_absorbed_validation_without_launch():
+    _no_gpu()
+    c = synth.CONFIGS["ouro14_21x"]
+    L = lla.lib()
+    params = lla.lla_params(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4096)
+
+    def call(codec, ws=None, wsb=0):
+        return L.lla_decode_attn_absorbed(ctypes.byref(codec), ctypes.byref(params),
+                                          ctypes.byref(cache), 0, FAKE, None, None, 0, 0.1, FAKE,
+                                          ws, wsb, None)
+    # fp32 codecs have no absorbed kernel; the rest validates like lla_decode_attn
+    assert call(lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_F32)) == lla.LLA_ERR_DTYPE
+    assert call(lla.make_codec(0, 4, 16, 128, 8, 32, lla.LLA_BF16)) == lla.LLA_ERR_UNSUPPORTED
+    assert call(_codec(c)) == lla.LLA_ERR_WORKSPACE

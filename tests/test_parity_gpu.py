@@ -307,3 +307,66 @@ def test_stream_read_reads_every_word(gpu, nbytes):
     torch.cuda.synchronize()
     expect = np.bitwise_xor.reduce(host)
     assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(expect)
+
+
+# ------------------------------------------------------------------ absorbed-attention decode
+@pytest.mark.parametrize("variant", ["plain", "ragged", "peaked", "noself"])
+@pytest.mark.parametrize("name", BF16_CFGS)
+def test_absorbed_decode_small(gpu, name, variant):
+    """lla_decode_attn_absorbed against the oracle's explicit reconstruction (exact up to rounding
+    without a rotation; the oracle pin P5 checks the identity itself)."""
+    cfg, B, N = _small(name)
+    lens = None
+    if variant == "ragged":
+        lens = synth.seq_lens(cfg, B, N, ragged=True, salt=3)
+        lens[0], lens[1] = 0, 1
+    p = tinycase.make(cfg, B=B, N=N, lens=lens, q_gain=8.0 if variant == "peaked" else 1.0,
+                      loud_tokens=3 if variant == "peaked" else 0)
+    dp = gpucase.DeviceProblem(p)
+    with_self = variant != "noself"
+    for t in sorted({0, cfg.T - 1}):
+        say(f"absorbed {name}/{variant} B={B} lens={list(p.seq_lens)} t={t}")
+        got = dp.decode(t, with_self, absorbed=True)
+        assert_close(got, dp.oracle_decode(t, with_self), "bf16", f"absorbed {name}/{variant} t={t}")
+
+
+def test_absorbed_split_context_and_empty(gpu):
+    """A single long sequence (the plan splits the context; partials go through combine) and an
+    all-empty batch without self term (zeros)."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    p = tinycase.make(cfg, B=1, N=1500, ragged=False)
+    dp = gpucase.DeviceProblem(p)
+    assert dp.layer.plan.splits > 1
+    say(f"absorbed split context splits={dp.layer.plan.splits}")
+    assert_close(dp.decode(1, True, absorbed=True), dp.oracle_decode(1, True), "bf16",
+                 "absorbed split")
+    p = tinycase.make(cfg, B=2, N=64, lens=np.zeros(2, np.int32))
+    dp = gpucase.DeviceProblem(p)
+    say("absorbed empty context")
+    assert np.all(dp.decode(0, with_self=False, absorbed=True) == 0.0)
+
+
+def test_absorbed_matches_reconstructing_kernel_full_size(gpu):
+    """Headline shape at full size: the absorbed kernel agrees with the oracle on sampled
+    sequences, and with the reconstructing kernel everywhere within the same bar."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    layer, host = _full_layer(cfg, gpu)
+    sel = [0, cfg.B // 2, cfg.B - 1]
+    xk = synth.staging(cfg, 0, synth.AX_K, cfg.B)
+    xv = synth.staging(cfg, 0, synth.AX_V, cfg.B)
+    xkd, xvd = synth.to_device(xk, "bf16", gpu), synth.to_device(xv, "bf16", gpu)
+    ws = layer.workspace(gpu)
+    t = cfg.T - 1
+    q = synth.queries(cfg, 0, t, cfg.B)
+    qd = synth.to_device(q, "bf16", gpu)
+    outs = []
+    for absorbed in (False, True):
+        out = torch.empty((cfg.B, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
+        run = layer.decode_absorbed if absorbed else layer.decode
+        say(f"full size absorbed={absorbed}")
+        run(t, qd, out, ws, xkd[:, t], xvd[:, t], cfg.T * cfg.H * cfg.d)
+        torch.cuda.synchronize()
+        outs.append(synth.from_device(out))
+    ref = _sampled_oracle(cfg, layer, host, sel, t, q, xk[:, t], xv[:, t])
+    assert_close(outs[1][sel], ref, "bf16", "absorbed full size vs oracle")
+    assert_close(outs[1], outs[0], "bf16", "absorbed vs reconstructing kernel")
