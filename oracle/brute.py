@@ -56,3 +56,33 @@ def decode(mode, T, H, d, t, W_up_k, W_up_v, mu_k, mu_v, ck, cv, lens, q, k_self
     K = reconstruct(t, ck, W_up_k, mu_k, T).reshape(B, N, H, d)
     V = reconstruct(t, cv, W_up_v, mu_v, T).reshape(B, N, H, d)
     return attention(q, K, V, lens, k_self, v_self, scale)
+
+
+def rotation_matrix(d, rot_dims, style, theta, pos):
+    """The d x d rotary matrix of position pos (RoFormer's rotation, cited by the pages), built
+    as a block matrix: the identity with a 2 x 2 rotation block [[cos, -sin], [sin, cos]] placed
+    on each rotated pair of coordinates; y = R x."""
+    R = np.eye(d)
+    half = rot_dims // 2
+    for m in range(half):
+        ang = pos * theta ** (-2.0 * m / rot_dims)
+        a, b = (m, m + half) if style == 0 else (2 * m, 2 * m + 1)
+        R[a, a], R[a, b] = np.cos(ang), -np.sin(ang)
+        R[b, a], R[b, b] = np.sin(ang), np.cos(ang)
+    return R
+
+
+def decode_rope(mode, T, H, d, t, W_up_k, W_up_v, mu_k, mu_v, ck, cv, lens, q, k_self=None,
+                v_self=None, scale=None, theta=10000.0, rot_dims=None, style=0):
+    """decode() with each cached key rotated to its position j and the self key to lens[b]."""
+    if rot_dims is None:
+        rot_dims = d
+    B, N = ck.shape[:2]
+    K = reconstruct(t, ck, W_up_k, mu_k, T).reshape(B, N, H, d)
+    V = reconstruct(t, cv, W_up_v, mu_v, T).reshape(B, N, H, d)
+    Rj = np.stack([rotation_matrix(d, rot_dims, style, theta, j) for j in range(N)])  # [N][d][d]
+    K = np.einsum("nij,bnhj->bnhi", Rj, K)
+    if k_self is not None:
+        Rs = np.stack([rotation_matrix(d, rot_dims, style, theta, n) for n in lens])   # [B][d][d]
+        k_self = np.einsum("bij,bhj->bhi", Rs, k_self)
+    return attention(q, K, V, lens, k_self, v_self, scale)

@@ -181,6 +181,142 @@ int oracle_decode(int mode, int T, int H, int d, int r_k, int r_v, int t,
 }
 
 /*
+ * Rotary position embedding (the rotation of RoFormer, which the pages cite; their free-parameter
+ * ledger records the assumption that a token keeps one position at every recurrence step, so the
+ * rotation can be applied after reconstruction to the pre-rotation K the codec stores).
+ * Rotates the first rot_dims entries of x (length >= rot_dims, rot_dims even) to position pos:
+ * pair m (0 <= m < rot_dims/2) has frequency f_m = theta^(-2m/rot_dims) and angle a = pos f_m,
+ *   style 0 (half split):  pair (m, m + rot_dims/2)
+ *   style 1 (interleaved): pair (2m, 2m + 1)
+ * and (x_a, x_b) -> (x_a cos a - x_b sin a, x_a sin a + x_b cos a).  Entries past rot_dims are
+ * left unchanged.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_rope_rotate(double *x, int rot_dims, int style, double theta, double pos) {
+    if (rot_dims < 0 || (rot_dims & 1) || theta <= 0.0 || (style != 0 && style != 1)) return -1;
+    const int half = rot_dims / 2;
+    for (int m = 0; m < half; ++m) {
+        const double f = pow(theta, -2.0 * m / (double)rot_dims);
+        const double a = pos * f;
+        const double c = cos(a), s = sin(a);
+        const int ia = style == 0 ? m : 2 * m;
+        const int ib = style == 0 ? m + half : 2 * m + 1;
+        const double xa = x[ia], xb = x[ib];
+        x[ia] = xa * c - xb * s;
+        x[ib] = xa * s + xb * c;
+    }
+    return 0;
+}
+
+/*
+ * Decode attention for loop t with the rotation applied after reconstruction: every cached
+ * token j's K_hat_t(j) (mu_t included) is rotated to position j, the current token's own key
+ * k_self to position seq_lens[b] (its position in the sequence); q is taken as given (already
+ * rotated by the caller to that same position); V is not rotated.  Otherwise identical to
+ * oracle_decode (explicit reconstruction, two-pass softmax, same self-term convention).
+ * rot_dims in [0, d] and even; rot_dims = 0 reproduces oracle_decode exactly.
+ */
+int oracle_decode_rope(int mode, int T, int H, int d, int r_k, int r_v, int t,
+                       const double *W_up_k, const double *W_up_v,
+                       const double *mu_k, const double *mu_v,
+                       const double *k_pool, const double *v_pool,
+                       const int32_t *block_table, const int32_t *seq_lens,
+                       int B, int P, int max_pages,
+                       const double *q, const double *k_self, const double *v_self,
+                       long self_stride, double scale, double theta, int rot_dims, int style,
+                       double *out) {
+    if (t < 0 || t >= T || (k_self == NULL) != (v_self == NULL)) return -1;
+    if (rot_dims < 0 || rot_dims > d || (rot_dims & 1) || theta <= 0.0 ||
+        (style != 0 && style != 1))
+        return -1;
+    const int G = (mode == 1) ? 1 : H;
+    const int Dg = (mode == 1) ? H * d : d;
+    const int hpg = H / G;
+    const size_t X = (size_t)T * Dg;
+    if (self_stride <= 0) self_stride = (long)H * d;
+
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < G; ++g) {
+            const int len = seq_lens[b];
+            const int n_scores = len + (k_self ? 1 : 0);
+            double *xk = (double *)malloc(sizeof(double) * Dg);
+            double *xv = (double *)malloc(sizeof(double) * Dg);
+            double *ks = (double *)malloc(sizeof(double) * d);
+            double *s = (double *)malloc(sizeof(double) * ((size_t)n_scores * hpg + 1));
+            double *acc = (double *)calloc((size_t)hpg * d, sizeof(double));
+            if (!xk || !xv || !ks || !s || !acc) {
+#pragma omp atomic write
+                failed = 1;
+                free(xk); free(xv); free(ks); free(s); free(acc);
+                continue;
+            }
+            const double *Wk = W_up_k + ((size_t)t * G + g) * r_k * Dg;
+            const double *Wv = W_up_v + ((size_t)t * G + g) * r_v * Dg;
+            const double *mk = mu_k + (size_t)g * X + (size_t)t * Dg;
+            const double *mv = mu_v + (size_t)g * X + (size_t)t * Dg;
+
+            for (int j = 0; j < len; ++j) {
+                const double *ck = latent_at(k_pool, block_table, max_pages, G, P, r_k, b, j, g);
+                reconstruct(ck, r_k, Wk, mk, Dg, xk);
+                for (int hl = 0; hl < hpg; ++hl) {
+                    double *kh = xk + (size_t)hl * d;
+                    oracle_rope_rotate(kh, rot_dims, style, theta, (double)j);
+                    const int h = g * hpg + hl;
+                    const double *qh = q + ((size_t)b * H + h) * d;
+                    double dot = 0.0;
+                    for (int i = 0; i < d; ++i) dot += qh[i] * kh[i];
+                    s[(size_t)j * hpg + hl] = scale * dot;
+                }
+            }
+            if (k_self) {
+                for (int hl = 0; hl < hpg; ++hl) {
+                    const int h = g * hpg + hl;
+                    const double *qh = q + ((size_t)b * H + h) * d;
+                    memcpy(ks, k_self + (size_t)b * self_stride + (size_t)h * d,
+                           sizeof(double) * d);
+                    oracle_rope_rotate(ks, rot_dims, style, theta, (double)len);
+                    double dot = 0.0;
+                    for (int i = 0; i < d; ++i) dot += qh[i] * ks[i];
+                    s[(size_t)len * hpg + hl] = scale * dot;
+                }
+            }
+            for (int hl = 0; hl < hpg; ++hl) {
+                double m = -INFINITY, Z = 0.0;
+                for (int j = 0; j < n_scores; ++j) m = fmax(m, s[(size_t)j * hpg + hl]);
+                for (int j = 0; j < n_scores; ++j) {
+                    double w = exp(s[(size_t)j * hpg + hl] - m);
+                    s[(size_t)j * hpg + hl] = w;
+                    Z += w;
+                }
+                for (int j = 0; j < n_scores; ++j) s[(size_t)j * hpg + hl] /= (Z > 0 ? Z : 1.0);
+            }
+            for (int j = 0; j < len; ++j) {
+                const double *cv = latent_at(v_pool, block_table, max_pages, G, P, r_v, b, j, g);
+                reconstruct(cv, r_v, Wv, mv, Dg, xv);
+                for (int hl = 0; hl < hpg; ++hl)
+                    for (int i = 0; i < d; ++i)
+                        acc[hl * d + i] += s[(size_t)j * hpg + hl] * xv[hl * d + i];
+            }
+            if (v_self) {
+                for (int hl = 0; hl < hpg; ++hl) {
+                    const int h = g * hpg + hl;
+                    const double *vh = v_self + (size_t)b * self_stride + (size_t)h * d;
+                    for (int i = 0; i < d; ++i)
+                        acc[hl * d + i] += s[(size_t)len * hpg + hl] * vh[i];
+                }
+            }
+            for (int hl = 0; hl < hpg; ++hl) {
+                const int h = g * hpg + hl;
+                for (int i = 0; i < d; ++i) out[((size_t)b * H + h) * d + i] = acc[hl * d + i];
+            }
+            free(xk); free(xv); free(ks); free(s); free(acc);
+        }
+    }
+    return failed ? -2 : 0;
+}
+
+/*
  * Encode: c = (x - mu) W_down for one axis (pith.science paper page, "What carries the
  * argument": the T per-loop vectors are stacked and centred, then projected).
  * x is the staging buffer [B][T][H][d].  The stacked vector of group g is

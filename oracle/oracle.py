@@ -30,6 +30,11 @@ def lib():
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_decode.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, ip, ip, i, i, i,
                                     dp, dp, dp, lng, dbl, dp]
+        L.oracle_rope_rotate.restype = ctypes.c_int
+        L.oracle_rope_rotate.argtypes = [dp, i, i, dbl, dbl]
+        L.oracle_decode_rope.restype = ctypes.c_int
+        L.oracle_decode_rope.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, ip, ip, i, i,
+                                         i, dp, dp, dp, lng, dbl, dbl, i, i, dp]
         L.oracle_encode.restype = ctypes.c_int
         L.oracle_encode.argtypes = [i, i, i, i, i, dp, dp, dp, i, dp]
         L.oracle_append.restype = ctypes.c_int
@@ -81,6 +86,39 @@ def decode(mode, T, H, d, r_k, r_v, t, W_up_k, W_up_v, mu_k, mu_v, k_pool, v_poo
                              H * d, float(scale), _p(out))
     if rc != 0:
         raise RuntimeError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def rope_rotate(x, rot_dims, style, theta, pos):
+    """A copy of the vector x with its first rot_dims entries rotated to position pos."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    rc = lib().oracle_rope_rotate(_p(y), int(rot_dims), int(style), float(theta), float(pos))
+    if rc != 0:
+        raise RuntimeError(f"oracle_rope_rotate failed ({rc})")
+    return y
+
+
+def decode_rope(mode, T, H, d, r_k, r_v, t, W_up_k, W_up_v, mu_k, mu_v, k_pool, v_pool,
+                block_table, seq_lens, P, q, k_self=None, v_self=None, scale=None,
+                theta=10000.0, rot_dims=None, style=0):
+    """decode() with the rotation applied after reconstruction: cached K_hat(j) at position j,
+    k_self at position seq_lens[b]; q as given.  rot_dims defaults to d."""
+    block_table = _i32(block_table)
+    seq_lens = _i32(seq_lens)
+    B, max_pages = block_table.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if rot_dims is None:
+        rot_dims = d
+    arrs = [_f64(a) for a in (W_up_k, W_up_v, mu_k, mu_v, k_pool, v_pool, q, k_self, v_self)]
+    out = np.zeros((B, H, d), dtype=np.float64)
+    rc = lib().oracle_decode_rope(mode, T, H, d, r_k, r_v, t, *[_p(a) for a in arrs[:6]],
+                                  _p(block_table, ctypes.c_int32), _p(seq_lens, ctypes.c_int32),
+                                  B, P, max_pages, _p(arrs[6]), _p(arrs[7]), _p(arrs[8]),
+                                  H * d, float(scale), float(theta), int(rot_dims), int(style),
+                                  _p(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_decode_rope failed ({rc})")
     return out
 
 
