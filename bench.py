@@ -239,6 +239,9 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling probe")
     ap.add_argument("--no-absorbed", action="store_true",
                     help="skip timing the absorbed-attention decode (lla_decode_attn_absorbed)")
+    ap.add_argument("--no-rope", action="store_true",
+                    help="skip timing the decode with rotation after reconstruction "
+                         "(lla_decode_attn_rope, theta 10^4, whole-head half-split pairs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -393,39 +396,49 @@ def main():
         "encode_bytes_per_call": enc_bytes,
         "encode_GBps": round(enc_bytes / (enc_us * 1e-6) / 1e9, 1),
     }
-    if not args.no_absorbed:
-        log("timing the absorbed-attention decode")
-
-        def absorbed_all():
+    def time_variant(run_one):
+        """Per-call time of `run_one(t, l)` over the whole step (T x L calls), graph-launched
+        like the main decode."""
+        def all_calls():
             for t in range(T):
                 for l in range(L):
-                    layers[l].decode_absorbed(t, q[t][l], out, ws, xk[l][:, t], xv[l][:, t],
-                                              stride)
-
-        absorbed_all()
+                    run_one(t, l)
+        all_calls()
         torch.cuda.synchronize()
-        run_abs = absorbed_all
+        run = all_calls
         if launch == "hip_graph":
-            g_abs = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_abs):
-                absorbed_all()
-            run_abs = g_abs.replay
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                all_calls()
+            run = g.replay
         for _ in range(args.warmup):
-            run_abs()
+            run()
         torch.cuda.synchronize()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record()
         for _ in range(K):
-            run_abs()
+            run()
         a1.record()
         torch.cuda.synchronize()
-        abs_us = a0.elapsed_time(a1) * 1e3 / (K * T * L)
-        abs_gbs = latent_bytes / (abs_us * 1e-6) / 1e9
-        result["absorbed"] = {
-            "kernel": "lla_decode_attn_absorbed", "us_per_call": round(abs_us, 3),
-            "latent_GBps": round(abs_gbs, 1), "frac_of_hbm_peak": round(abs_gbs / HBM_PEAK_GBS, 4),
-            "frac_of_read_ceiling": round(abs_gbs / ceiling["GBps"], 4) if ceiling else None,
-            "token_loops_per_s_per_call": round(B * N / (abs_us * 1e-6), 1)}
+        us = a0.elapsed_time(a1) * 1e3 / (K * T * L)
+        gbs = latent_bytes / (us * 1e-6) / 1e9
+        return {"us_per_call": round(us, 3), "latent_GBps": round(gbs, 1),
+                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "frac_of_read_ceiling": round(gbs / ceiling["GBps"], 4) if ceiling else None,
+                "token_loops_per_s_per_call": round(B * N / (us * 1e-6), 1)}
+
+    if not args.no_absorbed:
+        log("timing the absorbed-attention decode")
+        result["absorbed"] = {"kernel": "lla_decode_attn_absorbed", **time_variant(
+            lambda t, l: layers[l].decode_absorbed(t, q[t][l], out, ws, xk[l][:, t], xv[l][:, t],
+                                                   stride))}
+    if not args.no_rope:
+        log("timing the decode with rotation after reconstruction")
+        rope = lla.lla_rope(10000.0, d, 0)
+        result["rope"] = {"kernel": "lla_decode_attn_rope", "theta": 10000.0, "rot_dims": d,
+                          "style": "half_split", **time_variant(
+            lambda t, l: layers[l].decode_rope(t, rope, q[t][l], out, ws, xk[l][:, t],
+                                               xv[l][:, t], stride))}
     if not args.no_flat:
         log("timing the flat comparator")
         result["flat_ref"] = flat_comparator(cfg, dev, max(5, K))

@@ -133,6 +133,29 @@ lla_status lla_decode_attn(const lla_codec *codec, const lla_params *params,
                            const void *v_self, int64_t self_stride, float scale, void *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Rotary position embedding applied after reconstruction (see lla_decode_attn_rope). */
+typedef struct {
+    float theta;       /* base: pair m of the d head dims turns by pos * theta^(-2m/d); > 1 */
+    int32_t rot_dims;  /* rotated head dims; must equal d_head (whole-head rotation) */
+    int32_t style;     /* 0: pairs (m, m + d/2) (half split); 1: pairs (2m, 2m + 1) (interleaved) */
+} lla_rope;
+
+/*
+ * Decode attention with the rotation applied after reconstruction (the "full-RoPE" read path the
+ * pages' free-parameter ledger describes: a token keeps one position at every recurrence step,
+ * so each reconstructed pre-rotation key K_hat_t(j) = c_k(j) W_up,t^K + mu_t^K is rotated to its
+ * position j; the rotation is RoFormer's, which the pages cite).  The current token's own key
+ * k_self is rotated to its position seq_lens[b]; q is taken as given (the caller rotates it to
+ * that same position); values are not rotated.  Otherwise as lla_decode_attn (same plan and
+ * workspace).  bf16 codecs only (LLA_ERR_DTYPE); rope NULL -> LLA_ERR_NULL; theta <= 1 or a
+ * style other than 0/1 -> LLA_ERR_SHAPE; rot_dims != d_head -> LLA_ERR_UNSUPPORTED.
+ */
+lla_status lla_decode_attn_rope(const lla_codec *codec, const lla_params *params,
+                                const lla_cache *cache, int32_t t, const lla_rope *rope,
+                                const void *q, const void *k_self, const void *v_self,
+                                int64_t self_stride, float scale, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /*
  * Absorbed-attention decode (the form the editorial letter on the pith.science paper page for
  * "Looped Latent Attention" discusses): the same result as lla_decode_attn up to rounding, computed

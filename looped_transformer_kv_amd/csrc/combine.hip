@@ -15,7 +15,7 @@ namespace lla {
 namespace {
 
 template <int D, typename TS>
-__global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a, int has_mu) {
+__global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a, int has_mu, int self_in_record) {
     __shared__ float red[D / 64 + 1];
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh % a.H;
@@ -27,7 +27,12 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a, int has_mu) {
 
     const bool has_self = a.k_self != nullptr;
     float s_self = -INFINITY, v_self = 0.f;
-    if (has_self) {
+    if (has_self && self_in_record) {
+        s_self = rec0[D + 2];
+        v_self = ld_elt<TS>(static_cast<const TS *>(a.v_self) + (size_t)b * a.self_stride +
+                            (size_t)h * D + i);
+        M = fmaxf(M, s_self);
+    } else if (has_self) {
         const TS *qp = static_cast<const TS *>(a.q) + ((size_t)b * a.H + h) * D;
         const TS *ks = static_cast<const TS *>(a.k_self) + (size_t)b * a.self_stride +
                        (size_t)h * D;
@@ -67,19 +72,20 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a, int has_mu) {
 
 }  // namespace
 
-hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, hipStream_t st) {
+hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, bool self_in_record,
+                          hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H;
-    const int hm = has_mu ? 1 : 0;
+    const int hm = has_mu ? 1 : 0, sr = self_in_record ? 1 : 0;
     if (d == 128) {
         if (bf16)
-            hipLaunchKernelGGL((combine_kernel<128, uint16_t>), dim3(blocks), dim3(128), 0, st, a, hm);
+            hipLaunchKernelGGL((combine_kernel<128, uint16_t>), dim3(blocks), dim3(128), 0, st, a, hm, sr);
         else
-            hipLaunchKernelGGL((combine_kernel<128, float>), dim3(blocks), dim3(128), 0, st, a, hm);
+            hipLaunchKernelGGL((combine_kernel<128, float>), dim3(blocks), dim3(128), 0, st, a, hm, sr);
     } else if (d == 64) {
         if (bf16)
-            hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(blocks), dim3(64), 0, st, a, hm);
+            hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(blocks), dim3(64), 0, st, a, hm, sr);
         else
-            hipLaunchKernelGGL((combine_kernel<64, float>), dim3(blocks), dim3(64), 0, st, a, hm);
+            hipLaunchKernelGGL((combine_kernel<64, float>), dim3(blocks), dim3(64), 0, st, a, hm, sr);
     } else {
         return hipErrorInvalidValue;
     }

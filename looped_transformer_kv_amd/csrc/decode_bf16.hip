@@ -70,7 +70,7 @@ struct Chunk {
     uint4 k[KK], v[KV];
 };
 
-template <int D, int RK, int RV>
+template <int D, int RK, int RV, bool ROPE>
 struct Shape {
     static constexpr int MT = D / 32;                  // 32-column tiles over the head dim
     static constexpr int KK = RK / 16, KV = RV / 16;   // MFMA k-steps over the latent ranks
@@ -78,18 +78,24 @@ struct Shape {
     // weight on the value latents) and V_hat accumulates in the matrix-core accumulators across
     // chunks; W_up operands live in registers.  Larger ranks: W_up operands from LDS, explicit
     // per-chunk V_hat tiles, query and output in VALU registers.
-    static constexpr bool FUSED = KK <= 2 && KV <= 2;
+    static constexpr bool FUSED = !ROPE && KK <= 2 && KV <= 2;
     static constexpr int WAVES = 4;
-    static constexpr int DEPTH = KK + KV <= 3 ? 3 : (KK + KV <= 4 ? 2 : 1);   // chunks in flight per wave
+    static constexpr int DEPTH =
+        ROPE ? 1 : (KK + KV <= 3 ? 3 : (KK + KV <= 4 ? 2 : 1));   // chunks in flight per wave
 };
 
-template <int D, int RK, int RV>
-constexpr int kThreads = 64 * Shape<D, RK, RV>::WAVES;
+template <int D, int RK, int RV, bool ROPE>
+constexpr int kThreads = 64 * Shape<D, RK, RV, ROPE>::WAVES;
 
-template <int D, int RK, int RV>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, kThreads<D, RK, RV>)))
+// ROPE: the rotation follows reconstruction (lla_decode_attn_rope).  Every K_hat tile (mu_t
+// included, through one more MFMA of the mu row against a row of ones) is rotated in registers
+// to its token's position before the dot with q: with the rotation over all d head dims, every
+// pair of a tile element is held by the same lane (half split: the same register of the tile
+// d/2 ahead; interleaved: the neighbouring register).  The explicit path always runs.
+template <int D, int RK, int RV, bool ROPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, kThreads<D, RK, RV, ROPE>)))
 void decode_bf16_kernel(DecodeArgs a) {
-    using SH = Shape<D, RK, RV>;
+    using SH = Shape<D, RK, RV, ROPE>;
     constexpr int MT = SH::MT, KK = SH::KK, KV = SH::KV, WAVES = SH::WAVES;
     constexpr bool FUSED = SH::FUSED;
     constexpr int RKP = RK + 8, RVP = RV + 8;   // padded LDS rows (keeps 16-byte alignment)
@@ -225,31 +231,39 @@ void decode_bf16_kernel(DecodeArgs a) {
                           (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
     const bool has_self = a.k_self != nullptr;
     const bool self_here = S == 1 && has_self;
+    const bool self_score = has_self && (S == 1 || ROPE);   // ROPE: stored for the combine
     const uint16_t *muvp = static_cast<const uint16_t *>(a.mu_v) +
                            (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
     // without a self term these read q / mu_v instead and the values are dropped
-    const uint16_t *ksp = self_here ? static_cast<const uint16_t *>(a.k_self) +
-                                          (size_t)b * a.self_stride + (size_t)h * D
-                                    : qp;
+    const uint16_t *ksp = self_score ? static_cast<const uint16_t *>(a.k_self) +
+                                           (size_t)b * a.self_stride + (size_t)h * D
+                                     : qp;
     const uint16_t *vsp = self_here ? static_cast<const uint16_t *>(a.v_self) +
                                           (size_t)b * a.self_stride + (size_t)h * D
                                     : muvp;
-    uint16_t qv[UD], mkv[UD], ksv[UD];
+    // ROPE: the rotation partner of element i (half split: i +- d/2, interleaved: i ^ 1)
+    auto partner = [&](int i) {
+        return a.rope_style ? (i ^ 1) : (i < D / 2 ? i + D / 2 : i - D / 2);
+    };
+    uint16_t qv[UD], mkv[UD], ksv[UD], kpv[ROPE ? UD : 1];
 #pragma unroll
     for (int u = 0; u < UD; ++u) {
         const int i = lane + 64 * u;
         qv[u] = qp[i];
         mkv[u] = muk[i];
         ksv[u] = ksp[i];
+        if constexpr (ROPE) kpv[u] = ksp[partner(i)];
     }
     // element tid of the output (threads tid < D use them)
     const uint16_t vs_raw = vsp[tid % D], muv_raw = muvp[tid % D];
     // fused path: q_i for this lane's columns i = 32M + l32; explicit path: q rows
     // 32M + 8bb + 4h2 + 0..3 of the K tile
     uint16_t qcol[FUSED ? MT : 1];
+    uint16_t mucol[ROPE ? MT : 1];   // ROPE: mu_t^K of this lane's K_hat tile rows 32M + l32
     uint2 qrow[FUSED ? 1 : MT][4];
 #pragma unroll
     for (int M = 0; M < MT; ++M) {
+        if constexpr (ROPE) mucol[M] = muk[32 * M + l32];
         if constexpr (FUSED) {
             qcol[M] = qp[32 * M + l32];
         } else {
@@ -297,16 +311,33 @@ void decode_bf16_kernel(DecodeArgs a) {
             }
         }
     }
+    // ROPE: revolutions per position of pair m, theta^(-2m/d) / (2 pi); the angle pos * f is
+    // reduced to [0, 1) revolutions before the hardware sine / cosine
+    auto rope_rev = [&](int m) {
+        return exp2_(-2.0f * (float)m / (float)D * a.rope_log2_theta) * 0.15915494309189535f;
+    };
     float qm, s_self = -INFINITY;   // log2-scaled
     {
         float am = 0.f, as = 0.f;
 #pragma unroll
         for (int u = 0; u < UD; ++u) {
             am += bf2f(qv[u]) * bf2f(mkv[u]);
-            as += bf2f(qv[u]) * bf2f(ksv[u]);
+            float kk = bf2f(ksv[u]);
+            if constexpr (ROPE) {
+                // the current token's key turns to its position, seq_lens[b]
+                const int i = lane + 64 * u;
+                const bool first = a.rope_style ? !(i & 1) : i < D / 2;
+                const int m = a.rope_style ? i >> 1 : (first ? i : i - D / 2);
+                const float rev = __builtin_amdgcn_fractf((float)len * rope_rev(m));
+                const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                const float kp = bf2f(kpv[u]);
+                kk = first ? kk * cs - kp * sn : kp * sn + kk * cs;
+            }
+            as += bf2f(qv[u]) * kk;
         }
-        qm = wave_sum(am) * a.scale_log2;
-        if (self_here) s_self = wave_sum(as) * a.scale_log2;
+        // ROPE: mu_t^K is part of the rotated key, so it is not a constant of the scores
+        qm = ROPE ? 0.f : wave_sum(am) * a.scale_log2;
+        if (self_score) s_self = wave_sum(as) * a.scale_log2;
     }
     float qs[FUSED ? 1 : MT][16];
     if constexpr (!FUSED) {
@@ -349,6 +380,24 @@ void decode_bf16_kernel(DecodeArgs a) {
         for (int N = 0; N < MT; ++N)
 #pragma unroll
             for (int ks = 0; ks < KV; ++ks) wvr[N * KV + ks] = pack8(wvraw[N * KV + ks]);
+    }
+    // ROPE operands: the mu k-step (A: mu_t^K of row l32 in k-slot 0; B: ones in k-slot 0) and
+    // this lane's pair frequencies (rotation slot k: half split rows (k/16, k%16) of the first
+    // half of the tiles; interleaved the even register 2(k%8) of tile k/8)
+    uint4 amu[ROPE ? MT : 1];
+    uint4 bone = make_uint4(0, 0, 0, 0);
+    float fr[ROPE ? MT * 8 : 1];
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int M = 0; M < MT; ++M) amu[M] = make_uint4(h2 == 0 ? (uint32_t)mucol[M] : 0u, 0, 0, 0);
+        bone = make_uint4(h2 == 0 ? 0x3F80u : 0u, 0, 0, 0);   // bf16 1.0
+#pragma unroll
+        for (int k = 0; k < MT * 8; ++k) {
+            const int Ma = a.rope_style ? k / 8 : k / 16;
+            const int va = a.rope_style ? 2 * (k % 8) : k % 16;
+            const int i = 32 * Ma + 8 * (va / 4) + 4 * h2 + (va % 4);
+            fr[k] = rope_rev(a.rope_style ? i >> 1 : i);
+        }
     }
 
     float m_run = -INFINITY, l_lane = 0.f;
@@ -428,14 +477,57 @@ void decode_bf16_kernel(DecodeArgs a) {
         {
             // ---- scores: K_hat tiles (d rows x 32 token columns) dotted with q per lane
             float sp[MT];                           // independent chains, one per tile
+            if constexpr (ROPE) {
+                // token l32 sits at position j_begin + 32c + l32; row i = 32M + 8(v/4) + 4h2 + v%4
+                const float pos = (float)(j_begin + 32 * c + l32);
+                auto turn = [&](int k, float xa, float xb) {   // (xa, xb) turned, as a pair
+                    const float rev = __builtin_amdgcn_fractf(pos * fr[k]);
+                    const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                    return f32x2{xa * cs - xb * sn, xa * sn + xb * cs};
+                };
+                auto khat = [&](int M) {         // mu_t^K rows plus c_k W_up,t^K, tile M
+                    f32x16 t4 = mfma32x32x16(amu[M], bone, f32x16{});
 #pragma unroll
-            for (int M = 0; M < MT; ++M) {
-                f32x16 acc = {};
+                    for (int ks = 0; ks < KK; ++ks) t4 = mfma32x32x16(wk_op(M, ks), x.k[ks], t4);
+                    return t4;
+                };
 #pragma unroll
-                for (int ks = 0; ks < KK; ++ks) acc = mfma32x32x16(wk_op(M, ks), x.k[ks], acc);
-                sp[M] = 0.f;
+                for (int M = 0; M < MT; ++M) sp[M] = 0.f;
+                // the style branch sits outside the unrolled loops, so every register index is a
+                // compile-time constant; tiles are taken a rotation group at a time
+                if (a.rope_style == 0) {          // half split: (M, v) with (M + MT/2, v)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) sp[M] += qs[M][v] * acc[v];
+                    for (int M = 0; M < MT / 2; ++M) {
+                        f32x16 ta = khat(M), tb = khat(M + MT / 2);
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const f32x2 r = turn(16 * M + v, ta[v], tb[v]);
+                            sp[M] += qs[M][v] * r.x;
+                            sp[M + MT / 2] += qs[M + MT / 2][v] * r.y;
+                        }
+                    }
+                } else {                          // interleaved: (M, 2j) with (M, 2j + 1)
+#pragma unroll
+                    for (int M = 0; M < MT; ++M) {
+                        f32x16 t4 = khat(M);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const f32x2 r = turn(8 * M + j, t4[2 * j], t4[2 * j + 1]);
+                            sp[M] += qs[M][2 * j] * r.x + qs[M][2 * j + 1] * r.y;
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int M = 0; M < MT; ++M) {
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int ks = 0; ks < KK; ++ks)
+                        acc = mfma32x32x16(wk_op(M, ks), x.k[ks], acc);
+                    sp[M] = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sp[M] += qs[M][v] * acc[v];
+                }
             }
             float tot = sp[0];
 #pragma unroll
@@ -445,13 +537,16 @@ void decode_bf16_kernel(DecodeArgs a) {
             if (sSlot[c] < 0) sc = __builtin_nanf("");
 
             // ---- V_hat tiles (32 token rows x d columns), issued before the softmax chain
-            f32x16 vacc[MT];
+            // (ROPE: one at a time after it, to keep the rotation's registers free)
+            f32x16 vacc[ROPE ? 1 : MT];
+            if constexpr (!ROPE) {
 #pragma unroll
-            for (int N = 0; N < MT; ++N) {
-                vacc[N] = f32x16{};
+                for (int N = 0; N < MT; ++N) {
+                    vacc[N] = f32x16{};
 #pragma unroll
-                for (int ks = 0; ks < KV; ++ks)
-                    vacc[N] = mfma32x32x16(x.v[ks], wv_op(N, ks), vacc[N]);
+                    for (int ks = 0; ks < KV; ++ks)
+                        vacc[N] = mfma32x32x16(x.v[ks], wv_op(N, ks), vacc[N]);
+                }
             }
             const float p = softmax_step(sc);
 
@@ -466,9 +561,18 @@ void decode_bf16_kernel(DecodeArgs a) {
                 pr[4 * bb + 2] = t4.z; pr[4 * bb + 3] = t4.w;
             }
 #pragma unroll
-            for (int N = 0; N < MT; ++N)
+            for (int N = 0; N < MT; ++N) {
+                if constexpr (ROPE) {
+                    f32x16 vt = {};
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[N][v];
+                    for (int ks = 0; ks < KV; ++ks) vt = mfma32x32x16(x.v[ks], wv_op(N, ks), vt);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[N] += pr[v] * vt[v];
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[N][v];
+                }
+            }
             __builtin_amdgcn_wave_barrier();
         }
     };
@@ -586,23 +690,28 @@ void decode_bf16_kernel(DecodeArgs a) {
             if (tid == 0) {
                 rec[D] = M;
                 rec[D + 1] = L;
+                if (ROPE && s == 0) rec[D + 2] = s_self;   // the rotated self score, for combine
             }
         }
     }
 }
 
 template <int D, int RK, int RV>
-hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
+hipError_t launch_t(const DecodeArgs &a, bool rope, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.S;
-    hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV>), dim3(blocks),
-                       dim3(64 * Shape<D, RK, RV>::WAVES), 0, st, a);
+    if (rope)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, true>), dim3(blocks),
+                           dim3(64 * Shape<D, RK, RV, true>::WAVES), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_bf16_kernel<D, RK, RV, false>), dim3(blocks),
+                           dim3(64 * Shape<D, RK, RV, false>::WAVES), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs &a, hipStream_t st) {
+hipError_t launch_d(const DecodeArgs &a, bool rope, hipStream_t st) {
 #define LLA_CASE(RK, RV) \
-    if (a.r_k == RK && a.r_v == RV) return launch_t<D, RK, RV>(a, st);
+    if (a.r_k == RK && a.r_v == RV) return launch_t<D, RK, RV>(a, rope, st);
     LLA_CASE(16, 16)
     LLA_CASE(16, 32)
     LLA_CASE(32, 32)
@@ -624,11 +733,10 @@ bool decode_bf16_supported(int d, int r_k, int r_v) {
     return false;
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs &a, int waves, hipStream_t st) {
-    (void)waves;
+hipError_t launch_decode_bf16(const DecodeArgs &a, bool rope, hipStream_t st) {
     const int d = a.mode ? a.Dg / a.H : a.Dg;
-    if (d == 128) return launch_d<128>(a, st);
-    if (d == 64) return launch_d<64>(a, st);
+    if (d == 128) return launch_d<128>(a, rope, st);
+    if (d == 64) return launch_d<64>(a, rope, st);
     return hipErrorInvalidValue;
 }
 

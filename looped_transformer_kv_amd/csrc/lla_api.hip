@@ -3,6 +3,8 @@
 #include <cstdint>
 #include <cstdlib>
 
+#include <cmath>
+
 #include "lla_internal.h"
 
 namespace lla {
@@ -147,12 +149,12 @@ lla_status lla_decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) 
 
 namespace {
 
-// Validation and kernel arguments shared by the two latent decode entry points.  `absorbed`
-// restricts to bf16 (the absorbed kernel has no fp32 variant).
+// Validation and kernel arguments shared by the latent decode entry points.  `bf16_only` rejects
+// fp32 codecs (the absorbed and rotary kernels have no fp32 variant).
 lla_status prepare_decode(const lla_codec *c, const lla_params *prm, const lla_cache *k, int32_t t,
                           const void *q, const void *k_self, const void *v_self,
                           int64_t self_stride, float scale, void *out, void *workspace,
-                          size_t workspace_bytes, bool absorbed, DecodeArgs *args,
+                          size_t workspace_bytes, bool bf16_only, DecodeArgs *args,
                           lla_plan *plan) {
     lla_status st = check_codec(c);
     if (st != LLA_OK) return st;
@@ -161,7 +163,7 @@ lla_status prepare_decode(const lla_codec *c, const lla_params *prm, const lla_c
     if (!q || !out || (k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_NULL;
     if (t < 0 || t >= c->T || self_stride < 0) return LLA_ERR_SHAPE;
     const bool bf16 = c->dtype == LLA_BF16;
-    if (absorbed && !bf16) return LLA_ERR_DTYPE;
+    if (bf16_only && !bf16) return LLA_ERR_DTYPE;
     if (bf16) {
         if (!decode_bf16_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
         if (k->page_size % 32 != 0) return LLA_ERR_SHAPE;
@@ -225,11 +227,35 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     if (k->batch == 0) return LLA_OK;
     const bool bf16 = c->dtype == LLA_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = bf16 ? launch_decode_bf16(a, plan.waves_per_block, s) : launch_decode_f32(a, s);
+    hipError_t e = bf16 ? launch_decode_bf16(a, false, s) : launch_decode_f32(a, s);
     if (e != hipSuccess) return LLA_ERR_HIP;
     if (bf16 && plan.splits == 1) return LLA_OK;   // the latent kernel finished the output itself
-    e = launch_combine(a, c->d_head, bf16, true, s);
+    e = launch_combine(a, c->d_head, bf16, true, false, s);
     return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+lla_status lla_decode_attn_rope(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                                int32_t t, const lla_rope *rope, const void *q,
+                                const void *k_self, const void *v_self, int64_t self_stride,
+                                float scale, void *out, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    if (!rope) return LLA_ERR_NULL;
+    DecodeArgs a;
+    lla_plan plan;
+    lla_status st = prepare_decode(c, prm, k, t, q, k_self, v_self, self_stride, scale, out,
+                                   workspace, workspace_bytes, true, &a, &plan);
+    if (st != LLA_OK) return st;
+    if (!(rope->theta > 1.0f) || !std::isfinite(rope->theta) ||
+        (rope->style != 0 && rope->style != 1))
+        return LLA_ERR_SHAPE;
+    if (rope->rot_dims != c->d_head) return LLA_ERR_UNSUPPORTED;   // whole-head rotation only
+    if (k->batch == 0) return LLA_OK;
+    a.rope_log2_theta = std::log2(rope->theta);
+    a.rope_style = rope->style;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_decode_bf16(a, true, s) != hipSuccess) return LLA_ERR_HIP;
+    if (plan.splits == 1) return LLA_OK;
+    return launch_combine(a, c->d_head, true, true, true, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
 lla_status lla_decode_attn_absorbed(const lla_codec *c, const lla_params *prm,
@@ -246,7 +272,7 @@ lla_status lla_decode_attn_absorbed(const lla_codec *c, const lla_params *prm,
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_decode_absorbed(a, s) != hipSuccess) return LLA_ERR_HIP;
     if (plan.splits == 1) return LLA_OK;
-    return launch_combine(a, c->d_head, true, true, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    return launch_combine(a, c->d_head, true, true, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
 lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const lla_cache *k,
@@ -338,7 +364,7 @@ lla_status lla_ref_attn(int32_t H, int32_t d, int32_t dtype, const lla_cache *k,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == LLA_BF16;
     if (launch_flat(a, d, bf16, s) != hipSuccess) return LLA_ERR_HIP;
-    return launch_combine(a, d, bf16, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    return launch_combine(a, d, bf16, false, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
 lla_status lla_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {

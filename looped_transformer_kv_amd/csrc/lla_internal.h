@@ -38,6 +38,10 @@ struct DecodeArgs {
     int S, tokens_per_split;
     int mode;                        // 0 per-head, 1 LLA-2D
     float scale_log2;                // softmax scale * log2(e): scores live in the log2 domain
+    // rotation after reconstruction (lla_decode_attn_rope only): pair m of the d head dims turns
+    // by pos * theta^(-2m/d); style 0 pairs (m, m + d/2), style 1 pairs (2m, 2m + 1)
+    float rope_log2_theta;
+    int rope_style;
 };
 
 // One encode+append call.
@@ -54,12 +58,15 @@ struct EncodeArgs {
 
 // ---------------------------------------------------------------- launchers (host)
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
-hipError_t launch_decode_bf16(const DecodeArgs &a, int waves, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, bool rope, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_absorbed(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t s);
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
-hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, hipStream_t s);
+// self_in_record: the current token's score was computed by the decode kernel and stored in
+// split 0's record (slot d + 2, log2 domain) instead of being formed here from q and k_self
+hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, bool self_in_record,
+                          hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
                          hipStream_t s);
 bool decode_bf16_supported(int d, int r_k, int r_v);

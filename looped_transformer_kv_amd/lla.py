@@ -42,6 +42,10 @@ class lla_cache(ctypes.Structure):
                 ("max_seq_len", ctypes.c_int32)]
 
 
+class lla_rope(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_float), ("rot_dims", ctypes.c_int32), ("style", ctypes.c_int32)]
+
+
 class lla_plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("tokens_per_split", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
@@ -73,6 +77,9 @@ def lib():
         L.lla_decode_attn.restype = i32
         L.lla_decode_attn.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp, vp, vp,
                                       i64, f32, vp, vp, sz, vp]
+        L.lla_decode_attn_rope.restype = i32
+        L.lla_decode_attn_rope.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32,
+                                           P(lla_rope), vp, vp, vp, i64, f32, vp, vp, sz, vp]
         L.lla_decode_attn_absorbed.restype = i32
         L.lla_decode_attn_absorbed.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp,
                                                vp, vp, i64, f32, vp, vp, sz, vp]
@@ -171,6 +178,17 @@ def lla_decode_attn(codec, params, cache, t, q, k_self, v_self, self_stride, sca
                                float(scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
                                _stream(stream))
     return _check("lla_decode_attn", st, check)
+
+
+def lla_decode_attn_rope(codec, params, cache, t, rope, q, k_self, v_self, self_stride, scale,
+                         out, workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lla_decode_attn_rope(ctypes.byref(codec), ctypes.byref(params), ctypes.byref(cache),
+                                    int(t), ctypes.byref(rope), _ptr(q), _ptr(k_self),
+                                    _ptr(v_self), int(self_stride), float(scale), _ptr(out),
+                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _check("lla_decode_attn_rope", st, check)
 
 
 def lla_decode_attn_absorbed(codec, params, cache, t, q, k_self, v_self, self_stride, scale, out,

@@ -50,6 +50,15 @@ class LatentLayer:
         return lla.lla_decode_attn(self.codec, self.params, self.cache, t, q, k_self, v_self,
                                    self_stride, scale, out, workspace, stream=stream, check=check)
 
+    def decode_rope(self, t, rope, q, out, workspace, k_self=None, v_self=None, self_stride=0,
+                    scale=None, stream=None, check=True):
+        """Decode with the rotation after reconstruction (lla_decode_attn_rope); same workspace."""
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.codec.d_head)
+        return lla.lla_decode_attn_rope(self.codec, self.params, self.cache, t, rope, q, k_self,
+                                        v_self, self_stride, scale, out, workspace,
+                                        stream=stream, check=check)
+
     def decode_absorbed(self, t, q, out, workspace, k_self=None, v_self=None, self_stride=0,
                         scale=None, stream=None, check=True):
         """The same attention in the latent space (lla_decode_attn_absorbed); same workspace."""

@@ -42,7 +42,7 @@ class DeviceProblem:
                                  self.block_table, self.seq_lens, c.page, p.max_seq_len)
         self.device = device
 
-    def decode(self, t, with_self=True, q=None, absorbed=False):
+    def decode(self, t, with_self=True, q=None, absorbed=False, rope=None):
         c = self.p.cfg
         q = self.q[t] if q is None else q
         out = torch.full((self.p.B, c.H, c.d), float("nan"), dtype=TORCH_DT[c.dtype],
@@ -51,8 +51,11 @@ class DeviceProblem:
         ks = self.x_k[:, t] if with_self else None
         vs = self.x_v[:, t] if with_self else None
         stride = c.T * c.H * c.d if with_self else 0
-        run = self.layer.decode_absorbed if absorbed else self.layer.decode
-        run(t, q, out, ws, ks, vs, stride)
+        if rope is not None:
+            self.layer.decode_rope(t, rope, q, out, ws, ks, vs, stride)
+        else:
+            run = self.layer.decode_absorbed if absorbed else self.layer.decode
+            run(t, q, out, ws, ks, vs, stride)
         torch.cuda.synchronize()
         return synth.from_device(out)
 
@@ -64,3 +67,12 @@ class DeviceProblem:
                         p.mu_v, p.k_pool if k_pool is None else k_pool,
                         p.v_pool if v_pool is None else v_pool, p.block_table,
                         p.seq_lens if seq_lens is None else seq_lens, c.page, p.q[t], ks, vs)
+
+    def oracle_decode_rope(self, t, rope, with_self=True):
+        from oracle import oracle as O
+        p, c = self.p, self.p.cfg
+        ks, vs = p.self_kv(t) if with_self else (None, None)
+        return O.decode_rope(c.mode, c.T, c.H, c.d, c.r_k, c.r_v, t, p.W_up_k, p.W_up_v, p.mu_k,
+                             p.mu_v, p.k_pool, p.v_pool, p.block_table, p.seq_lens, c.page,
+                             p.q[t], ks, vs, theta=rope.theta, rot_dims=rope.rot_dims,
+                             style=rope.style)

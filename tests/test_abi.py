@@ -157,3 +157,26 @@ def test_absorbed_validation_without_launch():
     assert call(lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_F32)) == lla.LLA_ERR_DTYPE
     assert call(lla.make_codec(0, 4, 16, 128, 8, 32, lla.LLA_BF16)) == lla.LLA_ERR_UNSUPPORTED
     assert call(_codec(c)) == lla.LLA_ERR_WORKSPACE
+
+
+def test_rope_validation_without_launch():
+    _no_gpu()
+    c = synth.CONFIGS["ouro14_21x"]
+    L = lla.lib()
+    params = lla.lla_params(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4096)
+    ws = FAKE            # validation stops before the workspace would be read
+
+    def call(rope, codec=None, wsb=1 << 30):
+        codec = codec or _codec(c)
+        return L.lla_decode_attn_rope(ctypes.byref(codec), ctypes.byref(params),
+                                      ctypes.byref(cache), 0,
+                                      None if rope is None else ctypes.byref(rope), FAKE, None,
+                                      None, 0, 0.1, FAKE, ws, wsb, None)
+    assert call(None) == lla.LLA_ERR_NULL
+    assert call(lla.lla_rope(10000.0, 128, 0), lla.make_codec(0, 4, 16, 128, 16, 32,
+                                                              lla.LLA_F32)) == lla.LLA_ERR_DTYPE
+    assert call(lla.lla_rope(1.0, 128, 0)) == lla.LLA_ERR_SHAPE
+    assert call(lla.lla_rope(10000.0, 128, 2)) == lla.LLA_ERR_SHAPE
+    assert call(lla.lla_rope(10000.0, 64, 0)) == lla.LLA_ERR_UNSUPPORTED
+    assert call(lla.lla_rope(10000.0, 128, 0), wsb=0) == lla.LLA_ERR_WORKSPACE

@@ -256,7 +256,7 @@ def _full_layer(cfg, gpu):
     return layer, host
 
 
-def _sampled_oracle(cfg, layer, host, sel, t, q, ks, vs):
+def _sampled_oracle(cfg, layer, host, sel, t, q, ks, vs, rope=None):
     """Oracle on the sequences in `sel`, from a read-back of exactly their pages."""
     bt = host["bt"][sel]
     pages = np.unique(bt)
@@ -265,6 +265,11 @@ def _sampled_oracle(cfg, layer, host, sel, t, q, ks, vs):
     idx = torch.from_numpy(pages.astype(np.int64)).to(layer.tensors["k_pool"].device)
     kp = synth.from_device(layer.tensors["k_pool"].index_select(0, idx))
     vp = synth.from_device(layer.tensors["v_pool"].index_select(0, idx))
+    if rope is not None:
+        return O.decode_rope(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, host["Wuk"],
+                             host["Wuv"], host["muk"], host["muv"], kp, vp, bt2,
+                             host["lens"][sel], cfg.page, q[sel], ks[sel], vs[sel],
+                             theta=rope.theta, rot_dims=rope.rot_dims, style=rope.style)
     return O.decode(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, host["Wuk"], host["Wuv"],
                     host["muk"], host["muv"], kp, vp, bt2, host["lens"][sel], cfg.page, q[sel],
                     ks[sel], vs[sel])
@@ -370,3 +375,61 @@ def test_absorbed_matches_reconstructing_kernel_full_size(gpu):
     ref = _sampled_oracle(cfg, layer, host, sel, t, q, xk[:, t], xv[:, t])
     assert_close(outs[1][sel], ref, "bf16", "absorbed full size vs oracle")
     assert_close(outs[1], outs[0], "bf16", "absorbed vs reconstructing kernel")
+
+
+# ------------------------------------------------------------------ rotation after reconstruction
+@pytest.mark.parametrize("style", [0, 1])
+@pytest.mark.parametrize("variant", ["plain", "ragged", "noself"])
+@pytest.mark.parametrize("name", BF16_CFGS)
+def test_rope_decode_small(gpu, name, variant, style):
+    """lla_decode_attn_rope against the oracle's explicit reconstruction + rotation."""
+    cfg, B, N = _small(name)
+    lens = None
+    if variant == "ragged":
+        lens = synth.seq_lens(cfg, B, N, ragged=True, salt=3)
+        lens[0], lens[1] = 0, 1
+    p = tinycase.make(cfg, B=B, N=N, lens=lens)
+    dp = gpucase.DeviceProblem(p)
+    rope = lla.lla_rope(10000.0, cfg.d, style)
+    with_self = variant != "noself"
+    for t in sorted({0, cfg.T - 1}):
+        say(f"rope {name}/{variant} style={style} B={B} lens={list(p.seq_lens)} t={t}")
+        got = dp.decode(t, with_self, rope=rope)
+        assert_close(got, dp.oracle_decode_rope(t, rope, with_self), "bf16",
+                     f"rope {name}/{variant}/{style} t={t}")
+
+
+def test_rope_split_context_long_positions(gpu):
+    """One sequence of 4000 tokens (positions up to 4000, split context: the rotated self score
+    reaches combine through the partial record), with a self term."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    p = tinycase.make(cfg, B=1, N=4000)
+    dp = gpucase.DeviceProblem(p)
+    assert dp.layer.plan.splits > 1
+    for style in (0, 1):
+        rope = lla.lla_rope(10000.0, cfg.d, style)
+        say(f"rope split context splits={dp.layer.plan.splits} style={style}")
+        assert_close(dp.decode(2, True, rope=rope), dp.oracle_decode_rope(2, rope, True), "bf16",
+                     f"rope split style {style}")
+
+
+def test_rope_full_size_sampled(gpu):
+    cfg = synth.CONFIGS["ouro14_21x"]
+    layer, host = _full_layer(cfg, gpu)
+    sel = [0, cfg.B - 1]
+    xk = synth.staging(cfg, 0, synth.AX_K, cfg.B)
+    xv = synth.staging(cfg, 0, synth.AX_V, cfg.B)
+    xkd, xvd = synth.to_device(xk, "bf16", gpu), synth.to_device(xv, "bf16", gpu)
+    ws = layer.workspace(gpu)
+    t = 1
+    q = synth.queries(cfg, 0, t, cfg.B)
+    rope = lla.lla_rope(10000.0, cfg.d, 0)
+    out = torch.empty((cfg.B, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
+    say("rope full size")
+    layer.decode_rope(t, rope, synth.to_device(q, "bf16", gpu), out, ws, xkd[:, t], xvd[:, t],
+                      cfg.T * cfg.H * cfg.d)
+    torch.cuda.synchronize()
+    got = synth.from_device(out)
+    assert np.all(np.isfinite(got))
+    ref = _sampled_oracle(cfg, layer, host, sel, t, q, xk[:, t], xv[:, t], rope=rope)
+    assert_close(got[sel], ref, "bf16", "rope full size")
