@@ -14,6 +14,8 @@ Recipe (synthetic stand-ins for Ouro / Huginn activations, which are not availab
   * q ~ N(0, 1).  Staging trajectories x (and hence the current token's loop-t self key/value)
     ~ N(0, s^2) with s^2 = sum_i decay^i / X + 0.01, the per-element energy of a cached vector.
   * block tables: a seeded random permutation of the physical pages (tests paging for real).
+  * prefill chunks: Pn new tokens per sequence with queries ~ N(0, 1) and trajectories ~ N(0, s^2)
+    as above; ragged chunk sizes are uniform in [0, Pn] with the two ends always present.
 Floating inputs are drawn in fp64 and cast once to fp32, then to bf16 with round-to-nearest-even.
 """
 from dataclasses import dataclass, replace
@@ -87,7 +89,7 @@ def rng(cfg: Config, *keys) -> np.random.Generator:
 
 
 # kinds of draws (seed keys)
-K_CODEC, K_MU, K_LAT, K_Q, K_X, K_PAGES, K_LENS, K_POS = range(8)
+K_CODEC, K_MU, K_LAT, K_Q, K_X, K_PAGES, K_LENS, K_POS, K_PQ, K_PX, K_PN = range(11)
 AX_K, AX_V = 0, 1
 
 
@@ -167,6 +169,33 @@ def staging(cfg: Config, layer: int, axis: int, B: int, salt: int = 0) -> np.nda
     s = np.sqrt(np.sum(cfg.decay ** np.arange(r)) / cfg.X + 0.01)
     x = s * rng(cfg, K_X, layer, axis, salt).standard_normal((B, cfg.T, cfg.H, cfg.d))
     return quantize(x, cfg.dtype)
+
+
+def chunk_queries(cfg: Config, layer: int, t: int, B: int, Pn: int,
+                  gain: float = 1.0) -> np.ndarray:
+    """Loop-t queries of a chunk of Pn new tokens per sequence, [B][Pn][H][d]."""
+    q = gain * rng(cfg, K_PQ, layer, t).standard_normal((B, Pn, cfg.H, cfg.d))
+    return quantize(q, cfg.dtype)
+
+
+def chunk_staging(cfg: Config, layer: int, axis: int, B: int, Pn: int,
+                  salt: int = 0) -> np.ndarray:
+    """Loop trajectories of a chunk of Pn new tokens per sequence, [B][Pn][T][H][d] for one axis
+    (same per-element spread as the single-token staging)."""
+    r = cfg.r_k if axis == AX_K else cfg.r_v
+    s = np.sqrt(np.sum(cfg.decay ** np.arange(r)) / cfg.X + 0.01)
+    x = s * rng(cfg, K_PX, layer, axis, salt).standard_normal((B, Pn, cfg.T, cfg.H, cfg.d))
+    return quantize(x, cfg.dtype)
+
+
+def chunk_counts(cfg: Config, B: int, Pn: int, ragged: bool = False, salt: int = 0) -> np.ndarray:
+    """New tokens per sequence in a chunk: all Pn, or ragged in [0, Pn] (ends included)."""
+    if not ragged:
+        return np.full(B, Pn, dtype=np.int32)
+    n = rng(cfg, K_PN, salt).integers(0, Pn + 1, size=B).astype(np.int32)
+    if B >= 2:
+        n[0], n[-1] = 0, Pn
+    return n
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda"):

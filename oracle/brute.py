@@ -86,3 +86,26 @@ def decode_rope(mode, T, H, d, t, W_up_k, W_up_v, mu_k, mu_v, ck, cv, lens, q, k
         Rs = np.stack([rotation_matrix(d, rot_dims, style, theta, n) for n in lens])   # [B][d][d]
         k_self = np.einsum("bij,bhj->bhi", Rs, k_self)
     return attention(q, K, V, lens, k_self, v_self, scale)
+
+
+def prefill(mode, T, H, d, t, W_up_k, W_up_v, mu_k, mu_v, ck, cv, lens, q, k_new, v_new, n_new,
+            scale=None):
+    """Chunked prefill: q, k_new, v_new [B][Pn][H][d]; query i sees cached j < lens[b] and new
+    i' <= i (a causal mask over the concatenated key axis).  Rows i >= n_new[b] are zero."""
+    B, N = ck.shape[:2]
+    Pn = q.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    K = np.concatenate([reconstruct(t, ck, W_up_k, mu_k, T).reshape(B, N, H, d), k_new], axis=1)
+    V = np.concatenate([reconstruct(t, cv, W_up_v, mu_v, T).reshape(B, N, H, d), v_new], axis=1)
+    s = scale * np.einsum("bihd,bjhd->bhij", q, K)                  # [B][H][Pn][N + Pn]
+    j = np.arange(N + Pn)
+    cached = j[None, :] < np.asarray(lens)[:, None]                  # [B][N + Pn]
+    causal = (j[None, :] >= N) & (j[None, :] - N <= np.arange(Pn)[:, None])  # [Pn][N + Pn]
+    ok = cached[:, None, None, :] | causal[None, None, :, :]
+    s = np.where(ok, s, -np.inf)
+    w = np.exp(s - s.max(-1, keepdims=True))
+    p = w / w.sum(-1, keepdims=True)
+    out = np.einsum("bhij,bjhd->bihd", p, V)
+    live = np.arange(Pn)[None, :] < np.asarray(n_new)[:, None]
+    return np.where(live[..., None, None], out, 0.0)

@@ -422,3 +422,93 @@ int oracle_flat_attn(int H, int d, const double *k_pool, const double *v_pool,
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * Chunked prefill attention for loop t (0-based).  The pages say nothing of prefill; the reading
+ * taken is the decode rule above applied to a chunk of new tokens at once: new token i of
+ * sequence b (0 <= i < n_new[b], logical position seq_lens[b] + i) attends to every cached token
+ * j < seq_lens[b] through the codec (K_hat_t(j), V_hat_t(j) reconstructed explicitly, as in
+ * oracle_decode) and, causally, to the chunk's own loop-t keys/values i' <= i, taken as given
+ * (their latents are written only after the last loop, like the decode self term).
+ *   q, out        [B][Pn][H][d]
+ *   k_new, v_new  rows at k_new[(b*Pn + i)*new_stride + h*d]  (new_stride <= 0 means H*d)
+ *   n_new         [B], values clamped to [0, Pn]
+ * Rows i >= n_new[b] of out are not written.  Two-pass softmax per (b, i, h).
+ * Returns 0, -1 on bad arguments, -2 when memory runs out.
+ */
+int oracle_prefill(int mode, int T, int H, int d, int r_k, int r_v, int t,
+                   const double *W_up_k, const double *W_up_v,
+                   const double *mu_k, const double *mu_v,
+                   const double *k_pool, const double *v_pool,
+                   const int32_t *block_table, const int32_t *seq_lens,
+                   int B, int P, int max_pages, int Pn, const int32_t *n_new,
+                   const double *q, const double *k_new, const double *v_new,
+                   long new_stride, double scale, double *out) {
+    if (t < 0 || t >= T || Pn < 0 || !k_new || !v_new || !n_new) return -1;
+    const int G = (mode == 1) ? 1 : H;
+    const int Dg = (mode == 1) ? H * d : d;
+    const int hpg = H / G;
+    const size_t X = (size_t)T * Dg;
+    if (new_stride <= 0) new_stride = (long)H * d;
+
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < G; ++g) {
+            const int len = seq_lens[b];
+            const int nn = n_new[b] < 0 ? 0 : (n_new[b] > Pn ? Pn : n_new[b]);
+            /* every cached token reconstructed once for loop t: Kc, Vc [len][Dg] */
+            double *Kc = (double *)malloc(sizeof(double) * ((size_t)len * Dg + 1));
+            double *Vc = (double *)malloc(sizeof(double) * ((size_t)len * Dg + 1));
+            double *s = (double *)malloc(sizeof(double) * ((size_t)len + nn + 1));
+            if (!Kc || !Vc || !s) {
+#pragma omp atomic write
+                failed = 1;
+                free(Kc); free(Vc); free(s);
+                continue;
+            }
+            const double *Wk = W_up_k + ((size_t)t * G + g) * r_k * Dg;
+            const double *Wv = W_up_v + ((size_t)t * G + g) * r_v * Dg;
+            const double *mk = mu_k + (size_t)g * X + (size_t)t * Dg;
+            const double *mv = mu_v + (size_t)g * X + (size_t)t * Dg;
+            for (int j = 0; j < len; ++j) {
+                reconstruct(latent_at(k_pool, block_table, max_pages, G, P, r_k, b, j, g), r_k,
+                            Wk, mk, Dg, Kc + (size_t)j * Dg);
+                reconstruct(latent_at(v_pool, block_table, max_pages, G, P, r_v, b, j, g), r_v,
+                            Wv, mv, Dg, Vc + (size_t)j * Dg);
+            }
+            for (int i = 0; i < nn; ++i) {
+                for (int hl = 0; hl < hpg; ++hl) {
+                    const int h = g * hpg + hl;
+                    const double *qh = q + (((size_t)b * Pn + i) * H + h) * d;
+                    const int n = len + i + 1;          /* cached tokens, then new 0..i */
+                    for (int j = 0; j < n; ++j) {
+                        const double *kj = j < len
+                            ? Kc + (size_t)j * Dg + (size_t)hl * d
+                            : k_new + ((size_t)b * Pn + (j - len)) * new_stride + (size_t)h * d;
+                        double dot = 0.0;
+                        for (int e = 0; e < d; ++e) dot += qh[e] * kj[e];
+                        s[j] = scale * dot;
+                    }
+                    double m = -INFINITY, Z = 0.0;
+                    for (int j = 0; j < n; ++j) m = fmax(m, s[j]);
+                    for (int j = 0; j < n; ++j) {
+                        s[j] = exp(s[j] - m);
+                        Z += s[j];
+                    }
+                    double *o = out + (((size_t)b * Pn + i) * H + h) * d;
+                    for (int e = 0; e < d; ++e) o[e] = 0.0;
+                    for (int j = 0; j < n; ++j) {
+                        const double *vj = j < len
+                            ? Vc + (size_t)j * Dg + (size_t)hl * d
+                            : v_new + ((size_t)b * Pn + (j - len)) * new_stride + (size_t)h * d;
+                        const double w = s[j] / Z;
+                        for (int e = 0; e < d; ++e) o[e] += w * vj[e];
+                    }
+                }
+            }
+            free(Kc); free(Vc); free(s);
+        }
+    }
+    return failed ? -2 : 0;
+}

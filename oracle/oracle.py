@@ -35,6 +35,9 @@ def lib():
         L.oracle_decode_rope.restype = ctypes.c_int
         L.oracle_decode_rope.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, ip, ip, i, i,
                                          i, dp, dp, dp, lng, dbl, dbl, i, i, dp]
+        L.oracle_prefill.restype = ctypes.c_int
+        L.oracle_prefill.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, ip, ip, i, i, i,
+                                     i, ip, dp, dp, dp, lng, dbl, dp]
         L.oracle_encode.restype = ctypes.c_int
         L.oracle_encode.argtypes = [i, i, i, i, i, dp, dp, dp, i, dp]
         L.oracle_append.restype = ctypes.c_int
@@ -122,6 +125,30 @@ def decode_rope(mode, T, H, d, r_k, r_v, t, W_up_k, W_up_v, mu_k, mu_v, k_pool, 
     return out
 
 
+def prefill(mode, T, H, d, r_k, r_v, t, W_up_k, W_up_v, mu_k, mu_v, k_pool, v_pool,
+            block_table, seq_lens, P, q, k_new, v_new, n_new, scale=None):
+    """Chunked prefill attention of loop t: q, k_new, v_new [B][Pn][H][d]; new token i of
+    sequence b attends to its cached context (reconstructed) and to new tokens 0..i.  Returns
+    out [B][Pn][H][d] (fp64), zero in rows i >= n_new[b]."""
+    block_table = _i32(block_table)
+    seq_lens = _i32(seq_lens)
+    n_new = _i32(n_new)
+    B, max_pages = block_table.shape
+    q = _f64(q)
+    Pn = q.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    arrs = [_f64(a) for a in (W_up_k, W_up_v, mu_k, mu_v, k_pool, v_pool, k_new, v_new)]
+    out = np.zeros((B, Pn, H, d), dtype=np.float64)
+    rc = lib().oracle_prefill(mode, T, H, d, r_k, r_v, t, *[_p(a) for a in arrs[:6]],
+                              _p(block_table, ctypes.c_int32), _p(seq_lens, ctypes.c_int32),
+                              B, P, max_pages, Pn, _p(n_new, ctypes.c_int32), _p(q),
+                              _p(arrs[6]), _p(arrs[7]), H * d, float(scale), _p(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill failed ({rc})")
+    return out
+
+
 def encode(mode, T, H, d, r, W_down, mu, x):
     """c = (x - mu) W_down for one axis; x is the staging buffer [B][T][H][d]; returns [B][G][r]."""
     x = _f64(x)
@@ -163,3 +190,27 @@ def flat_attn(H, d, k_pool, v_pool, block_table, seq_lens, P, q, k_self=None, v_
     if rc != 0:
         raise RuntimeError(f"oracle_flat_attn failed ({rc})")
     return out
+
+
+def encode_prefill(mode, T, H, d, r, W_down, mu, x, write_pos, n_new, block_table, P, pool):
+    """Bulk encode and append of a chunk: x is the chunk's staging [B][Pn][T][H][d]; row i of
+    sequence b (i < n_new[b]) is encoded as one token (encode above) and written at logical
+    position write_pos[b] + i (append above).  Returns (c [B][Pn][G][r], the updated fp64 pool);
+    c is zero in rows i >= n_new[b]."""
+    x = _f64(x)
+    B, Pn = x.shape[:2]
+    G = 1 if mode == 1 else H
+    c = encode(mode, T, H, d, r, W_down, mu, x.reshape((B * Pn,) + x.shape[2:]))
+    c = c.reshape(B, Pn, G, r)
+    n = np.clip(_i32(n_new), 0, Pn)
+    block_table = _i32(block_table)
+    rows = [(b, i) for b in range(B) for i in range(int(n[b]))]
+    if rows:
+        bs = np.array([b for b, _ in rows])
+        pos = np.array([int(write_pos[b]) + i for b, i in rows], dtype=np.int32)
+        pool = append(np.stack([c[b, i] for b, i in rows]), pos, block_table[bs], P, pool)
+    else:
+        pool = np.array(pool, dtype=np.float64, copy=True)
+    for b in range(B):
+        c[b, int(n[b]):] = 0.0
+    return c, pool
