@@ -189,6 +189,49 @@ lla_status lla_encode_append(const lla_codec *codec, const lla_params *params,
                              const int32_t *write_pos, float *c_k_out, float *c_v_out,
                              void *stream);
 
+/*
+ * Bulk encode and append of a chunk of new tokens (a prefill chunk), after its last loop: the same
+ * operation as lla_encode_append (pith.science paper page, "What carries the argument":
+ * c = (x - mu) W_down) over `chunk` rows per sequence.  Row i of sequence b (i < n_new[b]) is
+ * encoded and written to the pool slot of logical position write_pos[b] + i.
+ *   x_k, x_v        staging [B][chunk][T][H][d] (dtype, 16-byte aligned; mu_k / mu_v too)
+ *   n_new           device int32 [B]: live rows per sequence (rows i >= n_new[b] are ignored)
+ *   write_pos       device int32 [B]: position of row 0; positions outside the block table
+ *                   (< 0 or >= max_pages*P) are skipped
+ *   c_k_out/c_v_out optional device fp32 [B][chunk][G][r] copies of c before rounding, written
+ *                   for live rows only (NULL = none)
+ * chunk = 0 (or batch 0) enqueues nothing.  chunk < 0 or batch*chunk > 2^30 -> LLA_ERR_SHAPE;
+ * n_new NULL -> LLA_ERR_NULL; otherwise validated like lla_encode_append.
+ */
+lla_status lla_encode_chunk(const lla_codec *codec, const lla_params *params,
+                            const lla_cache *cache, int32_t chunk, const int32_t *n_new,
+                            const void *x_k, const void *x_v, const int32_t *write_pos,
+                            float *c_k_out, float *c_v_out, void *stream);
+
+/*
+ * Chunked prefill attention for loop t.  The pages do not describe prefill; this is the decode
+ * rule above applied to a chunk of new tokens at once: new token i of sequence b (i < n_new[b],
+ * logical position seq_lens[b] + i) attends to every cached token j < seq_lens[b], reconstructed
+ * through the codec as in lla_decode_attn, and causally to the chunk's own loop-t keys/values
+ * i' <= i, which are taken as given (they are encoded with lla_encode_chunk after the last loop).
+ *   s_j = scale <q[b][i][h], K_hat_t(j)[h]> (cached) or scale <q[b][i][h], k_new[b][i'][h]>;
+ *   out[b][i][h] = sum softmax(s) V.
+ *   q, out          [B][chunk][H][d] bf16, 16-byte aligned
+ *   k_new, v_new    chunk rows: row (b, i) at + (b*chunk + i)*new_stride, head h at + h*d (bf16,
+ *                   16-byte aligned); new_stride in elements, 0 means H*d, else a multiple of 8
+ *                   and >= H*d (T*H*d reads loop t of a [B][chunk][T][H][d] staging buffer
+ *                   offset by t*H*d)
+ *   n_new           device int32 [B], clamped to [0, chunk]
+ * Rows i >= n_new[b] of out are not written.  No workspace.  bf16 codecs only (LLA_ERR_DTYPE);
+ * d_head 64 or 128 with (r_k, r_v) in {(16,16), (16,32), (32,32)}, else LLA_ERR_UNSUPPORTED;
+ * page_size a multiple of 32 and 0 <= t < T, else LLA_ERR_SHAPE.  chunk = 0 enqueues nothing.
+ */
+lla_status lla_prefill_attn(const lla_codec *codec, const lla_params *params,
+                            const lla_cache *cache, int32_t t, int32_t chunk,
+                            const int32_t *n_new, const void *q, const void *k_new,
+                            const void *v_new, int64_t new_stride, float scale, void *out,
+                            void *stream);
+
 /* Split plan and workspace size of lla_ref_attn. */
 lla_status lla_ref_plan(int32_t n_heads, int32_t d_head, int32_t dtype, const lla_cache *flat,
                         lla_plan *plan);

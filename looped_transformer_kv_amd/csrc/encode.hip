@@ -15,7 +15,9 @@
 // are in flight while the current stage is multiplied.  Every output is summed in increasing
 // stacked index.  The result is rounded once to the pool dtype (bf16 round-to-nearest-even) and
 // written to the slot of logical position write_pos[b]; the optional fp32 copy keeps the value
-// before rounding.
+// before rounding.  A chunk of several tokens per sequence (bulk encode after a prefill) is the
+// same contraction over more rows: row i of sequence b goes to write_pos[b] + i, and rows past
+// the sequence's chunk size are neither stored nor copied out.
 #include "lla_internal.h"
 
 namespace lla {
@@ -159,10 +161,11 @@ __global__ __launch_bounds__(NT) void encode_kernel(EncodePair pr) {
     for (int i = 0; i < RPT; ++i) {
         const int b = b0 + rg + RG * i;
         if (b >= a.B) continue;
+        int seq, pos;
+        if (!encode_row(a, b, seq, pos)) continue;           // row past its sequence's chunk
         if (a.c_out) a.c_out[((size_t)b * a.G + g) * a.r + k] = acc[i];
-        const int pos = a.write_pos[b];
         if (pos < 0 || pos >= a.max_pages * a.P) continue;
-        const int page = a.block_table[(size_t)b * a.max_pages + pos / a.P];
+        const int page = a.block_table[(size_t)seq * a.max_pages + pos / a.P];
         if ((unsigned)page >= (unsigned)a.n_pages) continue;
         st_elt<TS>(static_cast<TS *>(a.pool) + (((size_t)page * a.G + g) * a.P + pos % a.P) * a.r +
                        k,
@@ -226,9 +229,12 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
     // ---- append slots of this thread's outputs (rows tid / 32 and tid / 32 + 16 of the tile),
     // fetched first; the page-table reads wait only for the write positions
     constexpr int OUTS = 32 * 32 / (64 * EWAVES);        // outputs per thread
-    int wpos[OUTS], page[OUTS];
+    int wpos[OUTS], wseq[OUTS], page[OUTS];
+    bool wlive[OUTS];
 #pragma unroll
-    for (int o = 0; o < OUTS; ++o) wpos[o] = a.write_pos[min(b0 + (tid + 64 * EWAVES * o) / 32, a.B - 1)];
+    for (int o = 0; o < OUTS; ++o)
+        wlive[o] = encode_row(a, min(b0 + (tid + 64 * EWAVES * o) / 32, a.B - 1), wseq[o],
+                              wpos[o]);
 
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
     const uint16_t *W = static_cast<const uint16_t *>(a.W_down) + (size_t)g * X * a.r;
@@ -276,8 +282,7 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
     for (int o = 0; o < OUTS; ++o) {
         const int pos = wpos[o];
         const int pi = min(max(pos, 0) / a.P, a.max_pages - 1);
-        page[o] = a.block_table[(size_t)min(b0 + (tid + 64 * EWAVES * o) / 32, a.B - 1) *
-                                a.max_pages + pi];
+        page[o] = a.block_table[(size_t)wseq[o] * a.max_pages + pi];
     }
     for (int kg = ks0; kg < ks1; kg += 2 * EGRP) {
         load_grp(kg + EGRP, Bq);
@@ -300,8 +305,9 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
         float c = 0.f;
 #pragma unroll
         for (int w = 0; w < EWAVES; ++w) c += sAcc[w][row][col];
-        if (a.c_out) a.c_out[((size_t)bb * a.G + g) * a.r + k] = c;
         const int pos = wpos[o];
+        if (!wlive[o]) continue;                             // row past its sequence's chunk
+        if (a.c_out) a.c_out[((size_t)bb * a.G + g) * a.r + k] = c;
         if (pos < 0 || pos >= a.max_pages * a.P) continue;
         if ((unsigned)page[o] >= (unsigned)a.n_pages) continue;
         static_cast<uint16_t *>(a.pool)[(((size_t)page[o] * a.G + g) * a.P + pos % a.P) * a.r +

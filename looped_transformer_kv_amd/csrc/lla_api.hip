@@ -275,9 +275,13 @@ lla_status lla_decode_attn_absorbed(const lla_codec *c, const lla_params *prm,
     return launch_combine(a, c->d_head, true, true, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }
 
-lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const lla_cache *k,
-                             const void *x_k, const void *x_v, const int32_t *write_pos,
-                             float *c_k_out, float *c_v_out, void *stream) {
+namespace {
+
+// Shared by lla_encode_append (one row per sequence) and lla_encode_chunk (rps rows per
+// sequence, n_rows live).
+lla_status encode_rows(const lla_codec *c, const lla_params *prm, const lla_cache *k, int rps,
+                       const int32_t *n_rows, const void *x_k, const void *x_v,
+                       const int32_t *write_pos, float *c_k_out, float *c_v_out, void *stream) {
     lla_status st = check_codec(c);
     if (st != LLA_OK) return st;
     if (!prm || !prm->W_down_k || !prm->W_down_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
@@ -285,7 +289,7 @@ lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const ll
     if (!x_k || !x_v || !write_pos) return LLA_ERR_NULL;
     if (!aligned16(x_k) || !aligned16(x_v) || !aligned16(prm->mu_k) || !aligned16(prm->mu_v))
         return LLA_ERR_ALIGN;
-    if (k->batch == 0) return LLA_OK;
+    if (k->batch == 0 || rps == 0) return LLA_OK;
     const Shape sh = shape_of(c);
     const bool bf16 = c->dtype == LLA_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -299,8 +303,10 @@ lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const ll
         a.pool = axis ? k->v_pool : k->k_pool;
         a.block_table = k->block_table;
         a.write_pos = write_pos;
+        a.n_rows = n_rows;
         a.c_out = axis ? c_v_out : c_k_out;
-        a.B = k->batch;
+        a.B = k->batch * rps;
+        a.rps = rps;
         a.H = c->n_heads;
         a.G = sh.G;
         a.Dg = sh.Dg;
@@ -313,6 +319,81 @@ lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const ll
         a.mode = c->mode;
     }
     return launch_encode(ax[0], ax[1], bf16, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+}  // namespace
+
+lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                             const void *x_k, const void *x_v, const int32_t *write_pos,
+                             float *c_k_out, float *c_v_out, void *stream) {
+    return encode_rows(c, prm, k, 1, nullptr, x_k, x_v, write_pos, c_k_out, c_v_out, stream);
+}
+
+lla_status lla_encode_chunk(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                            int32_t chunk, const int32_t *n_new, const void *x_k,
+                            const void *x_v, const int32_t *write_pos, float *c_k_out,
+                            float *c_v_out, void *stream) {
+    if (!n_new) return LLA_ERR_NULL;
+    if (chunk < 0 || (k && (long)k->batch * chunk > (1L << 30))) return LLA_ERR_SHAPE;
+    return encode_rows(c, prm, k, chunk, n_new, x_k, x_v, write_pos, c_k_out, c_v_out, stream);
+}
+
+lla_status lla_prefill_attn(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                            int32_t t, int32_t chunk, const int32_t *n_new, const void *q,
+                            const void *k_new, const void *v_new, int64_t new_stride,
+                            float scale, void *out, void *stream) {
+    lla_status st = check_codec(c);
+    if (st != LLA_OK) return st;
+    if (c->dtype != LLA_BF16) return LLA_ERR_DTYPE;
+    if (!prefill_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
+    if (!prm || !prm->W_up_k || !prm->W_up_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
+    if ((st = check_cache(k, true)) != LLA_OK) return st;
+    if (!n_new || !q || !k_new || !v_new || !out) return LLA_ERR_NULL;
+    if (t < 0 || t >= c->T || chunk < 0 || k->page_size % 32 != 0) return LLA_ERR_SHAPE;
+    const long hd = (long)c->n_heads * c->d_head;
+    if (new_stride == 0) new_stride = hd;
+    if (new_stride < hd || new_stride % 8 != 0) return LLA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return LLA_ERR_ALIGN;
+    if (k->batch == 0 || chunk == 0) return LLA_OK;
+    const int qpb = prefill_queries_per_block();
+    const long QB = ((long)chunk + qpb - 1) / qpb;
+    if ((long)k->batch * c->n_heads * QB > (1L << 30) || (long)k->batch * chunk > (1L << 30))
+        return LLA_ERR_SHAPE;
+    const Shape sh = shape_of(c);
+    PrefillArgs a{};
+    a.k_pool = k->k_pool;
+    a.v_pool = k->v_pool;
+    a.block_table = k->block_table;
+    a.seq_lens = k->seq_lens;
+    a.W_up_k = prm->W_up_k;
+    a.W_up_v = prm->W_up_v;
+    a.mu_k = prm->mu_k;
+    a.mu_v = prm->mu_v;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.n_new = n_new;
+    a.out = out;
+    a.new_stride = new_stride;
+    a.B = k->batch;
+    a.H = c->n_heads;
+    a.G = sh.G;
+    a.Dg = sh.Dg;
+    a.T = c->T;
+    a.t = t;
+    a.r_k = c->r_k;
+    a.r_v = c->r_v;
+    a.P = k->page_size;
+    a.max_pages = k->max_pages;
+    a.n_pages = k->n_pages;
+    a.max_seq_len = k->max_seq_len;
+    a.Pn = chunk;
+    a.QB = (int)QB;
+    a.mode = c->mode;
+    a.scale_log2 = scale * kLog2e;
+    return launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LLA_OK
+                                                                              : LLA_ERR_HIP;
 }
 
 lla_status lla_ref_plan(int32_t H, int32_t d, int32_t dtype, const lla_cache *k, lla_plan *p) {

@@ -44,17 +44,46 @@ struct DecodeArgs {
     int rope_style;
 };
 
+// One chunked prefill call (bf16).
+struct PrefillArgs {
+    const void *k_pool, *v_pool;     // latent pools [n_pages][G][P][r]
+    const int32_t *block_table;      // [B][max_pages]
+    const int32_t *seq_lens;         // [B]: cached tokens before the chunk
+    const void *W_up_k, *W_up_v;     // [T][G][r][Dg]
+    const void *mu_k, *mu_v;         // [G][X]
+    const void *q;                   // [B][Pn][H][d]
+    const void *k_new, *v_new;       // chunk rows at + (b*Pn + i)*new_stride + h*d
+    const int32_t *n_new;            // [B]: chunk tokens per sequence (clamped to [0, Pn])
+    void *out;                       // [B][Pn][H][d]
+    int64_t new_stride;
+    int B, H, G, Dg, T, t, r_k, r_v, P, max_pages, n_pages, max_seq_len;
+    int Pn, QB;                      // chunk capacity; query blocks per (sequence, head)
+    int mode;
+    float scale_log2;
+};
+
 // One encode+append call.
 struct EncodeArgs {
-    const void *x;                   // staging [B][T][H][d]
+    const void *x;                   // staging rows [B][T][H][d] (B = rows)
     const void *W_down;              // [G][X][r]
     const void *mu;                  // [G][X]
     void *pool;                      // [n_pages][G][P][r]
-    const int32_t *block_table;      // [B][max_pages]
-    const int32_t *write_pos;        // [B]
+    const int32_t *block_table;      // [sequences][max_pages]
+    const int32_t *write_pos;        // [sequences]
+    const int32_t *n_rows;           // optional [sequences]: live rows of each sequence
     float *c_out;                    // optional [B][G][r]
     int B, H, G, Dg, T, d, r, P, max_pages, n_pages, mode;
+    int rps;                         // rows per sequence: row -> (row / rps, row % rps)
 };
+
+// Staging row `row` belongs to sequence seq = row / rps as its chunk index i = row % rps and is
+// appended at pos = write_pos[seq] + i.  Returns whether the row is live (i < n_rows[seq]).
+__device__ __forceinline__ bool encode_row(const EncodeArgs &a, int row, int &seq, int &pos) {
+    seq = row / a.rps;
+    const int i = row - seq * a.rps;
+    pos = a.write_pos[seq] + i;
+    return !a.n_rows || i < a.n_rows[seq];
+}
 
 // ---------------------------------------------------------------- launchers (host)
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
@@ -70,6 +99,9 @@ hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, bo
 hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
                          hipStream_t s);
 bool decode_bf16_supported(int d, int r_k, int r_v);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+bool prefill_supported(int d, int r_k, int r_v);
+int prefill_queries_per_block();
 
 constexpr int kPartialPad = 4;   // partial record = d + 4 floats (16-byte aligned records)
 constexpr int kMaxChunksPerSplit = 512;   // 32-token chunks one latent-decode workgroup covers

@@ -86,6 +86,12 @@ def lib():
         L.lla_encode_append.restype = i32
         L.lla_encode_append.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), vp, vp, vp, vp,
                                         vp, vp]
+        L.lla_encode_chunk.restype = i32
+        L.lla_encode_chunk.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp, vp, vp,
+                                       vp, vp, vp, vp]
+        L.lla_prefill_attn.restype = i32
+        L.lla_prefill_attn.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, i32, vp, vp,
+                                       vp, vp, i64, f32, vp, vp]
         L.lla_ref_plan.restype = i32
         L.lla_ref_plan.argtypes = [i32, i32, i32, P(lla_cache), P(lla_plan)]
         L.lla_ref_attn.restype = i32
@@ -208,6 +214,23 @@ def lla_encode_append(codec, params, cache, x_k, x_v, write_pos, c_k_out=None, c
                                  _ptr(x_k), _ptr(x_v), _ptr(write_pos), _ptr(c_k_out),
                                  _ptr(c_v_out), _stream(stream))
     return _check("lla_encode_append", st, check)
+
+
+def lla_encode_chunk(codec, params, cache, chunk, n_new, x_k, x_v, write_pos, c_k_out=None,
+                     c_v_out=None, stream=None, check=True) -> int:
+    st = lib().lla_encode_chunk(ctypes.byref(codec), ctypes.byref(params), ctypes.byref(cache),
+                                int(chunk), _ptr(n_new), _ptr(x_k), _ptr(x_v), _ptr(write_pos),
+                                _ptr(c_k_out), _ptr(c_v_out), _stream(stream))
+    return _check("lla_encode_chunk", st, check)
+
+
+def lla_prefill_attn(codec, params, cache, t, chunk, n_new, q, k_new, v_new, new_stride, scale,
+                     out, stream=None, check=True) -> int:
+    st = lib().lla_prefill_attn(ctypes.byref(codec), ctypes.byref(params), ctypes.byref(cache),
+                                int(t), int(chunk), _ptr(n_new), _ptr(q), _ptr(k_new),
+                                _ptr(v_new), int(new_stride), float(scale), _ptr(out),
+                                _stream(stream))
+    return _check("lla_prefill_attn", st, check)
 
 
 def lla_ref_plan(n_heads, d_head, dtype, flat: lla_cache) -> lla_plan:

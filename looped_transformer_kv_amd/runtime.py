@@ -72,3 +72,18 @@ class LatentLayer:
                       check=True):
         return lla.lla_encode_append(self.codec, self.params, self.cache, x_k, x_v, write_pos,
                                      c_k_out, c_v_out, stream=stream, check=check)
+
+    def prefill(self, t, chunk, n_new, q, k_new, v_new, out, new_stride=0, scale=None,
+                stream=None, check=True):
+        """Chunked prefill attention of loop t (lla_prefill_attn): q, out [B][chunk][H][d]."""
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.codec.d_head)
+        return lla.lla_prefill_attn(self.codec, self.params, self.cache, t, chunk, n_new, q,
+                                    k_new, v_new, new_stride, scale, out, stream=stream,
+                                    check=check)
+
+    def encode_chunk(self, chunk, n_new, x_k, x_v, write_pos, c_k_out=None, c_v_out=None,
+                     stream=None, check=True):
+        """Bulk encode and append of a chunk (lla_encode_chunk): x [B][chunk][T][H][d]."""
+        return lla.lla_encode_chunk(self.codec, self.params, self.cache, chunk, n_new, x_k, x_v,
+                                    write_pos, c_k_out, c_v_out, stream=stream, check=check)

@@ -180,3 +180,49 @@ def test_rope_validation_without_launch():
     assert call(lla.lla_rope(10000.0, 128, 2)) == lla.LLA_ERR_SHAPE
     assert call(lla.lla_rope(10000.0, 64, 0)) == lla.LLA_ERR_UNSUPPORTED
     assert call(lla.lla_rope(10000.0, 128, 0), wsb=0) == lla.LLA_ERR_WORKSPACE
+
+
+def test_prefill_validation_without_launch():
+    _no_gpu()
+    c = synth.CONFIGS["ouro14_21x"]
+    L = lla.lib()
+    params = lla.lla_params(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4096)
+
+    def call(codec=None, t=0, chunk=8, n_new=FAKE, stride=0, q=FAKE, cache_=None):
+        codec = codec or _codec(c)
+        return L.lla_prefill_attn(ctypes.byref(codec), ctypes.byref(params),
+                                  ctypes.byref(cache_ or cache), t, chunk, n_new, q, FAKE, FAKE,
+                                  stride, 0.1, FAKE, None)
+    assert call(lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_F32)) == lla.LLA_ERR_DTYPE
+    assert call(lla.make_codec(0, 4, 16, 128, 96, 160, lla.LLA_BF16)) == lla.LLA_ERR_UNSUPPORTED
+    assert call(n_new=None) == lla.LLA_ERR_NULL
+    assert call(t=4) == lla.LLA_ERR_SHAPE
+    assert call(chunk=-1) == lla.LLA_ERR_SHAPE
+    assert call(stride=16 * 128 - 8) == lla.LLA_ERR_SHAPE          # shorter than a row
+    assert call(stride=16 * 128 + 4) == lla.LLA_ERR_SHAPE          # not a multiple of 8
+    assert call(q=FAKE + 8) == lla.LLA_ERR_ALIGN
+    odd_pages = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 48, 64, 64, 3072)
+    assert call(cache_=odd_pages) == lla.LLA_ERR_SHAPE
+    assert call(chunk=0) == lla.LLA_OK                              # nothing to do
+    empty = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 64, 0)
+    assert call(cache_=empty) == lla.LLA_OK
+
+
+def test_encode_chunk_validation_without_launch():
+    _no_gpu()
+    c = synth.CONFIGS["ouro14_21x"]
+    L = lla.lib()
+    params = lla.lla_params(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4096)
+
+    def call(chunk=8, n_new=FAKE, x=FAKE):
+        return L.lla_encode_chunk(ctypes.byref(_codec(c)), ctypes.byref(params),
+                                  ctypes.byref(cache), chunk, n_new, x, FAKE, FAKE, None, None,
+                                  None)
+    assert call(n_new=None) == lla.LLA_ERR_NULL
+    assert call(chunk=-1) == lla.LLA_ERR_SHAPE
+    assert call(chunk=(1 << 30) + 1) == lla.LLA_ERR_SHAPE
+    assert call(x=None) == lla.LLA_ERR_NULL
+    assert call(x=FAKE + 8) == lla.LLA_ERR_ALIGN
+    assert call(chunk=0) == lla.LLA_OK

@@ -1,0 +1,208 @@
+"""GPU parity of the chunked prefill (lla_prefill_attn) and the bulk encode (lla_encode_chunk),
+through the C ABI, against the fp64 oracle on seeded inputs.
+
+Bar (as for decode): bf16 max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3 over the live rows; rows
+past a sequence's chunk size must stay untouched.  Small cases span two query blocks of 256,
+several 32-token tiles of cached context and of chunk, ragged tails, empty contexts and empty
+chunks; the full-size case runs the benchmark's launch (32 sequences x 4096 cached tokens, a
+chunk of 512) and checks sampled sequences.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from looped_transformer_kv_amd import lla, synth
+from looped_transformer_kv_amd.runtime import LatentLayer
+from oracle import oracle as O
+import gpucase
+import tinycase
+from gpucase import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# codec shapes the prefill kernel instantiates: (mode, H, d, T, r_k, r_v)
+SHAPES = {
+    "ouro14_21x": synth.CONFIGS["ouro14_21x"],
+    "h4_d128_2d_r32": synth.Config("pf_2d", L=1, H=4, d=128, T=2, r_k=32, r_v=32, B=1, N=1,
+                                   mode=1, cid=140),
+    "h2_d64_r16": synth.Config("pf_d64", L=1, H=2, d=64, T=3, r_k=16, r_v=16, B=1, N=1, cid=141),
+    "h2_d64_2d_r16_32": synth.Config("pf_d64_2d", L=1, H=2, d=64, T=2, r_k=16, r_v=32, B=1, N=1,
+                                     mode=1, cid=142),
+}
+
+
+class Chunk:
+    """A decode problem with room for a chunk of Pn new tokens per sequence, plus the chunk's
+    inputs (host fp64 and device bf16)."""
+
+    def __init__(self, cfg, B, N, Pn, lens, n_new, gpu, q_gain=1.0):
+        cfg = synth.scaled(cfg, B=B, N=N + Pn)
+        self.cfg, self.B, self.Pn = cfg, B, Pn
+        self.p = tinycase.make(cfg, B=B, N=N + Pn, lens=np.asarray(lens, dtype=np.int32))
+        self.dp = gpucase.DeviceProblem(self.p)
+        self.n_new = np.asarray(n_new, dtype=np.int32)
+        self.q = {t: synth.chunk_queries(cfg, 0, t, B, Pn, q_gain) for t in range(cfg.T)}
+        self.xk = synth.chunk_staging(cfg, 0, synth.AX_K, B, Pn)
+        self.xv = synth.chunk_staging(cfg, 0, synth.AX_V, B, Pn)
+        up = lambda a: synth.to_device(a, "bf16", gpu)
+        self.qd = {t: up(self.q[t]) for t in self.q}
+        self.xkd, self.xvd = up(self.xk), up(self.xv)
+        self.nd = torch.from_numpy(self.n_new).to(gpu)
+        self.gpu = gpu
+
+    def run(self, t, strided=True):
+        c = self.cfg
+        out = torch.full((self.B, self.Pn, c.H, c.d), float("nan"), dtype=torch.bfloat16,
+                         device=self.gpu)
+        if strided:        # loop t read in place from the [B][Pn][T][H][d] staging buffers
+            kn, vn, stride = self.xkd[:, :, t], self.xvd[:, :, t], c.T * c.H * c.d
+        else:
+            kn, vn, stride = self.xkd[:, :, t].contiguous(), self.xvd[:, :, t].contiguous(), 0
+        self.dp.layer.prefill(t, self.Pn, self.nd, self.qd[t], kn, vn, out, new_stride=stride)
+        torch.cuda.synchronize()
+        return synth.from_device(out)
+
+    def oracle(self, t):
+        p, c = self.p, self.cfg
+        return O.prefill(c.mode, c.T, c.H, c.d, c.r_k, c.r_v, t, p.W_up_k, p.W_up_v, p.mu_k,
+                         p.mu_v, p.k_pool, p.v_pool, p.block_table, p.seq_lens, c.page,
+                         self.q[t], self.xk[:, :, t], self.xv[:, :, t], self.n_new)
+
+    def check(self, got, ref, what):
+        live = np.arange(self.Pn)[None, :] < self.n_new[:, None]            # [B][Pn]
+        assert np.all(np.isnan(got[~live])), f"{what}: rows past the chunk were written"
+        assert_close(got[live], ref[live], "bf16", what)
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_prefill_small(gpu, shape):
+    """Two query blocks (Pn = 300), ragged cached lengths including 0 and a partial tile, ragged
+    chunk sizes including 0 and Pn."""
+    cfg = SHAPES[shape]
+    lens, n_new = [0, 137, 64], [300, 0, 77]
+    ch = Chunk(cfg, 3, 137, 300, lens, n_new, gpu)
+    for t in sorted({0, cfg.T - 1}):
+        for strided in (True, False):
+            say(f"prefill {shape} t={t} strided={strided} lens={lens} n_new={n_new}")
+            ch.check(ch.run(t, strided), ch.oracle(t), f"{shape} t={t}")
+
+
+@pytest.mark.parametrize("variant", ["peaked", "long_context", "tiny_chunks"])
+def test_prefill_variants(gpu, variant):
+    cfg = SHAPES["ouro14_21x"]
+    if variant == "peaked":            # sharp softmax: q x 8
+        ch = Chunk(cfg, 2, 500, 64, [500, 31], [64, 33], gpu, q_gain=8.0)
+    elif variant == "long_context":    # context much longer than the chunk
+        ch = Chunk(cfg, 2, 2000, 40, [2000, 1999], [40, 1], gpu)
+    else:                              # one-token and two-token chunks, empty context
+        ch = Chunk(cfg, 4, 70, 2, [0, 70, 1, 33], [1, 2, 2, 1], gpu)
+    t = cfg.T - 1
+    say(f"prefill {variant}")
+    ch.check(ch.run(t), ch.oracle(t), variant)
+
+
+def test_prefill_single_token_chunk_matches_decode(gpu):
+    """A chunk of one token is the decode step with that token as its self term (oracle pin F1):
+    the prefill kernel and the decode kernel both meet the oracle on the same inputs."""
+    cfg = SHAPES["ouro14_21x"]
+    ch = Chunk(cfg, 3, 300, 1, [300, 5, 0], [1, 1, 1], gpu)
+    c = ch.cfg
+    t = 1
+    say("prefill one-token chunk vs decode")
+    got = ch.run(t)[:, 0]
+    ref = ch.oracle(t)[:, 0]
+    assert_close(got, ref, "bf16", "prefill, one token")
+    out = torch.empty((3, c.H, c.d), dtype=torch.bfloat16, device=gpu)
+    layer = ch.dp.layer
+    layer.decode(t, ch.qd[t][:, 0].contiguous(), out, layer.workspace(gpu), ch.xkd[:, 0, t],
+                 ch.xvd[:, 0, t], c.T * c.H * c.d)
+    torch.cuda.synchronize()
+    assert_close(synth.from_device(out), ref, "bf16", "decode with the chunk token as self")
+
+
+@pytest.mark.parametrize("shape", ["ouro14_21x", "h4_d128_2d_r32"])
+def test_encode_chunk(gpu, shape):
+    """lla_encode_chunk: c against the oracle; the pool holds c rounded once at write_pos + i for
+    live rows only; every other slot keeps its bytes."""
+    cfg = SHAPES[shape]
+    B, N, Pn = 3, 90, 70
+    ch = Chunk(cfg, B, N, Pn, [90, 0, 33], [70, 0, 41], gpu)
+    c, p = ch.cfg, ch.p
+    wpos_h = p.seq_lens.copy()
+    wpos = torch.from_numpy(wpos_h).to(gpu)
+    ck = torch.full((B, Pn, c.G, c.r_k), float("nan"), dtype=torch.float32, device=gpu)
+    cv = torch.full((B, Pn, c.G, c.r_v), float("nan"), dtype=torch.float32, device=gpu)
+    kb, vb = synth.from_device(ch.dp.k_pool), synth.from_device(ch.dp.v_pool)
+    say(f"encode_chunk {shape} B={B} Pn={Pn}")
+    ch.dp.layer.encode_chunk(Pn, ch.nd, ch.xkd, ch.xvd, wpos, ck, cv)
+    torch.cuda.synchronize()
+    live = np.arange(Pn)[None, :] < ch.n_new[:, None]
+    for axis, cgpu, W, mu, r, before, pool, x in (
+            (0, ck, p.W_down_k, p.mu_k, c.r_k, kb, ch.dp.k_pool, ch.xk),
+            (1, cv, p.W_down_v, p.mu_v, c.r_v, vb, ch.dp.v_pool, ch.xv)):
+        got = cgpu.double().cpu().numpy()
+        ref, _ = O.encode_prefill(c.mode, c.T, c.H, c.d, r, W, mu, x, wpos_h, ch.n_new,
+                                  p.block_table, c.page, before)
+        assert np.all(np.isnan(got[~live])), f"axis {axis}: rows past the chunk were written"
+        assert_close(got[live], ref[live], "bf16", f"{shape} c axis {axis}")
+        # the pool: the rounding of the kernel's own c, at write_pos + i, live rows only
+        stored = synth.quantize(np.nan_to_num(got), "bf16")
+        expect = before.copy()
+        for b in range(B):
+            for i in range(int(ch.n_new[b])):
+                pos = wpos_h[b] + i
+                expect[p.block_table[b, pos // c.page], :, pos % c.page] = stored[b, i]
+        after = synth.from_device(pool)
+        assert np.array_equal(after, expect), f"{shape} axis {axis}: pool differs"
+
+
+def test_prefill_bench_shape_sampled(gpu):
+    """The benchmark's launch: 32 sequences x 4096 cached tokens, a chunk of 512, all 16 heads;
+    the oracle checks three sampled sequences."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    B, N, Pn = cfg.B, cfg.N, 512
+    cfgp = synth.scaled(cfg, N=N + Pn)
+    max_pages = cfgp.max_pages
+    n_pages = B * max_pages
+    Wdk, Wuk, muk = synth.codec(cfg, 0, synth.AX_K)
+    Wdv, Wuv, muv = synth.codec(cfg, 0, synth.AX_V)
+    kpool = synth.device_latent_pool(cfg, 0, synth.AX_K, n_pages, gpu)
+    vpool = synth.device_latent_pool(cfg, 0, synth.AX_V, n_pages, gpu)
+    bt = synth.block_table(cfgp, B, max_pages)
+    lens = synth.seq_lens(cfg, B, N)
+    up = lambda a: synth.to_device(a, "bf16", gpu)
+    codec = lla.make_codec(0, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
+    layer = LatentLayer(codec, up(Wdk), up(Wdv), up(Wuk), up(Wuv), up(muk), up(muv), kpool, vpool,
+                        torch.from_numpy(bt).to(gpu), torch.from_numpy(lens).to(gpu), cfg.page, N)
+    t = cfg.T - 1
+    q = synth.chunk_queries(cfg, 0, t, B, Pn)
+    xk = synth.chunk_staging(cfg, 0, synth.AX_K, B, Pn)
+    xv = synth.chunk_staging(cfg, 0, synth.AX_V, B, Pn)
+    n_new = np.full(B, Pn, dtype=np.int32)
+    xkd, xvd = up(xk), up(xv)
+    out = torch.empty((B, Pn, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
+    say(f"prefill full size B={B} N={N} Pn={Pn}")
+    layer.prefill(t, Pn, torch.from_numpy(n_new).to(gpu), up(q), xkd[:, :, t], xvd[:, :, t], out,
+                  new_stride=cfg.T * cfg.H * cfg.d)
+    torch.cuda.synchronize()
+    got = synth.from_device(out)
+    assert np.all(np.isfinite(got))
+    sel = [0, B // 2, B - 1]
+    pages = np.unique(bt[sel])
+    remap = {int(pg): i for i, pg in enumerate(pages)}
+    bt2 = np.vectorize(lambda x: remap[int(x)])(bt[sel]).astype(np.int32)
+    idx = torch.from_numpy(pages.astype(np.int64)).to(gpu)
+    kp = synth.from_device(kpool.index_select(0, idx))
+    vp = synth.from_device(vpool.index_select(0, idx))
+    say(f"prefill full size: oracle on sequences {sel}")
+    ref = O.prefill(0, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, Wuk, Wuv, muk, muv, kp, vp, bt2,
+                    lens[sel], cfg.page, q[sel], xk[sel][:, :, t], xv[sel][:, :, t], n_new[sel])
+    assert_close(got[sel], ref, "bf16", "prefill full size")
