@@ -223,6 +223,87 @@ def flat_comparator(cfg, dev, steps):
             "splits": plan.splits}
 
 
+PREFILL_CHUNK = 512
+
+
+def prefill_leg(cfg, layers, dev, launch, steps, warmup):
+    """Chunked prefill on the same layers: a chunk of PREFILL_CHUNK new tokens per sequence after
+    the N cached ones, all L layers x T loops of lla_prefill_attn, then one lla_encode_chunk per
+    layer.  Inputs are fresh device draws (q ~ N(0, 1), chunk trajectories with the staging
+    spread).  The chunk's latents are written at positions 0 .. chunk - 1, which the block table
+    holds (overwriting cached values changes no timing)."""
+    import torch
+    from looped_transformer_kv_amd import synth
+
+    B, N, T, H, d = cfg.B, cfg.N, cfg.T, cfg.H, cfg.d
+    L, Pn = len(layers), PREFILL_CHUNK
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.ROOT_SEED + 7)
+    xs = math.sqrt(sum(cfg.decay ** i for i in range(cfg.r_k)) / cfg.X + 0.01)
+    qc = [torch.randn((B, Pn, H, d), generator=gen, device=dev).to(torch.bfloat16)
+          for _ in range(T)]
+    xkc = (xs * torch.randn((B, Pn, T, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+    xvc = (xs * torch.randn((B, Pn, T, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+    n_new = torch.full((B,), Pn, dtype=torch.int32, device=dev)
+    wpos = torch.zeros((B,), dtype=torch.int32, device=dev)
+    outc = torch.empty((B, Pn, H, d), dtype=torch.bfloat16, device=dev)
+    stride = T * H * d
+
+    def attn_all():
+        for t in range(T):
+            for l in range(L):
+                layers[l].prefill(t, Pn, n_new, qc[t], xkc[:, :, t], xvc[:, :, t], outc,
+                                  new_stride=stride)
+
+    def enc_all():
+        for l in range(L):
+            layers[l].encode_chunk(Pn, n_new, xkc, xvc, wpos)
+
+    attn_all()
+    enc_all()
+    torch.cuda.synchronize()
+    run_a, run_e = attn_all, enc_all
+    if launch == "hip_graph":
+        ga, ge = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ga):
+            attn_all()
+        with torch.cuda.graph(ge):
+            enc_all()
+        run_a, run_e = ga.replay, ge.replay
+    for _ in range(warmup):
+        run_a()
+        run_e()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(steps):
+        run_a()
+    ev[1].record()
+    for _ in range(steps):
+        run_e()
+    ev[2].record()
+    torch.cuda.synchronize()
+    attn_us = ev[0].elapsed_time(ev[1]) * 1e3 / (steps * T * L)
+    enc_us = ev[1].elapsed_time(ev[2]) * 1e3 / (steps * L)
+    # algorithmic work of one call: every query against its cached context and its causal part
+    # of the chunk (4 d flops per query-key pair: QK and PV), plus one expansion of every cached
+    # token per sequence and group (K and V)
+    pairs = B * H * (Pn * N + Pn * (Pn + 1) // 2)
+    flops = pairs * 4 * d + B * N * cfg.G * 2 * (cfg.r_k + cfg.r_v) * cfg.Dg
+    tflops = flops / (attn_us * 1e-6) / 1e12
+    enc_bytes = sum(B * Pn * T * H * d * 2 + cfg.G * cfg.X * r * 2 + cfg.G * cfg.X * 2 +
+                    B * Pn * cfg.G * r * 2 for r in (cfg.r_k, cfg.r_v))
+    step_s = (attn_us * T * L + enc_us * L) * 1e-6
+    return {"kernel": "lla_prefill_attn + lla_encode_chunk", "chunk": Pn, "cached": N,
+            "attn_us_per_call": round(attn_us, 3), "attn_flops_per_call": flops,
+            "attn_TFLOPs": round(tflops, 1),
+            "attn_frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "encode_chunk_us_per_call": round(enc_us, 3),
+            "encode_chunk_bytes_per_call": enc_bytes,
+            "encode_chunk_GBps": round(enc_bytes / (enc_us * 1e-6) / 1e9, 1),
+            "prefill_tokens_per_s": round(B * Pn / step_s, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +323,9 @@ def main():
     ap.add_argument("--no-rope", action="store_true",
                     help="skip timing the decode with rotation after reconstruction "
                          "(lla_decode_attn_rope, theta 10^4, whole-head half-split pairs)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip timing the chunked prefill (lla_prefill_attn, a chunk of "
+                         f"{PREFILL_CHUNK} after the cached context, then lla_encode_chunk)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -439,6 +523,10 @@ def main():
                           "style": "half_split", **time_variant(
             lambda t, l: layers[l].decode_rope(t, rope, q[t][l], out, ws, xk[l][:, t],
                                                xv[l][:, t], stride))}
+    if not args.no_prefill and cfg.mode == 0 and (cfg.r_k, cfg.r_v) in ((16, 16), (16, 32),
+                                                                         (32, 32)):
+        log("timing the chunked prefill")
+        result["prefill"] = prefill_leg(cfg, layers, dev, launch, K, args.warmup)
     if not args.no_flat:
         log("timing the flat comparator")
         result["flat_ref"] = flat_comparator(cfg, dev, max(5, K))

@@ -61,23 +61,29 @@ __device__ __forceinline__ float max_swap32(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-constexpr int PWAVES = 4;                  // waves per workgroup
-constexpr int QT = 2;                      // 32-query tiles per wave
-constexpr int QWG = PWAVES * QT * 32;      // queries per workgroup
+constexpr int PWAVES = 8;                  // waves per workgroup (two per SIMD)
+constexpr int QWG = PWAVES * 32;           // queries per workgroup: one 32-query tile per wave
 
 template <int D, int RK, int RV>
 struct PShape {
     static constexpr int MT = D / 32;                  // 32-wide tiles of the head dim
     static constexpr int KS = D / 16;                  // k-steps of the score MFMA
     static constexpr int KK = RK / 16, KV = RV / 16;   // k-steps of the expansions
-    static constexpr int NEWK = KS * 64 / (64 * PWAVES);        // chunk key pieces per thread
-    static constexpr int NEWV = 32 * D / 8 / (64 * PWAVES);     // chunk value pieces per thread
-    static constexpr int NST = (KK + KV > NEWK + NEWV) ? KK + KV : NEWK + NEWV;   // stage regs
+    static constexpr int KMAX = KK > KV ? KK : KV;    // k-steps of this wave's expansion job
+    // 16-byte pieces of a 32-token chunk tile per axis (32 rows x D / 8), per thread
+    static constexpr int PIECES = 32 * D / 8;
+    static constexpr int NEWP = (PIECES + 64 * PWAVES - 1) / (64 * PWAVES);
+    // stage registers per thread: the latent slices of its wave's job (a cached tile) or its
+    // pieces of both axes (a chunk tile)
+    static constexpr int NST = KMAX > 2 * NEWP ? KMAX : 2 * NEWP;
+    static_assert(2 * MT <= PWAVES, "one expansion job per wave");
     static_assert(MT == 2 || MT == 4, "head dim 64 or 128");
 };
 
-// Registers holding one tile's inputs while they are in flight: latent slices (cached tiles:
-// k-steps of c_k, then of c_v) or chunk rows (new tiles: key pieces, then value pieces).
+// Registers holding one tile's inputs while they are in flight: for a cached tile the lane's
+// latent slices (k-steps of c_k, then of c_v), for a chunk tile the thread's 16-byte pieces of the
+// chunk rows (key pieces, then value pieces).  Every slot is one unconditional 16-byte load whose
+// address is chosen by the tile's kind, so the registers stay registers.
 template <int N>
 struct Stage {
     uint4 r[N];
@@ -86,8 +92,9 @@ struct Stage {
 template <int D, int RK, int RV>
 __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     using SH = PShape<D, RK, RV>;
-    constexpr int MT = SH::MT, KS = SH::KS, KK = SH::KK, KV = SH::KV;
-    constexpr int NEWK = SH::NEWK, NEWV = SH::NEWV, NST = SH::NST;
+    constexpr int MT = SH::MT, KS = SH::KS, KK = SH::KK, KV = SH::KV, KMAX = SH::KMAX;
+    constexpr int NEWP = SH::NEWP, NST = SH::NST;
+    using St = Stage<NST>;
 
     // operand tiles: sK[buf][k-step][lane], sV[buf][2N + kj][lane] (16 bytes each)
     __shared__ __align__(16) uint4 sK[2][KS][64];
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     const int qend = min(nn, q0 + QWG);                 // this block's queries: [q0, qend)
     const int ctiles = (len + 31) >> 5;                 // cached tiles
     const int tiles = ctiles + ((qend + 31) >> 5);      // then chunk tiles up to the last query
-    const int wq0 = q0 + 64 * wave;                     // this wave's first query
+    const int wq0 = q0 + 32 * wave;                     // this wave's first query
     const bool wlive = wq0 < qend;
 
     const uint16_t *qp = static_cast<const uint16_t *>(a.q);
@@ -122,145 +129,129 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new);
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
 
-    // ---- expansion jobs of this wave: key tile mk and/or value tile nv (-1: none)
-    const int mk = MT == 4 ? wave : (wave < 2 ? wave : -1);
-    const int nv = MT == 4 ? wave : (wave >= 2 ? wave - 2 : -1);
-    const int mkc = mk < 0 ? 0 : mk, nvc = nv < 0 ? 0 : nv;   // clamped for the (unused) loads
-    // A operand of the key expansion: W_up,t^K transposed, lane (l32, h2) holds column
-    // col0 + 32 mk + l32, ranks 16 ks + 8 h2 .. + 7.  B operand of the value expansion: W_up,t^V,
-    // lane (l32, h2) holds column col0 + 32 nv + l32, the same ranks.
-    const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
-                         ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
-    const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
-                         ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
-    uint4 wk[KK], wv[KV];
+    // ---- this wave's expansion job: key tile `jt` (job < MT) or value tile `jt` (MT <= job < 2MT);
+    // waves 2MT.. have none.  Both kinds take their W_up,t operand with the same lane layout:
+    // lane (l32, h2) holds column col0 + 32 jt + l32 at ranks 16 ks + 8 h2 .. + 7 (the A operand
+    // W^T of the key expansion, the B operand W of the value expansion).
+    const int job = wave;
+    const bool kjob = job < MT, vjob = job >= MT && job < 2 * MT;
+    const int jt = kjob ? job : (vjob ? job - MT : 0);
+    const int RJ = kjob ? RK : RV;
+    const uint16_t *Wj = static_cast<const uint16_t *>(kjob ? a.W_up_k : a.W_up_v) +
+                         ((size_t)a.t * a.G + g) * RJ * a.Dg + col0 + 32 * jt + l32;
+    uint4 wj[KMAX];
 #pragma unroll
-    for (int ks = 0; ks < KK; ++ks) {
+    for (int ks = 0; ks < KMAX; ++ks) {
+        const int k0 = min(16 * ks, RJ - 16) + 8 * h2;      // k-steps past RJ are unused
         uint16_t e[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) e[x] = Wk[(size_t)(16 * ks + 8 * h2 + x) * a.Dg + 32 * mkc + l32];
-        wk[ks] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+        for (int x = 0; x < 8; ++x) e[x] = Wj[(size_t)(k0 + x) * a.Dg];
+        wj[ks] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
                             e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
     }
+    // mu_t at the dims of this lane's results: a key tile's lane holds dims
+    // 32 jt + 8 (v / 4) + 4 h2 + v % 4, a value tile's lane holds dim 32 jt + l32
+    const uint16_t *muj = static_cast<const uint16_t *>(kjob ? a.mu_k : a.mu_v) +
+                          (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0 + 32 * jt;
+    float mj[16];
 #pragma unroll
-    for (int ks = 0; ks < KV; ++ks) {
-        uint16_t e[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) e[x] = Wv[(size_t)(16 * ks + 8 * h2 + x) * a.Dg + 32 * nvc + l32];
-        wv[ks] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
-                            e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
-    }
-    // mu_t: the key tile's lane holds dims 32 mk + 8 (v / 4) + 4 h2 + v % 4; the value tile's
-    // lane holds dim 32 nv + l32
-    const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) +
-                          (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
-    const uint16_t *muv = static_cast<const uint16_t *>(a.mu_v) +
-                          (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
-    float mkv[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mkv[v] = bf2f(muk[32 * mkc + 8 * (v >> 2) + 4 * h2 + (v & 3)]);
-    const float mvv = bf2f(muv[32 * nvc + l32]);
+    for (int v = 0; v < 16; ++v)
+        mj[v] = bf2f(muj[kjob ? 8 * (v >> 2) + 4 * h2 + (v & 3) : l32]);
 
     // ---- query operands (B of the score MFMA): lane (l32, h2) holds query row wq0 + 32u + l32,
     // k-step ks covers dims 32 (ks / 2) + 16 (ks % 2) + 4 h2 + {0..3} and + 8 + {0..3}.  Rows past
     // the chunk read the last valid row (their results are not stored).
-    uint4 qop[QT][KS];
-#pragma unroll
-    for (int u = 0; u < QT; ++u) {
-        const int i = min(wq0 + 32 * u + l32, nn - 1);
+    uint4 qop[KS];
+    {
+        const int i = min(wq0 + l32, nn - 1);
         const uint16_t *row = qp + (((size_t)b * a.Pn + i) * a.H + h) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int d0 = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * h2;
             const uint2 lo = *reinterpret_cast<const uint2 *>(row + d0);
             const uint2 hi = *reinterpret_cast<const uint2 *>(row + d0 + 8);
-            qop[u][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            qop[ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
     }
 
-    // ---- tile inputs.  Cached tile c: token 32c + l32 (the last valid token past the end) of
-    // one page (P is a multiple of 32); an out-of-range page id poisons the tile with NaN.
-    // Chunk tile n: rows 32n .. 32n + 31 of k_new / v_new (clamped to the last valid row).
-    auto issue = [&](int tile, Stage<NST> &st) {
+    // ---- tile inputs.  Cached tile c: this wave's job's latents (c_k for a key job, c_v for a
+    // value job) of token 32c + l32 (the last valid token past the end), in one page (P is a
+    // multiple of 32); an out-of-range page id poisons the tile with NaN.  Chunk tile n: piece
+    // p = tid + 512 x of each axis is row 32n + p / (D / 8) (clamped to the last valid row),
+    // dims 8 (p % (D / 8)) .. + 7; slots [0, NEWP) hold key pieces, [NEWP, 2 NEWP) value pieces.
+    const uint16_t *pool_j = kjob ? kp : vp;
+    auto issue = [&](int tile, St &st) __attribute__((always_inline)) {
         tile = min(tile, tiles - 1);
-        if (tile < ctiles) {
-            const int j = min(32 * tile + l32, len - 1);
-            int page = bt[(32 * tile) / a.P];
-            page = (unsigned)page < (unsigned)a.n_pages ? page : 0;
-            const size_t row = ((size_t)page * a.G + g) * a.P + j % a.P;
+        const bool cached = tile < ctiles;
+        const int j = min(32 * tile + l32, max(len - 1, 0));
+        int page = bt[min((32 * tile) / a.P, a.max_pages - 1)];
+        page = (unsigned)page < (unsigned)a.n_pages ? page : 0;
+        const size_t row = ((size_t)page * a.G + g) * a.P + j % a.P;
+        const int n0 = 32 * (tile - ctiles);
 #pragma unroll
-            for (int ks = 0; ks < KK; ++ks)
-                st.r[ks] = *reinterpret_cast<const uint4 *>(kp + row * RK + 16 * ks + 8 * h2);
-#pragma unroll
-            for (int ks = 0; ks < KV; ++ks)
-                st.r[KK + ks] = *reinterpret_cast<const uint4 *>(vp + row * RV + 16 * ks + 8 * h2);
-        } else {
-            const int n0 = 32 * (tile - ctiles);
-#pragma unroll
-            for (int x = 0; x < NEWK; ++x) {
-                const int idx = tid + 64 * PWAVES * x;          // (k-step, lane) of the operand
-                const int ks = idx >> 6, ln = idx & 63;
-                const int i = min(n0 + (ln & 31), nn - 1);
-                const int d0 = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * (ln >> 5);
-                const uint16_t *row = kn + ((size_t)b * a.Pn + i) * a.new_stride + (size_t)h * D;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(row + d0);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(row + d0 + 8);
-                st.r[x] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-#pragma unroll
-            for (int x = 0; x < NEWV; ++x) {
-                const int idx = tid + 64 * PWAVES * x;          // (token, 8-dim piece)
-                const int i = min(n0 + idx / (D / 8), nn - 1);
-                const uint16_t *row = vn + ((size_t)b * a.Pn + i) * a.new_stride + (size_t)h * D;
-                st.r[NEWK + x] = *reinterpret_cast<const uint4 *>(row + 8 * (idx % (D / 8)));
-            }
+        for (int x = 0; x < NST; ++x) {
+            const uint16_t *lat = pool_j + row * RJ + min(16 * x, RJ - 16) + 8 * h2;
+            const int pc = min(tid + 64 * PWAVES * (x % NEWP), SH::PIECES - 1);
+            const int i = min(n0 + pc / (D / 8), nn - 1);
+            const uint16_t *chk = (x < NEWP ? kn : vn) + ((size_t)b * a.Pn + i) * a.new_stride +
+                                  (size_t)h * D + 8 * (pc % (D / 8));
+            st.r[x] = *reinterpret_cast<const uint4 *>(cached ? lat : chk);
         }
     };
 
     // ---- write tile `tile` into LDS buffer `buf` in operand layout
-    auto produce = [&](int tile, const Stage<NST> &st, int buf) {
+    auto produce = [&](int tile, const St &st, int buf) __attribute__((always_inline)) {
         if (tile >= tiles) return;
         if (tile < ctiles) {
             const int page = bt[(32 * tile) / a.P];
             const float poison = (unsigned)page < (unsigned)a.n_pages ? 0.f : __builtin_nanf("");
-            if (mk >= 0) {
-                // K_hat^T tile mk: D[m = dim][n = token]; lane (token l32, h2) gets dims
-                // 32 mk + 8 (v / 4) + 4 h2 + v % 4, i.e. k-steps 2 mk (v < 8) and 2 mk + 1
+            if (kjob) {
+                // K_hat^T tile jt: D[m = dim][n = token]; lane (token l32, h2) gets dims
+                // 32 jt + 8 (v / 4) + 4 h2 + v % 4, i.e. k-steps 2 jt (v < 8) and 2 jt + 1
                 f32x16 acc = {};
 #pragma unroll
-                for (int ks = 0; ks < KK; ++ks) acc = mfma(wk[ks], st.r[ks], acc);
+                for (int ks = 0; ks < KK; ++ks) acc = mfma(wj[ks], st.r[ks], acc);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] += mkv[v] + poison;
-                sK[buf][2 * mk][lane] = pack8(acc, 0);
-                sK[buf][2 * mk + 1][lane] = pack8(acc, 1);
-            }
-            if (nv >= 0) {
-                // V_hat tile nv: D[m = token][n = dim]; lane (dim l32, h2) gets tokens
+                for (int v = 0; v < 16; ++v) acc[v] += mj[v] + poison;
+                sK[buf][2 * jt][lane] = pack8(acc, 0);
+                sK[buf][2 * jt + 1][lane] = pack8(acc, 1);
+            } else if (vjob) {
+                // V_hat tile jt: D[m = token][n = dim]; lane (dim l32, h2) gets tokens
                 // 8 (v / 4) + 4 h2 + v % 4: token k-steps 0 (v < 8) and 1
                 f32x16 acc = {};
 #pragma unroll
-                for (int ks = 0; ks < KV; ++ks) acc = mfma(st.r[KK + ks], wv[ks], acc);
+                for (int ks = 0; ks < KV; ++ks) acc = mfma(st.r[ks], wj[ks], acc);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] += mvv + poison;
-                sV[buf][2 * nv][lane] = pack8(acc, 0);
-                sV[buf][2 * nv + 1][lane] = pack8(acc, 1);
+                for (int v = 0; v < 16; ++v) acc[v] += mj[v] + poison;
+                sV[buf][2 * jt][lane] = pack8(acc, 0);
+                sV[buf][2 * jt + 1][lane] = pack8(acc, 1);
             }
         } else {
+            // key piece (row jt, dims 8c .. 8c + 7): dims 8c + 4 hh + {0..3} are elements
+            // 4 (c % 2) .. + 3 of lane 32 hh + jt in k-step 2 (c / 4) + (c / 2) % 2
 #pragma unroll
-            for (int x = 0; x < NEWK; ++x) {
-                const int idx = tid + 64 * PWAVES * x;
-                sK[buf][idx >> 6][idx & 63] = st.r[x];
+            for (int x = 0; x < NEWP; ++x) {
+                const int pc = tid + 64 * PWAVES * x;
+                if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
+                const int jr = pc / (D / 8), c8 = pc % (D / 8);
+                const int ks = 2 * (c8 >> 2) + ((c8 >> 1) & 1);
+                const uint4 w = st.r[x];
+                uint2 *d0 = reinterpret_cast<uint2 *>(&sK[buf][ks][jr]) + (c8 & 1);
+                uint2 *d1 = reinterpret_cast<uint2 *>(&sK[buf][ks][32 + jr]) + (c8 & 1);
+                *d0 = make_uint2(w.x, w.y);
+                *d1 = make_uint2(w.z, w.w);
             }
-            // value piece (token jt, dims 8p .. 8p + 7) -> the V^T operand of each dim: lane
+            // value piece (row jt, dims 8p .. 8p + 7) -> the V^T operand of each dim: lane
             // (dim % 32, h2) of slot 2 (dim / 32) + jt / 16 holds tokens 16 kj + 8 (e / 4) + 4 h2 +
             // e % 4 at element e
 #pragma unroll
-            for (int x = 0; x < NEWV; ++x) {
-                const int idx = tid + 64 * PWAVES * x;
-                const int jt = idx / (D / 8), p8 = 8 * (idx % (D / 8));
-                const int kj = jt >> 4, rem = jt & 15;
+            for (int x = 0; x < NEWP; ++x) {
+                const int pc = tid + 64 * PWAVES * x;
+                if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
+                const int jr = pc / (D / 8), p8 = 8 * (pc % (D / 8));
+                const int kj = jr >> 4, rem = jr & 15;
                 const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
-                const uint4 w = st.r[NEWK + x];
+                const uint4 w = st.r[NEWP + x];
                 const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                 for (int y = 0; y < 8; ++y) {
@@ -273,89 +264,83 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // ---- online softmax state per query tile (log2 domain); O^T accumulators per 32-dim tile
-    float m_run[QT], l_run[QT];
-    f32x16 oacc[QT][MT];
+    // ---- online softmax state of this wave's 32 queries (log2 domain); O^T accumulators per
+    // 32-dim tile
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 oacc[MT];
 #pragma unroll
-    for (int u = 0; u < QT; ++u) {
-        m_run[u] = -INFINITY;
-        l_run[u] = 0.f;
-#pragma unroll
-        for (int n = 0; n < MT; ++n) oacc[u][n] = f32x16{};
-    }
+    for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
 
-    auto consume = [&](int tile, int buf) {
+    // Scores stay raw (q . k) until the exponent: p = 2^(s c - m) with c = scale log2(e) is one FMA
+    // and one exp2 per score; the running max m is kept in the scaled log2 domain.  Lazy rescale:
+    // the accumulators are rescaled only when a lane's max grows by more than kSlack (p <= 2^kSlack
+    // meanwhile, exact after the final normalisation by l).
+    constexpr float kSlack = 8.f;
+    const float csc = a.scale_log2;
+    const int wlast = min(wq0 + 31, qend - 1);          // this wave's last query
+
+    auto consume = [&](int tile, int buf) __attribute__((always_inline)) {
         if (!wlive) return;
         const bool cached = tile < ctiles;
         const int j0 = cached ? 32 * tile : 32 * (tile - ctiles);
-        if (!cached && j0 > min(wq0 + 63, qend - 1)) return;   // every token is after every query
-        uint4 kop[KS];
+        if (!cached && j0 > wlast) return;                  // every token is after every query
+        uint4 kop[KS], vop[2 * MT];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kop[ks] = sK[buf][ks][lane];
-        f32x16 sacc[QT];
+        f32x16 sc = {};
 #pragma unroll
-        for (int u = 0; u < QT; ++u) sacc[u] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int u = 0; u < QT; ++u) sacc[u] = mfma(kop[ks], qop[u][ks], sacc[u]);
-        uint4 vop[2 * MT];
+        for (int ks = 0; ks < KS; ++ks) sc = mfma(kop[ks], qop[ks], sc);
+        // the value operands take the key operands' registers
 #pragma unroll
         for (int x = 0; x < 2 * MT; ++x) vop[x] = sV[buf][x][lane];
-
-        uint4 pop[QT][2];
+        // edge tiles mask some score: the cached context's last tile, chunk tiles that reach past
+        // this wave's first query.  Lane (query, h2), element v: token 8 (v / 4) + 4 h2 + v % 4.
+        if (cached ? j0 + 32 > len : j0 + 31 > wq0) {
+            const int lim = cached ? len - 1 - j0 : wq0 + l32 - j0;   // last visible token
 #pragma unroll
-        for (int u = 0; u < QT; ++u) {
-            // lane (query, h2), element v: token j0 + 8 (v / 4) + 4 h2 + v % 4
-            const int iq = wq0 + 32 * u + l32;
-            const int lim = cached ? len - 1 - j0 : iq - j0;   // last visible token, tile-relative
-            float sv[16];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int j = 8 * (v >> 2) + 4 * h2 + (v & 3);
-                sv[v] = j <= lim ? sacc[u][v] * a.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, sv[v]);
-            }
-            mx = max_swap32(mx);
-            const float m_new = fmaxf(m_run[u], mx);
-            if (__builtin_amdgcn_ballot_w64(m_new > m_run[u]) != 0) {
-                const float alpha = exp2_(m_run[u] - m_new);
-                l_run[u] *= alpha;
-#pragma unroll
-                for (int n = 0; n < MT; ++n)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) oacc[u][n][v] *= alpha;
-                m_run[u] = m_new;
-            }
-            f32x16 p;
-            float ls = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                p[v] = exp2_(sv[v] - m_run[u]);
-                ls += p[v];
-            }
-            l_run[u] += ls;
-            pop[u][0] = pack8(p, 0);
-            pop[u][1] = pack8(p, 1);
+            for (int v = 0; v < 16; ++v)
+                if (8 * (v >> 2) + 4 * h2 + (v & 3) > lim) sc[v] = -INFINITY;
         }
+        float mx = sc[0];
 #pragma unroll
-        for (int n = 0; n < MT; ++n)
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+        mx = max_swap32(mx) * csc;
+        const float m_cand = fmaxf(m_run, mx);
+        if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kSlack) != 0) {
+            const float alpha = m_cand == -INFINITY ? 1.f : exp2_(m_run - m_cand);
+            l_run *= alpha;
 #pragma unroll
-            for (int kj = 0; kj < 2; ++kj)
+            for (int n = 0; n < MT; ++n)
 #pragma unroll
-                for (int u = 0; u < QT; ++u)
-                    oacc[u][n] = mfma(vop[2 * n + kj], pop[u][kj], oacc[u][n]);
+                for (int v = 0; v < 16; ++v) oacc[n][v] *= alpha;
+            m_run = m_cand;
+        }
+        // softmax weights as the two bf16 B operands of the value MFMAs
+        const float nm = -m_run;
+        f32x16 pr;
+        float ls = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            pr[v] = exp2_(fmaf(sc[v], csc, nm));
+            ls += pr[v];
+        }
+        l_run += ls;
+        const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
+#pragma unroll
+        for (int n = 0; n < MT; ++n) {
+            oacc[n] = mfma(vop[2 * n], p0, oacc[n]);
+            oacc[n] = mfma(vop[2 * n + 1], p1, oacc[n]);
+        }
     };
 
     // ---- pipeline: tile i + 1 produced while tile i is consumed; tile i + 2's inputs in flight
-    Stage<NST> s0, s1;
+    St s0, s1;
     issue(0, s0);
     issue(1, s1);
     produce(0, s0, 0);
     issue(2, s0);
     __syncthreads();
-    auto step = [&](int it, Stage<NST> &next) {
+    auto step = [&](int it, St &next) __attribute__((always_inline)) {
         produce(it + 1, next, (it + 1) & 1);
         issue(it + 3, next);
         consume(it, it & 1);
@@ -369,24 +354,19 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
 
     // ---- normalise and store: lane (query, h2) holds dims 32n + 8a + 4 h2 + {0..3}
     if (!wlive) return;
-    uint16_t *op = static_cast<uint16_t *>(a.out);
+    const int iq = wq0 + l32;
+    const float inv = 1.f / (l_run + __shfl_xor(l_run, 32, 64));
+    if (iq >= qend) return;
+    uint16_t *row = static_cast<uint16_t *>(a.out) + (((size_t)b * a.Pn + iq) * a.H + h) * D;
 #pragma unroll
-    for (int u = 0; u < QT; ++u) {
-        const int iq = wq0 + 32 * u + l32;
-        const float lsum = l_run[u] + __shfl_xor(l_run[u], 32, 64);
-        const float inv = 1.f / lsum;
-        if (iq >= qend) continue;
-        uint16_t *row = op + (((size_t)b * a.Pn + iq) * a.H + h) * D;
+    for (int n = 0; n < MT; ++n)
 #pragma unroll
-        for (int n = 0; n < MT; ++n)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x16 &o = oacc[u][n];
-                const uint2 w = make_uint2(pk_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
-                                           pk_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
-                *reinterpret_cast<uint2 *>(row + 32 * n + 8 * q4 + 4 * h2) = w;
-            }
-    }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x16 &o = oacc[n];
+            const uint2 w = make_uint2(pk_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
+                                       pk_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
+            *reinterpret_cast<uint2 *>(row + 32 * n + 8 * q4 + 4 * h2) = w;
+        }
 }
 
 template <int D, int RK, int RV>
