@@ -11,10 +11,11 @@
 // each expanded once per workgroup and shared by all its queries, so the d x r expansion of a
 // cached token is amortised over up to 256 queries.
 //
-// Layout of the work: one workgroup of 4 waves per (sequence, head, block of 256 queries); wave w
-// owns queries [64w, 64w + 64) of the block as two 32-query tiles.  Per 32-token tile:
-//   * the waves split the expansion (key tile M and value tile N = one MFMA chain each) and store
-//     the bf16 results in LDS directly in the lane layout of the attention MFMAs' operands;
+// Layout of the work: one workgroup of 8 waves (two per SIMD) per (sequence, head, block of 256
+// queries); wave w owns queries [32w, 32w + 32) of the block.  Per 32-token tile:
+//   * the waves split the expansion (key tile w or value tile w - 4: one MFMA chain each, mu_t
+//     entering exactly as one more k-step) and store the bf16 results in LDS directly in the lane
+//     layout of the attention MFMAs' operands;
 //     chunk tiles are copied into the same layout from the caller's rows;
 //   * every wave computes S^T = K_hat Q^T (32 tokens x 32 queries per query tile, v_mfma 32x32x16,
 //     K from LDS, Q^T in registers), so each lane holds 16 scores of one query: the softmax row
@@ -149,14 +150,14 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
         wj[ks] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
                             e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
     }
-    // mu_t at the dims of this lane's results: a key tile's lane holds dims
-    // 32 jt + 8 (v / 4) + 4 h2 + v % 4, a value tile's lane holds dim 32 jt + l32
+    // mu_t enters the expansion exactly through one more MFMA k-step: a key tile adds the mu row
+    // (A, k-slot 0 of lanes h2 = 0: mu at this lane's dim) times a row of ones (B); a value tile
+    // adds a column of ones (A) times the mu row (B).
     const uint16_t *muj = static_cast<const uint16_t *>(kjob ? a.mu_k : a.mu_v) +
-                          (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0 + 32 * jt;
-    float mj[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-        mj[v] = bf2f(muj[kjob ? 8 * (v >> 2) + 4 * h2 + (v & 3) : l32]);
+                          (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0 + 32 * jt + l32;
+    const uint32_t mu_bits = h2 == 0 ? *muj : 0u;
+    const uint4 mu_op = make_uint4(mu_bits, 0, 0, 0);
+    const uint4 one_op = make_uint4(h2 == 0 ? 0x3F80u : 0u, 0, 0, 0);
 
     // ---- query operands (B of the score MFMA): lane (l32, h2) holds query row wq0 + 32u + l32,
     // k-step ks covers dims 32 (ks / 2) + 16 (ks % 2) + 4 h2 + {0..3} and + 8 + {0..3}.  Rows past
@@ -179,23 +180,38 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     // multiple of 32); an out-of-range page id poisons the tile with NaN.  Chunk tile n: piece
     // p = tid + 512 x of each axis is row 32n + p / (D / 8) (clamped to the last valid row),
     // dims 8 (p % (D / 8)) .. + 7; slots [0, NEWP) hold key pieces, [NEWP, 2 NEWP) value pieces.
-    const uint16_t *pool_j = kjob ? kp : vp;
+    // Addresses are a per-lane constant plus a per-tile scalar: a cached tile lies in one page at
+    // slot (32c) % P, and a chunk piece's row offset inside its tile is fixed per thread.
+    const uint16_t *pool_j = (kjob ? kp : vp) + (size_t)g * a.P * RJ + 8 * h2;
+    const size_t page_elems = (size_t)a.G * a.P * RJ;
+    int pc_row[NST], pc_col[NST];                       // chunk piece of each stage slot
+#pragma unroll
+    for (int x = 0; x < NST; ++x) {
+        const int pc = min(tid + 64 * PWAVES * (x % NEWP), SH::PIECES - 1);
+        pc_row[x] = pc / (D / 8);
+        pc_col[x] = 8 * (pc % (D / 8));
+    }
+    const uint16_t *kn_b = kn + (size_t)b * a.Pn * a.new_stride + (size_t)h * D;
+    const uint16_t *vn_b = vn + (size_t)b * a.Pn * a.new_stride + (size_t)h * D;
     auto issue = [&](int tile, St &st) __attribute__((always_inline)) {
         tile = min(tile, tiles - 1);
         const bool cached = tile < ctiles;
-        const int j = min(32 * tile + l32, max(len - 1, 0));
+        // cached: token 32 tile + min(l32, last valid) in page bt[32 tile / P]
         int page = bt[min((32 * tile) / a.P, a.max_pages - 1)];
         page = (unsigned)page < (unsigned)a.n_pages ? page : 0;
-        const size_t row = ((size_t)page * a.G + g) * a.P + j % a.P;
+        const uint16_t *lat = pool_j + page * page_elems +
+                              (size_t)((32 * tile) % a.P + min(l32, max(len - 1 - 32 * tile, 0))) *
+                                  RJ;
+        // chunk: rows 32n + r, clamped to the last valid row
         const int n0 = 32 * (tile - ctiles);
+        const int rmax = nn - 1 - n0;
 #pragma unroll
         for (int x = 0; x < NST; ++x) {
-            const uint16_t *lat = pool_j + row * RJ + min(16 * x, RJ - 16) + 8 * h2;
-            const int pc = min(tid + 64 * PWAVES * (x % NEWP), SH::PIECES - 1);
-            const int i = min(n0 + pc / (D / 8), nn - 1);
-            const uint16_t *chk = (x < NEWP ? kn : vn) + ((size_t)b * a.Pn + i) * a.new_stride +
-                                  (size_t)h * D + 8 * (pc % (D / 8));
-            st.r[x] = *reinterpret_cast<const uint4 *>(cached ? lat : chk);
+            const uint16_t *chk = (x < NEWP ? kn_b : vn_b) +
+                                  (uint32_t)((n0 + min(pc_row[x], rmax)) * (int)a.new_stride +
+                                             pc_col[x]);
+            const uint16_t *l = lat + min(16 * x, RJ - 16);
+            st.r[x] = *reinterpret_cast<const uint4 *>(cached ? l : chk);
         }
     };
 
@@ -203,26 +219,24 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     auto produce = [&](int tile, const St &st, int buf) __attribute__((always_inline)) {
         if (tile >= tiles) return;
         if (tile < ctiles) {
-            const int page = bt[(32 * tile) / a.P];
-            const float poison = (unsigned)page < (unsigned)a.n_pages ? 0.f : __builtin_nanf("");
+            // an out-of-range page id poisons the tile: mu becomes NaN (bf16 0x7FC0), which the
+            // mu k-step spreads to every element
+            const bool bad = (unsigned)bt[(32 * tile) / a.P] >= (unsigned)a.n_pages;
+            const uint4 mu_t = make_uint4(bad && h2 == 0 ? 0x7FC0u : mu_op.x, 0, 0, 0);
             if (kjob) {
                 // K_hat^T tile jt: D[m = dim][n = token]; lane (token l32, h2) gets dims
                 // 32 jt + 8 (v / 4) + 4 h2 + v % 4, i.e. k-steps 2 jt (v < 8) and 2 jt + 1
-                f32x16 acc = {};
+                f32x16 acc = mfma(mu_t, one_op, f32x16{});
 #pragma unroll
                 for (int ks = 0; ks < KK; ++ks) acc = mfma(wj[ks], st.r[ks], acc);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] += mj[v] + poison;
                 sK[buf][2 * jt][lane] = pack8(acc, 0);
                 sK[buf][2 * jt + 1][lane] = pack8(acc, 1);
             } else if (vjob) {
                 // V_hat tile jt: D[m = token][n = dim]; lane (dim l32, h2) gets tokens
                 // 8 (v / 4) + 4 h2 + v % 4: token k-steps 0 (v < 8) and 1
-                f32x16 acc = {};
+                f32x16 acc = mfma(one_op, mu_t, f32x16{});
 #pragma unroll
                 for (int ks = 0; ks < KV; ++ks) acc = mfma(st.r[ks], wj[ks], acc);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] += mj[v] + poison;
                 sV[buf][2 * jt][lane] = pack8(acc, 0);
                 sV[buf][2 * jt + 1][lane] = pack8(acc, 1);
             }
