@@ -319,6 +319,161 @@ int mfma_blocks_of(const EncodeArgs &a) {
     return a.G * ((a.r + 31) / 32) * ((a.B + 31) / 32);
 }
 
+// ---------------------------------------------------------------- bf16, many rows
+// The bulk encode of a prefill chunk (thousands of rows): a workgroup owns (axis, group, 32 latent
+// columns, 512 rows).  It stages its column slice of W_down transposed in LDS once (W^T[col][x]);
+// each of its waves then streams whole rows: C^T = W^T X^T on v_mfma_f32_32x32x16_bf16 with
+// A = W^T from LDS (16 bytes per lane per k-step) and B = X^T straight from the staging rows
+// (16 bytes per lane per k-step), over the full stacked axis, so no partial tiles are exchanged.
+// A lane's results are one row (its B column) at 16 latent columns, so its append slot is one
+// lookup.  mu W is formed once per wave, in its own fp32 chain, and subtracted at the end.
+constexpr int RWAVES = 4;            // waves per workgroup
+constexpr int RXMAX = 512;           // largest stacked axis it serves (LDS: 32 x 520 bf16)
+constexpr int RTILES = 16;           // 32-row tiles per workgroup
+constexpr int RGRP = 8;              // k-steps per load group
+
+__global__ __launch_bounds__(64 * RWAVES) void encode_rows_kernel(EncodePair pr) {
+    __shared__ __align__(16) uint16_t sWt[32][RXMAX + 8];
+
+    int blk = blockIdx.x;
+    const int axis = blk < pr.blocks_k ? 0 : 1;
+    if (axis) blk -= pr.blocks_k;
+    const EncodeArgs a = axis ? pr.ax[1] : pr.ax[0];
+    const int ctiles = (a.r + 31) / 32;
+    const int rblocks = (a.B + 32 * RTILES - 1) / (32 * RTILES);
+    const int ct = blk % ctiles;
+    const int rb = (blk / ctiles) % rblocks;
+    const int g = blk / (ctiles * rblocks);
+    const int c0 = ct * 32;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int X = a.T * a.Dg;
+    const int KS = X / 16;                               // X is a multiple of 64
+
+    // ---- W^T slice into LDS: 8-column pieces of W_down rows (columns past r are zero)
+    const uint16_t *W = static_cast<const uint16_t *>(a.W_down) + (size_t)g * X * a.r;
+    for (int idx = tid; idx < X * 4; idx += 64 * RWAVES) {
+        const int xr = idx >> 2, cg = 8 * (idx & 3);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (c0 + cg < a.r) w = *reinterpret_cast<const uint4 *>(W + (size_t)xr * a.r + c0 + cg);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sWt[cg + e][xr] = static_cast<uint16_t>(wd[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    auto wt = [&](int ks) {           // A operand: column l32, stacked 16 ks + 8 h2 .. + 7
+        return *reinterpret_cast<const uint4 *>(&sWt[l32][16 * ks + 8 * h2]);
+    };
+
+    // ---- mu W (the same for every row): B = mu at stacked 16 ks + 8 h2 .. + 7
+    const uint16_t *mu = static_cast<const uint16_t *>(a.mu) + (size_t)g * X;
+    f32x16 muacc = {};
+    for (int ks = 0; ks < KS; ++ks)
+        muacc = mfma32(wt(ks), *reinterpret_cast<const uint4 *>(mu + 16 * ks + 8 * h2), muacc);
+
+    // this wave's row tiles: r0 = 32 (rb RTILES + wave + RWAVES i).  The append slot of this
+    // lane's row in every tile is fetched first, so the row stream below waits on nothing else.
+    constexpr int TPW = RTILES / RWAVES;                 // row tiles per wave
+    const uint16_t *x = static_cast<const uint16_t *>(a.x);
+    int ntile = 0;
+    while (ntile < TPW && 32 * (rb * RTILES + wave + RWAVES * ntile) < a.B) ++ntile;
+    uint16_t *dst[TPW];
+    bool live[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int rr = 32 * (rb * RTILES + wave + RWAVES * i) + l32;
+        int seq, pos;
+        live[i] = rr < a.B && encode_row(a, min(rr, a.B - 1), seq, pos);
+        const bool store = live[i] && pos >= 0 && pos < a.max_pages * a.P;
+        const int page = store ? a.block_table[(size_t)seq * a.max_pages + pos / a.P] : -1;
+        dst[i] = (unsigned)page < (unsigned)a.n_pages
+            ? static_cast<uint16_t *>(a.pool) + (((size_t)page * a.G + g) * a.P + pos % a.P) * a.r
+            : nullptr;
+    }
+    // staging offset of stacked index k: k + t (H d - d) with t = k / d per head ((t, i) of head
+    // g), plain k for LLA-2D ((t, h, i) order); d is a power of two
+    const int dsh = 31 - __builtin_clz(a.d);
+    const int tjump = a.mode ? 0 : (a.H - 1) * a.d;
+    const int ngrp = (KS + RGRP - 1) / RGRP;
+    const int nsteps = ntile * ngrp;
+    // the stream of (tile, k-group) steps is double-buffered: the next group's rows are in
+    // flight during the current group's MFMAs
+    auto load = [&](int st, uint4 *xv) {
+        st = min(st, max(nsteps - 1, 0));
+        const int i = st / ngrp, k0 = RGRP * (st - i * ngrp);
+        const int row = min(32 * (rb * RTILES + wave + RWAVES * i) + l32, a.B - 1);
+        const uint16_t *xr = x + (a.mode ? (size_t)row * X : ((size_t)row * a.T * a.H + g) * a.d);
+#pragma unroll
+        for (int j = 0; j < RGRP; ++j) {
+            const int k = 16 * min(k0 + j, KS - 1) + 8 * h2;
+            xv[j] = *reinterpret_cast<const uint4 *>(xr + k + (k >> dsh) * tjump);
+        }
+    };
+    f32x16 acc = {};
+    auto step = [&](int st, const uint4 *xv) {
+        const int i = st / ngrp, k0 = RGRP * (st - i * ngrp);
+        if (k0 + RGRP <= KS) {
+#pragma unroll
+            for (int j = 0; j < RGRP; ++j) acc = mfma32(wt(k0 + j), xv[j], acc);
+        } else {
+#pragma unroll
+            for (int j = 0; j < RGRP; ++j)
+                if (k0 + j < KS) acc = mfma32(wt(k0 + j), xv[j], acc);
+        }
+        if (k0 + RGRP < KS) return;
+        // tile done.  Lane (row, h2), element v: latent column c0 + 8 (v / 4) + 4 h2 + v % 4
+        const int rr = 32 * (rb * RTILES + wave + RWAVES * i) + l32;
+        const f32x16 res = acc;
+        acc = f32x16{};
+        bool lv = false;
+        uint16_t *d = nullptr;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+            if (u == i) { lv = live[u]; d = dst[u]; }
+        if (!lv) return;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = c0 + 8 * q + 4 * h2;
+            if (col >= a.r) continue;                    // r is a multiple of 8
+            const float c[4] = {res[4 * q] - muacc[4 * q], res[4 * q + 1] - muacc[4 * q + 1],
+                                res[4 * q + 2] - muacc[4 * q + 2],
+                                res[4 * q + 3] - muacc[4 * q + 3]};
+            if (a.c_out)
+                *reinterpret_cast<float4 *>(a.c_out + ((size_t)rr * a.G + g) * a.r + col) =
+                    make_float4(c[0], c[1], c[2], c[3]);
+            if (d)
+                *reinterpret_cast<uint2 *>(d + col) =
+                    make_uint2((uint32_t)f2bf(c[0]) | (uint32_t)f2bf(c[1]) << 16,
+                               (uint32_t)f2bf(c[2]) | (uint32_t)f2bf(c[3]) << 16);
+        }
+    };
+    uint4 xa[RGRP], xb[RGRP];
+    load(0, xa);
+    for (int st = 0; st < nsteps; st += 2) {
+        load(st + 1, xb);
+        step(st, xa);
+        if (st + 1 >= nsteps) break;
+        load(st + 2, xa);
+        step(st + 1, xb);
+    }
+}
+
+int rows_blocks_of(const EncodeArgs &a) {
+    return a.G * ((a.r + 31) / 32) * ((a.B + 32 * RTILES - 1) / (32 * RTILES));
+}
+
+// The row-streaming kernel serves bf16 codecs with a short stacked axis, many rows, and 16-byte
+// aligned rows of W_down; everything else takes encode_mfma_kernel.
+bool rows_kernel_fits(const EncodeArgs &a) {
+    const int X = a.T * a.Dg;
+    return X <= RXMAX && a.B >= 256 && a.r % 8 == 0 &&
+           (reinterpret_cast<uintptr_t>(a.W_down) & 15) == 0 &&
+           (reinterpret_cast<uintptr_t>(a.mu) & 15) == 0 &&
+           (reinterpret_cast<uintptr_t>(a.c_out) & 15) == 0;
+}
+
 }  // namespace
 
 hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
@@ -326,7 +481,11 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
     EncodePair pr;
     pr.ax[0] = k_axis;
     pr.ax[1] = v_axis;
-    if (bf16) {
+    if (bf16 && rows_kernel_fits(k_axis) && rows_kernel_fits(v_axis)) {
+        pr.blocks_k = rows_blocks_of(k_axis);
+        const unsigned blocks = (unsigned)(pr.blocks_k + rows_blocks_of(v_axis));
+        hipLaunchKernelGGL(encode_rows_kernel, dim3(blocks), dim3(64 * RWAVES), 0, st, pr);
+    } else if (bf16) {
         pr.blocks_k = mfma_blocks_of(k_axis);
         const unsigned blocks = (unsigned)(pr.blocks_k + mfma_blocks_of(v_axis));
         hipLaunchKernelGGL(encode_mfma_kernel, dim3(blocks), dim3(64 * EWAVES), 0, st, pr);

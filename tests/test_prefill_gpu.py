@@ -128,13 +128,15 @@ def test_prefill_single_token_chunk_matches_decode(gpu):
     assert_close(synth.from_device(out), ref, "bf16", "decode with the chunk token as self")
 
 
-@pytest.mark.parametrize("shape", ["ouro14_21x", "h4_d128_2d_r32"])
-def test_encode_chunk(gpu, shape):
+@pytest.mark.parametrize("shape,Pn", [("ouro14_21x", 70), ("h4_d128_2d_r32", 70),
+                                      ("ouro14_21x", 100), ("h2_d64_r16", 100)])
+def test_encode_chunk(gpu, shape, Pn):
     """lla_encode_chunk: c against the oracle; the pool holds c rounded once at write_pos + i for
-    live rows only; every other slot keeps its bytes."""
+    live rows only; every other slot keeps its bytes.  210 rows take the split-axis kernel, 300
+    rows of a short stacked axis the row-streaming one."""
     cfg = SHAPES[shape]
-    B, N, Pn = 3, 90, 70
-    ch = Chunk(cfg, B, N, Pn, [90, 0, 33], [70, 0, 41], gpu)
+    B, N = 3, 90
+    ch = Chunk(cfg, B, N, Pn, [90, 0, 33], [Pn, 0, 41], gpu)
     c, p = ch.cfg, ch.p
     wpos_h = p.seq_lens.copy()
     wpos = torch.from_numpy(wpos_h).to(gpu)
