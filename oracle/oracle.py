@@ -214,3 +214,40 @@ def encode_prefill(mode, T, H, d, r, W_down, mu, x, write_pos, n_new, block_tabl
     for b in range(B):
         c[b, int(n[b]):] = 0.0
     return c, pool
+
+
+def stack_rows(mode, x):
+    """Trajectory rows x [n][T][H][d] -> stacked vectors [G][n][X], in the order the encode uses
+    (per head: (t, i) of head g; LLA-2D: (t, h, i))."""
+    x = _f64(x)
+    n, T, H, d = x.shape
+    if mode == 1:
+        return x.reshape(1, n, T * H * d)
+    return np.ascontiguousarray(np.transpose(x, (2, 0, 1, 3)).reshape(H, n, T * d))
+
+
+def fit_svd(mode, T, H, d, r, x):
+    """Codec initialisation from the top right singular vectors of the activations (pith.science
+    paper page, "What carries the argument"): per group, mu = mean of the stacked rows,
+    W_down = the r leading right singular vectors of the centred stacked matrix (columns in
+    decreasing singular value; sign fixed so each column's entry of largest magnitude is
+    positive), W_up,t = the transpose of W_down's rows t*D_g .. (t+1)*D_g - 1.
+    x: rows [n][T][H][d].  Returns (mu [G][X], W_down [G][X][r], W_up [T][G][r][D_g],
+    sigma [G][r])."""
+    A = stack_rows(mode, x)
+    G, n, X = A.shape
+    Dg = X // T
+    mu = A.mean(axis=1)
+    Wd = np.empty((G, X, r))
+    sig = np.empty((G, r))
+    for g in range(G):
+        _, s, vt = np.linalg.svd(A[g] - mu[g][None, :], full_matrices=False)
+        V = vt[:r].T.copy()
+        for j in range(r):
+            k = int(np.argmax(np.abs(V[:, j])))
+            if V[k, j] < 0:
+                V[:, j] = -V[:, j]
+        Wd[g] = V
+        sig[g] = s[:r]
+    Wup = np.ascontiguousarray(np.transpose(Wd.reshape(G, T, Dg, r), (1, 0, 3, 2)))
+    return mu, Wd, Wup, sig
