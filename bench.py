@@ -304,6 +304,54 @@ def prefill_leg(cfg, layers, dev, launch, steps, warmup):
             "prefill_tokens_per_s": round(B * Pn / step_s, 1)}
 
 
+FIT_ITERS = 40
+
+
+def fit_leg(cfg, dev, steps):
+    """Codec fit of one layer (both axes) from n = B x N rows of staged trajectories
+    (lla_fit_svd, FIT_ITERS steps of subspace iteration).  The rows are i.i.d. draws with the
+    staging spread: the work per call does not depend on the data."""
+    import torch
+    from looped_transformer_kv_amd import lla, synth
+
+    T, H, d = cfg.T, cfg.H, cfg.d
+    n = cfg.B * cfg.N
+    codec = lla.make_codec(cfg.mode, T, H, d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.ROOT_SEED + 11)
+    xs = math.sqrt(sum(cfg.decay ** i for i in range(cfg.r_k)) / cfg.X + 0.01)
+    x = [(xs * torch.randn((n, T, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+         for _ in range(2)]
+    G, X, Dg = cfg.G, cfg.X, cfg.Dg
+    outs, wss = [], []
+    for r in (cfg.r_k, cfg.r_v):
+        outs.append((torch.empty((G, X), dtype=torch.bfloat16, device=dev),
+                     torch.empty((G, X, r), dtype=torch.bfloat16, device=dev),
+                     torch.empty((T, G, r, Dg), dtype=torch.bfloat16, device=dev)))
+        wss.append(torch.empty(lla.lla_fit_plan(codec, r, n) // 4 + 4, dtype=torch.float32,
+                               device=dev))
+
+    def run():
+        for ax, r in enumerate((cfg.r_k, cfg.r_v)):
+            mu, Wd, Wu = outs[ax]
+            lla.lla_fit_svd(codec, r, x[ax], n, FIT_ITERS, mu, Wd, Wu, None, wss[ax])
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cov_flops = 2 * 2 * n * X * X * G           # A^T A of both axes (full X x X)
+    return {"kernel": "lla_fit_svd (K and V of one layer)", "rows": n, "iters": FIT_ITERS,
+            "ms_per_layer": round(ms, 3), "covariance_flops": cov_flops,
+            "covariance_TFLOPs_over_call": round(cov_flops / (ms * 1e-3) / 1e12, 1),
+            "staged_bytes": 2 * n * T * H * d * 2}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,6 +374,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing the chunked prefill (lla_prefill_attn, a chunk of "
                          f"{PREFILL_CHUNK} after the cached context, then lla_encode_chunk)")
+    ap.add_argument("--no-fit", action="store_true",
+                    help="skip timing the codec fit (lla_fit_svd of one layer's K and V from "
+                         "B x N staged rows)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -527,6 +578,9 @@ def main():
                                                                          (32, 32)):
         log("timing the chunked prefill")
         result["prefill"] = prefill_leg(cfg, layers, dev, launch, K, args.warmup)
+    if not args.no_fit and cfg.X % 128 == 0 and max(cfg.r_k, cfg.r_v) <= 64:
+        log("timing the codec fit")
+        result["fit"] = fit_leg(cfg, dev, 3)
     if not args.no_flat:
         log("timing the flat comparator")
         result["flat_ref"] = flat_comparator(cfg, dev, max(5, K))

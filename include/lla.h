@@ -232,6 +232,31 @@ lla_status lla_prefill_attn(const lla_codec *codec, const lla_params *params,
                             const void *v_new, int64_t new_stride, float scale, void *out,
                             void *stream);
 
+/*
+ * Codec fit from the top right singular vectors of activations (pith.science paper page for
+ * "Looped Latent Attention", "What carries the argument": the codec is initialised from the top
+ * right singular vectors of teacher activations).  For every group g, with a_j the stacked
+ * vector of row j (the encode's stacking order) and n rows:
+ *   mu[g] = mean_j a_j;   W_down[g] = the r leading right singular vectors of [a_j - mu], as
+ *   columns in decreasing singular value, each column's entry of largest magnitude positive;
+ *   W_up[t][g] = the transpose of W_down[g]'s rows t*D_g .. (t+1)*D_g - 1;
+ *   sigma[g] (optional, fp32 [G][r]) = the r leading singular values.
+ * Computed on the GPU as the centred covariance A^T A - n mu^T mu (matrix cores, fp32
+ * accumulation of the exact bf16 inputs), `iters` steps of subspace iteration with r + 8 columns
+ * (CholeskyQR2), then a Rayleigh-Ritz step; the result converges to the exact one as
+ * (lambda_{r+9} / lambda_r)^iters.  Outputs are rounded once to bf16.
+ *   x          rows [n][T][H][d] bf16 (e.g. a layer's staged K or V trajectories), 16-byte aligned
+ *   mu         [G][X], W_down [G][X][r], W_up [T][G][r][D_g], bf16, caller-owned
+ *   workspace  device, >= lla_fit_plan bytes, 16-byte aligned
+ * bf16 codecs only (LLA_ERR_DTYPE); r in [1, 64] and X = T*D_g a multiple of 128 (at most 8192)
+ * else LLA_ERR_UNSUPPORTED (r > X: LLA_ERR_SHAPE); n >= r + 9 (+1 if r is odd), <= 2^30;
+ * 0 <= iters <= 10000.
+ */
+lla_status lla_fit_plan(const lla_codec *codec, int32_t r, int64_t n, size_t *workspace_bytes);
+lla_status lla_fit_svd(const lla_codec *codec, int32_t r, const void *x, int64_t n,
+                       int32_t iters, void *mu, void *W_down, void *W_up, float *sigma,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Split plan and workspace size of lla_ref_attn. */
 lla_status lla_ref_plan(int32_t n_heads, int32_t d_head, int32_t dtype, const lla_cache *flat,
                         lla_plan *plan);

@@ -475,3 +475,70 @@ const char *lla_status_str(lla_status s) {
 const char *lla_version(void) { return "0.1.0"; }
 
 }  // extern "C"
+
+namespace {
+
+lla_status fit_check(const lla_codec *c, int32_t r, int64_t n, int *S, size_t *bytes) {
+    lla_status st = check_codec(c);
+    if (st != LLA_OK) return st;
+    if (c->dtype != LLA_BF16) return LLA_ERR_DTYPE;
+    const Shape sh = shape_of(c);
+    if (r < 1 || r > sh.X) return LLA_ERR_SHAPE;
+    if (r > 64 || sh.X % 128 != 0 || sh.X > 8192) return LLA_ERR_UNSUPPORTED;
+    if (n < fit_block_cols(r) + 1 || n > (int64_t)1 << 30) return LLA_ERR_SHAPE;
+    *bytes = fit_workspace_floats(sh.G, (int)sh.X, r, (long)n, S) * sizeof(float);
+    return LLA_OK;
+}
+
+}  // namespace
+
+lla_status lla_fit_plan(const lla_codec *c, int32_t r, int64_t n, size_t *workspace_bytes) {
+    if (!workspace_bytes) return LLA_ERR_NULL;
+    int S;
+    return fit_check(c, r, n, &S, workspace_bytes);
+}
+
+lla_status lla_fit_svd(const lla_codec *c, int32_t r, const void *x, int64_t n, int32_t iters,
+                       void *mu, void *W_down, void *W_up, float *sigma, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    int S;
+    size_t need;
+    lla_status st = fit_check(c, r, n, &S, &need);
+    if (st != LLA_OK) return st;
+    if (iters < 0 || iters > 10000) return LLA_ERR_SHAPE;
+    if (!x || !mu || !W_down || !W_up || !workspace) return LLA_ERR_NULL;
+    if (workspace_bytes < need) return LLA_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(workspace)) return LLA_ERR_ALIGN;
+    const Shape sh = shape_of(c);
+    FitArgs a{};
+    a.x = x;
+    a.n = (long)n;
+    a.T = c->T;
+    a.H = c->n_heads;
+    a.d = c->d_head;
+    a.G = sh.G;
+    a.X = (int)sh.X;
+    a.r = r;
+    a.rb = fit_block_cols(r);
+    a.mode = c->mode;
+    a.iters = iters;
+    a.S = S;
+    a.bf16 = 1;
+    float *w = static_cast<float *>(workspace);
+    a.part = w;
+    w += (size_t)S * a.G * a.X * a.X;
+    a.colsum = w;
+    w += (size_t)S * a.G * a.X;
+    a.C = w;
+    w += (size_t)a.G * a.X * a.X;
+    a.mu32 = w;
+    w += (size_t)a.G * a.X;
+    a.V = w;
+    w += (size_t)a.G * a.X * a.rb;
+    a.W = w;
+    a.mu_out = mu;
+    a.Wd_out = W_down;
+    a.Wu_out = W_up;
+    a.sigma = sigma;
+    return launch_fit(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}

@@ -62,6 +62,22 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+// One codec fit (bf16): workspace pointers are fp32 regions carved by the host.
+constexpr int kFitMaxCols = 72;      // columns of the iterated block (r + 8, r <= 64)
+constexpr int kFitSweeps = 12;       // Jacobi sweeps of the Rayleigh-Ritz step
+struct FitArgs {
+    const void *x;                   // trajectory rows [n][T][H][d]
+    long n;
+    int T, H, d, G, X, r, rb, mode, iters, S, bf16;
+    float *part;                     // [S][G][X][X] partial A^T A (blocks bi <= bj)
+    float *colsum;                   // [S][G][X] partial column sums
+    float *C;                        // [G][X][X] centred covariance
+    float *mu32;                     // [G][X]
+    float *V, *W;                    // [G][X][rb] iterate and product
+    void *mu_out, *Wd_out, *Wu_out;  // [G][X], [G][X][r], [T][G][r][X/T] in the codec dtype
+    float *sigma;                    // optional [G][r]
+};
+
 // One encode+append call.
 struct EncodeArgs {
     const void *x;                   // staging rows [B][T][H][d] (B = rows)
@@ -101,6 +117,9 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
 bool decode_bf16_supported(int d, int r_k, int r_v);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 bool prefill_supported(int d, int r_k, int r_v);
+hipError_t launch_fit(FitArgs a, hipStream_t s);
+size_t fit_workspace_floats(int G, int X, int r, long n, int *S_out);
+int fit_block_cols(int r);
 int prefill_queries_per_block();
 
 constexpr int kPartialPad = 4;   // partial record = d + 4 floats (16-byte aligned records)

@@ -92,6 +92,10 @@ def lib():
         L.lla_prefill_attn.restype = i32
         L.lla_prefill_attn.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, i32, vp, vp,
                                        vp, vp, i64, f32, vp, vp]
+        L.lla_fit_plan.restype = i32
+        L.lla_fit_plan.argtypes = [P(lla_codec), i32, i64, P(sz)]
+        L.lla_fit_svd.restype = i32
+        L.lla_fit_svd.argtypes = [P(lla_codec), i32, vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
         L.lla_ref_plan.restype = i32
         L.lla_ref_plan.argtypes = [i32, i32, i32, P(lla_cache), P(lla_plan)]
         L.lla_ref_attn.restype = i32
@@ -231,6 +235,23 @@ def lla_prefill_attn(codec, params, cache, t, chunk, n_new, q, k_new, v_new, new
                                 _ptr(v_new), int(new_stride), float(scale), _ptr(out),
                                 _stream(stream))
     return _check("lla_prefill_attn", st, check)
+
+
+def lla_fit_plan(codec, r, n) -> int:
+    out = ctypes.c_size_t(0)
+    _check("lla_fit_plan", lib().lla_fit_plan(ctypes.byref(codec), int(r), int(n),
+                                              ctypes.byref(out)), True)
+    return int(out.value)
+
+
+def lla_fit_svd(codec, r, x, n, iters, mu, W_down, W_up, sigma, workspace, workspace_bytes=None,
+                stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lla_fit_svd(ctypes.byref(codec), int(r), _ptr(x), int(n), int(iters), _ptr(mu),
+                           _ptr(W_down), _ptr(W_up), _ptr(sigma), _ptr(workspace),
+                           int(workspace_bytes), _stream(stream))
+    return _check("lla_fit_svd", st, check)
 
 
 def lla_ref_plan(n_heads, d_head, dtype, flat: lla_cache) -> lla_plan:

@@ -226,3 +226,31 @@ def test_encode_chunk_validation_without_launch():
     assert call(x=None) == lla.LLA_ERR_NULL
     assert call(x=FAKE + 8) == lla.LLA_ERR_ALIGN
     assert call(chunk=0) == lla.LLA_OK
+
+
+def test_fit_validation_without_launch():
+    _no_gpu()
+    L = lla.lib()
+    bf = lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_BF16)
+    sz = ctypes.c_size_t(0)
+    assert L.lla_fit_plan(ctypes.byref(bf), 16, 4096, ctypes.byref(sz)) == lla.LLA_OK
+    need = sz.value
+    assert need > 0
+    assert L.lla_fit_plan(ctypes.byref(bf), 16, 4096, None) == lla.LLA_ERR_NULL
+    f32 = lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_F32)
+    assert L.lla_fit_plan(ctypes.byref(f32), 16, 4096, ctypes.byref(sz)) == lla.LLA_ERR_DTYPE
+    assert L.lla_fit_plan(ctypes.byref(bf), 0, 4096, ctypes.byref(sz)) == lla.LLA_ERR_SHAPE
+    assert L.lla_fit_plan(ctypes.byref(bf), 65, 4096, ctypes.byref(sz)) == \
+        lla.LLA_ERR_UNSUPPORTED
+    odd = lla.make_codec(0, 3, 16, 64, 16, 32, lla.LLA_BF16)          # X = 192
+    assert L.lla_fit_plan(ctypes.byref(odd), 16, 4096, ctypes.byref(sz)) == \
+        lla.LLA_ERR_UNSUPPORTED
+    assert L.lla_fit_plan(ctypes.byref(bf), 16, 24, ctypes.byref(sz)) == lla.LLA_ERR_SHAPE
+
+    def call(ws=FAKE, wsb=need, x=FAKE, iters=10):
+        return L.lla_fit_svd(ctypes.byref(bf), 16, x, 4096, iters, FAKE, FAKE, FAKE, None, ws,
+                             wsb, None)
+    assert call(wsb=need - 4) == lla.LLA_ERR_WORKSPACE
+    assert call(ws=None) == lla.LLA_ERR_NULL
+    assert call(x=FAKE + 8) == lla.LLA_ERR_ALIGN
+    assert call(iters=-1) == lla.LLA_ERR_SHAPE
