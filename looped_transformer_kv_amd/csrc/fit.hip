@@ -192,21 +192,26 @@ __global__ __launch_bounds__(FT) void fit_init_kernel(FitArgs a) {
     a.W[idx] = hash_unit(idx);
 }
 
-// W = C V: workgroup (g, rows 32 q .. + 31); thread (row tid / 8, columns tid % 8 + 8 u)
+// W = C V: workgroup (g, rows 32 q .. + 31); 64-wide k-chunks of C's rows and V's rows are staged
+// in LDS with coalesced loads; thread (row tid / 8, columns tid % 8 + 8 u) accumulates in fp32
 __global__ __launch_bounds__(FT) void fit_mul_kernel(FitArgs a) {
+    __shared__ float sC[32][64 + 1];
     __shared__ float sV[64][kFitMaxCols + 1];
     const int rows_per = a.X / 32;
     const int g = blockIdx.x / rows_per, q = blockIdx.x % rows_per;
-    const int i = 32 * q + threadIdx.x / 8, c0 = threadIdx.x % 8;
-    const float *C = a.C + ((size_t)g * a.X + i) * a.X;
+    const int tid = threadIdx.x;
+    const int il = tid / 8, c0 = tid % 8;
+    const float *C = a.C + ((size_t)g * a.X + 32 * q) * a.X;
     const float *V = a.V + (size_t)g * a.X * a.rb;
     float acc[kFitMaxCols / 8] = {};
     for (int k0 = 0; k0 < a.X; k0 += 64) {
         __syncthreads();
-        for (int e = threadIdx.x; e < 64 * a.rb; e += FT) sV[e / a.rb][e % a.rb] = V[(size_t)(k0 + e / a.rb) * a.rb + e % a.rb];
+        for (int e = tid; e < 32 * 64; e += FT) sC[e / 64][e % 64] = C[(size_t)(e / 64) * a.X + k0 + e % 64];
+        for (int e = tid; e < 64 * a.rb; e += FT)
+            sV[e / a.rb][e % a.rb] = V[(size_t)k0 * a.rb + e];
         __syncthreads();
         for (int k = 0; k < 64; ++k) {
-            const float cik = C[k0 + k];
+            const float cik = sC[il][k];
 #pragma unroll
             for (int u = 0; u < kFitMaxCols / 8; ++u)
                 if (c0 + 8 * u < a.rb) acc[u] += cik * sV[k][c0 + 8 * u];
@@ -214,23 +219,47 @@ __global__ __launch_bounds__(FT) void fit_mul_kernel(FitArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kFitMaxCols / 8; ++u)
-        if (c0 + 8 * u < a.rb) a.W[((size_t)g * a.X + i) * a.rb + c0 + 8 * u] = acc[u];
+        if (c0 + 8 * u < a.rb) a.W[((size_t)g * a.X + 32 * q + il) * a.rb + c0 + 8 * u] = acc[u];
 }
 
 // Cholesky factor L (lower, rb x rb, in LDS) of the Gram matrix of the X x rb block Y (global).
-// A pivot below a tiny fraction of the trace is clamped (rank-deficient blocks stay finite).
-__device__ void gram_cholesky(const FitArgs &a, const float *Y, float (*L)[kFitMaxCols + 1]) {
-    const int rb = a.rb;
-    for (int e = threadIdx.x; e < rb * rb; e += FT) {
-        const int p = e / rb, q = e % rb;
-        if (q > p) continue;
-        float s = 0.f;
-        for (int k = 0; k < a.X; ++k) s += Y[(size_t)k * rb + p] * Y[(size_t)k * rb + q];
-        L[p][q] = s;
+// The Gram matrix accumulates over 64-row chunks of Y staged in LDS.  A pivot below a tiny
+// fraction of the trace is clamped (rank-deficient blocks stay finite).
+__device__ void gram_cholesky(const FitArgs &a, const float *Y, float (*L)[kFitMaxCols + 1],
+                              float (*sY)[kFitMaxCols + 1]) {
+    const int rb = a.rb, tid = threadIdx.x;
+    constexpr int PMAX = kFitMaxCols * (kFitMaxCols + 1) / 2;
+    constexpr int PPT = (PMAX + FT - 1) / FT;            // pairs per thread
+    float acc[PPT] = {};
+    const int npairs = rb * (rb + 1) / 2;
+    int pp[PPT], qq[PPT];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {                      // pair e -> (p >= q)
+        int e = tid + FT * u, p = 0;
+        if (e >= npairs) e = 0;
+        while (e >= p + 1) { e -= p + 1; ++p; }
+        pp[u] = p;
+        qq[u] = e;
+    }
+    for (int k0 = 0; k0 < a.X; k0 += 64) {
+        __syncthreads();
+        for (int e = tid; e < 64 * rb; e += FT) sY[e / rb][e % rb] = Y[(size_t)k0 * rb + e];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+            if (tid + FT * u >= npairs) continue;
+            float s = acc[u];
+            for (int k = 0; k < 64; ++k) s += sY[k][pp[u]] * sY[k][qq[u]];
+            acc[u] = s;
+        }
     }
     __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PPT; ++u)
+        if (tid + FT * u < npairs) L[pp[u]][qq[u]] = acc[u];
+    __syncthreads();
     __shared__ float tr;
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         float t = 0.f;
         for (int p = 0; p < rb; ++p) t += L[p][p];
         tr = t;
@@ -238,13 +267,13 @@ __device__ void gram_cholesky(const FitArgs &a, const float *Y, float (*L)[kFitM
     __syncthreads();
     const float floor_ = 1e-12f * tr + 1e-30f;
     for (int j = 0; j < rb; ++j) {
-        if (threadIdx.x == 0) {
+        if (tid == 0) {
             float d = L[j][j];
             for (int k = 0; k < j; ++k) d -= L[j][k] * L[j][k];
             L[j][j] = sqrtf(fmaxf(d, floor_));
         }
         __syncthreads();
-        for (int p = j + 1 + threadIdx.x; p < rb; p += FT) {
+        for (int p = j + 1 + tid; p < rb; p += FT) {
             float v = L[p][j];
             for (int k = 0; k < j; ++k) v -= L[p][k] * L[j][k];
             L[p][j] = v / L[j][j];
@@ -253,33 +282,50 @@ __device__ void gram_cholesky(const FitArgs &a, const float *Y, float (*L)[kFitM
     }
 }
 
-// out = Y L^{-T} row by row (forward substitution), X rows over the workgroup
+// out = Y L^{-T}.  L^{-1} (lower triangular) is formed in LDS, one column per thread by forward
+// substitution; then every 64-row chunk of Y is staged in LDS and multiplied by L^{-T}
+// (out[i][j] = sum_{k <= j} Y[i][k] Linv[j][k]).  out may alias Y: a chunk is read completely
+// before any of it is written.
 __device__ void solve_rows(const FitArgs &a, const float *Y, float *out,
-                           const float (*L)[kFitMaxCols + 1]) {
-    const int rb = a.rb;
-    for (int row = threadIdx.x; row < a.X; row += FT) {
-        float v[kFitMaxCols];
-        for (int j = 0; j < rb; ++j) {
-            float s = Y[(size_t)row * rb + j];
-            for (int k = 0; k < j; ++k) s -= v[k] * L[j][k];
-            v[j] = s / L[j][j];
+                           float (*L)[kFitMaxCols + 1], float (*Li)[kFitMaxCols + 1],
+                           float (*sY)[kFitMaxCols + 1]) {
+    const int rb = a.rb, tid = threadIdx.x;
+    if (tid < rb) {
+        const int c = tid;
+        for (int j = 0; j < rb; ++j) Li[j][c] = 0.f;
+        Li[c][c] = 1.f / L[c][c];
+        for (int j = c + 1; j < rb; ++j) {
+            float s = 0.f;
+            for (int k = c; k < j; ++k) s += L[j][k] * Li[k][c];
+            Li[j][c] = -s / L[j][j];
         }
-        for (int j = 0; j < rb; ++j) out[(size_t)row * rb + j] = v[j];
+    }
+    __syncthreads();
+    for (int k0 = 0; k0 < a.X; k0 += 64) {
+        for (int e = tid; e < 64 * rb; e += FT) sY[e / rb][e % rb] = Y[(size_t)k0 * rb + e];
+        __syncthreads();
+        for (int e = tid; e < 64 * rb; e += FT) {
+            const int i = e / rb, j = e % rb;
+            float s = 0.f;
+            for (int k = 0; k <= j; ++k) s += sY[i][k] * Li[j][k];
+            out[(size_t)(k0 + i) * rb + j] = s;
+        }
+        __syncthreads();
     }
 }
 
 // V = orth(W) by CholeskyQR2 (W L1^-T, then once more)
 __global__ __launch_bounds__(FT) void fit_orth_kernel(FitArgs a) {
     __shared__ float L[kFitMaxCols][kFitMaxCols + 1];
+    __shared__ float Li[kFitMaxCols][kFitMaxCols + 1];
+    __shared__ float sY[64][kFitMaxCols + 1];
     const int g = blockIdx.x;
     float *W = a.W + (size_t)g * a.X * a.rb;
     float *V = a.V + (size_t)g * a.X * a.rb;
-    gram_cholesky(a, W, L);
-    solve_rows(a, W, V, L);
-    __threadfence_block();
-    __syncthreads();
-    gram_cholesky(a, V, L);
-    solve_rows(a, V, V, L);
+    gram_cholesky(a, W, L, sY);
+    solve_rows(a, W, V, L, Li, sY);
+    gram_cholesky(a, V, L, sY);
+    solve_rows(a, V, V, L, Li, sY);
 }
 
 // Rayleigh-Ritz: H = V^T W (W = C V), Jacobi eigenvectors, sorted top r, outputs
