@@ -4,6 +4,8 @@ import torch
 
 from looped_transformer_kv_amd import lla, synth
 from looped_transformer_kv_amd.runtime import LatentLayer
+from oracle import oracle as O
+import tinycase
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 CODE_DT = {"bf16": lla.LLA_BF16, "f32": lla.LLA_F32}
@@ -76,3 +78,46 @@ class DeviceProblem:
                              p.mu_v, p.k_pool, p.v_pool, p.block_table, p.seq_lens, c.page,
                              p.q[t], ks, vs, theta=rope.theta, rot_dims=rope.rot_dims,
                              style=rope.style)
+
+
+class Chunk:
+    """A decode problem with room for a chunk of Pn new tokens per sequence, plus the chunk's
+    inputs (host fp64 and device bf16)."""
+
+    def __init__(self, cfg, B, N, Pn, lens, n_new, gpu, q_gain=1.0):
+        cfg = synth.scaled(cfg, B=B, N=N + Pn)
+        self.cfg, self.B, self.Pn = cfg, B, Pn
+        self.p = tinycase.make(cfg, B=B, N=N + Pn, lens=np.asarray(lens, dtype=np.int32))
+        self.dp = DeviceProblem(self.p)
+        self.n_new = np.asarray(n_new, dtype=np.int32)
+        self.q = {t: synth.chunk_queries(cfg, 0, t, B, Pn, q_gain) for t in range(cfg.T)}
+        self.xk = synth.chunk_staging(cfg, 0, synth.AX_K, B, Pn)
+        self.xv = synth.chunk_staging(cfg, 0, synth.AX_V, B, Pn)
+        up = lambda a: synth.to_device(a, "bf16", gpu)
+        self.qd = {t: up(self.q[t]) for t in self.q}
+        self.xkd, self.xvd = up(self.xk), up(self.xv)
+        self.nd = torch.from_numpy(self.n_new).to(gpu)
+        self.gpu = gpu
+
+    def run(self, t, strided=True):
+        c = self.cfg
+        out = torch.full((self.B, self.Pn, c.H, c.d), float("nan"), dtype=torch.bfloat16,
+                         device=self.gpu)
+        if strided:        # loop t read in place from the [B][Pn][T][H][d] staging buffers
+            kn, vn, stride = self.xkd[:, :, t], self.xvd[:, :, t], c.T * c.H * c.d
+        else:
+            kn, vn, stride = self.xkd[:, :, t].contiguous(), self.xvd[:, :, t].contiguous(), 0
+        self.dp.layer.prefill(t, self.Pn, self.nd, self.qd[t], kn, vn, out, new_stride=stride)
+        torch.cuda.synchronize()
+        return synth.from_device(out)
+
+    def oracle(self, t):
+        p, c = self.p, self.cfg
+        return O.prefill(c.mode, c.T, c.H, c.d, c.r_k, c.r_v, t, p.W_up_k, p.W_up_v, p.mu_k,
+                         p.mu_v, p.k_pool, p.v_pool, p.block_table, p.seq_lens, c.page,
+                         self.q[t], self.xk[:, :, t], self.xv[:, :, t], self.n_new)
+
+    def check(self, got, ref, what):
+        live = np.arange(self.Pn)[None, :] < self.n_new[:, None]            # [B][Pn]
+        assert np.all(np.isnan(got[~live])), f"{what}: rows past the chunk were written"
+        assert_close(got[live], ref[live], "bf16", what)
