@@ -481,7 +481,10 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
     EncodePair pr;
     pr.ax[0] = k_axis;
     pr.ax[1] = v_axis;
-    if (bf16 && rows_kernel_fits(k_axis) && rows_kernel_fits(v_axis)) {
+    // the row-streaming kernel only pays when its grid fills the chip (a workgroup per CU);
+    // fewer, longer row blocks lose to the split-axis kernel's many short ones
+    if (bf16 && rows_kernel_fits(k_axis) && rows_kernel_fits(v_axis) &&
+        rows_blocks_of(k_axis) + rows_blocks_of(v_axis) >= 256) {
         pr.blocks_k = rows_blocks_of(k_axis);
         const unsigned blocks = (unsigned)(pr.blocks_k + rows_blocks_of(v_axis));
         hipLaunchKernelGGL(encode_rows_kernel, dim3(blocks), dim3(64 * RWAVES), 0, st, pr);

@@ -85,15 +85,11 @@ def test_prefill_single_token_chunk_matches_decode(gpu):
     assert_close(synth.from_device(out), ref, "bf16", "decode with the chunk token as self")
 
 
-@pytest.mark.parametrize("shape,Pn", [("ouro14_21x", 70), ("h4_d128_2d_r32", 70),
-                                      ("ouro14_21x", 100), ("h2_d64_r16", 100)])
-def test_encode_chunk(gpu, shape, Pn):
+def _check_encode_chunk(gpu, shape, B, N, Pn, lens, n_new):
     """lla_encode_chunk: c against the oracle; the pool holds c rounded once at write_pos + i for
-    live rows only; every other slot keeps its bytes.  210 rows take the split-axis kernel, 300
-    rows of a short stacked axis the row-streaming one."""
+    live rows only; every other slot keeps its bytes."""
     cfg = SHAPES[shape]
-    B, N = 3, 90
-    ch = Chunk(cfg, B, N, Pn, [90, 0, 33], [Pn, 0, 41], gpu)
+    ch = Chunk(cfg, B, N, Pn, lens, n_new, gpu)
     c, p = ch.cfg, ch.p
     wpos_h = p.seq_lens.copy()
     wpos = torch.from_numpy(wpos_h).to(gpu)
@@ -121,6 +117,20 @@ def test_encode_chunk(gpu, shape, Pn):
                 expect[p.block_table[b, pos // c.page], :, pos % c.page] = stored[b, i]
         after = synth.from_device(pool)
         assert np.array_equal(after, expect), f"{shape} axis {axis}: pool differs"
+
+
+@pytest.mark.parametrize("shape,Pn", [("ouro14_21x", 70), ("h4_d128_2d_r32", 70),
+                                      ("ouro14_21x", 100), ("h2_d64_r16", 100)])
+def test_encode_chunk(gpu, shape, Pn):
+    """A few hundred rows: the split-axis kernel."""
+    _check_encode_chunk(gpu, shape, 3, 90, Pn, [90, 0, 33], [Pn, 0, 41])
+
+
+def test_encode_chunk_row_streaming(gpu):
+    """4096 rows of a short stacked axis over 16 heads (256 workgroups, one per CU): the
+    row-streaming kernel, with empty, full and ragged chunks and writes starting mid-page."""
+    _check_encode_chunk(gpu, "ouro14_21x", 8, 64, 512, [64, 0, 33, 5, 64, 17, 40, 1],
+                        [512, 0, 512, 300, 7, 511, 512, 64])
 
 
 def test_prefill_bench_shape_sampled(gpu):
