@@ -26,6 +26,9 @@
  *     h; LLA-2D x[(t*H + h)*d + i].  mu_t is block t of mu (length D_g).
  *   - Out-of-range page ids in a block table make the affected outputs NaN (never a fault).
  *     Lengths are clamped to [0, max_seq_len].
+ *   - Pool size: the bf16 decode entry points (lla_decode_attn, _absorbed, _rope) need
+ *     n_pages * G * page_size < 2^31 pool rows, lla_ref_attn n_pages * H * page_size < 2^31;
+ *     larger pools return LLA_ERR_UNSUPPORTED.
  */
 #ifndef LLA_H
 #define LLA_H
@@ -224,7 +227,8 @@ lla_status lla_encode_chunk(const lla_codec *codec, const lla_params *params,
  *   n_new           device int32 [B], clamped to [0, chunk]
  * Rows i >= n_new[b] of out are not written.  No workspace.  bf16 codecs only (LLA_ERR_DTYPE);
  * d_head 64 or 128 with (r_k, r_v) in {(16,16), (16,32), (32,32)}, else LLA_ERR_UNSUPPORTED;
- * page_size a multiple of 32 and 0 <= t < T, else LLA_ERR_SHAPE.  chunk = 0 enqueues nothing.
+ * page_size a multiple of 32, 0 <= t < T and chunk * new_stride < 2^31, else LLA_ERR_SHAPE.
+ * chunk = 0 enqueues nothing.
  */
 lla_status lla_prefill_attn(const lla_codec *codec, const lla_params *params,
                             const lla_cache *cache, int32_t t, int32_t chunk,

@@ -167,6 +167,9 @@ lla_status prepare_decode(const lla_codec *c, const lla_params *prm, const lla_c
     if (bf16) {
         if (!decode_bf16_supported(c->d_head, c->r_k, c->r_v)) return LLA_ERR_UNSUPPORTED;
         if (k->page_size % 32 != 0) return LLA_ERR_SHAPE;
+        // the kernels address a pool row (page, group, slot) with a signed 32-bit index
+        if ((long)k->n_pages * shape_of(c).G * k->page_size > (1L << 31) - 1)
+            return LLA_ERR_UNSUPPORTED;
         if (!aligned16(q) || !aligned16(prm->W_up_k) || !aligned16(prm->W_up_v))
             return LLA_ERR_ALIGN;
     } else if (decode_f32_lds_bytes(c->d_head, c->r_k, c->r_v) > kMaxDynLds) {
@@ -360,6 +363,8 @@ lla_status lla_prefill_attn(const lla_codec *c, const lla_params *prm, const lla
     const long QB = ((long)chunk + qpb - 1) / qpb;
     if ((long)k->batch * c->n_heads * QB > (1L << 30) || (long)k->batch * chunk > (1L << 30))
         return LLA_ERR_SHAPE;
+    // the kernel forms a chunk row's offset inside its sequence in 32-bit arithmetic
+    if ((long)chunk * new_stride > (1L << 31) - 1) return LLA_ERR_SHAPE;
     const Shape sh = shape_of(c);
     PrefillArgs a{};
     a.k_pool = k->k_pool;
@@ -413,6 +418,8 @@ lla_status lla_ref_attn(int32_t H, int32_t d, int32_t dtype, const lla_cache *k,
     if (st != LLA_OK) return st;
     if (!q || !out || (k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_NULL;
     if (self_stride < 0 || k->page_size % 32 != 0) return LLA_ERR_SHAPE;
+    // the kernel addresses a pool row (page, head, slot) with a signed 32-bit index
+    if ((long)k->n_pages * H * k->page_size > (1L << 31) - 1) return LLA_ERR_UNSUPPORTED;
     lla_plan plan;
     ref_plan(H, d, dtype, k, &plan);
     if ((st = check_workspace(plan, workspace, workspace_bytes)) != LLA_OK) return st;

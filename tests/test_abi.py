@@ -123,6 +123,14 @@ def test_validation_codes_without_launch():
         lla.LLA_ERR_SHAPE                                                # P not a multiple of 32
     assert _status() == lla.LLA_ERR_WORKSPACE                            # no workspace
     assert _status(ws=FAKE + 4, wsb=1 << 20) == lla.LLA_ERR_ALIGN
+    # 2^21 pages x 16 heads x 64 slots = 2^31 pool rows: past the kernels' 32-bit row index
+    huge = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 1 << 21, 4096)
+    assert _status(cache=huge) == lla.LLA_ERR_UNSUPPORTED
+    assert _status(cache=lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, (1 << 21) - 1,
+                                       4096)) == lla.LLA_ERR_WORKSPACE   # one page fewer is fine
+    L = lla.lib()
+    assert L.lla_ref_attn(16, 128, lla.LLA_BF16, ctypes.byref(huge), FAKE, None, None, 0, 0.1,
+                          FAKE, None, 0, None) == lla.LLA_ERR_UNSUPPORTED
 
 
 def test_status_strings():
@@ -201,6 +209,7 @@ def test_prefill_validation_without_launch():
     assert call(chunk=-1) == lla.LLA_ERR_SHAPE
     assert call(stride=16 * 128 - 8) == lla.LLA_ERR_SHAPE          # shorter than a row
     assert call(stride=16 * 128 + 4) == lla.LLA_ERR_SHAPE          # not a multiple of 8
+    assert call(chunk=1 << 14, stride=1 << 17) == lla.LLA_ERR_SHAPE  # row offsets past 2^31
     assert call(q=FAKE + 8) == lla.LLA_ERR_ALIGN
     odd_pages = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 48, 64, 64, 3072)
     assert call(cache_=odd_pages) == lla.LLA_ERR_SHAPE
