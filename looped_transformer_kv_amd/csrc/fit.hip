@@ -36,7 +36,7 @@ __device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
 }
 
 constexpr int CB = 128;          // covariance block edge
-constexpr int CK = 32;           // rows per staged chunk
+constexpr int CK = 64;           // rows per staged chunk
 constexpr int FT = 256;          // threads of every fit kernel
 
 // Stacked index k of row `row`, group g: staging offset ((row T + t) H + g) d + i per head with
@@ -54,11 +54,13 @@ __global__ __launch_bounds__(FT) void fit_cov_kernel(FitArgs a) {
 
     const int nb = a.X / CB;
     const int pairs = nb * (nb + 1) / 2;
-    int id = blockIdx.x;
-    const int s = id % a.S;
-    id /= a.S;
+    // work item (g, s, pair), pair fastest: the pairs of one (group, row range) are consecutive
+    // items of one XCD and run together, so its L2 serves the strips they share
+    int id = xcd_work_item(blockIdx.x, gridDim.x);
     int pr = id % pairs;
-    const int g = id / pairs;
+    id /= pairs;
+    const int s = id % a.S;
+    const int g = id / a.S;
     int bi = 0;                                          // pair -> (bi <= bj)
     while (pr >= nb - bi) { pr -= nb - bi; ++bi; }
     const int bj = bi + pr;
@@ -72,16 +74,21 @@ __global__ __launch_bounds__(FT) void fit_cov_kernel(FitArgs a) {
     const int r0 = (int)min((long)a.n, per * s), r1 = (int)min((long)a.n, per * (s + 1));
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
 
-    // staging: thread tid loads the 16-byte piece (row tid / 16, columns 8 (tid % 16) ..) of each
-    // strip, i.e. both strips are 32 rows x 128 columns = 512 pieces, two per thread each
-    uint4 pi[2], pj[2];
+    // staging: slot u of thread tid holds the 16-byte piece of token tid % 32 + 32 (u % 2) of the
+    // 64-row chunk and columns 8 cg .. + 7, cg = tid / 32 + 8 (u / 2), of each strip.  Written
+    // transposed (sI[col][token]) one element per instruction: the 32 lanes of a half-wave write
+    // consecutive tokens of one row; the second half-wave takes its elements rotated by four,
+    // which puts its rows 12 apart from the first half's, i.e. on the other 16 banks (rows are 36
+    // dwords apart).  Conflict-free.
+    const int rr = tid & 31, hw = (tid >> 5) & 1;
+    uint4 pi[4], pj[4];
     auto fetch = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = tid + FT * u;
-            const int row = min(c0 + p / 16, max(r1 - 1, 0));
-            const bool live = c0 + p / 16 < r1;
-            const int col = 8 * (p % 16);
+        for (int u = 0; u < 4; ++u) {
+            const int tok = c0 + rr + 32 * (u & 1);
+            const int row = min(tok, max(r1 - 1, 0));
+            const bool live = tok < r1;
+            const int col = 8 * ((tid >> 5) + 8 * (u >> 1));
             pi[u] = live ? *reinterpret_cast<const uint4 *>(x + stage_off(a, row, g, CB * bi + col))
                          : make_uint4(0, 0, 0, 0);
             pj[u] = live ? *reinterpret_cast<const uint4 *>(x + stage_off(a, row, g, CB * bj + col))
@@ -90,15 +97,19 @@ __global__ __launch_bounds__(FT) void fit_cov_kernel(FitArgs a) {
     };
     auto stage = [&]() {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = tid + FT * u;
-            const int rr = p / 16, col = 8 * (p % 16);
+        for (int u = 0; u < 4; ++u) {
+            const int col = 8 * ((tid >> 5) + 8 * (u >> 1));
+            const int tk = rr + 32 * (u & 1);
             const uint32_t wi[4] = {pi[u].x, pi[u].y, pi[u].z, pi[u].w};
             const uint32_t wj[4] = {pj[u].x, pj[u].y, pj[u].z, pj[u].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                sI[col + e][rr] = static_cast<uint16_t>(wi[e >> 1] >> (16 * (e & 1)));
-                sJ[col + e][rr] = static_cast<uint16_t>(wj[e >> 1] >> (16 * (e & 1)));
+                const int er = (e + 4) & 7;                  // the rotated element (same parity)
+                const int el = hw ? er : e;
+                const uint32_t di = hw ? wi[er >> 1] : wi[e >> 1];
+                const uint32_t dj = hw ? wj[er >> 1] : wj[e >> 1];
+                sI[col + el][tk] = static_cast<uint16_t>(di >> (16 * (e & 1)));
+                sJ[col + el][tk] = static_cast<uint16_t>(dj >> (16 * (e & 1)));
             }
         }
     };
@@ -192,71 +203,141 @@ __global__ __launch_bounds__(FT) void fit_init_kernel(FitArgs a) {
     a.W[idx] = hash_unit(idx);
 }
 
-// W = C V: workgroup (g, rows 32 q .. + 31); 64-wide k-chunks of C's rows and V's rows are staged
-// in LDS with coalesced loads; thread (row tid / 8, columns tid % 8 + 8 u) accumulates in fp32
+// W = C V: workgroup (g, rows 32 q .. + 31).  64-wide k-chunks of C's rows (sC) and of V's rows
+// (sV, row-major at pitch rb) pass through LDS, the next chunk's loads in flight while the current
+// one is multiplied; thread (row tid / 8, columns tid % 8 + 8 u) accumulates in fp32.
+// NB = ceil(rb / 16): every thread sums MU = 2 NB column slots (columns past rb read in-bounds
+// LDS and are never stored), so the inner loop has no guard.
+constexpr int MV = (64 * kFitMaxCols / 2 + FT - 1) / FT;  // float2 pieces of a V chunk per thread
+template <int NB>
 __global__ __launch_bounds__(FT) void fit_mul_kernel(FitArgs a) {
+    constexpr int MU = 2 * NB;                            // column slots per thread
     __shared__ float sC[32][64 + 1];
-    __shared__ float sV[64][kFitMaxCols + 1];
+    // + 16: the unguarded slots of the last rows reach 8 floats past a chunk of 64 x 72
+    __shared__ __align__(8) float sV[64 * kFitMaxCols + 16];
     const int rows_per = a.X / 32;
     const int g = blockIdx.x / rows_per, q = blockIdx.x % rows_per;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, rb = a.rb;
     const int il = tid / 8, c0 = tid % 8;
+    const int nu = (rb - c0 + 7) / 8;                    // this thread's columns
     const float *C = a.C + ((size_t)g * a.X + 32 * q) * a.X;
-    const float *V = a.V + (size_t)g * a.X * a.rb;
-    float acc[kFitMaxCols / 8] = {};
+    const float *V = a.V + (size_t)g * a.X * rb;
+    const int npv = 64 * rb / 2;                          // float2 pieces per V chunk (rb even)
+    float4 pc[2];
+    float2 pv[MV];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {                    // C: 32 rows x 16 float4
+            const int e = tid + FT * m;
+            pc[m] = *reinterpret_cast<const float4 *>(C + (size_t)(e / 16) * a.X + k0 + 4 * (e % 16));
+        }
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+            const int e = min(tid + FT * m, npv - 1);
+            pv[m] = *reinterpret_cast<const float2 *>(V + (size_t)k0 * rb + 2 * e);
+        }
+    };
+    float acc[MU] = {};
+    fetch(0);
     for (int k0 = 0; k0 < a.X; k0 += 64) {
+        __syncthreads();                                 // the previous chunk is consumed
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + FT * m;
+            float *d = &sC[e / 16][4 * (e % 16)];
+            d[0] = pc[m].x; d[1] = pc[m].y; d[2] = pc[m].z; d[3] = pc[m].w;
+        }
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+            const int e = tid + FT * m;
+            if (e < npv) *reinterpret_cast<float2 *>(&sV[2 * e]) = pv[m];
+        }
         __syncthreads();
-        for (int e = tid; e < 32 * 64; e += FT) sC[e / 64][e % 64] = C[(size_t)(e / 64) * a.X + k0 + e % 64];
-        for (int e = tid; e < 64 * a.rb; e += FT)
-            sV[e / a.rb][e % a.rb] = V[(size_t)k0 * a.rb + e];
-        __syncthreads();
+        if (k0 + 64 < a.X) fetch(k0 + 64);
+#pragma unroll 8
         for (int k = 0; k < 64; ++k) {
             const float cik = sC[il][k];
+            const float *vr = &sV[k * rb + c0];
 #pragma unroll
-            for (int u = 0; u < kFitMaxCols / 8; ++u)
-                if (c0 + 8 * u < a.rb) acc[u] += cik * sV[k][c0 + 8 * u];
+            for (int u = 0; u < MU; ++u) acc[u] += cik * vr[8 * u];
         }
     }
 #pragma unroll
-    for (int u = 0; u < kFitMaxCols / 8; ++u)
-        if (c0 + 8 * u < a.rb) a.W[((size_t)g * a.X + 32 * q + il) * a.rb + c0 + 8 * u] = acc[u];
+    for (int u = 0; u < MU; ++u)
+        if (u < nu) a.W[((size_t)g * a.X + 32 * q + il) * rb + c0 + 8 * u] = acc[u];
 }
 
-// Cholesky factor L (lower, rb x rb, in LDS) of the Gram matrix of the X x rb block Y (global).
-// The Gram matrix accumulates over 64-row chunks of Y staged in LDS.  A pivot below a tiny
-// fraction of the trace is clamped (rank-deficient blocks stay finite).
-__device__ void gram_cholesky(const FitArgs &a, const float *Y, float (*L)[kFitMaxCols + 1],
-                              float (*sY)[kFitMaxCols + 1]) {
-    const int rb = a.rb, tid = threadIdx.x;
-    constexpr int PMAX = kFitMaxCols * (kFitMaxCols + 1) / 2;
-    constexpr int PPT = (PMAX + FT - 1) / FT;            // pairs per thread
-    float acc[PPT] = {};
-    const int npairs = rb * (rb + 1) / 2;
-    int pp[PPT], qq[PPT];
+// 64-row chunks of an X x rb block (row-major, pitch rb) stream through sY (pitch kFitMaxCols + 1,
+// odd, so rows read across lanes fall in different banks); slot m of thread tid is chunk element
+// tid + FT m, i.e. one fixed (row, column) per slot, and the next chunk's loads are in flight while
+// the current one is used.
+constexpr int CHE = (64 * kFitMaxCols + FT - 1) / FT;    // chunk elements per thread
+struct ChunkStream {
+    int row[CHE], col[CHE], n;
+    float pre[CHE];
+    __device__ void init(int rb) {
+        n = 64 * rb;
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) {                      // pair e -> (p >= q)
-        int e = tid + FT * u, p = 0;
-        if (e >= npairs) e = 0;
-        while (e >= p + 1) { e -= p + 1; ++p; }
-        pp[u] = p;
-        qq[u] = e;
+        for (int m = 0; m < CHE; ++m) {
+            const int e = min((int)threadIdx.x + FT * m, n - 1);
+            row[m] = e / rb;
+            col[m] = e - row[m] * rb;
+        }
     }
+    __device__ void fetch(const float *Y, int k0, int rb) {
+#pragma unroll
+        for (int m = 0; m < CHE; ++m)
+            pre[m] = Y[(size_t)k0 * rb + (size_t)row[m] * rb + col[m]];
+    }
+    __device__ void stage(float (*sY)[kFitMaxCols + 1]) {
+#pragma unroll
+        for (int m = 0; m < CHE; ++m)
+            if ((int)threadIdx.x + FT * m < n) sY[row[m]][col[m]] = pre[m];
+    }
+};
+
+// Cholesky factor L (lower, rb x rb, in LDS) of the Gram matrix of the X x rb block Y (global).
+// Thread (tp, tq) of a 16 x 16 grid accumulates entries (tp + 16u, tq + 16v) over the row chunks.
+// A pivot below a tiny fraction of the trace is clamped (rank-deficient blocks stay finite).
+// NB = ceil(rb / 16) (at most 5) is a template parameter so the inner loops carry no guards (a
+// guard per term would make every LDS read wait on its own).
+template <int NB>
+__device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
+                                              float (*L)[kFitMaxCols + 1],
+                                              float (*sY)[kFitMaxCols + 1]) {
+    const int rb = a.rb, tid = threadIdx.x;
+    const int tp = tid >> 4, tq = tid & 15;
+    float acc[NB][NB] = {};
+    ChunkStream cs;
+    cs.init(rb);
+    cs.fetch(Y, 0, rb);
     for (int k0 = 0; k0 < a.X; k0 += 64) {
         __syncthreads();
-        for (int e = tid; e < 64 * rb; e += FT) sY[e / rb][e % rb] = Y[(size_t)k0 * rb + e];
+        cs.stage(sY);
         __syncthreads();
+        if (k0 + 64 < a.X) cs.fetch(Y, k0 + 64, rb);
+#pragma unroll 4
+        for (int k = 0; k < 64; ++k) {
+            float yp[NB], yq[NB];
 #pragma unroll
-        for (int u = 0; u < PPT; ++u) {
-            if (tid + FT * u >= npairs) continue;
-            float s = acc[u];
-            for (int k = 0; k < 64; ++k) s += sY[k][pp[u]] * sY[k][qq[u]];
-            acc[u] = s;
+            for (int u = 0; u < NB; ++u) {
+                yp[u] = sY[k][min(tp + 16 * u, kFitMaxCols)];
+                yq[u] = sY[k][min(tq + 16 * u, kFitMaxCols)];
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+#pragma unroll
+                for (int v = 0; v < NB; ++v) acc[u][v] += yp[u] * yq[v];
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < PPT; ++u)
-        if (tid + FT * u < npairs) L[pp[u]][qq[u]] = acc[u];
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int v = 0; v < NB; ++v) {
+            const int p = tp + 16 * u, q = tq + 16 * v;
+            if (p < rb && q <= p) L[p][q] = acc[u][v];
+        }
     __syncthreads();
     __shared__ float tr;
     if (tid == 0) {
@@ -265,56 +346,92 @@ __device__ void gram_cholesky(const FitArgs &a, const float *Y, float (*L)[kFitM
         tr = t;
     }
     __syncthreads();
+    // right-looking: pivot j, then its column, then the trailing lower triangle, each step O(1)
+    // work per thread of the 16 x 16 grid
     const float floor_ = 1e-12f * tr + 1e-30f;
     for (int j = 0; j < rb; ++j) {
-        if (tid == 0) {
-            float d = L[j][j];
-            for (int k = 0; k < j; ++k) d -= L[j][k] * L[j][k];
-            L[j][j] = sqrtf(fmaxf(d, floor_));
-        }
+        if (tid == 0) L[j][j] = sqrtf(fmaxf(L[j][j], floor_));
         __syncthreads();
-        for (int p = j + 1 + tid; p < rb; p += FT) {
-            float v = L[p][j];
-            for (int k = 0; k < j; ++k) v -= L[p][k] * L[j][k];
-            L[p][j] = v / L[j][j];
-        }
+        if (tid > j && tid < rb) L[tid][j] /= L[j][j];
+        __syncthreads();
+        // every (p, q) of the thread's block is rewritten, the update selected to zero outside
+        // the trailing rows and columns (p, q > j, below rb): no branch per entry; entries above
+        // the diagonal change but are never read, and the others keep their exact value
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+#pragma unroll
+            for (int v = 0; v < NB; ++v) {
+                const int p = tp + 16 * u, q = tq + 16 * v;
+                if (NB == 5 && (p >= kFitMaxCols || q >= kFitMaxCols)) continue;
+                const float lp = L[p][j], lq = L[q][j];
+                L[p][q] -= p > j && q > j && p < rb && q < rb ? lp * lq : 0.f;
+            }
         __syncthreads();
     }
 }
 
-// out = Y L^{-T}.  L^{-1} (lower triangular) is formed in LDS, one column per thread by forward
-// substitution; then every 64-row chunk of Y is staged in LDS and multiplied by L^{-T}
-// (out[i][j] = sum_{k <= j} Y[i][k] Linv[j][k]).  out may alias Y: a chunk is read completely
-// before any of it is written.
-__device__ void solve_rows(const FitArgs &a, const float *Y, float *out,
-                           float (*L)[kFitMaxCols + 1], float (*Li)[kFitMaxCols + 1],
-                           float (*sY)[kFitMaxCols + 1]) {
+// out = Y L^{-T}.  L^{-1} (lower triangular, zero above the diagonal) is formed in LDS by
+// elimination; then each 64-row chunk of Y is multiplied by it in full:
+// thread (row tid / 4, columns tid % 4 + 4v) sums over k < rb.  out may alias Y: a chunk is read
+// completely (and the next one fetched) before any of it is written.
+template <int NB>
+__device__ __forceinline__ void solve_rows(const FitArgs &a, const float *Y, float *out,
+                                           float (*L)[kFitMaxCols + 1],
+                                           float (*Li)[kFitMaxCols + 1],
+                                           float (*sY)[kFitMaxCols + 1]) {
+    constexpr int SV = 4 * NB;                           // output column slots per thread
     const int rb = a.rb, tid = threadIdx.x;
-    if (tid < rb) {
-        const int c = tid;
-        for (int j = 0; j < rb; ++j) Li[j][c] = 0.f;
-        Li[c][c] = 1.f / L[c][c];
-        for (int j = c + 1; j < rb; ++j) {
-            float s = 0.f;
-            for (int k = c; k < j; ++k) s += L[j][k] * Li[k][c];
-            Li[j][c] = -s / L[j][j];
+    // L^{-1} by elimination on [L | I]: step j scales row j, then clears column j below it
+    const int tp = tid >> 4, tq = tid & 15;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int v = 0; v < NB; ++v) {
+            const int p = tp + 16 * u, q = tq + 16 * v;
+            if (p < rb && q < rb) Li[p][q] = p == q ? 1.f : 0.f;
         }
-    }
     __syncthreads();
+    for (int j = 0; j < rb; ++j) {
+        if (tid <= j) Li[j][tid] /= L[j][j];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+#pragma unroll
+            for (int v = 0; v < NB; ++v) {
+                const int p = tp + 16 * u, c = tq + 16 * v;
+                if (NB == 5 && (p >= kFitMaxCols || c >= kFitMaxCols)) continue;
+                const float lp = L[p][j], xc = Li[j][c];
+                Li[p][c] -= p > j && p < rb && c <= j ? lp * xc : 0.f;
+            }
+        __syncthreads();
+    }
+    const int i = tid >> 2, jq = tid & 3;
+    const int nv = (rb - jq + 3) / 4;
+    ChunkStream cs;
+    cs.init(rb);
+    cs.fetch(Y, 0, rb);
     for (int k0 = 0; k0 < a.X; k0 += 64) {
-        for (int e = tid; e < 64 * rb; e += FT) sY[e / rb][e % rb] = Y[(size_t)k0 * rb + e];
+        __syncthreads();                                 // the previous chunk is used
+        cs.stage(sY);
         __syncthreads();
-        for (int e = tid; e < 64 * rb; e += FT) {
-            const int i = e / rb, j = e % rb;
-            float s = 0.f;
-            for (int k = 0; k <= j; ++k) s += sY[i][k] * Li[j][k];
-            out[(size_t)(k0 + i) * rb + j] = s;
+        if (k0 + 64 < a.X) cs.fetch(Y, k0 + 64, rb);
+        // all SV column slots are summed (rows of Li past rb hold whatever they hold and their
+        // sums are never stored), so the loop body has no guard
+        float acc[SV] = {};
+#pragma unroll 4
+        for (int k = 0; k < rb; ++k) {
+            const float y = sY[i][k];
+#pragma unroll
+            for (int v = 0; v < SV; ++v) acc[v] += y * Li[min(jq + 4 * v, kFitMaxCols - 1)][k];
         }
-        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < SV; ++v)
+            if (v < nv) out[(size_t)(k0 + i) * rb + jq + 4 * v] = acc[v];
     }
 }
 
 // V = orth(W) by CholeskyQR2 (W L1^-T, then once more)
+template <int NB>
 __global__ __launch_bounds__(FT) void fit_orth_kernel(FitArgs a) {
     __shared__ float L[kFitMaxCols][kFitMaxCols + 1];
     __shared__ float Li[kFitMaxCols][kFitMaxCols + 1];
@@ -322,10 +439,10 @@ __global__ __launch_bounds__(FT) void fit_orth_kernel(FitArgs a) {
     const int g = blockIdx.x;
     float *W = a.W + (size_t)g * a.X * a.rb;
     float *V = a.V + (size_t)g * a.X * a.rb;
-    gram_cholesky(a, W, L, sY);
-    solve_rows(a, W, V, L, Li, sY);
-    gram_cholesky(a, V, L, sY);
-    solve_rows(a, V, V, L, Li, sY);
+    gram_cholesky<NB>(a, W, L, sY);
+    solve_rows<NB>(a, W, V, L, Li, sY);
+    gram_cholesky<NB>(a, V, L, sY);
+    solve_rows<NB>(a, V, V, L, Li, sY);
 }
 
 // Rayleigh-Ritz: H = V^T W (W = C V), Jacobi eigenvectors, sorted top r, outputs
@@ -474,6 +591,25 @@ int fit_block_cols(int r) {
     return rb > kFitMaxCols ? kFitMaxCols : rb;
 }
 
+template <int NB>
+void launch_step(const FitArgs &a, bool mul, hipStream_t st) {
+    if (mul)
+        hipLaunchKernelGGL(fit_mul_kernel<NB>, dim3(a.G * (a.X / 32)), dim3(FT), 0, st, a);
+    else
+        hipLaunchKernelGGL(fit_orth_kernel<NB>, dim3(a.G), dim3(FT), 0, st, a);
+}
+
+// W = C V (mul) or V = orth(W), instantiated for NB = ceil(rb / 16)
+void launch_iter(const FitArgs &a, bool mul, hipStream_t st) {
+    switch ((a.rb + 15) / 16) {
+    case 1: launch_step<1>(a, mul, st); break;
+    case 2: launch_step<2>(a, mul, st); break;
+    case 3: launch_step<3>(a, mul, st); break;
+    case 4: launch_step<4>(a, mul, st); break;
+    default: launch_step<5>(a, mul, st); break;
+    }
+}
+
 hipError_t launch_fit(FitArgs a, hipStream_t st) {
     const int nb = a.X / CB;
     const int pairs = nb * (nb + 1) / 2;
@@ -484,12 +620,12 @@ hipError_t launch_fit(FitArgs a, hipStream_t st) {
     const size_t vcells = (size_t)a.G * a.X * a.rb;
     hipLaunchKernelGGL(fit_init_kernel, dim3((unsigned)((vcells + FT - 1) / FT)), dim3(FT), 0, st,
                        a);
-    hipLaunchKernelGGL(fit_orth_kernel, dim3(a.G), dim3(FT), 0, st, a);
+    launch_iter(a, false, st);
     for (int it = 0; it < a.iters; ++it) {
-        hipLaunchKernelGGL(fit_mul_kernel, dim3(a.G * (a.X / 32)), dim3(FT), 0, st, a);
-        hipLaunchKernelGGL(fit_orth_kernel, dim3(a.G), dim3(FT), 0, st, a);
+        launch_iter(a, true, st);
+        launch_iter(a, false, st);
     }
-    hipLaunchKernelGGL(fit_mul_kernel, dim3(a.G * (a.X / 32)), dim3(FT), 0, st, a);
+    launch_iter(a, true, st);
     hipLaunchKernelGGL(fit_ritz_kernel, dim3(a.G), dim3(FT), 0, st, a);
     return hipGetLastError();
 }

@@ -42,19 +42,24 @@ def _planted(mode, T, H, d, r_true, n, seed, noise=0.02, decay=0.8):
     return synth.quantize(x, "bf16")
 
 
-CASES = {                                    # (mode, T, H, d, r, n)
+CASES = {                                    # (mode, T, H, d, r, n[, factor decay])
     "per_head_X128_r16": (0, 2, 2, 64, 16, 3000),
     "lla2d_X256_r16": (1, 2, 2, 64, 16, 3000),
     "ouro14_X512_r16": (0, 4, 2, 128, 16, 4096),
     "ouro14_X512_r32": (0, 4, 2, 128, 32, 4096),
     "odd_rank_r13": (0, 2, 2, 64, 13, 700),
+    # block widths r + 8 of 16, 56 and 72 columns (the kernels' 1, 4 and 5 column tiles); the
+    # larger ranks get a slower spectrum so every planted direction stays well above the noise
+    "r8_block16": (0, 2, 2, 64, 8, 2000),
+    "r48_block56": (0, 2, 2, 64, 48, 3000, 0.95),
+    "r64_block72": (0, 2, 1, 128, 64, 3000, 0.95),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_fit_matches_oracle(gpu, name):
-    mode, T, H, d, r, n = CASES[name]
-    x = _planted(mode, T, H, d, r + 12, n, seed=len(name))
+    mode, T, H, d, r, n, *rest = CASES[name]
+    x = _planted(mode, T, H, d, r + 12, n, seed=len(name), decay=rest[0] if rest else 0.8)
     codec = lla.make_codec(mode, T, H, d, r, r, lla.LLA_BF16)
     G = 1 if mode == 1 else H
     X = T * (H * d if mode == 1 else d)
