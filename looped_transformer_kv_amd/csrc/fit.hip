@@ -340,6 +340,7 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
         }
     __syncthreads();
     __shared__ float tr;
+    __shared__ float sink[FT];                           // target of stores that must not land
     if (tid == 0) {
         float t = 0.f;
         for (int p = 0; p < rb; ++p) t += L[p][p];
@@ -354,17 +355,18 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
         __syncthreads();
         if (tid > j && tid < rb) L[tid][j] /= L[j][j];
         __syncthreads();
-        // every (p, q) of the thread's block is rewritten, the update selected to zero outside
-        // the trailing rows and columns (p, q > j, below rb): no branch per entry; entries above
-        // the diagonal change but are never read, and the others keep their exact value
+        // the trailing entries (p, q > j, below rb; the thread's whole block is visited) are
+        // updated branch-free: every visit stores, to a per-thread dummy slot when it is not a
+        // trailing entry, so no entry that another thread reads in this phase is written
 #pragma unroll
         for (int u = 0; u < NB; ++u)
 #pragma unroll
             for (int v = 0; v < NB; ++v) {
                 const int p = tp + 16 * u, q = tq + 16 * v;
                 if (NB == 5 && (p >= kFitMaxCols || q >= kFitMaxCols)) continue;
-                const float lp = L[p][j], lq = L[q][j];
-                L[p][q] -= p > j && q > j && p < rb && q < rb ? lp * lq : 0.f;
+                const bool upd = p > j && q > j && p < rb && q < rb;
+                const float val = L[p][q] - L[p][j] * L[q][j];
+                *(upd ? &L[p][q] : &sink[tid]) = val;
             }
         __syncthreads();
     }
@@ -383,6 +385,7 @@ __device__ __forceinline__ void solve_rows(const FitArgs &a, const float *Y, flo
     const int rb = a.rb, tid = threadIdx.x;
     // L^{-1} by elimination on [L | I]: step j scales row j, then clears column j below it
     const int tp = tid >> 4, tq = tid & 15;
+    __shared__ float sink[FT];                           // target of stores that must not land
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
@@ -400,8 +403,9 @@ __device__ __forceinline__ void solve_rows(const FitArgs &a, const float *Y, flo
             for (int v = 0; v < NB; ++v) {
                 const int p = tp + 16 * u, c = tq + 16 * v;
                 if (NB == 5 && (p >= kFitMaxCols || c >= kFitMaxCols)) continue;
-                const float lp = L[p][j], xc = Li[j][c];
-                Li[p][c] -= p > j && p < rb && c <= j ? lp * xc : 0.f;
+                const bool upd = p > j && p < rb && c <= j;
+                const float val = Li[p][c] - L[p][j] * Li[j][c];
+                *(upd ? &Li[p][c] : &sink[tid]) = val;   // dummy slot: see gram_cholesky
             }
         __syncthreads();
     }
