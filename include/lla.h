@@ -225,10 +225,11 @@ lla_status lla_encode_chunk(const lla_codec *codec, const lla_params *params,
  *                   and >= H*d (T*H*d reads loop t of a [B][chunk][T][H][d] staging buffer
  *                   offset by t*H*d)
  *   n_new           device int32 [B], clamped to [0, chunk]
- * Rows i >= n_new[b] of out are not written.  No workspace.  bf16 codecs only (LLA_ERR_DTYPE);
- * d_head 64 or 128 with (r_k, r_v) in {(16,16), (16,32), (32,32)}, else LLA_ERR_UNSUPPORTED;
- * page_size a multiple of 32, 0 <= t < T and chunk * new_stride < 2^31, else LLA_ERR_SHAPE.
- * chunk = 0 enqueues nothing.
+ * Rows i >= n_new[b] of out are not written; rows below are also used as scratch between the
+ * call's two kernels, so out must not overlap any input.  No workspace.  bf16 codecs only
+ * (LLA_ERR_DTYPE); d_head 64 or 128 with (r_k, r_v) in {(16,16), (16,32), (32,32)} and
+ * n_pages * G * page_size < 2^31, else LLA_ERR_UNSUPPORTED; page_size a multiple of 32,
+ * 0 <= t < T and chunk * new_stride < 2^31, else LLA_ERR_SHAPE.  chunk = 0 enqueues nothing.
  */
 lla_status lla_prefill_attn(const lla_codec *codec, const lla_params *params,
                             const lla_cache *cache, int32_t t, int32_t chunk,

@@ -366,6 +366,8 @@ lla_status lla_prefill_attn(const lla_codec *c, const lla_params *prm, const lla
     // the kernel forms a chunk row's offset inside its sequence in 32-bit arithmetic
     if ((long)chunk * new_stride > (1L << 31) - 1) return LLA_ERR_SHAPE;
     const Shape sh = shape_of(c);
+    // and a pool row (page, group, slot) as a signed 32-bit index
+    if ((long)k->n_pages * sh.G * k->page_size > (1L << 31) - 1) return LLA_ERR_UNSUPPORTED;
     PrefillArgs a{};
     a.k_pool = k->k_pool;
     a.v_pool = k->v_pool;

@@ -13,21 +13,27 @@
 // the identity the absorbed decode uses.  Per cached 32-token tile a wave then runs one score
 // MFMA per 16 key ranks (A = the latent rows, B = q'^T) and two value MFMAs into a 32 x 32
 // latent accumulator O_lat^T = C_v^T P^T (rank x query); the chunk's own tiles are ordinary flash
-// attention over the given keys and values.  Both kinds share one online softmax; at the end
-// O^T += W_up,t^V^T O_lat^T (one MFMA per 16 value ranks and 32-dim tile) and (sum p) mu_t^V are
-// added to the chunk part's accumulators.
+// attention over the given keys and values, and one online softmax spans both.
 //
-// Layout of the work: one workgroup of 8 waves (two per SIMD) per (sequence, head, block of 256
-// queries); wave w owns queries [32w, 32w + 32) of the block.  Every score tile is S^T (32 tokens
-// x 32 queries, v_mfma_f32_32x32x16_bf16), so each lane holds 16 scores of one query: the softmax
-// row statistics need in-lane reductions and one exchange between lanes l and l ^ 32, and every
-// accumulator keeps one query per lane, so the online rescale is a per-lane multiply.  Tiles are
-// staged in LDS in the lane layout of the MFMA operands (cached: the latent rows and the value
-// latents transposed; chunk: key and value rows); LDS is double-buffered, one barrier per tile,
-// and the inputs of tile i + 2 are in flight in registers meanwhile.
-// Precision: q', the latents, the chunk keys and values, the softmax weights and O_lat are bf16
-// MFMA operands (the precision class of a bf16 KV cache in a flash-attention kernel); scores,
-// statistics and accumulators are fp32; out is rounded once (RNE).
+// Two passes, launched back to back on the caller's stream:
+// * the cached pass (one workgroup of 8 waves per (sequence, head, block of 256 queries); wave w
+//   owns queries [32w, 32w + 32) of the block) runs the online softmax over the cached tiles in
+//   latent space and parks each query's partial state (O_lat, running max, weight sum) in its own
+//   out row.  It holds only latent-sized state, so four waves share a SIMD, and it stages 8 tiles
+//   per step with two steps of loads in flight: the bytes in flight per CU, not the arithmetic,
+//   set its speed.
+// * the chunk pass (same grid) starts from that state, O^T = W_up,t^V^T O_lat^T, runs ordinary
+//   flash attention over the chunk's own tiles up to each query, adds (sum of cached weights)
+//   mu_t^V, normalises and overwrites the row with the result.
+// Every score tile is S^T (32 tokens x 32 queries, v_mfma_f32_32x32x16_bf16), so each lane holds
+// 16 scores of one query: the softmax row statistics need in-lane reductions and one exchange
+// between lanes l and l ^ 32, and every accumulator keeps one query per lane, so the online
+// rescale is a per-lane multiply.  Tiles are staged in LDS in the lane layout of the MFMA
+// operands (cached: the latent rows and the value latents transposed; chunk: key and value rows);
+// LDS is double-buffered with one barrier per step.
+// Precision: q', the latents, the chunk keys and values, the softmax weights and O_lat (rounded
+// once, when parked) are bf16 MFMA operands (the precision class of a bf16 KV cache in a
+// flash-attention kernel); scores, statistics and accumulators are fp32; out is rounded once (RNE).
 #include "lla_internal.h"
 
 namespace lla {
@@ -61,52 +67,363 @@ __device__ __forceinline__ float max_swap32(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-constexpr int PWAVES = 8;                  // waves per workgroup (two per SIMD)
+constexpr int PWAVES = 8;                  // waves per workgroup
 constexpr int QWG = PWAVES * 32;           // queries per workgroup: one 32-query tile per wave
+constexpr int CGT = 8;                     // cached tiles per pipeline step of the cached pass
+constexpr float kSlack = 8.f;              // lazy rescale threshold (log2 domain)
 
-template <int D, int RK, int RV>
-struct PShape {
-    static constexpr int MT = D / 32;                  // 32-wide tiles of the head dim
-    static constexpr int KS = D / 16;                  // k-steps of a full-width score MFMA
+// An operand slot in LDS holds one 16-byte row per lane; a 16-byte pad after every 8 rows spreads
+// the transposed 2-byte writes of the value operands over the banks (a group of 8 lanes still
+// reads 128 contiguous bytes).
+constexpr int kSlot = 72;                  // uint4 per operand slot
+__device__ __forceinline__ int srow(int r) { return r + (r >> 3); }
+
+// Query operands (B of a full-width score MFMA over the head dims): lane (l32, h2) holds query row
+// wq0 + l32, k-step ks covers dims 32 (ks / 2) + 16 (ks % 2) + 4 h2 + {0..3} and + 8 + {0..3} (a
+// permutation of the head dims that the chunk keys' LDS layout shares).  Rows past the chunk read
+// the last valid row (their results are not stored).
+template <int D>
+__device__ __forceinline__ void load_query_operands(const PrefillArgs &a, int b, int h, int qrow,
+                                                    int h2, uint4 (&qop)[D / 16]) {
+    const uint16_t *row = static_cast<const uint16_t *>(a.q) + (((size_t)b * a.Pn + qrow) * a.H + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const int d0 = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * h2;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(row + d0);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(row + d0 + 8);
+        qop[ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+}
+
+// Partial softmax state of the cached pass, parked per query in that query's own out row until
+// the chunk pass overwrites the row with its result: O_lat as bf16 in the lane order of the
+// W_up,t^V MFMA's B operand (lane (query, h2), k-step ks at uint4 KV h2 + ks), then the running
+// max and the weight sum (fp32).  32 KV + 8 <= 72 bytes, inside a row of 64 bf16.
+__device__ __forceinline__ uint4 *state_row(const PrefillArgs &a, int b, int iq, int h, int D) {
+    return reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) +
+                                     (((size_t)b * a.Pn + iq) * a.H + h) * D);
+}
+
+// ================================================================ cached pass
+template <int RK, int RV>
+struct CShape {
     static constexpr int KK = RK / 16, KV = RV / 16;   // k-steps over the key / value ranks
     // 16-byte latent pieces (8 ranks of one token) of a cached tile: key pieces, then value pieces
     static constexpr int CPK = 32 * RK / 8, CPV = 32 * RV / 8, CP = CPK + CPV;
+    static constexpr int NP = CP * CGT / (64 * PWAVES);   // pieces per thread per step
+    static constexpr int SL = KK + 2;                     // 1 KB operand slots per tile
+    static_assert(CP * CGT % (64 * PWAVES) == 0, "whole pieces per thread");
+    static_assert(CPK % 64 == 0, "each wave's pieces are all keys or all values");
+    static_assert(RK <= 32 && RV <= 32, "one 32-row MFMA tile of latent ranks");
+};
+
+// Registers holding one step's latent pieces (this thread's) while they are in flight.
+template <int N>
+struct CStage {
+    uint4 r[N];
+    bool bad;                                  // uniform: a page id of the step was out of range
+};
+
+// One workgroup per (sequence, head, block of 256 queries), 8 waves, two workgroups per CU.
+// Only the latent state (q', O_lat, max, sum) lives in registers, so four waves share a SIMD; a
+// step stages 8 tiles (256 tokens) through LDS and the next two steps' latents are in flight,
+// enough bytes per CU to cover HBM latency.
+template <int D, int RK, int RV>
+__global__ __launch_bounds__(64 * PWAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void prefill_cached_kernel(PrefillArgs a) {
+    using CS = CShape<RK, RV>;
+    constexpr int KS = D / 16, KK = CS::KK, KV = CS::KV, NP = CS::NP, SL = CS::SL;
+    constexpr int CP = CS::CP, CPK = CS::CPK;
+    using St = CStage<NP>;
+
+    // per buffer and tile: slots [0, KK) the key latents (A of the score MFMA), [KK, KK + 2) the
+    // value latents transposed (A of the value MFMA)
+    __shared__ __align__(16) uint4 cbuf[2][CGT][SL][kSlot];
+    __shared__ int sbad[PWAVES];
+
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
+    const int qb = id % a.QB;
+    const int h = (id / a.QB) % a.H;
+    const int b = id / (a.QB * a.H);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int g = a.mode ? 0 : h;
+    const int col0 = a.mode ? h * D : 0;
+
+    int nn = a.n_new[b];
+    nn = nn < 0 ? 0 : (nn > a.Pn ? a.Pn : nn);
+    const int q0 = qb * QWG;
+    if (q0 >= nn) return;                               // the whole block is past the chunk
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    if (len == 0) return;                               // nothing cached: the chunk pass starts empty
+    const int qend = min(nn, q0 + QWG);
+    const int ctiles = (len + 31) >> 5;
+    const int steps = (ctiles + CGT - 1) / CGT;
+    const int wq0 = q0 + 32 * wave;
+    const bool wlive = wq0 < qend;
+    const float csc = a.scale_log2;
+
+    // ---- q' = c W_up,t^K q for this wave's queries, on the matrix cores: q'^T = W q^T with
+    // A = W_up,t^K (lane (rank l32, h2): the rank's row at the query operand's dims; ranks past
+    // RK are zero), B = the query operands.  Lane (query, h2) gets ranks 8 (v / 4) + 4 h2 + v % 4,
+    // which packs straight into the B operand of the score MFMA (k-step ks: ranks
+    // 16 ks + 8 (e / 4) + 4 h2 + e % 4 at element e).  q mu_t^K (scaled) is one in-lane dot over
+    // this lane's half of the dims plus an exchange.
+    uint4 qlat[KK];
+    float qmu;
+    {
+        uint4 qop[KS];
+        load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
+        const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
+                             ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
+        const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
+                              (size_t)a.t * a.Dg + col0;
+        const int rk = min(l32, RK - 1);
+        f32x16 qa = {};
+        float qm = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint16_t w[8];
+            const uint32_t qv[4] = {qop[ks].x, qop[ks].y, qop[ks].z, qop[ks].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int dim = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * h2 + (e < 4 ? e : e + 4);
+                w[e] = l32 < RK ? Wk[(size_t)rk * a.Dg + dim] : (uint16_t)0;
+                qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(muk[dim]);
+            }
+            const uint4 wop = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
+                                         w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
+            qa = mfma(wop, qop[ks], qa);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) qa[v] *= csc;
+#pragma unroll
+        for (int ks = 0; ks < KK; ++ks) qlat[ks] = pack8(qa, ks);
+        qmu = (qm + __shfl_xor(qm, 32, 64)) * csc;
+    }
+
+    // ---- step inputs.  Piece p = tid + 512 x of step s belongs to tile 8 s + p / CP (clamped to
+    // the last cached tile); within the tile, piece p' = p % CP is (token p' / (R / 8), clamped to
+    // the last valid token; ranks 8 (p' % (R / 8)) .. + 7) of c_k (p' < CPK) or of c_v (p' - CPK),
+    // in one page (P is a multiple of 32).  CP and CPK are multiples of 64, so a wave's pieces of
+    // one slot are all keys or all values of one tile: the page lookup is scalar, per wave and
+    // slot, and only the token and rank are per lane.
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
+    const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+    const int tpp = a.P >> 5;                           // tiles per page
+    // tile / tpp = mulhi(tile, tmag) or one more (tile < 2^32)
+    const uint32_t tmag = 0xFFFFFFFFu / (uint32_t)tpp;
+    auto slot_tile = [&](int x) { return (64 * wave + 64 * PWAVES * x) / CP; };
+    auto slot_key = [&](int x) { return (64 * wave + 64 * PWAVES * x) % CP < CPK; };
+    auto lane_piece = [&](int x) { return ((64 * wave + 64 * PWAVES * x) % CP) + lane - (slot_key(x) ? 0 : CPK); };
+    bool bad_w = false;                                 // uniform: this wave met a bad page id
+    auto issue = [&](int s, St &st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < NP; ++x) {
+            const int tile = min(CGT * s + slot_tile(x), ctiles - 1);
+            uint32_t pidx = __umulhi((uint32_t)tile, tmag);
+            int toff = tile - (int)pidx * tpp;
+            if (toff >= tpp) {
+                toff -= tpp;
+                ++pidx;
+            }
+            int page = bt[pidx];
+            const bool ok = (unsigned)page < (unsigned)a.n_pages;
+            st.bad |= !ok;
+            page = ok ? page : 0;
+            const int row = (page * a.G + g) * a.P + 32 * toff;   // pool row of the tile's token 0
+            const int lim = len - 1 - 32 * tile;                   // >= 0: last valid token
+            const bool key = slot_key(x);
+            const int R = key ? RK : RV;
+            const int pi = lane_piece(x);
+            const int tok = pi / (R / 8), rank = 8 * (pi % (R / 8));
+            const uint16_t *src = (key ? kp : vp) + (size_t)(row + min(tok, lim)) * R + rank;
+            st.r[x] = *reinterpret_cast<const uint4 *>(src);
+        }
+    };
+
+    // ---- write step s's pieces into LDS buffer `buf` in operand layout
+    auto produce = [&](int s, St &st, int buf) __attribute__((always_inline)) {
+        if (s >= steps) return;
+        bad_w |= st.bad;
+        st.bad = false;
+#pragma unroll
+        for (int x = 0; x < NP; ++x) {
+            const int tg = slot_tile(x);
+            const int pi = lane_piece(x);
+            const uint4 w = st.r[x];
+            if (slot_key(x)) {
+                // A operand of the score MFMA, lane (token, h2) of k-step ks: ranks
+                // 16 ks + 8 (e / 4) + 4 h2 + e % 4 at element e.  Ranks 8 p' .. + 3 of this piece
+                // go to lane (token, 0), + 4 .. + 7 to lane (token, 1), elements 4 (p' % 2) .. + 3,
+                // k-step p' / 2 (p' = rank / 8).
+                const int tok = pi / (RK / 8), pq = pi % (RK / 8);
+                uint2 *d0 = reinterpret_cast<uint2 *>(&cbuf[buf][tg][pq >> 1][srow(tok)]) + (pq & 1);
+                uint2 *d1 =
+                    reinterpret_cast<uint2 *>(&cbuf[buf][tg][pq >> 1][srow(32 + tok)]) + (pq & 1);
+                *d0 = make_uint2(w.x, w.y);
+                *d1 = make_uint2(w.z, w.w);
+            } else {
+                // A operand of the value MFMA, lane (rank, h2) of token k-step kj: tokens
+                // 16 kj + 8 (e / 4) + 4 h2 + e % 4 at element e
+                const int tok = pi / (RV / 8), rank = 8 * (pi % (RV / 8));
+                const int kj = tok >> 4, rem = tok & 15;
+                const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int y = 0; y < 8; ++y) {
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(
+                        &cbuf[buf][tg][KK + kj][srow(32 * hh + rank + y)]);
+                    dst[e] = static_cast<uint16_t>(wd[y >> 1] >> (16 * (y & 1)));
+                }
+            }
+        }
+    };
+
+    // ---- online softmax over the cached tokens (log2 domain), with the matrix cores doing the
+    // per-score additions.  Scores are taken relative to a reference m_b: the score MFMA starts
+    // from a bias MFMA that adds c q mu_t^K - m_b to every score (A = 1 at ranks 0..2 of lanes
+    // h2 = 0, B = that bias split into three bf16 terms, whose sum is exact to 2^-27 relative),
+    // so p = 2^sc needs no per-score add, and the weight sum is an MFMA of the packed weights
+    // against ones (every lane gets its query's full sum).  Lazy rescale: m_b moves only when a
+    // score exceeds it by more than kSlack (p <= 2^kSlack meanwhile, exact after the final
+    // normalisation); the first tile always sets it.
+    const uint32_t one2 = 0x3F803F80u;                  // two bf16 ones
+    const uint4 onesA = make_uint4(one2, one2, one2, one2);
+    const uint4 biasA = h2 ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(one2, 0x3F80u, 0u, 0u);
+    auto bias_op = [&](float bv) __attribute__((always_inline)) {
+        const uint16_t hi = f2bf(bv);
+        const float r1 = bv - bf2f(hi);
+        const uint16_t mid = f2bf(r1);
+        const uint16_t lo = f2bf(r1 - bf2f(mid));
+        return h2 ? make_uint4(0u, 0u, 0u, 0u)
+                  : make_uint4(hi | (uint32_t)mid << 16, lo, 0u, 0u);
+    };
+    float m_b = 0.f, l_run = 0.f;
+    bool started = false;                               // uniform: m_b has been set
+    uint4 biasB = bias_op(qmu);
+    f32x16 olat = {};
+    const int rd = srow(lane);                          // this lane's operand row
+    auto consume = [&](int s, int buf) __attribute__((always_inline)) {
+        if (!wlive || s >= steps) return;
+        const int nt = min(CGT, ctiles - CGT * s);
+        for (int j = 0; j < nt; ++j) {
+            const int j0 = 32 * (CGT * s + j);
+            f32x16 sc = mfma(biasA, biasB, f32x16{});
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) sc = mfma(cbuf[buf][j][ks][rd], qlat[ks], sc);
+            // the last tile masks tokens past len.  Lane (query, h2), element v: token
+            // 8 (v / 4) + 4 h2 + v % 4.
+            if (j0 + 32 > len) {
+                const int lm = len - 1 - j0 - 4 * h2;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (8 * (v >> 2) + (v & 3) > lm) sc[v] = -INFINITY;
+            }
+            float mx = sc[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+            if (!started || __builtin_amdgcn_ballot_w64(mx > kSlack) != 0) {
+                // new reference m_b + delta for the query (both of its lanes agree)
+                float delta = max_swap32(mx);
+                if (started) delta = fmaxf(delta, 0.f);
+                if (delta == -INFINITY) delta = 0.f;
+                const float alpha = started ? exp2_(-delta) : 0.f;
+                l_run *= alpha;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) olat[v] *= alpha;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sc[v] -= delta;
+                m_b += delta;
+                biasB = bias_op(qmu - m_b);
+                started = true;
+            }
+            f32x16 pr;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pr[v] = exp2_(sc[v]);
+            const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
+            const f32x16 ls = mfma(onesA, p1, mfma(onesA, p0, f32x16{}));
+            olat = mfma(cbuf[buf][j][KK][rd], p0, olat);
+            olat = mfma(cbuf[buf][j][KK + 1][rd], p1, olat);
+            l_run += ls[0];
+        }
+    };
+
+    // ---- pipeline: step i + 1 produced while step i is consumed; step i + 2's inputs in flight
+    St s0, s1;
+    s0.bad = s1.bad = false;
+    issue(0, s0);
+    issue(1, s1);
+    produce(0, s0, 0);
+    issue(2, s0);
+    __syncthreads();
+    for (int it = 0; it < steps; it += 2) {
+        produce(it + 1, s1, 1);
+        issue(it + 3, s1);
+        consume(it, 0);
+        __syncthreads();
+        produce(it + 2, s0, 0);
+        issue(it + 4, s0);
+        consume(it + 1, 1);
+        __syncthreads();
+    }
+
+    // ---- park the state in the query's out row (an out-of-range page anywhere in the cached
+    // context makes the sum NaN)
+    if (lane == 0) sbad[wave] = bad_w;
+    __syncthreads();
+    bool bad_any = false;
+#pragma unroll
+    for (int w = 0; w < PWAVES; ++w) bad_any |= sbad[w] != 0;
+    if (!wlive) return;
+    const int iq = wq0 + l32;
+    if (iq >= qend) return;
+    uint4 *st = state_row(a, b, iq, h, D);
+#pragma unroll
+    for (int ks = 0; ks < KV; ++ks) st[KV * h2 + ks] = pack8(olat, ks);
+    if (h2 == 0)
+        *reinterpret_cast<float2 *>(st + 2 * KV) =
+            make_float2(m_b, bad_any ? __builtin_nanf("") : l_run);
+}
+
+// ================================================================ chunk pass
+template <int D>
+struct PShape {
+    static constexpr int MT = D / 32;                  // 32-wide tiles of the head dim
+    static constexpr int KS = D / 16;                  // k-steps of a full-width score MFMA
     // 16-byte pieces of a 32-token chunk tile per axis (32 rows x D / 8), per thread
     static constexpr int PIECES = 32 * D / 8;
     static constexpr int NEWP = (PIECES + 64 * PWAVES - 1) / (64 * PWAVES);
     static constexpr int NST = 2 * NEWP;               // stage registers per thread
     static constexpr int SLOTS = KS + 2 * MT;          // 1 KB operand slots per LDS buffer
-    static_assert(CP <= 64 * PWAVES, "one latent piece per thread");
-    static_assert(KK + 2 <= SLOTS, "cached operands fit a buffer");
     static_assert(MT == 2 || MT == 4, "head dim 64 or 128");
-    static_assert(RK <= 32 && RV <= 32, "one 32-row MFMA tile of latent ranks");
 };
 
-// Registers holding one tile's inputs while they are in flight: for a cached tile the thread's
-// latent piece (slot 0; threads past the pieces load a duplicate), for a chunk tile its 16-byte
-// pieces of the chunk rows (key pieces, then value pieces).  Every slot is one unconditional
-// 16-byte load whose address is chosen by the tile's kind, so the registers stay registers.
+// Registers holding one chunk tile's 16-byte pieces of the key and value rows while they are in
+// flight (key pieces, then value pieces).
 template <int N>
 struct Stage {
     uint4 r[N];
-    bool bad;                                // a cached tile whose page id is out of range
 };
 
-template <int D, int RK, int RV>
-__global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
-    using SH = PShape<D, RK, RV>;
-    constexpr int MT = SH::MT, KS = SH::KS, KK = SH::KK, KV = SH::KV;
+// One workgroup of 8 waves (two per SIMD) per (sequence, head, block of 256 queries).  Starts from
+// the cached pass's state (O^T = W_up,t^V^T O_lat^T, weights and max) and runs flash attention
+// over the chunk's own tiles up to each query; normalises and stores.
+template <int D, int RV>
+__global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs a) {
+    using SH = PShape<D>;
+    constexpr int MT = SH::MT, KS = SH::KS, KV = RV / 16;
     constexpr int NEWP = SH::NEWP, NST = SH::NST;
     using St = Stage<NST>;
 
-    // operand slots per buffer: a chunk tile uses [0, KS) for the keys (sK) and [KS, KS + 2 MT)
-    // for the values (sV); a cached tile uses [0, KK) for the key latents and [KK, KK + 2) for the
-    // value latents transposed
+    // operand slots per buffer: [0, KS) for the keys (sK), [KS, KS + 2 MT) for the values (sV)
     __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][64];
-    // each wave's query operands: used at set-up and by the few chunk tiles, so they wait in LDS
-    // rather than in registers
+    // each wave's query operands: read by every tile's score MFMAs, so they wait in LDS rather
+    // than in registers
     __shared__ __align__(16) uint4 sQ[PWAVES][KS][64];
-    __shared__ int sBad[2];
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -125,90 +442,65 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
     const int qend = min(nn, q0 + QWG);                 // this block's queries: [q0, qend)
-    const int ctiles = (len + 31) >> 5;                 // cached tiles
-    const int tiles = ctiles + ((qend + 31) >> 5);      // then chunk tiles up to the last query
+    const int tiles = (qend + 31) >> 5;                 // chunk tiles up to the last query
     const int wq0 = q0 + 32 * wave;                     // this wave's first query
     const bool wlive = wq0 < qend;
+    const int iq = wq0 + l32;
     const float csc = a.scale_log2;
 
-    const uint16_t *qp = static_cast<const uint16_t *>(a.q);
-    const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
-    const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
+    {
+        uint4 qop[KS];
+        load_query_operands<D>(a, b, h, min(iq, nn - 1), h2, qop);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sQ[wave][ks][lane] = qop[ks];
+    }
+
+    // ---- state after the cached tokens.  The cached part back in model space:
+    // O^T = W_up,t^V^T O_lat^T (A: lane (dim, h2) of 32-dim tile n holds the dim's column at ranks
+    // 16 ks + 8 (e / 4) + 4 h2 + e % 4, the order O_lat's lanes are parked in); its weight sum
+    // l_lat later scales mu_t^V.  The sums live in the h2 = 0 lane (both lanes are added at the
+    // end); lanes of queries past the block start empty.
+    float m_run = -INFINITY, l_run = 0.f, l_lat = 0.f;
+    f32x16 oacc[MT];
+#pragma unroll
+    for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
+    if (wlive && len > 0) {
+        uint4 lop[KV];
+        float2 ml = make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int ks = 0; ks < KV; ++ks) lop[ks] = make_uint4(0u, 0u, 0u, 0u);
+        if (iq < qend) {
+            const uint4 *st = state_row(a, b, iq, h, D);
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) lop[ks] = st[KV * h2 + ks];
+            ml = *reinterpret_cast<const float2 *>(st + 2 * KV);
+        }
+        m_run = ml.x;
+        l_run = h2 ? 0.f : ml.y;
+        l_lat = l_run;
+        const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
+                             ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
+#pragma unroll
+        for (int n = 0; n < MT; ++n) {
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) {
+                uint16_t w[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    w[e] = Wv[(size_t)(16 * ks + 8 * (e >> 2) + 4 * h2 + (e & 3)) * a.Dg + 32 * n + l32];
+                const uint4 wop = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
+                                             w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
+                oacc[n] = mfma(wop, lop[ks], oacc[n]);
+            }
+        }
+    }
+
+    // ---- tile inputs.  Chunk tile n: piece p = tid + 512 x of each axis is row 32n + p / (D / 8)
+    // (clamped to the last valid row), dims 8 (p % (D / 8)) .. + 7; slots [0, NEWP) hold key
+    // pieces, [NEWP, 2 NEWP) value pieces.
     const uint16_t *kn = static_cast<const uint16_t *>(a.k_new);
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new);
-    const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
-
-    // ---- query operands (B of the full-width score MFMA): lane (l32, h2) holds query row
-    // wq0 + l32, k-step ks covers dims 32 (ks / 2) + 16 (ks % 2) + 4 h2 + {0..3} and + 8 + {0..3}
-    // (a permutation of the head dims that the chunk keys' layout shares).  Rows past the chunk
-    // read the last valid row (their results are not stored).
-    uint4 qop[KS];                                      // set-up only; then in sQ
-    const int qrow = min(wq0 + l32, nn - 1);
-    {
-        const uint16_t *row = qp + (((size_t)b * a.Pn + qrow) * a.H + h) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int d0 = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * h2;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(row + d0);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(row + d0 + 8);
-            qop[ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
-    }
-    auto qdim = [&](int ks, int e) { return 32 * (ks >> 1) + 16 * (ks & 1) + 4 * h2 + (e < 4 ? e : e + 4); };
-
-    // ---- q' = c W_up,t^K q for this wave's queries, on the matrix cores: q'^T = W q^T with
-    // A = W_up,t^K (lane (rank l32, h2): the rank's row at the query operand's dims; ranks past
-    // RK are zero), B = the query operands.  Lane (query, h2) gets ranks 8 (v / 4) + 4 h2 + v % 4,
-    // which packs straight into the B operand of the cached score MFMA (k-step ks: ranks
-    // 16 ks + 8 (e / 4) + 4 h2 + e % 4 at element e).  q mu_t^K (scaled) is one in-lane dot over
-    // this lane's half of the dims plus an exchange.
-    uint4 qlat[KK];
-    float qmu;
-    {
-        const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
-                             ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
-        const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
-                              (size_t)a.t * a.Dg + col0;
-        const int rk = min(l32, RK - 1);
-        f32x16 qa = {};
-        float qm = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint16_t w[8];
-            const uint32_t qv[4] = {qop[ks].x, qop[ks].y, qop[ks].z, qop[ks].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int dim = qdim(ks, e);
-                w[e] = l32 < RK ? Wk[(size_t)rk * a.Dg + dim] : (uint16_t)0;
-                qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(muk[dim]);
-            }
-            const uint4 wop = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
-                                         w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
-            qa = mfma(wop, qop[ks], qa);
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) qa[v] *= csc;
-#pragma unroll
-        for (int ks = 0; ks < KK; ++ks) qlat[ks] = pack8(qa, ks);
-        qmu = (qm + __shfl_xor(qm, 32, 64)) * csc;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sQ[wave][ks][lane] = qop[ks];   // read by chunk tiles
-    }
-
-    // ---- tile inputs.  Cached tile c: piece p = tid < CP is (token 32c + p / (R / 8), clamped to
-    // the last valid token; ranks 8 (p % (R / 8)) .. + 7) of c_k (p < CPK) or c_v, in one page
-    // (P is a multiple of 32).  Chunk tile n: piece p = tid + 512 x of each axis is row
-    // 32n + p / (D / 8) (clamped to the last valid row), dims 8 (p % (D / 8)) .. + 7; slots
-    // [0, NEWP) hold key pieces, [NEWP, 2 NEWP) value pieces.  Addresses are a per-thread constant
-    // plus a per-tile scalar.
-    const int cp = min(tid, SH::CP - 1);
-    const bool ckey = cp < SH::CPK;
-    const int cR = ckey ? RK : RV;
-    const int cpi = ckey ? cp : cp - SH::CPK;
-    const int ctok = cpi / (cR / 8), crank = 8 * (cpi % (cR / 8));
-    const uint16_t *cbase = (ckey ? kp : vp) + (size_t)g * a.P * cR + crank;
-    const size_t cpage = (size_t)a.G * a.P * cR;
-    int pc_row[NST], pc_col[NST];                       // chunk piece of each stage slot
+    int pc_row[NST], pc_col[NST];
 #pragma unroll
     for (int x = 0; x < NST; ++x) {
         const int pc = min(tid + 64 * PWAVES * (x % NEWP), SH::PIECES - 1);
@@ -219,133 +511,70 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
     const uint16_t *vn_b = vn + (size_t)b * a.Pn * a.new_stride + (size_t)h * D;
     auto issue = [&](int tile, St &st) __attribute__((always_inline)) {
         tile = min(tile, tiles - 1);
-        const bool cached = tile < ctiles;
-        int page = bt[min((32 * tile) / a.P, a.max_pages - 1)];
-        st.bad = cached && (unsigned)page >= (unsigned)a.n_pages;
-        page = (unsigned)page < (unsigned)a.n_pages ? page : 0;
-        const uint16_t *lat = cbase + page * cpage +
-                              (size_t)((32 * tile) % a.P + min(ctok, max(len - 1 - 32 * tile, 0))) * cR;
-        // chunk: rows 32n + r, clamped to the last valid row
-        const int n0 = 32 * (tile - ctiles);
+        const int n0 = 32 * tile;
         const int rmax = nn - 1 - n0;
 #pragma unroll
         for (int x = 0; x < NST; ++x) {
             const uint16_t *chk = (x < NEWP ? kn_b : vn_b) +
                                   (uint32_t)((n0 + min(pc_row[x], rmax)) * (int)a.new_stride +
                                              pc_col[x]);
-            st.r[x] = *reinterpret_cast<const uint4 *>(cached ? lat : chk);
+            st.r[x] = *reinterpret_cast<const uint4 *>(chk);
         }
     };
 
     // ---- write tile `tile` into LDS buffer `buf` in operand layout
     auto produce = [&](int tile, const St &st, int buf) __attribute__((always_inline)) {
         if (tile >= tiles) return;
-        if (tile < ctiles) {
-            if (tid == 0) sBad[buf] = st.bad;
-            if (tid >= SH::CP) return;
-            const uint4 w = st.r[0];
-            if (ckey) {
-                // A operand of the cached score MFMA, lane (token, h2) of k-step ks: ranks
-                // 16 ks + 8 (e / 4) + 4 h2 + e % 4 at element e.  Ranks 8 p' .. + 3 of this piece
-                // go to lane (ctok, 0), + 4 .. + 7 to lane (ctok, 1), elements 4 (p' % 2) .. + 3,
-                // k-step p' / 2 (p' = crank / 8).
-                const int pq = crank >> 3;
-                uint2 *d0 = reinterpret_cast<uint2 *>(&sbuf[buf][pq >> 1][ctok]) + (pq & 1);
-                uint2 *d1 = reinterpret_cast<uint2 *>(&sbuf[buf][pq >> 1][32 + ctok]) + (pq & 1);
-                *d0 = make_uint2(w.x, w.y);
-                *d1 = make_uint2(w.z, w.w);
-            } else {
-                // A operand of the value MFMA, lane (rank, h2) of token k-step kj: tokens
-                // 16 kj + 8 (e / 4) + 4 h2 + e % 4 at element e
-                const int kj = ctok >> 4, rem = ctok & 15;
-                const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
-                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        // key piece (row jr, dims 8c .. 8c + 7): dims 8c + 4 hh + {0..3} are elements
+        // 4 (c % 2) .. + 3 of lane 32 hh + jr in k-step 2 (c / 4) + (c / 2) % 2
 #pragma unroll
-                for (int y = 0; y < 8; ++y) {
-                    uint16_t *dst = reinterpret_cast<uint16_t *>(
-                        &sbuf[buf][KK + kj][32 * hh + crank + y]);
-                    dst[e] = static_cast<uint16_t>(wd[y >> 1] >> (16 * (y & 1)));
-                }
-            }
-        } else {
-            // key piece (row jr, dims 8c .. 8c + 7): dims 8c + 4 hh + {0..3} are elements
-            // 4 (c % 2) .. + 3 of lane 32 hh + jr in k-step 2 (c / 4) + (c / 2) % 2
+        for (int x = 0; x < NEWP; ++x) {
+            const int pc = tid + 64 * PWAVES * x;
+            if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
+            const int jr = pc / (D / 8), c8 = pc % (D / 8);
+            const int ks = 2 * (c8 >> 2) + ((c8 >> 1) & 1);
+            const uint4 w = st.r[x];
+            uint2 *d0 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][jr]) + (c8 & 1);
+            uint2 *d1 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][32 + jr]) + (c8 & 1);
+            *d0 = make_uint2(w.x, w.y);
+            *d1 = make_uint2(w.z, w.w);
+        }
+        // value piece (row jr, dims 8p .. 8p + 7) -> the V^T operand of each dim: lane
+        // (dim % 32, h2) of slot KS + 2 (dim / 32) + jr / 16 holds tokens 16 kj + 8 (e / 4) +
+        // 4 h2 + e % 4 at element e
 #pragma unroll
-            for (int x = 0; x < NEWP; ++x) {
-                const int pc = tid + 64 * PWAVES * x;
-                if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
-                const int jr = pc / (D / 8), c8 = pc % (D / 8);
-                const int ks = 2 * (c8 >> 2) + ((c8 >> 1) & 1);
-                const uint4 w = st.r[x];
-                uint2 *d0 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][jr]) + (c8 & 1);
-                uint2 *d1 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][32 + jr]) + (c8 & 1);
-                *d0 = make_uint2(w.x, w.y);
-                *d1 = make_uint2(w.z, w.w);
-            }
-            // value piece (row jr, dims 8p .. 8p + 7) -> the V^T operand of each dim: lane
-            // (dim % 32, h2) of slot KS + 2 (dim / 32) + jr / 16 holds tokens 16 kj + 8 (e / 4) +
-            // 4 h2 + e % 4 at element e
+        for (int x = 0; x < NEWP; ++x) {
+            const int pc = tid + 64 * PWAVES * x;
+            if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
+            const int jr = pc / (D / 8), p8 = 8 * (pc % (D / 8));
+            const int kj = jr >> 4, rem = jr & 15;
+            const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
+            const uint4 w = st.r[NEWP + x];
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int x = 0; x < NEWP; ++x) {
-                const int pc = tid + 64 * PWAVES * x;
-                if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
-                const int jr = pc / (D / 8), p8 = 8 * (pc % (D / 8));
-                const int kj = jr >> 4, rem = jr & 15;
-                const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
-                const uint4 w = st.r[NEWP + x];
-                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int y = 0; y < 8; ++y) {
-                    const int dim = p8 + y;
-                    uint16_t *dst = reinterpret_cast<uint16_t *>(
-                        &sbuf[buf][KS + 2 * (dim >> 5) + kj][32 * hh + (dim & 31)]);
-                    dst[e] = static_cast<uint16_t>(wd[y >> 1] >> (16 * (y & 1)));
-                }
+            for (int y = 0; y < 8; ++y) {
+                const int dim = p8 + y;
+                uint16_t *dst = reinterpret_cast<uint16_t *>(
+                    &sbuf[buf][KS + 2 * (dim >> 5) + kj][32 * hh + (dim & 31)]);
+                dst[e] = static_cast<uint16_t>(wd[y >> 1] >> (16 * (y & 1)));
             }
         }
     };
 
-    // ---- online softmax state of this wave's 32 queries (log2 domain): total and cached weight
-    // sums, O^T accumulators per 32-dim tile (chunk values, later the reconstructed cached part)
-    // and the latent accumulator O_lat^T (rank x query)
-    float m_run = -INFINITY, l_run = 0.f, l_lat = 0.f;
-    f32x16 oacc[MT], olat = {};
-#pragma unroll
-    for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
-
-    // Cached scores leave the MFMA already scaled (q' carries c) and need + c q mu_t^K; chunk
-    // scores are raw q . k and need * c: either way p = 2^(s scl + bias - m) is one FMA and one
-    // exp2.  Lazy rescale: the accumulators are rescaled only when a lane's max grows by more
-    // than kSlack (p <= 2^kSlack meanwhile, exact after the final normalisation by l).
-    constexpr float kSlack = 8.f;
+    // ---- online softmax over the chunk's tiles (log2 domain; raw q . k scores need * c), lazy
+    // rescale as in the cached pass
     const int wlast = min(wq0 + 31, qend - 1);          // this wave's last query
-
     auto consume = [&](int tile, int buf) __attribute__((always_inline)) {
         if (!wlive || tile >= tiles) return;
-        const bool cached = tile < ctiles;
-        const int j0 = cached ? 32 * tile : 32 * (tile - ctiles);
-        if (!cached && j0 > wlast) return;                  // every token is after every query
+        const int j0 = 32 * tile;
+        if (j0 > wlast) return;                         // every token is after every query
         f32x16 sc = {};
-        float scl, bias;
-        if (cached) {
 #pragma unroll
-            for (int ks = 0; ks < KK; ++ks) sc = mfma(sbuf[buf][ks][lane], qlat[ks], sc);
-            if (sBad[buf]) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sc[v] = __builtin_nanf("");
-            }
-            scl = 1.f;
-            bias = qmu;
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sc = mfma(sbuf[buf][ks][lane], sQ[wave][ks][lane], sc);
-            scl = csc;
-            bias = 0.f;
-        }
-        // edge tiles mask some score: the cached context's last tile, chunk tiles that reach past
-        // this wave's first query.  Lane (query, h2), element v: token 8 (v / 4) + 4 h2 + v % 4.
-        if (cached ? j0 + 32 > len : j0 + 31 > wq0) {
-            const int lim = cached ? len - 1 - j0 : wq0 + l32 - j0;   // last visible token
+        for (int ks = 0; ks < KS; ++ks) sc = mfma(sbuf[buf][ks][lane], sQ[wave][ks][lane], sc);
+        // tiles that reach past this wave's first query mask the tokens after each query.  Lane
+        // (query, h2), element v: token 8 (v / 4) + 4 h2 + v % 4.
+        if (j0 + 31 > wq0) {
+            const int lim = wq0 + l32 - j0;             // last visible token
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 if (8 * (v >> 2) + 4 * h2 + (v & 3) > lim) sc[v] = -INFINITY;
@@ -353,7 +582,7 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
         float mx = sc[0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-        mx = fmaf(max_swap32(mx), scl, bias);
+        mx = max_swap32(mx) * csc;
         const float m_cand = fmaxf(m_run, mx);
         if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kSlack) != 0) {
             const float alpha = m_cand == -INFINITY ? 1.f : exp2_(m_run - m_cand);
@@ -363,32 +592,22 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
             for (int n = 0; n < MT; ++n)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) oacc[n][v] *= alpha;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) olat[v] *= alpha;
             m_run = m_cand;
         }
         // softmax weights as the two bf16 B operands of the value MFMAs
-        const float nb = bias - m_run;
         f32x16 pr;
         float ls = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            pr[v] = exp2_(fmaf(sc[v], scl, nb));
+            pr[v] = exp2_(fmaf(sc[v], csc, -m_run));
             ls += pr[v];
         }
         l_run += ls;
         const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
-        if (cached) {
-            l_lat += ls;
-            olat = mfma(sbuf[buf][KK][lane], p0, olat);
-            olat = mfma(sbuf[buf][KK + 1][lane], p1, olat);
-        } else {
-            // (the value operands are read only now: a chunk tile is rare, registers are not)
 #pragma unroll
-            for (int n = 0; n < MT; ++n) {
-                oacc[n] = mfma(sbuf[buf][KS + 2 * n][lane], p0, oacc[n]);
-                oacc[n] = mfma(sbuf[buf][KS + 2 * n + 1][lane], p1, oacc[n]);
-            }
+        for (int n = 0; n < MT; ++n) {
+            oacc[n] = mfma(sbuf[buf][KS + 2 * n][lane], p0, oacc[n]);
+            oacc[n] = mfma(sbuf[buf][KS + 2 * n + 1][lane], p1, oacc[n]);
         }
     };
 
@@ -413,33 +632,12 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
         step(it + 1, s0);
     }
 
-    // ---- the cached part back in model space: O^T += W_up,t^V^T O_lat^T (A: lane (dim, h2) of
-    // 32-dim tile n holds the dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4, the order
-    // O_lat's lanes pack in), then + (sum of cached weights) mu_t^V; normalise and store.
+    // ---- + (sum of cached weights) mu_t^V; normalise and store
     if (!wlive) return;
-    const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
-                         ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
     const uint16_t *muv = static_cast<const uint16_t *>(a.mu_v) + (size_t)g * a.T * a.Dg +
                           (size_t)a.t * a.Dg + col0;
-    uint4 lop[KV];
-#pragma unroll
-    for (int ks = 0; ks < KV; ++ks) lop[ks] = pack8(olat, ks);
-#pragma unroll
-    for (int n = 0; n < MT; ++n) {
-#pragma unroll
-        for (int ks = 0; ks < KV; ++ks) {
-            uint16_t w[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                w[e] = Wv[(size_t)(16 * ks + 8 * (e >> 2) + 4 * h2 + (e & 3)) * a.Dg + 32 * n + l32];
-            const uint4 wop = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
-                                         w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
-            oacc[n] = mfma(wop, lop[ks], oacc[n]);
-        }
-    }
     const float lat_w = l_lat + __shfl_xor(l_lat, 32, 64);
     const float inv = 1.f / (l_run + __shfl_xor(l_run, 32, 64));
-    const int iq = wq0 + l32;
     if (iq >= qend) return;
     uint16_t *row = static_cast<uint16_t *>(a.out) + (((size_t)b * a.Pn + iq) * a.H + h) * D;
 #pragma unroll
@@ -458,7 +656,10 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_kernel(PrefillArgs a) {
 template <int D, int RK, int RV>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.QB;
-    hipLaunchKernelGGL((prefill_kernel<D, RK, RV>), dim3(blocks), dim3(64 * PWAVES), 0, st, a);
+    hipLaunchKernelGGL((prefill_cached_kernel<D, RK, RV>), dim3(blocks), dim3(64 * PWAVES), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, RV>), dim3(blocks), dim3(64 * PWAVES), 0, st, a);
     return hipGetLastError();
 }
 

@@ -213,6 +213,9 @@ def test_prefill_validation_without_launch():
     assert call(q=FAKE + 8) == lla.LLA_ERR_ALIGN
     odd_pages = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 48, 64, 64, 3072)
     assert call(cache_=odd_pages) == lla.LLA_ERR_SHAPE
+    # 2^21 pages x 16 heads x 64 slots = 2^31 pool rows: past the kernels' 32-bit row index
+    huge = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 1 << 21, 4096)
+    assert call(cache_=huge) == lla.LLA_ERR_UNSUPPORTED
     assert call(chunk=0) == lla.LLA_OK                              # nothing to do
     empty = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 64, 0)
     assert call(cache_=empty) == lla.LLA_OK
