@@ -70,6 +70,9 @@ __device__ __forceinline__ float max_swap32(float x) {
 constexpr int PWAVES = 8;                  // waves per workgroup
 constexpr int QWG = PWAVES * 32;           // queries per workgroup: one 32-query tile per wave
 constexpr int CGT = 8;                     // cached tiles per pipeline step of the cached pass
+constexpr int CNS = 2;                     // chunk tiles in flight in the chunk pass
+constexpr int CWAVES = 8;                  // waves per workgroup of the chunk pass
+constexpr int CQWG = CWAVES * 32;          // queries per workgroup of the chunk pass
 constexpr float kSlack = 8.f;              // lazy rescale threshold (log2 domain)
 
 // An operand slot in LDS holds one 16-byte row per lane; a 16-byte pad after every 8 rows spreads
@@ -396,7 +399,7 @@ struct PShape {
     static constexpr int KS = D / 16;                  // k-steps of a full-width score MFMA
     // 16-byte pieces of a 32-token chunk tile per axis (32 rows x D / 8), per thread
     static constexpr int PIECES = 32 * D / 8;
-    static constexpr int NEWP = (PIECES + 64 * PWAVES - 1) / (64 * PWAVES);
+    static constexpr int NEWP = (PIECES + 64 * CWAVES - 1) / (64 * CWAVES);
     static constexpr int NST = 2 * NEWP;               // stage registers per thread
     static constexpr int SLOTS = KS + 2 * MT;          // 1 KB operand slots per LDS buffer
     static_assert(MT == 2 || MT == 4, "head dim 64 or 128");
@@ -413,17 +416,14 @@ struct Stage {
 // the cached pass's state (O^T = W_up,t^V^T O_lat^T, weights and max) and runs flash attention
 // over the chunk's own tiles up to each query; normalises and stores.
 template <int D, int RV>
-__global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs a) {
     using SH = PShape<D>;
     constexpr int MT = SH::MT, KS = SH::KS, KV = RV / 16;
     constexpr int NEWP = SH::NEWP, NST = SH::NST;
     using St = Stage<NST>;
 
     // operand slots per buffer: [0, KS) for the keys (sK), [KS, KS + 2 MT) for the values (sV)
-    __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][64];
-    // each wave's query operands: read by every tile's score MFMAs, so they wait in LDS rather
-    // than in registers
-    __shared__ __align__(16) uint4 sQ[PWAVES][KS][64];
+    __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][kSlot];
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -437,23 +437,19 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
 
     int nn = a.n_new[b];
     nn = nn < 0 ? 0 : (nn > a.Pn ? a.Pn : nn);
-    const int q0 = qb * QWG;
+    const int q0 = qb * CQWG;
     if (q0 >= nn) return;                               // the whole block is past the chunk
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-    const int qend = min(nn, q0 + QWG);                 // this block's queries: [q0, qend)
+    const int qend = min(nn, q0 + CQWG);                 // this block's queries: [q0, qend)
     const int tiles = (qend + 31) >> 5;                 // chunk tiles up to the last query
     const int wq0 = q0 + 32 * wave;                     // this wave's first query
     const bool wlive = wq0 < qend;
     const int iq = wq0 + l32;
     const float csc = a.scale_log2;
 
-    {
-        uint4 qop[KS];
-        load_query_operands<D>(a, b, h, min(iq, nn - 1), h2, qop);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sQ[wave][ks][lane] = qop[ks];
-    }
+    uint4 qop[KS];
+    load_query_operands<D>(a, b, h, min(iq, nn - 1), h2, qop);
 
     // ---- state after the cached tokens.  The cached part back in model space:
     // O^T = W_up,t^V^T O_lat^T (A: lane (dim, h2) of 32-dim tile n holds the dim's column at ranks
@@ -495,17 +491,20 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
         }
     }
 
-    // ---- tile inputs.  Chunk tile n: piece p = tid + 512 x of each axis is row 32n + p / (D / 8)
-    // (clamped to the last valid row), dims 8 (p % (D / 8)) .. + 7; slots [0, NEWP) hold key
-    // pieces, [NEWP, 2 NEWP) value pieces.
+    // ---- tile inputs.  Chunk tile n: piece p = tid + 512 x of each axis is row 32n + (p % 128) / 4
+    // (clamped to the last valid row), dims 32 (p / 128) + 8 (p % 4) .. + 7: a wave covers 16 rows
+    // of one 32-dim tile, so the transposed value writes of half a wave fall in 16 distinct banks.
+    // Slots [0, NEWP) hold key pieces, [NEWP, 2 NEWP) value pieces.
     const uint16_t *kn = static_cast<const uint16_t *>(a.k_new);
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new);
+    auto piece_row = [](int pc) { return (pc & 127) >> 2; };
+    auto piece_dim = [](int pc) { return 32 * (pc >> 7) + 8 * (pc & 3); };
     int pc_row[NST], pc_col[NST];
 #pragma unroll
     for (int x = 0; x < NST; ++x) {
-        const int pc = min(tid + 64 * PWAVES * (x % NEWP), SH::PIECES - 1);
-        pc_row[x] = pc / (D / 8);
-        pc_col[x] = 8 * (pc % (D / 8));
+        const int pc = min(tid + 64 * CWAVES * (x % NEWP), SH::PIECES - 1);
+        pc_row[x] = piece_row(pc);
+        pc_col[x] = piece_dim(pc);
     }
     const uint16_t *kn_b = kn + (size_t)b * a.Pn * a.new_stride + (size_t)h * D;
     const uint16_t *vn_b = vn + (size_t)b * a.Pn * a.new_stride + (size_t)h * D;
@@ -529,13 +528,13 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
         // 4 (c % 2) .. + 3 of lane 32 hh + jr in k-step 2 (c / 4) + (c / 2) % 2
 #pragma unroll
         for (int x = 0; x < NEWP; ++x) {
-            const int pc = tid + 64 * PWAVES * x;
-            if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
-            const int jr = pc / (D / 8), c8 = pc % (D / 8);
+            const int pc = tid + 64 * CWAVES * x;
+            if (SH::PIECES % (64 * CWAVES) != 0 && pc >= SH::PIECES) break;
+            const int jr = piece_row(pc), c8 = piece_dim(pc) >> 3;
             const int ks = 2 * (c8 >> 2) + ((c8 >> 1) & 1);
             const uint4 w = st.r[x];
-            uint2 *d0 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][jr]) + (c8 & 1);
-            uint2 *d1 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][32 + jr]) + (c8 & 1);
+            uint2 *d0 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][srow(jr)]) + (c8 & 1);
+            uint2 *d1 = reinterpret_cast<uint2 *>(&sbuf[buf][ks][srow(32 + jr)]) + (c8 & 1);
             *d0 = make_uint2(w.x, w.y);
             *d1 = make_uint2(w.z, w.w);
         }
@@ -544,9 +543,9 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
         // 4 h2 + e % 4 at element e
 #pragma unroll
         for (int x = 0; x < NEWP; ++x) {
-            const int pc = tid + 64 * PWAVES * x;
-            if (SH::PIECES % (64 * PWAVES) != 0 && pc >= SH::PIECES) break;
-            const int jr = pc / (D / 8), p8 = 8 * (pc % (D / 8));
+            const int pc = tid + 64 * CWAVES * x;
+            if (SH::PIECES % (64 * CWAVES) != 0 && pc >= SH::PIECES) break;
+            const int jr = piece_row(pc), p8 = piece_dim(pc);
             const int kj = jr >> 4, rem = jr & 15;
             const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
             const uint4 w = st.r[NEWP + x];
@@ -555,7 +554,7 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
             for (int y = 0; y < 8; ++y) {
                 const int dim = p8 + y;
                 uint16_t *dst = reinterpret_cast<uint16_t *>(
-                    &sbuf[buf][KS + 2 * (dim >> 5) + kj][32 * hh + (dim & 31)]);
+                    &sbuf[buf][KS + 2 * (dim >> 5) + kj][srow(32 * hh + (dim & 31))]);
                 dst[e] = static_cast<uint16_t>(wd[y >> 1] >> (16 * (y & 1)));
             }
         }
@@ -564,13 +563,14 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
     // ---- online softmax over the chunk's tiles (log2 domain; raw q . k scores need * c), lazy
     // rescale as in the cached pass
     const int wlast = min(wq0 + 31, qend - 1);          // this wave's last query
+    const int rd = srow(lane);                          // this lane's operand row
     auto consume = [&](int tile, int buf) __attribute__((always_inline)) {
         if (!wlive || tile >= tiles) return;
         const int j0 = 32 * tile;
         if (j0 > wlast) return;                         // every token is after every query
         f32x16 sc = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc = mfma(sbuf[buf][ks][lane], sQ[wave][ks][lane], sc);
+        for (int ks = 0; ks < KS; ++ks) sc = mfma(sbuf[buf][ks][rd], qop[ks], sc);
         // tiles that reach past this wave's first query mask the tokens after each query.  Lane
         // (query, h2), element v: token 8 (v / 4) + 4 h2 + v % 4.
         if (j0 + 31 > wq0) {
@@ -606,30 +606,30 @@ __global__ __launch_bounds__(64 * PWAVES) void prefill_chunk_kernel(PrefillArgs 
         const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
 #pragma unroll
         for (int n = 0; n < MT; ++n) {
-            oacc[n] = mfma(sbuf[buf][KS + 2 * n][lane], p0, oacc[n]);
-            oacc[n] = mfma(sbuf[buf][KS + 2 * n + 1][lane], p1, oacc[n]);
+            oacc[n] = mfma(sbuf[buf][KS + 2 * n][rd], p0, oacc[n]);
+            oacc[n] = mfma(sbuf[buf][KS + 2 * n + 1][rd], p1, oacc[n]);
         }
     };
 
-    // ---- pipeline: tile i + 1 produced while tile i is consumed; tile i + 2's inputs in flight
-    St s0, s1;
-    issue(0, s0);
-    issue(1, s1);
-    produce(0, s0, 0);
-    issue(2, s0);
+    // ---- pipeline: tile i + 1 produced while tile i is consumed; the inputs of tiles i + 2 ..
+    // i + 1 + CNS in flight (stage set j % CNS holds tile j)
+    St S[CNS];
+#pragma unroll
+    for (int u = 0; u < CNS; ++u) issue(u, S[u]);
+    produce(0, S[0], 0);
+    issue(CNS, S[0]);
     __syncthreads();
-    auto step = [&](int it, St &next) __attribute__((always_inline)) {
-        produce(it + 1, next, (it + 1) & 1);
-        issue(it + 3, next);
-        consume(it, it & 1);
-        __syncthreads();
-    };
-    // Both half-steps run on every trip (an odd count ends with an empty step): a path that skips
-    // the second half's loads would make the compiler wait on loads issued one step earlier
-    // instead of two.
-    for (int it = 0; it < tiles; it += 2) {
-        step(it, s1);
-        step(it + 1, s0);
+    // All CNS sub-steps run on every trip (a count that is not a multiple ends with empty ones):
+    // a path that skips some of the loads would make the compiler wait on later loads too.
+    for (int it = 0; it < tiles; it += CNS) {
+#pragma unroll
+        for (int u = 0; u < CNS; ++u) {
+            St &nx = S[(u + 1) % CNS];
+            produce(it + u + 1, nx, (it + u + 1) & 1);
+            issue(it + u + 1 + CNS, nx);
+            consume(it + u, (it + u) & 1);
+            __syncthreads();
+        }
     }
 
     // ---- + (sum of cached weights) mu_t^V; normalise and store
@@ -659,7 +659,10 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((prefill_cached_kernel<D, RK, RV>), dim3(blocks), dim3(64 * PWAVES), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, RV>), dim3(blocks), dim3(64 * PWAVES), 0, st, a);
+    PrefillArgs c = a;
+    c.QB = (a.Pn + CQWG - 1) / CQWG;
+    const unsigned cblocks = (unsigned)a.B * a.H * c.QB;
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, RV>), dim3(cblocks), dim3(64 * CWAVES), 0, st, c);
     return hipGetLastError();
 }
 
