@@ -120,4 +120,5 @@ class Chunk:
     def check(self, got, ref, what):
         live = np.arange(self.Pn)[None, :] < self.n_new[:, None]            # [B][Pn]
         assert np.all(np.isnan(got[~live])), f"{what}: rows past the chunk were written"
-        assert_close(got[live], ref[live], "bf16", what)
+        err, bound = assert_close(got[live], ref[live], "bf16", what)
+        print(f"{what}: max err {err:.3e} = {err / bound if bound else 0.0:.3f} of the bound", flush=True)
