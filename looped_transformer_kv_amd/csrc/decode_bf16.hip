@@ -81,7 +81,7 @@ struct Shape {
     static constexpr bool FUSED = !ROPE && KK <= 2 && KV <= 2;
     static constexpr int WAVES = 4;
     static constexpr int DEPTH =
-        ROPE ? 1 : (KK + KV <= 3 ? 3 : (KK + KV <= 4 ? 2 : 1));   // chunks in flight per wave
+        KK + KV <= 3 ? 3 : (KK + KV <= 4 ? 2 : 1);   // chunks in flight per wave
 };
 
 template <int D, int RK, int RV, bool ROPE>
@@ -106,6 +106,12 @@ void decode_bf16_kernel(DecodeArgs a) {
     __shared__ __align__(16) float sO[WAVES][D];
     __shared__ float sM[WAVES], sL[WAVES];
     __shared__ int sSlot[kMaxChunksPerSplit];         // chunk -> first token row in the pool
+    // ROPE: A operands of the pair-space score MFMAs (tile T < PT: cosine part of pairs
+    // 32T .. 32T + 31; PT + T: sine part), per k-step and bf16 term (hi, then lo for ranks up to
+    // 32, where the matrix cores have room for the second term)
+    constexpr int PT = ROPE ? MT / 2 : 1;
+    constexpr int TERMS = KK <= 2 ? 2 : 1;
+    __shared__ __align__(16) uint4 sAq[ROPE ? 2 * PT * KK * TERMS : 1][64];
 
     const int S = a.S;
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
@@ -259,14 +265,12 @@ void decode_bf16_kernel(DecodeArgs a) {
     // fused path: q_i for this lane's columns i = 32M + l32; explicit path: q rows
     // 32M + 8bb + 4h2 + 0..3 of the K tile
     uint16_t qcol[FUSED ? MT : 1];
-    uint16_t mucol[ROPE ? MT : 1];   // ROPE: mu_t^K of this lane's K_hat tile rows 32M + l32
-    uint2 qrow[FUSED ? 1 : MT][4];
+    uint2 qrow[(FUSED || ROPE) ? 1 : MT][4];
 #pragma unroll
     for (int M = 0; M < MT; ++M) {
-        if constexpr (ROPE) mucol[M] = muk[32 * M + l32];
         if constexpr (FUSED) {
             qcol[M] = qp[32 * M + l32];
-        } else {
+        } else if constexpr (!ROPE) {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
                 qrow[M][bb] = *reinterpret_cast<const uint2 *>(qp + 32 * M + 8 * bb + 4 * h2);
@@ -339,10 +343,10 @@ void decode_bf16_kernel(DecodeArgs a) {
         qm = ROPE ? 0.f : wave_sum(am) * a.scale_log2;
         if (self_score) s_self = wave_sum(as) * a.scale_log2;
     }
-    float qs[FUSED ? 1 : MT][16];
+    float qs[(FUSED || ROPE) ? 1 : MT][16];
     if constexpr (!FUSED) {
 #pragma unroll
-        for (int M = 0; M < MT; ++M)
+        for (int M = 0; M < ((FUSED || ROPE) ? 0 : MT); ++M)
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const uint2 u = qrow[M][bb];
@@ -381,23 +385,72 @@ void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int ks = 0; ks < KV; ++ks) wvr[N * KV + ks] = pack8(wvraw[N * KV + ks]);
     }
-    // ROPE operands: the mu k-step (A: mu_t^K of row l32 in k-slot 0; B: ones in k-slot 0) and
-    // this lane's pair frequencies (rotation slot k: half split rows (k/16, k%16) of the first
-    // half of the tiles; interleaved the even register 2(k%8) of tile k/8)
-    uint4 amu[ROPE ? MT : 1];
+    // ROPE: the score in pair space.  With R_j the rotation to token j's position, pair m
+    // (head-dim elements i, i') contributes cos(phi_jm) (q_i x_i + q_i' x_i') +
+    // sin(phi_jm) (q_i' x_i - q_i x_i') to <q, R_j x>.  Both brackets are linear in the key
+    // x = c_k W_up,t^K + mu_t^K, so they come out of MFMAs: A = the pair coefficients over the
+    // ranks (q_i W[k][i] + q_i' W[k][i'], resp. q_i' W[k][i] - q_i W[k][i'], log2-scaled, bf16;
+    // hi + lo terms up to rank 32) against the chunk's latents, and one more MFMA adds the mu part (its three
+    // bf16 terms in k-slots 0..2 of the lanes h2 = 0, against ones).  A lane then needs, per
+    // pair, its angle's sine and cosine and two FMAs; the rotation style only changes which
+    // elements form pair m.
+    uint4 amu[ROPE ? 2 * PT : 1];
     uint4 bone = make_uint4(0, 0, 0, 0);
-    float fr[ROPE ? MT * 8 : 1];
+    float fr[ROPE ? PT * 16 : 1];
     if constexpr (ROPE) {
+        auto pair_elems = [&](int m, int &i, int &ip) {
+            if (a.rope_style) {
+                i = 2 * m;
+                ip = 2 * m + 1;
+            } else {
+                i = m;
+                ip = m + D / 2;
+            }
+        };
+        const float scl = a.scale_log2;
+        for (int T = wave; T < 2 * PT; T += WAVES) {     // each wave builds whole tiles
+            const int N = T % PT;
+            const bool sine = T >= PT;
+            int i, ip;
+            pair_elems(32 * N + l32, i, ip);
+            const float qi = bf2f(qp[i]), qip = bf2f(qp[ip]);
+            const float ca = (sine ? qip : qi) * scl, cb = (sine ? -qi : qip) * scl;
 #pragma unroll
-        for (int M = 0; M < MT; ++M) amu[M] = make_uint4(h2 == 0 ? (uint32_t)mucol[M] : 0u, 0, 0, 0);
-        bone = make_uint4(h2 == 0 ? 0x3F80u : 0u, 0, 0, 0);   // bf16 1.0
+            for (int ks = 0; ks < KK; ++ks) {
+                uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int k = 0; k < MT * 8; ++k) {
-            const int Ma = a.rope_style ? k / 8 : k / 16;
-            const int va = a.rope_style ? 2 * (k % 8) : k % 16;
-            const int i = 32 * Ma + 8 * (va / 4) + 4 * h2 + (va % 4);
-            fr[k] = rope_rev(a.rope_style ? i >> 1 : i);
+                for (int e = 0; e < 8; e += 2) {
+                    const int k = 16 * ks + 8 * h2 + e;
+                    const float v0 = ca * bf2f(sWk[i * RKP + k]) + cb * bf2f(sWk[ip * RKP + k]);
+                    const float v1 = ca * bf2f(sWk[i * RKP + k + 1]) + cb * bf2f(sWk[ip * RKP + k + 1]);
+                    const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
+                    hi[e / 2] = h0 | (uint32_t)h1 << 16;
+                    lo[e / 2] = f2bf(v0 - bf2f(h0)) | (uint32_t)f2bf(v1 - bf2f(h1)) << 16;
+                }
+                sAq[(T * KK + ks) * TERMS][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                if (TERMS == 2) sAq[(T * KK + ks) * TERMS + 1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            }
         }
+#pragma unroll
+        for (int T = 0; T < 2 * PT; ++T) {
+            const int N = T % PT;
+            int i, ip;
+            pair_elems(32 * N + l32, i, ip);
+            const float qi = bf2f(qp[i]), qip = bf2f(qp[ip]);
+            const float mi = bf2f(muk[i]), mip = bf2f(muk[ip]);
+            const float v = scl * (T >= PT ? qip * mi - qi * mip : qi * mi + qip * mip);
+            const uint16_t t0 = f2bf(v);
+            const float r1 = v - bf2f(t0);
+            const uint16_t t1 = f2bf(r1);
+            const uint16_t t2 = f2bf(r1 - bf2f(t1));
+            amu[T] = h2 ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(t0 | (uint32_t)t1 << 16, t2, 0u, 0u);
+        }
+        bone = h2 ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(0x3F803F80u, 0x3F80u, 0u, 0u);
+        // lane (l32, h2) holds pairs 32N + 8 (v / 4) + 4 h2 + v % 4 of pair tile N
+#pragma unroll
+        for (int k = 0; k < PT * 16; ++k)
+            fr[k] = rope_rev(32 * (k / 16) + 8 * ((k % 16) / 4) + 4 * h2 + (k % 4));
+        __syncthreads();                                 // the pair operands are shared
     }
 
     float m_run = -INFINITY, l_lane = 0.f;
@@ -478,45 +531,30 @@ void decode_bf16_kernel(DecodeArgs a) {
             // ---- scores: K_hat tiles (d rows x 32 token columns) dotted with q per lane
             float sp[MT];                           // independent chains, one per tile
             if constexpr (ROPE) {
-                // token l32 sits at position j_begin + 32c + l32; row i = 32M + 8(v/4) + 4h2 + v%4
+                // token l32 sits at position j_begin + 32c + l32
                 const float pos = (float)(j_begin + 32 * c + l32);
-                auto turn = [&](int k, float xa, float xb) {   // (xa, xb) turned, as a pair
-                    const float rev = __builtin_amdgcn_fractf(pos * fr[k]);
-                    const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-                    return f32x2{xa * cs - xb * sn, xa * sn + xb * cs};
-                };
-                auto khat = [&](int M) {         // mu_t^K rows plus c_k W_up,t^K, tile M
-                    f32x16 t4 = mfma32x32x16(amu[M], bone, f32x16{});
 #pragma unroll
-                    for (int ks = 0; ks < KK; ++ks) t4 = mfma32x32x16(wk_op(M, ks), x.k[ks], t4);
-                    return t4;
-                };
+                for (int N = 0; N < PT; ++N) {
+                    f32x16 tc = mfma32x32x16(amu[N], bone, f32x16{});
+                    f32x16 ts = mfma32x32x16(amu[PT + N], bone, f32x16{});
 #pragma unroll
-                for (int M = 0; M < MT; ++M) sp[M] = 0.f;
-                // the style branch sits outside the unrolled loops, so every register index is a
-                // compile-time constant; tiles are taken a rotation group at a time
-                if (a.rope_style == 0) {          // half split: (M, v) with (M + MT/2, v)
+                    for (int ks = 0; ks < KK; ++ks)
 #pragma unroll
-                    for (int M = 0; M < MT / 2; ++M) {
-                        f32x16 ta = khat(M), tb = khat(M + MT / 2);
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const f32x2 r = turn(16 * M + v, ta[v], tb[v]);
-                            sp[M] += qs[M][v] * r.x;
-                            sp[M + MT / 2] += qs[M + MT / 2][v] * r.y;
+                        for (int term = 0; term < TERMS; ++term) {
+                            tc = mfma32x32x16(sAq[(N * KK + ks) * TERMS + term][lane], x.k[ks], tc);
+                            ts = mfma32x32x16(sAq[((PT + N) * KK + ks) * TERMS + term][lane], x.k[ks], ts);
                         }
-                    }
-                } else {                          // interleaved: (M, 2j) with (M, 2j + 1)
+                    float ac = 0.f, as = 0.f;
 #pragma unroll
-                    for (int M = 0; M < MT; ++M) {
-                        f32x16 t4 = khat(M);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const f32x2 r = turn(8 * M + j, t4[2 * j], t4[2 * j + 1]);
-                            sp[M] += qs[M][2 * j] * r.x + qs[M][2 * j + 1] * r.y;
-                        }
+                    for (int v = 0; v < 16; ++v) {
+                        const float rev = __builtin_amdgcn_fractf(pos * fr[16 * N + v]);
+                        ac = fmaf(__builtin_amdgcn_cosf(rev), tc[v], ac);
+                        as = fmaf(__builtin_amdgcn_sinf(rev), ts[v], as);
                     }
+                    sp[N] = ac + as;
                 }
+#pragma unroll
+                for (int M = PT; M < MT; ++M) sp[M] = 0.f;
             } else {
 #pragma unroll
                 for (int M = 0; M < MT; ++M) {

@@ -23,6 +23,7 @@ def assert_close(gpu, ref, dtype, what=""):
     bound = tol(dtype)(ref) if ref.size else 0.0
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
     assert err <= bound, f"{what}: max|gpu-oracle| = {err:.3e} > {bound:.3e}"
+    print(f"{what}: max err {err:.3e} = {err / bound if bound else 0.0:.3f} of the bound", flush=True)
     return err, bound
 
 
@@ -120,5 +121,4 @@ class Chunk:
     def check(self, got, ref, what):
         live = np.arange(self.Pn)[None, :] < self.n_new[:, None]            # [B][Pn]
         assert np.all(np.isnan(got[~live])), f"{what}: rows past the chunk were written"
-        err, bound = assert_close(got[live], ref[live], "bf16", what)
-        print(f"{what}: max err {err:.3e} = {err / bound if bound else 0.0:.3f} of the bound", flush=True)
+        assert_close(got[live], ref[live], "bf16", what)
