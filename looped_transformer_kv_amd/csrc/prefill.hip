@@ -69,7 +69,6 @@ __device__ __forceinline__ float max_swap32(float x) {
 
 constexpr int PWAVES = 8;                  // waves per workgroup
 constexpr int QWG = PWAVES * 32;           // queries per workgroup: one 32-query tile per wave
-constexpr int CGT = 8;                     // cached tiles per pipeline step of the cached pass
 constexpr int CNS = 2;                     // chunk tiles in flight in the chunk pass
 constexpr int CWAVES = 8;                  // waves per workgroup of the chunk pass
 constexpr int CQWG = CWAVES * 32;          // queries per workgroup of the chunk pass
@@ -113,6 +112,9 @@ struct CShape {
     static constexpr int KK = RK / 16, KV = RV / 16;   // k-steps over the key / value ranks
     // 16-byte latent pieces (8 ranks of one token) of a cached tile: key pieces, then value pieces
     static constexpr int CPK = 32 * RK / 8, CPV = 32 * RV / 8, CP = CPK + CPV;
+    // cached tiles per pipeline step: 8 (256 tokens), 4 when a tile has more pieces than 3 per
+    // wave, which keeps the stage registers at 24
+    static constexpr int CGT = CP > 192 ? 4 : 8;
     static constexpr int NP = CP * CGT / (64 * PWAVES);   // pieces per thread per step
     static constexpr int SL = KK + 2;                     // 1 KB operand slots per tile
     static_assert(CP * CGT % (64 * PWAVES) == 0, "whole pieces per thread");
@@ -129,14 +131,15 @@ struct CStage {
 
 // One workgroup per (sequence, head, block of 256 queries), 8 waves, two workgroups per CU.
 // Only the latent state (q', O_lat, max, sum) lives in registers, so four waves share a SIMD; a
-// step stages 8 tiles (256 tokens) through LDS and the next two steps' latents are in flight,
+// step stages 8 tiles (256 tokens; 4 at key and value ranks 32) through LDS and the next two
+// steps' latents are in flight,
 // enough bytes per CU to cover HBM latency.
 template <int D, int RK, int RV>
 __global__ __launch_bounds__(64 * PWAVES) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_cached_kernel(PrefillArgs a) {
     using CS = CShape<RK, RV>;
     constexpr int KS = D / 16, KK = CS::KK, KV = CS::KV, NP = CS::NP, SL = CS::SL;
-    constexpr int CP = CS::CP, CPK = CS::CPK;
+    constexpr int CP = CS::CP, CPK = CS::CPK, CGT = CS::CGT;
     using St = CStage<NP>;
 
     // per buffer and tile: slots [0, KK) the key latents (A of the score MFMA), [KK, KK + 2) the
@@ -291,9 +294,12 @@ void prefill_cached_kernel(PrefillArgs a) {
     // from a bias MFMA that adds c q mu_t^K - m_b to every score (A = 1 at ranks 0..2 of lanes
     // h2 = 0, B = that bias split into three bf16 terms, whose sum is exact to 2^-27 relative),
     // so p = 2^sc needs no per-score add, and the weight sum is an MFMA of the packed weights
-    // against ones (every lane gets its query's full sum).  Lazy rescale: m_b moves only when a
-    // score exceeds it by more than kSlack (p <= 2^kSlack meanwhile, exact after the final
-    // normalisation); the first tile always sets it.
+    // against ones (every lane gets its query's full sum).  Lazy rescale, guarded by that sum:
+    // m_b moves (to the tile's max) only when a tile's weights sum past 2^32 (an overflowed
+    // weight included), and the tile's weights are then recomputed; no weight the accumulators
+    // take exceeds 2^32, and the result is exact after the final normalisation.  The first tile
+    // sets m_b from its max.
+    constexpr float kSumMax = 4294967296.f;             // 2^32
     const uint32_t one2 = 0x3F803F80u;                  // two bf16 ones
     const uint4 onesA = make_uint4(one2, one2, one2, one2);
     const uint4 biasA = h2 ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(one2, 0x3F80u, 0u, 0u);
@@ -310,6 +316,23 @@ void prefill_cached_kernel(PrefillArgs a) {
     uint4 biasB = bias_op(qmu);
     f32x16 olat = {};
     const int rd = srow(lane);                          // this lane's operand row
+    // move the reference to the tile's max (per query: both lanes agree); first: no history
+    auto rebase = [&](f32x16 &sc, bool first) __attribute__((always_inline)) {
+        float mx = sc[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+        float delta = max_swap32(mx);
+        if (!first) delta = fmaxf(delta, 0.f);
+        if (!(delta > -INFINITY)) delta = 0.f;          // all masked (or NaN): keep m_b
+        const float alpha = first ? 0.f : exp2_(-delta);
+        l_run *= alpha;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) olat[v] *= alpha;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[v] -= delta;
+        m_b += delta;
+        biasB = bias_op(qmu - m_b);
+    };
     auto consume = [&](int s, int buf) __attribute__((always_inline)) {
         if (!wlive || s >= steps) return;
         const int nt = min(CGT, ctiles - CGT * s);
@@ -326,29 +349,23 @@ void prefill_cached_kernel(PrefillArgs a) {
                 for (int v = 0; v < 16; ++v)
                     if (8 * (v >> 2) + (v & 3) > lm) sc[v] = -INFINITY;
             }
-            float mx = sc[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-            if (!started || __builtin_amdgcn_ballot_w64(mx > kSlack) != 0) {
-                // new reference m_b + delta for the query (both of its lanes agree)
-                float delta = max_swap32(mx);
-                if (started) delta = fmaxf(delta, 0.f);
-                if (delta == -INFINITY) delta = 0.f;
-                const float alpha = started ? exp2_(-delta) : 0.f;
-                l_run *= alpha;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) olat[v] *= alpha;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sc[v] -= delta;
-                m_b += delta;
-                biasB = bias_op(qmu - m_b);
+            if (!started) {
+                rebase(sc, true);
                 started = true;
             }
             f32x16 pr;
 #pragma unroll
             for (int v = 0; v < 16; ++v) pr[v] = exp2_(sc[v]);
-            const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
-            const f32x16 ls = mfma(onesA, p1, mfma(onesA, p0, f32x16{}));
+            uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
+            f32x16 ls = mfma(onesA, p1, mfma(onesA, p0, f32x16{}));
+            if (__builtin_amdgcn_ballot_w64(ls[0] > kSumMax) != 0) {
+                rebase(sc, false);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) pr[v] = exp2_(sc[v]);
+                p0 = pack8(pr, 0);
+                p1 = pack8(pr, 1);
+                ls = mfma(onesA, p1, mfma(onesA, p0, f32x16{}));
+            }
             olat = mfma(cbuf[buf][j][KK][rd], p0, olat);
             olat = mfma(cbuf[buf][j][KK + 1][rd], p1, olat);
             l_run += ls[0];
