@@ -20,8 +20,8 @@
 //   owns queries [32w, 32w + 32) of the block) runs the online softmax over the cached tiles in
 //   latent space and parks each query's partial state (O_lat, running max, weight sum) in its own
 //   out row.  It holds only latent-sized state, so four waves share a SIMD, and it stages 8 tiles
-//   per step with two steps of loads in flight: the bytes in flight per CU, not the arithmetic,
-//   set its speed.
+//   per step with two steps of loads in flight, enough to cover HBM latency; its speed is then
+//   set by the softmax's vector work and each wave's dependent chain per tile.
 // * the chunk pass (same grid) starts from that state, O^T = W_up,t^V^T O_lat^T, runs ordinary
 //   flash attention over the chunk's own tiles up to each query, adds (sum of cached weights)
 //   mu_t^V, normalises and overwrites the row with the result.
