@@ -433,3 +433,38 @@ def test_rope_full_size_sampled(gpu):
     assert np.all(np.isfinite(got))
     ref = _sampled_oracle(cfg, layer, host, sel, t, q, xk[:, t], xv[:, t], rope=rope)
     assert_close(got[sel], ref, "bf16", "rope full size")
+
+
+# ------------------------------------------------------------------ head dim 64
+# d_head = 64 instantiations (the rotary path then has a single 32-pair tile per lane)
+D64_CFGS = {
+    "h4_d64_r16_32": synth.Config("d64_r16_32", L=1, H=4, d=64, T=3, r_k=16, r_v=32, B=3, N=1,
+                                  cid=150),
+    "h4_d64_r64_128": synth.Config("d64_r64_128", L=1, H=4, d=64, T=2, r_k=64, r_v=128, B=3,
+                                   N=1, cid=151),
+    "h4_d64_2d_r32_64": synth.Config("d64_2d_r32_64", L=1, H=4, d=64, T=2, r_k=32, r_v=64, B=2,
+                                     N=1, mode=1, cid=152),
+}
+
+
+@pytest.mark.parametrize("style", [0, 1])
+@pytest.mark.parametrize("name", list(D64_CFGS))
+def test_head_dim_64_decode_forms(gpu, name, style):
+    """The reconstructing, absorbed and rotary decodes at d_head = 64 against the oracle, ragged
+    lengths including 0 and 1, with a self term; the rotary decode in both styles."""
+    cfg = D64_CFGS[name]
+    B, N = cfg.B, 300
+    lens = synth.seq_lens(cfg, B, N, ragged=True, salt=5)
+    lens[0], lens[1] = 0, 1
+    p = tinycase.make(cfg, B=B, N=N, lens=lens)
+    dp = gpucase.DeviceProblem(p)
+    rope = lla.lla_rope(10000.0, cfg.d, style)
+    for t in sorted({0, cfg.T - 1}):
+        say(f"d64 {name} style={style} B={B} lens={list(p.seq_lens)} t={t}")
+        if style == 0:
+            ref = dp.oracle_decode(t, True)
+            assert_close(dp.decode(t, True), ref, "bf16", f"d64 {name} t={t}")
+            assert_close(dp.decode(t, True, absorbed=True), ref, "bf16",
+                         f"d64 absorbed {name} t={t}")
+        assert_close(dp.decode(t, True, rope=rope), dp.oracle_decode_rope(t, rope, True), "bf16",
+                     f"d64 rope {name}/{style} t={t}")
