@@ -32,6 +32,7 @@ constexpr int NT = KC * RG;
 struct EncodePair {
     EncodeArgs ax[2];
     int blocks_k;         // workgroups of the K axis (the V axis follows)
+    int rows;             // encode_mfma_kernel: rows per workgroup (32, 16, 8 or 4)
 };
 
 // 16 bytes of fp32 storage -> float values
@@ -179,8 +180,11 @@ int blocks_of(const EncodeArgs &a) {
 
 // ---------------------------------------------------------------- bf16: matrix cores
 // C = X W - 1 (mu W) per (axis, group): a dense contraction over the stacked axis, run on
-// v_mfma_f32_32x32x16_bf16.  A workgroup owns one 32 x 32 output tile (32 sequences x 32 latent
-// columns); its EWAVES waves split the stacked axis into contiguous ranges of 16-element k-steps.
+// v_mfma_f32_32x32x16_bf16.  A workgroup owns the output rows of `rows` sequences (32, or 16, 8, 4
+// when a batch is too small to fill the chip with 32-row tiles: the 32-row MFMA tile then repeats
+// its rows and the workgroups of one column slice each read the whole W_down slice, from cache)
+// by 32 latent columns; its EWAVES waves split the stacked axis into contiguous ranges of
+// 16-element k-steps.
 // Every lane loads its own operands straight from memory: A = staging rows (16 bytes per lane
 // per k-step) and the mean mu (the same in every row), B = W_down rows 16ks + 8h2 + 0..7 of
 // column c0 + l32 (eight 2-byte loads; a wave's loads cover whole 64-byte row segments).  Groups
@@ -192,6 +196,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int EWAVES = 8;            // waves per workgroup
+// word 3 of a raw (untyped, unswizzled) buffer resource
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int EGRP = 4;              // k-steps per load group
 
 __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
@@ -211,12 +217,13 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
     const int axis = blk < pr.blocks_k ? 0 : 1;
     if (axis) blk -= pr.blocks_k;
     const EncodeArgs a = axis ? pr.ax[1] : pr.ax[0];
+    const int RS = pr.rows;
     const int ctiles = (a.r + 31) / 32;
-    const int rtiles = (a.B + 31) / 32;
+    const int rtiles = (a.B + RS - 1) / RS;
     const int ct = blk % ctiles;
     const int rt = (blk / ctiles) % rtiles;
     const int g = blk / (ctiles * rtiles);
-    const int c0 = ct * 32, b0 = rt * 32;
+    const int c0 = ct * 32, b0 = rt * RS;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,26 +246,45 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
     const uint16_t *W = static_cast<const uint16_t *>(a.W_down) + (size_t)g * X * a.r;
     const uint16_t *mu = static_cast<const uint16_t *>(a.mu) + (size_t)g * X;
-    const int brow = min(b0 + l32, a.B - 1);             // this lane's A-operand row (clamped)
+    const int brow = min(b0 + l32 % RS, a.B - 1);        // this lane's A-operand row (clamped)
     const int wcol = min(c0 + l32, a.r - 1);             // this lane's B-operand column (clamped)
+
+    // Operands come through buffer loads: a fixed byte offset per lane (vector) plus an offset
+    // uniform per k-step and element (scalar), so the loads take no per-element address
+    // arithmetic; the resources span exactly the workgroup's rows, its group's W_down and mu
+    // (out-of-range reads return zero).  d_head is 64 or 128, so a lane's 8 stacked elements
+    // never cross a head-dim row.
+    const size_t rowstride = a.mode ? (size_t)X : (size_t)a.T * a.H * a.d;   // staging row
+    const int nrows = min(RS, a.B - b0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x + (size_t)b0 * rowstride), 0, (int)(nrows * rowstride * 2),
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(W), 0, X * a.r * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(mu), 0, X * 2, kBufferWord3);
+    const int xl = (int)((size_t)(brow - b0) * rowstride + 8 * h2) * 2;
+    const int wl = (8 * h2 * a.r + wcol) * 2;
+    const int ml = 16 * h2;
+    const int dsh = a.d == 128 ? 7 : 6;
 
     // k-steps kg .. kg + EGRP - 1 of this wave; steps past its range load in bounds and are zeroed
     auto load_grp = [&](int kg, EncOps &op) {
 #pragma unroll
         for (int j = 0; j < EGRP; ++j) {
             const int ks = min(kg + j, max(ks1 - 1, 0));
-            const int xi = 16 * ks + 8 * h2;
-            size_t off;
+            int xo;                                             // the k-step's row offset
             if (a.mode) {
-                off = (size_t)brow * X + xi;                           // (t, h, i) order
+                xo = 16 * ks;                                          // (t, h, i) order
             } else {
-                const int t = xi / a.d, i = xi - t * a.d;              // (t, i) of head g
-                off = (((size_t)brow * a.T + t) * a.H + g) * a.d + i;
+                const int t = (16 * ks) >> dsh, i = (16 * ks) & (a.d - 1);   // (t, i) of head g
+                xo = (t * a.H + g) * a.d + i;
             }
-            op.x[j] = *reinterpret_cast<const uint4 *>(x + off);
-            op.m[j] = *reinterpret_cast<const uint4 *>(mu + xi);
+            op.x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xl, 2 * xo, 0));
+            op.m[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mr, ml, 32 * ks, 0));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) op.w[j][e] = W[(size_t)(xi + e) * a.r + wcol];
+            for (int e = 0; e < 8; ++e)
+                op.w[j][e] = __builtin_amdgcn_raw_buffer_load_b16(wr, wl, (16 * ks + e) * a.r * 2, 0);
         }
     };
     f32x16 acc = {}, accmu = {};
@@ -301,7 +327,7 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
         const int idx = tid + 64 * EWAVES * o;
         const int row = idx >> 5, col = idx & 31;
         const int bb = b0 + row, k = c0 + col;
-        if (bb >= a.B || k >= a.r) continue;
+        if (row >= RS || bb >= a.B || k >= a.r) continue;
         float c = 0.f;
 #pragma unroll
         for (int w = 0; w < EWAVES; ++w) c += sAcc[w][row][col];
@@ -315,8 +341,8 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
     }
 }
 
-int mfma_blocks_of(const EncodeArgs &a) {
-    return a.G * ((a.r + 31) / 32) * ((a.B + 31) / 32);
+int mfma_blocks_of(const EncodeArgs &a, int rows) {
+    return a.G * ((a.r + 31) / 32) * ((a.B + rows - 1) / rows);
 }
 
 // ---------------------------------------------------------------- bf16, many rows
@@ -489,8 +515,16 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
         const unsigned blocks = (unsigned)(pr.blocks_k + rows_blocks_of(v_axis));
         hipLaunchKernelGGL(encode_rows_kernel, dim3(blocks), dim3(64 * RWAVES), 0, st, pr);
     } else if (bf16) {
-        pr.blocks_k = mfma_blocks_of(k_axis);
-        const unsigned blocks = (unsigned)(pr.blocks_k + mfma_blocks_of(v_axis));
+        // 32-row tiles unless that leaves CUs idle: a small batch is latency-bound, and more,
+        // shorter workgroups put more loads in flight
+        pr.rows = 4;
+        for (int rows = 32; rows > 4; rows /= 2)
+            if (mfma_blocks_of(k_axis, rows) + mfma_blocks_of(v_axis, rows) >= 256) {
+                pr.rows = rows;
+                break;
+            }
+        pr.blocks_k = mfma_blocks_of(k_axis, pr.rows);
+        const unsigned blocks = (unsigned)(pr.blocks_k + mfma_blocks_of(v_axis, pr.rows));
         hipLaunchKernelGGL(encode_mfma_kernel, dim3(blocks), dim3(64 * EWAVES), 0, st, pr);
     } else {
         pr.blocks_k = blocks_of(k_axis);
