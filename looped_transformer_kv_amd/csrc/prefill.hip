@@ -73,6 +73,7 @@ constexpr int CNS = 2;                     // chunk tiles in flight in the chunk
 constexpr int CWAVES = 8;                  // waves per workgroup of the chunk pass
 constexpr int CQWG = CWAVES * 32;          // queries per workgroup of the chunk pass
 constexpr float kSlack = 8.f;              // lazy rescale threshold (log2 domain)
+constexpr int kBufferWord3 = 0x00020000;   // word 3 of a raw (untyped, unswizzled) buffer resource
 
 // An operand slot in LDS holds one 16-byte row per lane; a 16-byte pad after every 8 rows spreads
 // the transposed 2-byte writes of the value operands over the banks (a group of 8 lanes still
@@ -146,6 +147,9 @@ void prefill_cached_kernel(PrefillArgs a) {
     // value latents transposed (A of the value MFMA)
     __shared__ __align__(16) uint4 cbuf[2][CGT][SL][kSlot];
     __shared__ int sbad[PWAVES];
+    // A operands of the q' MFMA (W_up,t^K at the query operand's dims), one k-step per slot
+    __shared__ __align__(16) uint4 sWk[KS][kSlot];
+    static_assert(KS <= PWAVES, "one operand slot per wave");
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -180,29 +184,47 @@ void prefill_cached_kernel(PrefillArgs a) {
     uint4 qlat[KK];
     float qmu;
     {
-        uint4 qop[KS];
-        load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
+        // wave w < KS builds operand slot w (buffer loads: a fixed byte offset per lane plus a
+        // scalar one per element); the workgroup shares the slots
         const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
                              ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
         const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
                               (size_t)a.t * a.Dg + col0;
-        const int rk = min(l32, RK - 1);
-        f32x16 qa = {};
+        if (wave < KS) {
+            const int ks = wave;
+            const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(Wk), 0, ((RK - 1) * a.Dg + D) * 2, kBufferWord3);
+            const int wl = (min(l32, RK - 1) * a.Dg + 4 * h2) * 2;
+            uint16_t w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(
+                    wr, wl, (32 * (ks >> 1) + 16 * (ks & 1) + (e < 4 ? e : e + 4)) * 2, 0);
+                w[e] = l32 < RK ? v : (uint16_t)0;
+            }
+            sWk[ks][srow(lane)] = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
+                                             w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
+        }
+        uint4 qop[KS];
+        load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
+        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(muk), 0, D * 2, kBufferWord3);
         float qm = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint16_t w[8];
             const uint32_t qv[4] = {qop[ks].x, qop[ks].y, qop[ks].z, qop[ks].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int dim = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * h2 + (e < 4 ? e : e + 4);
-                w[e] = l32 < RK ? Wk[(size_t)rk * a.Dg + dim] : (uint16_t)0;
-                qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(muk[dim]);
+                const uint16_t m = __builtin_amdgcn_raw_buffer_load_b16(
+                    mr, 8 * h2, (32 * (ks >> 1) + 16 * (ks & 1) + (e < 4 ? e : e + 4)) * 2, 0);
+                qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(m);
             }
-            const uint4 wop = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
-                                         w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
-            qa = mfma(wop, qop[ks], qa);
         }
+        __syncthreads();                                // the W_up,t^K slots
+        f32x16 qa = {};
+        const int rdw = srow(lane);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa = mfma(sWk[ks][rdw], qop[ks], qa);
 #pragma unroll
         for (int v = 0; v < 16; ++v) qa[v] *= csc;
 #pragma unroll
@@ -441,6 +463,9 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
 
     // operand slots per buffer: [0, KS) for the keys (sK), [KS, KS + 2 MT) for the values (sV)
     __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][kSlot];
+    // W_up,t^V operands (32-dim tile n, k-step ks at slot KV n + ks), built once per workgroup
+    __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
+    static_assert(MT * KV <= CWAVES, "one operand slot per wave");
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -477,11 +502,11 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
     f32x16 oacc[MT];
 #pragma unroll
     for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
-    if (wlive && len > 0) {
-        uint4 lop[KV];
-        float2 ml = make_float2(-INFINITY, 0.f);
+    uint4 lop[KV];
 #pragma unroll
-        for (int ks = 0; ks < KV; ++ks) lop[ks] = make_uint4(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < KV; ++ks) lop[ks] = make_uint4(0u, 0u, 0u, 0u);
+    if (wlive && len > 0) {
+        float2 ml = make_float2(-INFINITY, 0.f);
         if (iq < qend) {
             const uint4 *st = state_row(a, b, iq, h, D);
 #pragma unroll
@@ -491,21 +516,24 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         m_run = ml.x;
         l_run = h2 ? 0.f : ml.y;
         l_lat = l_run;
+    }
+    // wave w < MT KV builds operand slot w: lane (dim, h2) of 32-dim tile n, k-step ks holds the
+    // dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4.  Buffer loads: a fixed byte offset
+    // per lane plus a scalar one per element.
+    if (len > 0 && wave < MT * KV) {
+        const int n = wave / KV, ks = wave % KV;
         const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
                              ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(Wv), 0, ((RV - 1) * a.Dg + D) * 2, kBufferWord3);
+        const int wl = (4 * h2 * a.Dg + 32 * n + l32) * 2;
+        uint16_t w[8];
 #pragma unroll
-        for (int n = 0; n < MT; ++n) {
-#pragma unroll
-            for (int ks = 0; ks < KV; ++ks) {
-                uint16_t w[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    w[e] = Wv[(size_t)(16 * ks + 8 * (e >> 2) + 4 * h2 + (e & 3)) * a.Dg + 32 * n + l32];
-                const uint4 wop = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
-                                             w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
-                oacc[n] = mfma(wop, lop[ks], oacc[n]);
-            }
-        }
+        for (int e = 0; e < 8; ++e)
+            w[e] = __builtin_amdgcn_raw_buffer_load_b16(
+                wr, wl, (16 * ks + 8 * (e >> 2) + (e & 3)) * a.Dg * 2, 0);
+        sW[wave][srow(lane)] = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
+                                          w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
     }
 
     // ---- tile inputs.  Chunk tile n: piece p = tid + 512 x of each axis is row 32n + (p % 128) / 4
@@ -636,6 +664,13 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
     produce(0, S[0], 0);
     issue(CNS, S[0]);
     __syncthreads();
+    // the cached part back in model space, from the shared W_up,t^V operands
+    if (wlive && len > 0) {
+#pragma unroll
+        for (int n = 0; n < MT; ++n)
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) oacc[n] = mfma(sW[n * KV + ks][rd], lop[ks], oacc[n]);
+    }
     // All CNS sub-steps run on every trip (a count that is not a multiple ends with empty ones):
     // a path that skips some of the loads would make the compiler wait on later loads too.
     for (int it = 0; it < tiles; it += CNS) {
