@@ -465,7 +465,6 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
     __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][kSlot];
     // W_up,t^V operands (32-dim tile n, k-step ks at slot KV n + ks), built once per workgroup
     __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
-    static_assert(MT * KV <= CWAVES, "one operand slot per wave");
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -517,11 +516,11 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         l_run = h2 ? 0.f : ml.y;
         l_lat = l_run;
     }
-    // wave w < MT KV builds operand slot w: lane (dim, h2) of 32-dim tile n, k-step ks holds the
-    // dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4.  Buffer loads: a fixed byte offset
-    // per lane plus a scalar one per element.
-    if (len > 0 && wave < MT * KV) {
-        const int n = wave / KV, ks = wave % KV;
+    // wave w builds operand slots w, w + CWAVES, ..: lane (dim, h2) of 32-dim tile n, k-step ks
+    // holds the dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4.  Buffer loads: a fixed
+    // byte offset per lane plus a scalar one per element.
+    for (int slot = wave; len > 0 && slot < MT * KV; slot += CWAVES) {
+        const int n = slot / KV, ks = slot % KV;
         const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
                              ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -532,7 +531,7 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         for (int e = 0; e < 8; ++e)
             w[e] = __builtin_amdgcn_raw_buffer_load_b16(
                 wr, wl, (16 * ks + 8 * (e >> 2) + (e & 3)) * a.Dg * 2, 0);
-        sW[wave][srow(lane)] = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
+        sW[slot][srow(lane)] = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
                                           w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
     }
 
