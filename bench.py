@@ -5,9 +5,10 @@ One step = one decode step of a weight-tied looped model on the Ouro-1.4B-like 2
 24 layers, 16 heads, d_head 128, T = 4 loops, per-head codec r_k = 16 / r_v = 32, bf16 latents,
 batch 32, 4096 cached tokens per sequence.  In loop-major order (loop t outer, layer inner) every
 (layer, loop) runs lla_decode_attn over that layer's whole latent cache (96 calls, each on a
-distinct 201 MB layer cache, so the 256 MB Infinity Cache cannot serve repeats), then every layer
-runs lla_encode_append for the new token (24 calls).  Each step decodes against the same 4096
-cached tokens and appends at slot 4096, so every timed step does identical work.
+distinct 201 MB layer cache, so the 256 MB Infinity Cache cannot serve repeats), then one
+lla_encode_append_layers call encodes and appends the new token for all 24 layers.  Each step
+decodes against the same 4096 cached tokens and appends at slot 4096, so every timed step does
+identical work.
 
 value      cached token-loops per second for the whole step (B * N * T * L per step)
 roofline   the decode kernel: latent bytes per launch / its average launch time (HIP events
@@ -409,6 +410,7 @@ def main():
 
     import torch
     from looped_transformer_kv_amd import lla, synth
+    from looped_transformer_kv_amd.runtime import LatentLayer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -444,8 +446,7 @@ def main():
                 layers[l].decode(t, q[t][l], out, ws, xk[l][:, t], xv[l][:, t], stride)
 
     def encode_all():
-        for l in range(L):
-            layers[l].encode_append(xk[l], xv[l], write_pos)
+        LatentLayer.encode_append_layers(layers, xk, xv, write_pos)
 
     decode_all()
     encode_all()
@@ -518,7 +519,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {DESCRIBE[cfg.name]}, {L} layers x {T} loops "
-                        f"of LLA decode attention + {L} encode/append calls",
+                        f"of LLA decode attention + one {L}-layer encode/append call",
             "mode": "lla_2d" if cfg.mode == 1 else "per_head",
             "layers": L, "heads": H, "d_head": d, "loops": T, "r_k": cfg.r_k, "r_v": cfg.r_v,
             "compression": round(lla.lla_compression_ratio(layers[0].codec), 3),
@@ -535,8 +536,8 @@ def main():
         "decode_flops_per_call": flops,
         "decode_TFLOPs": round(tflops, 2),
         "decode_token_loops_per_s_per_call": round(B * N / (dec_us * 1e-6), 1),
-        "encode_us_per_call": round(enc_us, 3),
-        "encode_bytes_per_call": enc_bytes,
+        "encode_us_per_layer": round(enc_us, 3),
+        "encode_bytes_per_layer": enc_bytes,
         "encode_GBps": round(enc_bytes / (enc_us * 1e-6) / 1e9, 1),
     }
     def time_variant(run_one):

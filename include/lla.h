@@ -212,6 +212,26 @@ lla_status lla_encode_chunk(const lla_codec *codec, const lla_params *params,
                             float *c_k_out, float *c_v_out, void *stream);
 
 /*
+ * Encode and append of the current token for several layers in one call: for each layer i,
+ * exactly lla_encode_append(codec, &params[i], &caches[i], x_k[i], x_v[i], write_pos, NULL,
+ * NULL, stream) (pith.science paper page for "Looped Latent Attention", "What carries the
+ * argument": the per-layer encode on write), with one launch for up to 32 layers on the
+ * matrix-core path.  After a decode step every layer's loop trajectories exist, so an engine
+ * appends all layers at once.
+ *   params, caches  host arrays of n_layers; every cache has the same batch, page_size,
+ *                   max_pages and n_pages (else LLA_ERR_SHAPE); each has its own pools and
+ *                   block table
+ *   x_k, x_v        host arrays of n_layers device pointers, each as in lla_encode_append
+ *   write_pos       device int32 [batch], shared by the layers
+ * n_layers < 0 -> LLA_ERR_SHAPE; n_layers = 0 enqueues nothing.  Every layer is validated as in
+ * lla_encode_append before anything is enqueued.  No fp32 copies of the latents.
+ */
+lla_status lla_encode_append_layers(const lla_codec *codec, int32_t n_layers,
+                                    const lla_params *params, const lla_cache *caches,
+                                    const void *const *x_k, const void *const *x_v,
+                                    const int32_t *write_pos, void *stream);
+
+/*
  * Chunked prefill attention for loop t.  The pages do not describe prefill; this is the decode
  * rule above applied to a chunk of new tokens at once: new token i of sequence b (i < n_new[b],
  * logical position seq_lens[b] + i) attends to every cached token j < seq_lens[b], reconstructed

@@ -210,14 +210,10 @@ struct EncOps {
     uint16_t w[EGRP][8];
 };
 
-__global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr) {
+// One workgroup's tile `blk` of axis `a` (RS rows per workgroup).
+__device__ __forceinline__ void encode_mfma_tile(const EncodeArgs a, int blk, const int RS) {
     __shared__ float sAcc[EWAVES][32][33];
 
-    int blk = blockIdx.x;
-    const int axis = blk < pr.blocks_k ? 0 : 1;
-    if (axis) blk -= pr.blocks_k;
-    const EncodeArgs a = axis ? pr.ax[1] : pr.ax[0];
-    const int RS = pr.rows;
     const int ctiles = (a.r + 31) / 32;
     const int rtiles = (a.B + RS - 1) / RS;
     const int ct = blk % ctiles;
@@ -339,6 +335,38 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
         static_cast<uint16_t *>(a.pool)[(((size_t)page[o] * a.G + g) * a.P + pos % a.P) * a.r +
                                         k] = f2bf(c);
     }
+}
+
+__global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr) {
+    int blk = blockIdx.x;
+    const int axis = blk < pr.blocks_k ? 0 : 1;
+    if (axis) blk -= pr.blocks_k;
+    encode_mfma_tile(axis ? pr.ax[1] : pr.ax[0], blk, pr.rows);
+}
+
+// Several layers' encodes in one launch (the same tiles as encode_mfma_kernel, layer after
+// layer): the fields every layer shares come from ax[], the per-layer pointers from the tables.
+constexpr int kEncLayersMax = 32;    // layers per launch (the tables sit in the kernel arguments)
+struct EncodeLayers {
+    EncodeArgs ax[2];
+    const void *src[kEncLayersMax][2][3];    // per layer and axis: staging x, W_down, mu
+    void *pool[kEncLayersMax][2];
+    const int32_t *block_table[kEncLayersMax];
+    int blocks_k, blocks_layer, rows;
+};
+
+__global__ __launch_bounds__(64 * EWAVES) void encode_layers_kernel(EncodeLayers el) {
+    const int layer = blockIdx.x / el.blocks_layer;
+    int blk = blockIdx.x - layer * el.blocks_layer;
+    const int axis = blk < el.blocks_k ? 0 : 1;
+    if (axis) blk -= el.blocks_k;
+    EncodeArgs a = el.ax[axis];
+    a.x = el.src[layer][axis][0];
+    a.W_down = el.src[layer][axis][1];
+    a.mu = el.src[layer][axis][2];
+    a.pool = el.pool[layer][axis];
+    a.block_table = el.block_table[layer];
+    encode_mfma_tile(a, blk, el.rows);
 }
 
 int mfma_blocks_of(const EncodeArgs &a, int rows) {
@@ -500,7 +528,56 @@ bool rows_kernel_fits(const EncodeArgs &a) {
            (reinterpret_cast<uintptr_t>(a.c_out) & 15) == 0;
 }
 
+// 32-row tiles unless that leaves CUs idle: a small batch is latency-bound, and more, shorter
+// workgroups put more loads in flight
+int rows_per_block(const EncodeArgs &k_axis, const EncodeArgs &v_axis, int layers) {
+    for (int rows = 32; rows > 4; rows /= 2)
+        if ((long)layers * (mfma_blocks_of(k_axis, rows) + mfma_blocks_of(v_axis, rows)) >= 256)
+            return rows;
+    return 4;
+}
+
 }  // namespace
+
+hipError_t launch_encode_layers(const EncodeArgs *k_axes, const EncodeArgs *v_axes, int n,
+                                bool bf16, hipStream_t st) {
+    // shapes a single call would not give to the matrix-core tile kernel (fp32 codecs, batches
+    // for the row-streaming kernel) go layer by layer, through the same kernels as single calls
+    if (!bf16 || (rows_kernel_fits(k_axes[0]) && rows_kernel_fits(v_axes[0]) &&
+                  rows_blocks_of(k_axes[0]) + rows_blocks_of(v_axes[0]) >= 256)) {
+        for (int i = 0; i < n; ++i) {
+            const hipError_t e = launch_encode(k_axes[i], v_axes[i], bf16, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    for (int i0 = 0; i0 < n; i0 += kEncLayersMax) {
+        const int m = n - i0 < kEncLayersMax ? n - i0 : kEncLayersMax;
+        EncodeLayers el{};
+        el.ax[0] = k_axes[i0];
+        el.ax[1] = v_axes[i0];
+        for (int j = 0; j < m; ++j) {
+            const EncodeArgs &k = k_axes[i0 + j], &v = v_axes[i0 + j];
+            el.src[j][0][0] = k.x;
+            el.src[j][0][1] = k.W_down;
+            el.src[j][0][2] = k.mu;
+            el.src[j][1][0] = v.x;
+            el.src[j][1][1] = v.W_down;
+            el.src[j][1][2] = v.mu;
+            el.pool[j][0] = k.pool;
+            el.pool[j][1] = v.pool;
+            el.block_table[j] = k.block_table;
+        }
+        el.rows = rows_per_block(el.ax[0], el.ax[1], m);
+        el.blocks_k = mfma_blocks_of(el.ax[0], el.rows);
+        el.blocks_layer = el.blocks_k + mfma_blocks_of(el.ax[1], el.rows);
+        hipLaunchKernelGGL(encode_layers_kernel, dim3((unsigned)(m * el.blocks_layer)),
+                           dim3(64 * EWAVES), 0, st, el);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
                          hipStream_t st) {
@@ -515,14 +592,7 @@ hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, boo
         const unsigned blocks = (unsigned)(pr.blocks_k + rows_blocks_of(v_axis));
         hipLaunchKernelGGL(encode_rows_kernel, dim3(blocks), dim3(64 * RWAVES), 0, st, pr);
     } else if (bf16) {
-        // 32-row tiles unless that leaves CUs idle: a small batch is latency-bound, and more,
-        // shorter workgroups put more loads in flight
-        pr.rows = 4;
-        for (int rows = 32; rows > 4; rows /= 2)
-            if (mfma_blocks_of(k_axis, rows) + mfma_blocks_of(v_axis, rows) >= 256) {
-                pr.rows = rows;
-                break;
-            }
+        pr.rows = rows_per_block(k_axis, v_axis, 1);
         pr.blocks_k = mfma_blocks_of(k_axis, pr.rows);
         const unsigned blocks = (unsigned)(pr.blocks_k + mfma_blocks_of(v_axis, pr.rows));
         hipLaunchKernelGGL(encode_mfma_kernel, dim3(blocks), dim3(64 * EWAVES), 0, st, pr);

@@ -4,6 +4,7 @@
 #include <cstdlib>
 
 #include <cmath>
+#include <vector>
 
 #include "lla_internal.h"
 
@@ -282,9 +283,11 @@ namespace {
 
 // Shared by lla_encode_append (one row per sequence) and lla_encode_chunk (rps rows per
 // sequence, n_rows live).
-lla_status encode_rows(const lla_codec *c, const lla_params *prm, const lla_cache *k, int rps,
+// Validation and kernel arguments of one layer's encode (both axes).
+lla_status encode_args(const lla_codec *c, const lla_params *prm, const lla_cache *k, int rps,
                        const int32_t *n_rows, const void *x_k, const void *x_v,
-                       const int32_t *write_pos, float *c_k_out, float *c_v_out, void *stream) {
+                       const int32_t *write_pos, float *c_k_out, float *c_v_out,
+                       EncodeArgs ax[2]) {
     lla_status st = check_codec(c);
     if (st != LLA_OK) return st;
     if (!prm || !prm->W_down_k || !prm->W_down_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
@@ -292,11 +295,7 @@ lla_status encode_rows(const lla_codec *c, const lla_params *prm, const lla_cach
     if (!x_k || !x_v || !write_pos) return LLA_ERR_NULL;
     if (!aligned16(x_k) || !aligned16(x_v) || !aligned16(prm->mu_k) || !aligned16(prm->mu_v))
         return LLA_ERR_ALIGN;
-    if (k->batch == 0 || rps == 0) return LLA_OK;
     const Shape sh = shape_of(c);
-    const bool bf16 = c->dtype == LLA_BF16;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    EncodeArgs ax[2];
     for (int axis = 0; axis < 2; ++axis) {
         EncodeArgs &a = ax[axis];
         a = EncodeArgs{};
@@ -321,7 +320,21 @@ lla_status encode_rows(const lla_codec *c, const lla_params *prm, const lla_cach
         a.n_pages = k->n_pages;
         a.mode = c->mode;
     }
-    return launch_encode(ax[0], ax[1], bf16, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    return LLA_OK;
+}
+
+lla_status encode_rows(const lla_codec *c, const lla_params *prm, const lla_cache *k, int rps,
+                       const int32_t *n_rows, const void *x_k, const void *x_v,
+                       const int32_t *write_pos, float *c_k_out, float *c_v_out, void *stream) {
+    EncodeArgs ax[2];
+    const lla_status st = encode_args(c, prm, k, rps, n_rows, x_k, x_v, write_pos, c_k_out,
+                                      c_v_out, ax);
+    if (st != LLA_OK) return st;
+    if (k->batch == 0 || rps == 0) return LLA_OK;
+    return launch_encode(ax[0], ax[1], c->dtype == LLA_BF16, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? LLA_OK
+               : LLA_ERR_HIP;
 }
 
 }  // namespace
@@ -330,6 +343,34 @@ lla_status lla_encode_append(const lla_codec *c, const lla_params *prm, const ll
                              const void *x_k, const void *x_v, const int32_t *write_pos,
                              float *c_k_out, float *c_v_out, void *stream) {
     return encode_rows(c, prm, k, 1, nullptr, x_k, x_v, write_pos, c_k_out, c_v_out, stream);
+}
+
+lla_status lla_encode_append_layers(const lla_codec *c, int32_t n_layers,
+                                    const lla_params *params, const lla_cache *caches,
+                                    const void *const *x_k, const void *const *x_v,
+                                    const int32_t *write_pos, void *stream) {
+    if (n_layers < 0) return LLA_ERR_SHAPE;
+    if (n_layers == 0) return LLA_OK;
+    if (!params || !caches || !x_k || !x_v) return LLA_ERR_NULL;
+    std::vector<EncodeArgs> ka(n_layers), va(n_layers);
+    for (int i = 0; i < n_layers; ++i) {
+        EncodeArgs ax[2];
+        const lla_status st = encode_args(c, &params[i], &caches[i], 1, nullptr, x_k[i], x_v[i],
+                                          write_pos, nullptr, nullptr, ax);
+        if (st != LLA_OK) return st;
+        const lla_cache &k = caches[i], &k0 = caches[0];
+        // one batch, page geometry and set of write positions for every layer
+        if (k.batch != k0.batch || k.page_size != k0.page_size || k.max_pages != k0.max_pages ||
+            k.n_pages != k0.n_pages)
+            return LLA_ERR_SHAPE;
+        ka[i] = ax[0];
+        va[i] = ax[1];
+    }
+    if (caches[0].batch == 0) return LLA_OK;
+    return launch_encode_layers(ka.data(), va.data(), n_layers, c->dtype == LLA_BF16,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LLA_OK
+               : LLA_ERR_HIP;
 }
 
 lla_status lla_encode_chunk(const lla_codec *c, const lla_params *prm, const lla_cache *k,

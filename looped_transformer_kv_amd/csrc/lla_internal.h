@@ -114,6 +114,9 @@ hipError_t launch_combine(const DecodeArgs &a, int d, bool bf16, bool has_mu, bo
                           hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
                          hipStream_t s);
+// n layers' encodes (per-layer K and V axis arguments that differ only in their pointers)
+hipError_t launch_encode_layers(const EncodeArgs *k_axes, const EncodeArgs *v_axes, int n,
+                                bool bf16, hipStream_t s);
 bool decode_bf16_supported(int d, int r_k, int r_v);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 bool prefill_supported(int d, int r_k, int r_v);

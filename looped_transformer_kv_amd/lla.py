@@ -87,6 +87,9 @@ def lib():
         L.lla_encode_append.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), vp, vp, vp, vp,
                                         vp, vp]
         L.lla_encode_chunk.restype = i32
+        L.lla_encode_append_layers.restype = i32
+        L.lla_encode_append_layers.argtypes = [P(lla_codec), i32, P(lla_params), P(lla_cache),
+                                               P(vp), P(vp), vp, vp]
         L.lla_encode_chunk.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp, vp, vp,
                                        vp, vp, vp, vp]
         L.lla_prefill_attn.restype = i32
@@ -218,6 +221,21 @@ def lla_encode_append(codec, params, cache, x_k, x_v, write_pos, c_k_out=None, c
                                  _ptr(x_k), _ptr(x_v), _ptr(write_pos), _ptr(c_k_out),
                                  _ptr(c_v_out), _stream(stream))
     return _check("lla_encode_append", st, check)
+
+
+def lla_encode_append_layers(codec, params, caches, x_k, x_v, write_pos, stream=None,
+                             check=True) -> int:
+    """Encode and append for len(params) layers in one call: params and caches are sequences of
+    lla_params / lla_cache, x_k and x_v sequences of staging tensors (or device pointers)."""
+    n = len(params)
+    assert len(caches) == n and len(x_k) == n and len(x_v) == n
+    pa = (lla_params * n)(*params)
+    ca = (lla_cache * n)(*caches)
+    xk = (ctypes.c_void_p * n)(*[_ptr(x) for x in x_k])
+    xv = (ctypes.c_void_p * n)(*[_ptr(x) for x in x_v])
+    st = lib().lla_encode_append_layers(ctypes.byref(codec), int(n), pa, ca, xk, xv,
+                                        _ptr(write_pos), _stream(stream))
+    return _check("lla_encode_append_layers", st, check)
 
 
 def lla_encode_chunk(codec, params, cache, chunk, n_new, x_k, x_v, write_pos, c_k_out=None,

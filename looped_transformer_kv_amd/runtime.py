@@ -73,6 +73,14 @@ class LatentLayer:
         return lla.lla_encode_append(self.codec, self.params, self.cache, x_k, x_v, write_pos,
                                      c_k_out, c_v_out, stream=stream, check=check)
 
+    @staticmethod
+    def encode_append_layers(layers, x_k, x_v, write_pos, stream=None, check=True):
+        """lla_encode_append for every layer of `layers` in one call (lla_encode_append_layers);
+        x_k[i], x_v[i] are layer i's staging tensors."""
+        return lla.lla_encode_append_layers(layers[0].codec, [L.params for L in layers],
+                                            [L.cache for L in layers], x_k, x_v, write_pos,
+                                            stream=stream, check=check)
+
     def prefill(self, t, chunk, n_new, q, k_new, v_new, out, new_stride=0, scale=None,
                 stream=None, check=True):
         """Chunked prefill attention of loop t (lla_prefill_attn): q, out [B][chunk][H][d]."""

@@ -266,3 +266,38 @@ def test_fit_validation_without_launch():
     assert call(ws=None) == lla.LLA_ERR_NULL
     assert call(x=FAKE + 8) == lla.LLA_ERR_ALIGN
     assert call(iters=-1) == lla.LLA_ERR_SHAPE
+
+
+def test_encode_layers_validation_without_launch():
+    _no_gpu()
+    c = synth.CONFIGS["ouro14_21x"]
+    codec = _codec(c)
+    L = lla.lib()
+    params = lla.lla_params(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4096)
+
+    def call(n=2, caches=None, xk=FAKE, prm=params, wp=FAKE):
+        m = max(n, 1)
+        pa = (lla.lla_params * m)(*[prm] * m)
+        ca = caches if caches is not None else (lla.lla_cache * m)(*[cache] * m)
+        xs = (ctypes.c_void_p * m)(*[xk] * m)
+        return L.lla_encode_append_layers(ctypes.byref(codec), n, pa, ca, xs, xs, wp, None)
+    assert call(n=-1) == lla.LLA_ERR_SHAPE
+    assert call(n=0) == lla.LLA_OK                                   # nothing to do
+    assert call(wp=None) == lla.LLA_ERR_NULL
+    assert call(xk=None) == lla.LLA_ERR_NULL
+    assert call(xk=FAKE + 8) == lla.LLA_ERR_ALIGN
+    assert call(prm=lla.lla_params(FAKE, None, FAKE, FAKE, FAKE, FAKE)) == lla.LLA_ERR_NULL
+    other_batch = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 2, 64, 64, 64, 4096)
+    assert call(caches=(lla.lla_cache * 2)(cache, other_batch)) == lla.LLA_ERR_SHAPE
+    other_pages = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 65, 4096)
+    assert call(caches=(lla.lla_cache * 2)(cache, other_pages)) == lla.LLA_ERR_SHAPE
+    empty = lla.lla_cache(FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 64, 0)
+    assert call(caches=(lla.lla_cache * 2)(empty, empty)) == lla.LLA_OK   # empty batch
+    bad_codec = lla.make_codec(0, 4, 16, 128, 16, 32, 5)
+    m = 2
+    assert L.lla_encode_append_layers(ctypes.byref(bad_codec), m, (lla.lla_params * m)(params, params),
+                                      (lla.lla_cache * m)(cache, cache),
+                                      (ctypes.c_void_p * m)(FAKE, FAKE),
+                                      (ctypes.c_void_p * m)(FAKE, FAKE), FAKE, None) == \
+        lla.LLA_ERR_DTYPE

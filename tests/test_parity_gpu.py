@@ -133,6 +133,40 @@ def test_encode_append(gpu, name):
         assert np.array_equal(after, expect), f"{name} axis {axis}: pool differs"
 
 
+@pytest.mark.parametrize("name,n_layers", [("ouro14_21x", 3), ("ouro14_21x", 35),
+                                           ("ouro26_2d_64x", 2), ("tiny_f32", 2)])
+def test_encode_append_layers_matches_single_calls(gpu, name, n_layers):
+    """lla_encode_append_layers writes bitwise what one lla_encode_append per layer writes:
+    several layers' codecs and pools, shared positions (one overwrite, one skipped slot); 35
+    layers take two launches of the multi-layer kernel, fp32 codecs go layer by layer."""
+    cfg = synth.CONFIGS[name]
+    B = 32 if cfg.mode == 0 else 4
+    N = 100
+    dps = [gpucase.DeviceProblem(tinycase.make(cfg, layer=l, B=B, N=N)) for l in range(n_layers)]
+    pos_h = np.full(B, N, dtype=np.int32)
+    pos_h[1] = 3
+    pos_h[2] = -1
+    pos = torch.from_numpy(pos_h).to(gpu)
+    before = [(synth.from_device(dp.k_pool), synth.from_device(dp.v_pool)) for dp in dps]
+    say(f"{name}: {n_layers} single encode_append calls")
+    for dp in dps:
+        dp.layer.encode_append(dp.x_k, dp.x_v, pos)
+    torch.cuda.synchronize()
+    single = [(synth.from_device(dp.k_pool), synth.from_device(dp.v_pool)) for dp in dps]
+    for dp, (kb, vb) in zip(dps, before):
+        dp.k_pool.copy_(synth.to_device(kb, cfg.dtype, gpu))
+        dp.v_pool.copy_(synth.to_device(vb, cfg.dtype, gpu))
+    torch.cuda.synchronize()
+    say(f"{name}: one encode_append_layers call over {n_layers} layers")
+    LatentLayer.encode_append_layers([dp.layer for dp in dps], [dp.x_k for dp in dps],
+                                     [dp.x_v for dp in dps], pos)
+    torch.cuda.synchronize()
+    for l, dp in enumerate(dps):
+        assert np.array_equal(synth.from_device(dp.k_pool), single[l][0]), f"layer {l} K pool"
+        assert np.array_equal(synth.from_device(dp.v_pool), single[l][1]), f"layer {l} V pool"
+    assert not np.array_equal(single[0][0], before[0][0]), "the single calls wrote nothing"
+
+
 # ------------------------------------------------------------------ flat comparator
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_flat_ref_attn_vs_oracle(gpu, dtype):
