@@ -541,10 +541,14 @@ int rows_per_block(const EncodeArgs &k_axis, const EncodeArgs &v_axis, int layer
 
 hipError_t launch_encode_layers(const EncodeArgs *k_axes, const EncodeArgs *v_axes, int n,
                                 bool bf16, hipStream_t st) {
-    // shapes a single call would not give to the matrix-core tile kernel (fp32 codecs, batches
-    // for the row-streaming kernel) go layer by layer, through the same kernels as single calls
-    if (!bf16 || (rows_kernel_fits(k_axes[0]) && rows_kernel_fits(v_axes[0]) &&
-                  rows_blocks_of(k_axes[0]) + rows_blocks_of(v_axes[0]) >= 256)) {
+    // when a single call would give any layer to another kernel (fp32 codecs; the row-streaming
+    // kernel, which also depends on each layer's operand alignment), every layer goes through
+    // the single-call launcher, so each pool is written exactly as a single call writes it
+    bool per_layer = !bf16;
+    for (int i = 0; i < n && !per_layer; ++i)
+        per_layer = rows_kernel_fits(k_axes[i]) && rows_kernel_fits(v_axes[i]) &&
+                    rows_blocks_of(k_axes[i]) + rows_blocks_of(v_axes[i]) >= 256;
+    if (per_layer) {
         for (int i = 0; i < n; ++i) {
             const hipError_t e = launch_encode(k_axes[i], v_axes[i], bf16, st);
             if (e != hipSuccess) return e;
