@@ -6,9 +6,9 @@
   Covered for the reconstructing, absorbed and rotary decodes (bf16), the fp32 decode and the
   chunked prefill.  An encode whose write position lands on such a page writes nothing for that
   row and leaves every other write as it was.
-* HIP-graph replay.  Decode, encode-append and prefill captured once and replayed several times,
-  with eager work and synchronisations between the replays, give bitwise the eager results on
-  every replay (the benchmark times graph launches).
+* HIP-graph replay.  Decode, encode-append (one layer or many) and prefill captured once and
+  replayed several times, with eager work and synchronisations between the replays, give
+  bitwise the eager results on every replay (the benchmark times graph launches).
 """
 import sys
 
@@ -17,6 +17,7 @@ import pytest
 import torch
 
 from looped_transformer_kv_amd import lla, synth
+from looped_transformer_kv_amd.runtime import LatentLayer
 import gpucase
 import tinycase
 from gpucase import Chunk
@@ -208,4 +209,44 @@ def test_graph_replay_matches_eager(gpu):
         # eager work of the program itself between replays
         dp.layer.decode(0, dp.q[0], other, ws, dp.x_k[:, 0], dp.x_v[:, 0], stride)
         _ = float(other.float().abs().sum())
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_of_multi_layer_encode(gpu):
+    """lla_encode_append_layers captured once writes, on every replay, the pools of its eager
+    call (the pools are put back to their earlier contents before each replay)."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    dps = [gpucase.DeviceProblem(tinycase.make(cfg, layer=l, B=5, N=120)) for l in range(3)]
+    pos = torch.tensor([120, 7, -1, 64, 119], dtype=torch.int32, device=gpu)
+    pools = [p for dp in dps for p in (dp.k_pool, dp.v_pool)]
+    before = [p.clone() for p in pools]
+
+    def work():
+        LatentLayer.encode_append_layers([dp.layer for dp in dps], [dp.x_k for dp in dps],
+                                         [dp.x_v for dp in dps], pos)
+
+    def restore():
+        for p, b in zip(pools, before):
+            p.copy_(b)
+
+    say("multi-layer encode: eager reference")
+    work()
+    torch.cuda.synchronize()
+    ref = [synth.from_device(p) for p in pools]
+    assert any(not np.array_equal(r, synth.from_device(b)) for r, b in zip(ref, before))
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        torch.cuda.synchronize()
+        say(f"multi-layer encode: graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (p, r) in enumerate(zip(pools, ref)):
+            assert np.array_equal(synth.from_device(p), r), f"replay {rep}: pool {i} differs"
+        _ = float(dps[0].x_k.float().abs().sum())     # eager work between replays
         torch.cuda.synchronize()
