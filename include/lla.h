@@ -105,15 +105,25 @@ typedef struct {
  * Returns 0.0 for a NULL or invalid codec. */
 double lla_compression_ratio(const lla_codec *codec);
 
-/* Bytes one cached token occupies per layer: G * (r_k + r_v) * sizeof(dtype) (0 if invalid). */
+/* Bytes one cached token occupies per layer in the latent cache: G * (r_k + r_v) * sizeof(dtype)
+ * (0 for a NULL or invalid codec).  Times the token count it is the whole cache, and against
+ * lla_flat_bytes_per_token it is exactly the reduction by rho: the arXiv abstract calls the
+ * reduction exact, and the Figure 10 caption (maximum decode batch against context) has the
+ * cache shrink by rho at every context length. */
 size_t lla_latent_bytes_per_token(const lla_codec *codec);
 
 /* Bytes the uncompressed loop-indexed cache would take per token and layer:
  * 2 * T * H * d * sizeof(dtype) (Figure 1: every loop keeps its own K_t, V_t). */
 size_t lla_flat_bytes_per_token(const lla_codec *codec);
 
-/* Split plan and workspace size of lla_decode_attn for this codec and cache (host call). */
+/* Split plan and workspace size of lla_decode_attn for this codec and cache (host call).  The
+ * plan depends on the codec, batch, n_heads and max_seq_len only; _rope and _absorbed use it too. */
 lla_status lla_decode_plan(const lla_codec *codec, const lla_cache *cache, lla_plan *plan);
+
+/* Workspace bytes lla_decode_attn (and _rope, _absorbed) needs for this codec and cache: the
+ * workspace_bytes of lla_decode_plan (0 when the call needs none).  bytes NULL -> LLA_ERR_NULL;
+ * otherwise the errors of lla_decode_plan, with *bytes untouched. */
+lla_status lla_decode_workspace_size(const lla_codec *codec, const lla_cache *cache, size_t *bytes);
 
 /*
  * Decode attention of loop t for every sequence and head of one layer, reading the latent cache

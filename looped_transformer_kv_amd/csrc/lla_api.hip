@@ -1,7 +1,6 @@
 // lla_api.hip -- the C ABI of liblla.so (declared in include/lla.h): argument validation, split
 // planning and kernel launches.  No allocation, no global mutable state, no host synchronisation.
 #include <cstdint>
-#include <cstdlib>
 
 #include <cmath>
 #include <vector>
@@ -59,22 +58,15 @@ lla_status check_cache(const lla_cache *k, bool need_lens) {
     return LLA_OK;
 }
 
-int target_blocks() {
-    // Workgroups a decode call aims for (context splits are added until B*H*S reaches it).
-    // LLA_TARGET_BLOCKS overrides the default for tuning sweeps.
-    static const int v = [] {
-        const char *e = std::getenv("LLA_TARGET_BLOCKS");
-        const int x = e ? std::atoi(e) : 0;
-        return x > 0 ? x : 512;
-    }();
-    return v;
-}
+// Workgroups a decode call aims for: context splits are added until B*H*S reaches it (two
+// workgroups of four waves per compute unit on the 256-CU chip).
+constexpr int kTargetBlocks = 512;
 
 // Context splits: enough workgroups to fill the chip, each covering a multiple of `unit`
 // tokens and at most `max_tps` tokens.
 void split_plan(int rows, int max_len, int unit, int max_tps, lla_plan *p) {
     const int chunks = (max_len + unit - 1) / unit;
-    int S = (target_blocks() + rows - 1) / (rows > 0 ? rows : 1);
+    int S = (kTargetBlocks + rows - 1) / (rows > 0 ? rows : 1);
     const int S_min = (max_len + max_tps - 1) / max_tps;
     if (S > chunks) S = chunks;
     if (S < S_min) S = S_min;
@@ -144,6 +136,15 @@ lla_status lla_decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) 
     if (!k || !p) return LLA_ERR_NULL;
     if (k->batch < 0 || k->max_seq_len < 0) return LLA_ERR_SHAPE;
     return decode_plan(c, k, p);
+}
+
+lla_status lla_decode_workspace_size(const lla_codec *c, const lla_cache *k, size_t *bytes) {
+    if (!bytes) return LLA_ERR_NULL;
+    lla_plan p;
+    const lla_status st = lla_decode_plan(c, k, &p);
+    if (st != LLA_OK) return st;
+    *bytes = p.workspace_bytes;
+    return LLA_OK;
 }
 
 }  // extern "C"

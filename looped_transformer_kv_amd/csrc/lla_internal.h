@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/lla.h"
+#include "lla.h"
 
 namespace lla {
 

@@ -74,6 +74,8 @@ def lib():
         L.lla_flat_bytes_per_token.argtypes = [P(lla_codec)]
         L.lla_decode_plan.restype = i32
         L.lla_decode_plan.argtypes = [P(lla_codec), P(lla_cache), P(lla_plan)]
+        L.lla_decode_workspace_size.restype = i32
+        L.lla_decode_workspace_size.argtypes = [P(lla_codec), P(lla_cache), P(sz)]
         L.lla_decode_attn.restype = i32
         L.lla_decode_attn.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp, vp, vp,
                                       i64, f32, vp, vp, sz, vp]
@@ -180,6 +182,13 @@ def lla_decode_plan(codec: lla_codec, cache: lla_cache) -> lla_plan:
            lib().lla_decode_plan(ctypes.byref(codec), ctypes.byref(cache), ctypes.byref(plan)),
            True)
     return plan
+
+
+def lla_decode_workspace_size(codec: lla_codec, cache: lla_cache) -> int:
+    out = ctypes.c_size_t(0)
+    _check("lla_decode_workspace_size", lib().lla_decode_workspace_size(
+        ctypes.byref(codec), ctypes.byref(cache), ctypes.byref(out)), True)
+    return int(out.value)
 
 
 def lla_decode_attn(codec, params, cache, t, q, k_self, v_self, self_stride, scale, out,

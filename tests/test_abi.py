@@ -80,6 +80,25 @@ def test_decode_plan_covers_the_context():
     assert plan.splits > 1 and plan.workspace_bytes == c.H * plan.splits * (c.d + 4) * 4
 
 
+
+@pytest.mark.parametrize("B,N", [(32, 4096), (1, 4096), (768, 4096), (3, 300), (0, 0)])
+def test_decode_workspace_size_matches_plan(B, N):
+    c = synth.CONFIGS["ouro14_21x"]
+    max_pages = max(1, (N + 1 + c.page - 1) // c.page)
+    cache = lla.lla_cache(None, None, None, None, B, c.page, max_pages, max(1, B * max_pages), N)
+    plan = lla.lla_decode_plan(_codec(c), cache)
+    assert lla.lla_decode_workspace_size(_codec(c), cache) == plan.workspace_bytes
+    L = lla.lib()
+    out = ctypes.c_size_t(12345)
+    assert L.lla_decode_workspace_size(ctypes.byref(_codec(c)), ctypes.byref(cache), None) == \
+        lla.LLA_ERR_NULL
+    bad = lla.make_codec(0, 4, 16, 96, 16, 32, 1)          # d_head 96: invalid codec
+    assert L.lla_decode_workspace_size(ctypes.byref(bad), ctypes.byref(cache),
+                                       ctypes.byref(out)) == lla.LLA_ERR_SHAPE
+    assert out.value == 12345                              # untouched on error
+    assert L.lla_decode_workspace_size(ctypes.byref(_codec(c)), None,
+                                       ctypes.byref(out)) == lla.LLA_ERR_NULL
+
 FAKE = 0x10000   # never dereferenced: every call below fails validation first
 
 
