@@ -142,7 +142,10 @@ def test_encode_append_layers_matches_single_calls(gpu, name, n_layers):
     cfg = synth.CONFIGS[name]
     B = 32 if cfg.mode == 0 else 4
     N = 100
-    dps = [gpucase.DeviceProblem(tinycase.make(cfg, layer=l, B=B, N=N)) for l in range(n_layers)]
+    # salt = layer: every layer gets its own block-table permutation (and staging rows)
+    dps = [gpucase.DeviceProblem(tinycase.make(cfg, layer=l, B=B, N=N, salt=l))
+           for l in range(n_layers)]
+    assert not np.array_equal(dps[0].p.block_table, dps[1].p.block_table)
     pos_h = np.full(B, N, dtype=np.int32)
     pos_h[1] = 3
     pos_h[2] = -1

@@ -36,7 +36,12 @@ SHAPES = {
     "h2_d64_r16": synth.Config("pf_d64", L=1, H=2, d=64, T=3, r_k=16, r_v=16, B=1, N=1, cid=141),
     "h2_d64_2d_r16_32": synth.Config("pf_d64_2d", L=1, H=2, d=64, T=2, r_k=16, r_v=32, B=1, N=1,
                                      mode=1, cid=142),
+    "h4_d128_r16_16": synth.Config("pf_d128_r16", L=1, H=4, d=128, T=4, r_k=16, r_v=16, B=1, N=1,
+                                   cid=143),
+    "h2_d64_r32_32": synth.Config("pf_d64_r32", L=1, H=2, d=64, T=4, r_k=32, r_v=32, B=1, N=1,
+                                  cid=144),
 }
+
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
