@@ -146,6 +146,23 @@ lla_status lla_decode_attn(const lla_codec *codec, const lla_params *params,
                            const void *v_self, int64_t self_stride, float scale, void *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * lla_decode_attn for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation and arguments,
+ * minus the workspace.  Context-split partials go to a file-scope device array of the library
+ * (4 MiB; each GPU the library runs on holds its own copy until the process ends), found with
+ * hipGetSymbolAddress on the first call on each device; no call allocates or frees anything.
+ * A plan whose workspace_bytes (lla_decode_plan) exceed 4 MiB returns LLA_ERR_WORKSPACE and
+ * enqueues nothing; LLA_ERR_HIP if the device or the array's address cannot be obtained.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU (concurrent streams,
+ * threads) race and must be serialised by the caller.  Nothing in the array needs clearing:
+ * every partial a call reads was written earlier in the same call.
+ */
+lla_status lla_decode_attn_noalloc(const lla_codec *codec, const lla_params *params,
+                                   const lla_cache *cache, int32_t t, const void *q,
+                                   const void *k_self, const void *v_self, int64_t self_stride,
+                                   float scale, void *out, void *stream);
+
 /* Rotary position embedding applied after reconstruction (see lla_decode_attn_rope). */
 typedef struct {
     float theta;       /* base: pair m of the d head dims turns by pos * theta^(-2m/d); > 1 */

@@ -3,6 +3,7 @@
 #include <cstdint>
 
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "lla_internal.h"
@@ -237,6 +238,57 @@ lla_status lla_decode_attn(const lla_codec *c, const lla_params *prm, const lla_
     if (bf16 && plan.splits == 1) return LLA_OK;   // the latent kernel finished the output itself
     e = launch_combine(a, c->d_head, bf16, true, false, s);
     return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode without allocation
+// lla_decode_attn_noalloc keeps its context-split partials in this file-scope device array
+// instead of a caller workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device, and only that address is used.
+namespace lla {
+constexpr size_t kScratchBytes = size_t(4) << 20;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+}  // namespace lla
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` on each device
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+lla_status scratch_of_current_device(float **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LLA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(lla::scratch)) != hipSuccess || !p)
+            return LLA_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return LLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lla_status lla_decode_attn_noalloc(const lla_codec *c, const lla_params *prm, const lla_cache *k,
+                                   int32_t t, const void *q, const void *k_self,
+                                   const void *v_self, int64_t self_stride, float scale, void *out,
+                                   void *stream) {
+    lla_plan plan;
+    lla_status st = lla_decode_plan(c, k, &plan);
+    if (st != LLA_OK) return st;
+    if (plan.workspace_bytes > lla::kScratchBytes) return LLA_ERR_WORKSPACE;
+    float *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != LLA_OK) return st;
+    return lla_decode_attn(c, prm, k, t, q, k_self, v_self, self_stride, scale, out, ws,
+                           lla::kScratchBytes, stream);
 }
 
 lla_status lla_decode_attn_rope(const lla_codec *c, const lla_params *prm, const lla_cache *k,

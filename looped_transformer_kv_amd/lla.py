@@ -79,6 +79,9 @@ def lib():
         L.lla_decode_attn.restype = i32
         L.lla_decode_attn.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp, vp, vp,
                                       i64, f32, vp, vp, sz, vp]
+        L.lla_decode_attn_noalloc.restype = i32
+        L.lla_decode_attn_noalloc.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32, vp,
+                                              vp, vp, i64, f32, vp, vp]
         L.lla_decode_attn_rope.restype = i32
         L.lla_decode_attn_rope.argtypes = [P(lla_codec), P(lla_params), P(lla_cache), i32,
                                            P(lla_rope), vp, vp, vp, i64, f32, vp, vp, sz, vp]
@@ -200,6 +203,16 @@ def lla_decode_attn(codec, params, cache, t, q, k_self, v_self, self_stride, sca
                                float(scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
                                _stream(stream))
     return _check("lla_decode_attn", st, check)
+
+
+def lla_decode_attn_noalloc(codec, params, cache, t, q, k_self, v_self, self_stride, scale, out,
+                            stream=None, check=True) -> int:
+    """lla_decode_attn without a workspace (the library's own per-device scratch array)."""
+    st = lib().lla_decode_attn_noalloc(ctypes.byref(codec), ctypes.byref(params),
+                                       ctypes.byref(cache), int(t), _ptr(q), _ptr(k_self),
+                                       _ptr(v_self), int(self_stride), float(scale), _ptr(out),
+                                       _stream(stream))
+    return _check("lla_decode_attn_noalloc", st, check)
 
 
 def lla_decode_attn_rope(codec, params, cache, t, rope, q, k_self, v_self, self_stride, scale,
