@@ -11,8 +11,9 @@
  *
  * Conventions shared by every entry point
  *   - Plain C: every pointer is a raw device pointer unless it says "host".  No torch types.
- *   - Ownership: the caller allocates and owns every buffer; the library allocates nothing, keeps
- *     no global mutable state and never frees anything.
+ *   - Ownership: the caller allocates and owns every buffer; the library allocates nothing and
+ *     never frees anything.  Its only global mutable state belongs to lla_decode_attn_noalloc: a
+ *     4 MiB device array per GPU and the host-side table of those arrays' addresses.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  *     call returns without synchronising.
  *   - Errors: arguments are validated on the host before anything is enqueued; on a validation
