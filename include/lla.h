@@ -326,10 +326,13 @@ lla_status lla_ref_attn(int32_t n_heads, int32_t d_head, int32_t dtype, const ll
                         size_t workspace_bytes, void *stream);
 
 /*
- * Measurement helper (not an LLA operation): streams `bytes` of `buf` once from device memory
- * and XORs every 32-bit word into sink[0] (the caller zeroes it first if it wants the checksum).
- * Its time gives the achievable HBM read bandwidth, the practical ceiling for the latent stream.
- * buf: device, 16-byte aligned, bytes a multiple of 16 (0 enqueues nothing); sink: device uint32.
+ * Measurement helper (not an LLA operation): streams `bytes` of `buf` once from device memory.
+ * Its time gives the achievable HBM read rate, the practical ceiling for the latent stream.
+ * Workgroup w (at most 512 of them) stores the XOR of the 32-bit words it read in sink[w]; the
+ * XOR of sink[0 .. 511] is the XOR of every word of the buffer if the caller zeroed sink first
+ * (entries of workgroups that do not exist are left untouched).
+ * buf: device, 16-byte aligned, bytes a multiple of 16 (0 enqueues nothing);
+ * sink: device uint32 [512].
  */
 lla_status lla_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 

@@ -85,7 +85,9 @@ lla_status decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
     const bool bf16 = c->dtype == LLA_BF16;
     p->kernel = bf16 ? 1 : 2;
     p->waves_per_block = 4;
-    split_plan(k->batch * c->n_heads, k->max_seq_len, bf16 ? 32 * 4 : 256,
+    // fp32 caches (small configurations) split in 32-token units: each split's workgroup rebuilds
+    // its tokens one per thread, so short contexts need several splits to use more than a few CUs
+    split_plan(k->batch * c->n_heads, k->max_seq_len, bf16 ? 32 * 4 : 32,
                bf16 ? 32 * kMaxChunksPerSplit : (1 << 30), p);
     // a single-split bf16 plan finishes in the latent kernel and needs no partials
     const bool direct = bf16 && p->splits == 1;

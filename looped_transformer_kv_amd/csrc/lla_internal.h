@@ -107,6 +107,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, bool rope, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_absorbed(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t s);
+constexpr int kStreamReadSlots = 512;   // sink entries of lla_stream_read (= its largest grid)
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 // self_in_record: the current token's score was computed by the decode kernel and stored in
 // split 0's record (slot d + 2, log2 domain) instead of being formed here from q and k_self

@@ -312,8 +312,9 @@ def lla_ref_attn(n_heads, d_head, dtype, flat, q, k_self, v_self, self_stride, s
 
 
 def lla_stream_read(buf, sink, nbytes=None, stream=None, check=True) -> int:
-    """Stream `nbytes` (default: all) of the device tensor `buf` once; XOR its 32-bit words
-    into the int32 device tensor `sink[0]` (a read-bandwidth probe)."""
+    """Stream `nbytes` (default: all) of the device tensor `buf` once (a read-bandwidth probe);
+    workgroup w stores the XOR of the 32-bit words it read in sink[w] (an int32 device tensor of
+    at least 512 entries)."""
     if nbytes is None:
         nbytes = buf.numel() * buf.element_size()
     st = lib().lla_stream_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream))

@@ -339,16 +339,17 @@ def test_full_size_sampled(gpu, name):
 # ------------------------------------------------------------------ read-bandwidth probe
 @pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 7])
 def test_stream_read_reads_every_word(gpu, nbytes):
-    """The probe behind the read ceiling: its checksum equals the XOR of every 32-bit word."""
+    """The probe behind the read ceiling: the XOR of its per-workgroup sink entries equals the XOR
+    of every 32-bit word of the buffer."""
     rng = np.random.default_rng(nbytes)
     host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).to(gpu)
-    sink = torch.zeros(1, dtype=torch.int32, device=gpu)
+    sink = torch.zeros(512, dtype=torch.int32, device=gpu)
     say(f"stream_read {nbytes} bytes")
     lla.lla_stream_read(buf, sink)
     torch.cuda.synchronize()
     expect = np.bitwise_xor.reduce(host)
-    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(expect)
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))) == int(expect)
 
 
 # ------------------------------------------------------------------ absorbed-attention decode
