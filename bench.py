@@ -57,6 +57,7 @@ DESCRIBE = {
 CPU_SAMPLE_SEQS = {"ouro14_21x": 32, "ouro14_21x_cap": 32, "ouro14_4x": 8,
                    "ouro26_2d_64x": 1, "huginn_32x": 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_ouro14_21x_traffic.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "decode_bf16_ouro14_21x_mfma.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "looped_transformer_kv_amd", "csrc", f)
                   for f in ("decode_bf16.hip", "lla_internal.h")]
 
@@ -73,13 +74,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None when it
-    is missing or was taken on a different version of the kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def recorded(path, key):
+    """A figure from a committed rocprofv3 summary under profiles/, or None when the file is
+    missing or was taken on a different version of the decode kernel's source."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
@@ -87,9 +88,20 @@ def recorded_traffic():
     if vals.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's)."""
+    return recorded(TRAFFIC_FILE, "traffic_bytes_per_launch")
+
+
+def recorded_mfma_util():
+    """The decode kernel's matrix-core busy fraction (rocprofv3 MfmaUtil, headline shape)."""
+    v = recorded(MFMA_FILE, "mfma_util_percent_median")
+    return None if v is None else round(v / 100.0, 4)
 
 
 def build_layers(cfg, dev, n_layers):
@@ -625,6 +637,7 @@ def main():
         "decode_frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4) if ceiling else None,
         "decode_flops_per_call": flops,
         "decode_TFLOPs": round(tflops, 2),
+        "decode_mfma_busy_frac": recorded_mfma_util() if cfg.name == WORKLOAD else None,
         "decode_token_loops_per_s_per_call": round(B * N / (dec_us * 1e-6), 1),
         "encode_us_per_layer": round(enc_us, 3),
         "encode_bytes_per_layer": enc_bytes,
