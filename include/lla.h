@@ -164,11 +164,14 @@ lla_status lla_decode_attn_noalloc(const lla_codec *codec, const lla_params *par
                                    const void *k_self, const void *v_self, int64_t self_stride,
                                    float scale, void *out, void *stream);
 
-/* Rotary position embedding applied after reconstruction (see lla_decode_attn_rope). */
+/* Rotary position embedding applied after reconstruction (see lla_decode_attn_rope).  The first
+ * rot_dims head dims rotate: pair m (m < rot_dims/2) turns by pos * theta^(-2m/rot_dims); the
+ * dims from rot_dims on are left as they are (rot_dims = d_head rotates the whole head,
+ * rot_dims = 0 none). */
 typedef struct {
-    float theta;       /* base: pair m of the d head dims turns by pos * theta^(-2m/d); > 1 */
-    int32_t rot_dims;  /* rotated head dims; must equal d_head (whole-head rotation) */
-    int32_t style;     /* 0: pairs (m, m + d/2) (half split); 1: pairs (2m, 2m + 1) (interleaved) */
+    float theta;       /* base; > 1 */
+    int32_t rot_dims;  /* rotated head dims: even, 0 <= rot_dims <= d_head */
+    int32_t style;     /* 0: pairs (m, m + rot_dims/2) (half split); 1: pairs (2m, 2m + 1) */
 } lla_rope;
 
 /*
@@ -178,8 +181,9 @@ typedef struct {
  * position j; the rotation is RoFormer's, which the pages cite).  The current token's own key
  * k_self is rotated to its position seq_lens[b]; q is taken as given (the caller rotates it to
  * that same position); values are not rotated.  Otherwise as lla_decode_attn (same plan and
- * workspace).  bf16 codecs only (LLA_ERR_DTYPE); rope NULL -> LLA_ERR_NULL; theta <= 1 or a
- * style other than 0/1 -> LLA_ERR_SHAPE; rot_dims != d_head -> LLA_ERR_UNSUPPORTED.
+ * workspace).  The ledger fixes neither the rotated width nor the pairing, so rot_dims and style
+ * are arguments.  bf16 codecs only (LLA_ERR_DTYPE); rope NULL -> LLA_ERR_NULL; theta <= 1, a
+ * style other than 0/1, or rot_dims odd, negative or above d_head -> LLA_ERR_SHAPE.
  */
 lla_status lla_decode_attn_rope(const lla_codec *codec, const lla_params *params,
                                 const lla_cache *cache, int32_t t, const lla_rope *rope,

@@ -247,9 +247,12 @@ void decode_bf16_kernel(DecodeArgs a) {
     const uint16_t *vsp = self_here ? static_cast<const uint16_t *>(a.v_self) +
                                           (size_t)b * a.self_stride + (size_t)h * D
                                     : muvp;
-    // ROPE: the rotation partner of element i (half split: i +- d/2, interleaved: i ^ 1)
+    // ROPE: the first R = rope_rot head dims rotate.  The rotation partner of element i < R
+    // (half split: i +- R/2, interleaved: i ^ 1); elements from R on have none
+    const int R = ROPE ? a.rope_rot : 0;
     auto partner = [&](int i) {
-        return a.rope_style ? (i ^ 1) : (i < D / 2 ? i + D / 2 : i - D / 2);
+        if (i >= R) return i;
+        return a.rope_style ? (i ^ 1) : (i < R / 2 ? i + R / 2 : i - R / 2);
     };
     uint16_t qv[UD], mkv[UD], ksv[UD], kpv[ROPE ? UD : 1];
 #pragma unroll
@@ -317,8 +320,11 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
     // ROPE: revolutions per position of pair m, theta^(-2m/d) / (2 pi); the angle pos * f is
     // reduced to [0, 1) revolutions before the hardware sine / cosine
+    // (pairs m >= R/2 stand for two unrotated dims: frequency 0)
     auto rope_rev = [&](int m) {
-        return exp2_(-2.0f * (float)m / (float)D * a.rope_log2_theta) * 0.15915494309189535f;
+        return m < R / 2
+                   ? exp2_(-2.0f * (float)m / (float)R * a.rope_log2_theta) * 0.15915494309189535f
+                   : 0.f;
     };
     float qm, s_self = -INFINITY;   // log2-scaled
     {
@@ -328,14 +334,16 @@ void decode_bf16_kernel(DecodeArgs a) {
             am += bf2f(qv[u]) * bf2f(mkv[u]);
             float kk = bf2f(ksv[u]);
             if constexpr (ROPE) {
-                // the current token's key turns to its position, seq_lens[b]
+                // the current token's key turns to its position, seq_lens[b] (its first R dims)
                 const int i = lane + 64 * u;
-                const bool first = a.rope_style ? !(i & 1) : i < D / 2;
-                const int m = a.rope_style ? i >> 1 : (first ? i : i - D / 2);
-                const float rev = __builtin_amdgcn_fractf((float)len * rope_rev(m));
-                const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-                const float kp = bf2f(kpv[u]);
-                kk = first ? kk * cs - kp * sn : kp * sn + kk * cs;
+                if (i < R) {
+                    const bool first = a.rope_style ? !(i & 1) : i < R / 2;
+                    const int m = a.rope_style ? i >> 1 : (first ? i : i - R / 2);
+                    const float rev = __builtin_amdgcn_fractf((float)len * rope_rev(m));
+                    const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                    const float kp = bf2f(kpv[u]);
+                    kk = first ? kk * cs - kp * sn : kp * sn + kk * cs;
+                }
             }
             as += bf2f(qv[u]) * kk;
         }
@@ -398,13 +406,18 @@ void decode_bf16_kernel(DecodeArgs a) {
     uint4 bone = make_uint4(0, 0, 0, 0);
     float fr[ROPE ? PT * 16 : 1];
     if constexpr (ROPE) {
+        // pair m: a rotated pair (m < R/2) or two unrotated dims R + 2k, R + 2k + 1 (k = m - R/2)
+        // taken as a pair with angle 0, so every pair tile has the same form
         auto pair_elems = [&](int m, int &i, int &ip) {
-            if (a.rope_style) {
+            if (m >= R / 2) {
+                i = R + 2 * (m - R / 2);
+                ip = i + 1;
+            } else if (a.rope_style) {
                 i = 2 * m;
                 ip = 2 * m + 1;
             } else {
                 i = m;
-                ip = m + D / 2;
+                ip = m + R / 2;
             }
         };
         const float scl = a.scale_log2;

@@ -307,10 +307,12 @@ lla_status lla_decode_attn_rope(const lla_codec *c, const lla_params *prm, const
     if (!(rope->theta > 1.0f) || !std::isfinite(rope->theta) ||
         (rope->style != 0 && rope->style != 1))
         return LLA_ERR_SHAPE;
-    if (rope->rot_dims != c->d_head) return LLA_ERR_UNSUPPORTED;   // whole-head rotation only
+    if (rope->rot_dims < 0 || rope->rot_dims > c->d_head || (rope->rot_dims & 1))
+        return LLA_ERR_SHAPE;
     if (k->batch == 0) return LLA_OK;
     a.rope_log2_theta = std::log2(rope->theta);
     a.rope_style = rope->style;
+    a.rope_rot = rope->rot_dims;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_decode_bf16(a, true, s) != hipSuccess) return LLA_ERR_HIP;
     if (plan.splits == 1) return LLA_OK;

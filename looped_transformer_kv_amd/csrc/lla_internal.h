@@ -38,10 +38,12 @@ struct DecodeArgs {
     int S, tokens_per_split;
     int mode;                        // 0 per-head, 1 LLA-2D
     float scale_log2;                // softmax scale * log2(e): scores live in the log2 domain
-    // rotation after reconstruction (lla_decode_attn_rope only): pair m of the d head dims turns
-    // by pos * theta^(-2m/d); style 0 pairs (m, m + d/2), style 1 pairs (2m, 2m + 1)
+    // rotation after reconstruction (lla_decode_attn_rope only): the first rope_rot head dims
+    // rotate, pair m (m < rope_rot / 2) by pos * theta^(-2m / rope_rot); style 0 pairs
+    // (m, m + rope_rot / 2), style 1 pairs (2m, 2m + 1); dims from rope_rot on stay put
     float rope_log2_theta;
     int rope_style;
+    int rope_rot;
 };
 
 // One chunked prefill call (bf16).

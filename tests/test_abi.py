@@ -205,7 +205,10 @@ def test_rope_validation_without_launch():
                                                               lla.LLA_F32)) == lla.LLA_ERR_DTYPE
     assert call(lla.lla_rope(1.0, 128, 0)) == lla.LLA_ERR_SHAPE
     assert call(lla.lla_rope(10000.0, 128, 2)) == lla.LLA_ERR_SHAPE
-    assert call(lla.lla_rope(10000.0, 64, 0)) == lla.LLA_ERR_UNSUPPORTED
+    assert call(lla.lla_rope(10000.0, 130, 0)) == lla.LLA_ERR_SHAPE     # wider than the head
+    assert call(lla.lla_rope(10000.0, 63, 0)) == lla.LLA_ERR_SHAPE      # odd
+    assert call(lla.lla_rope(10000.0, -2, 1)) == lla.LLA_ERR_SHAPE
+    assert call(lla.lla_rope(10000.0, 64, 0), wsb=0) == lla.LLA_ERR_WORKSPACE   # partial: valid
     assert call(lla.lla_rope(10000.0, 128, 0), wsb=0) == lla.LLA_ERR_WORKSPACE
 
 

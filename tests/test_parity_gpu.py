@@ -506,3 +506,38 @@ def test_head_dim_64_decode_forms(gpu, name, style):
                          f"d64 absorbed {name} t={t}")
         assert_close(dp.decode(t, True, rope=rope), dp.oracle_decode_rope(t, rope, True), "bf16",
                      f"d64 rope {name}/{style} t={t}")
+
+
+# ------------------------------------------------------------------ partial rotation
+@pytest.mark.parametrize("style", [0, 1])
+@pytest.mark.parametrize("rot", ["none", "quarter", "half", "all_but_two"])
+@pytest.mark.parametrize("name", ["ouro14_21x", "h4_d64_r16_32"])
+def test_rope_partial_rotation(gpu, name, rot, style):
+    """Rotation of the first rot_dims head dims only (the rest untouched), against the oracle's
+    rotary decode with the same rot_dims: ragged lengths including 0 and 1, a self term."""
+    cfg = synth.CONFIGS[name] if name in synth.CONFIGS else D64_CFGS[name]
+    rd = {"none": 0, "quarter": cfg.d // 4, "half": cfg.d // 2, "all_but_two": cfg.d - 2}[rot]
+    B, N = 3, 300
+    lens = synth.seq_lens(cfg, B, N, ragged=True, salt=13)
+    lens[0], lens[1] = 0, 1
+    p = tinycase.make(cfg, B=B, N=N, lens=lens)
+    dp = gpucase.DeviceProblem(p)
+    rope = lla.lla_rope(10000.0, rd, style)
+    for t in sorted({0, cfg.T - 1}):
+        say(f"rope partial {name} rot_dims={rd} style={style} lens={list(p.seq_lens)} t={t}")
+        assert_close(dp.decode(t, True, rope=rope), dp.oracle_decode_rope(t, rope, True), "bf16",
+                     f"rope partial {name} rot={rd} style={style} t={t}")
+
+
+def test_rope_partial_rotation_split_context(gpu):
+    """Partial rotation over a split context (positions up to 4000, the rotated self score reaches
+    combine through the partial record)."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    p = tinycase.make(cfg, B=1, N=4000)
+    dp = gpucase.DeviceProblem(p)
+    assert dp.layer.plan.splits > 1
+    for rd, style in ((64, 0), (32, 1)):
+        rope = lla.lla_rope(10000.0, rd, style)
+        say(f"rope partial split context rot_dims={rd} style={style}")
+        assert_close(dp.decode(1, True, rope=rope), dp.oracle_decode_rope(1, rope, True), "bf16",
+                     f"rope partial split rot={rd} style={style}")
