@@ -1,7 +1,8 @@
 // encode.hip -- encode a finished token's loop trajectories into latents and append them.
 //
-// pith.science paper page for "Looped Latent Attention", "What carries the argument": for each
-// layer, head and axis the T per-loop vectors are stacked and centred and projected,
+// pith.science paper page for "Looped Latent Attention", "What carries the argument": a token's
+// T loop-step vectors of one layer, head and axis are joined end to end into one vector x of
+// length T d, the codec mean mu is subtracted and W_down maps the rest to the rank-r latent,
 // c = (x - mu) W_down.  LLA-2D (abstract) stacks all heads of the layer into one vector; the
 // stacking order used here is (t, h, i), a reading, which makes the LLA-2D stacked vector of a
 // token simply its contiguous [T][H][d] staging row.

@@ -1,7 +1,8 @@
-// fit.hip -- codec fit from the top right singular vectors of the activations, bf16, gfx950.
+// fit.hip -- codec fit by truncated SVD of the (mean-removed) activations, bf16, gfx950.
 //
 // pith.science paper page for "Looped Latent Attention", "What carries the argument": the codec
-// is initialised from the top right singular vectors of teacher activations.  Per group g the
+// starts from an SVD of activation data, W_down spanning the leading right singular subspace of
+// the mean-removed activation matrix.  Per group g the
 // activations are the stacked rows a_j (X = T D_g values per token, the encode's stacking order);
 //   mu = mean_j a_j,   C = sum_j (a_j - mu)^T (a_j - mu) = A^T A - n mu^T mu   (X x X),
 // and the right singular vectors of the centred matrix are C's eigenvectors.  The top r are found

@@ -7,9 +7,10 @@
  *
  * What it follows (all citations are to the pages on "Looped Latent Attention: Cross-Loop KV
  * Compression for Looped Transformers", O'Neill & Reid, arXiv 2607.15456):
- *   - the codec, pith.science paper page, section "What carries the argument": for each layer,
- *     head and axis (K or V) the T per-loop vectors are stacked and centred, encoded as
- *     c = (x - mu) W_down of rank r, and loop t is reconstructed as x_hat_t = c W_up,t + mu_t;
+ *   - the codec, pith.science paper page, section "What carries the argument": per layer, head
+ *     and axis (K or V) a token's T loop-step vectors form one vector x of length T d; removing
+ *     the mean mu and multiplying by W_down gives the rank-r latent c = (x - mu) W_down, and
+ *     loop t reads back x_hat_t = c W_up,t + mu_t;
  *     attention itself is left unchanged; compression is rho = 2 T d_head / (r_k + r_v)
  *     (the referee report on the same page calls this Eq. 4 and says it is exact);
  *   - the read path, arXiv abstract: loop-specific K/V vectors are reconstructed only when
@@ -318,7 +319,7 @@ int oracle_decode_rope(int mode, int T, int H, int d, int r_k, int r_v, int t,
 
 /*
  * Encode: c = (x - mu) W_down for one axis (pith.science paper page, "What carries the
- * argument": the T per-loop vectors are stacked and centred, then projected).
+ * argument": the loop-step vectors joined into one, the mean removed, the rest projected).
  * x is the staging buffer [B][T][H][d].  The stacked vector of group g is
  *   per-head: xs[t*d + i]         = x[b][t][g][i]
  *   LLA-2D:   xs[(t*H + h)*d + i] = x[b][t][h][i]

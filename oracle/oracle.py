@@ -227,7 +227,7 @@ def stack_rows(mode, x):
 
 
 def fit_svd(mode, T, H, d, r, x):
-    """Codec initialisation from the top right singular vectors of the activations (pith.science
+    """Codec initialisation by truncated SVD of the mean-removed activations (pith.science
     paper page, "What carries the argument"): per group, mu = mean of the stacked rows,
     W_down = the r leading right singular vectors of the centred stacked matrix (columns in
     decreasing singular value; sign fixed so each column's entry of largest magnitude is

@@ -1,5 +1,5 @@
-"""Pins of the oracle's codec fit (CPU only): mu and W_down from the top right singular vectors of
-the centred, stacked activations (pith.science paper page, "What carries the argument").
+"""Pins of the oracle's codec fit (CPU only): mu and W_down from the leading right singular vectors
+of the mean-removed activation rows (pith.science paper page, "What carries the argument").
 
 S1 recovers a planted subspace exactly (projector, mean, singular values of the planted factor,
 exact reconstruction of every row) in both stacking modes; S2 checks Eckart-Young (the residual
