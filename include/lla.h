@@ -2,9 +2,9 @@
  * lla.h -- C ABI of liblla.so, the MI355X (gfx950) Looped Latent Attention decode hot path.
  *
  * Method: "Looped Latent Attention: Cross-Loop KV Compression for Looped Transformers"
- * (O'Neill & Reid, arXiv 2607.15456).  For each layer, head and axis (K or V) the T per-loop
- * vectors of a token are stacked and centred and stored as a latent c = (x - mu) W_down of rank
- * r; loop t reads it back as x_hat_t = c W_up,t + mu_t, and attention itself is unchanged
+ * (O'Neill & Reid, arXiv 2607.15456).  Per layer, head and axis (K or V) a token's T loop-step
+ * vectors are joined into one vector x; the cache keeps only the rank-r latent
+ * c = (x - mu) W_down, loop t reads it back as x_hat_t = c W_up,t + mu_t, and attention is as before
  * (pith.science paper page, "What carries the argument").  Loop-specific K/V are rebuilt only when
  * attention reads them; the default codec is per head, LLA-2D folds all heads of a layer into one
  * latent per axis (abstract).  Compression rho = 2 T d_head / (r_k + r_v) (Eq. 4).
@@ -94,8 +94,9 @@ typedef struct {
 
 /* How a decode call is split across the GPU (reported for tests and benchmarks). */
 typedef struct {
-    int32_t kernel;           /* 1 bf16 MFMA latent kernel, 2 fp32 latent kernel, 3 flat kernel */
-    int32_t splits;           /* context splits per (sequence, head) */
+    int32_t kernel;           /* 1 bf16 MFMA latent kernel, 2 fp32 latent kernel, 3 flat kernel,
+                                 4 all-heads absorbed LLA-2D kernel */
+    int32_t splits;           /* context splits per (sequence, head); kernel 4: per sequence */
     int32_t tokens_per_split;
     int32_t waves_per_block;
     size_t workspace_bytes;   /* what the call needs (0 if none) */
@@ -120,6 +121,16 @@ size_t lla_flat_bytes_per_token(const lla_codec *codec);
 /* Split plan and workspace size of lla_decode_attn for this codec and cache (host call).  The
  * plan depends on the codec, batch, n_heads and max_seq_len only; _rope and _absorbed use it too. */
 lla_status lla_decode_plan(const lla_codec *codec, const lla_cache *cache, lla_plan *plan);
+
+/* Split plan and workspace size of lla_decode_attn_absorbed.  For a bf16 LLA-2D codec with
+ * n_heads <= 16, r_k a multiple of 32 and r_v a multiple of 16 the call runs the all-heads kernel
+ * (kernel 4): one workgroup per (sequence, context split) serves every head, so each latent is
+ * read once per call; its workspace holds q~ for every (sequence, head) and each split's latent
+ * partials, and grows with batch x splits x 16 x r_v floats.  Every other codec gets the plan of
+ * lla_decode_plan.  Errors as lla_decode_plan; LLA_ERR_UNSUPPORTED if more than 1024 splits would
+ * be needed. */
+lla_status lla_decode_absorbed_plan(const lla_codec *codec, const lla_cache *cache,
+                                    lla_plan *plan);
 
 /* Workspace bytes lla_decode_attn (and _rope, _absorbed) needs for this codec and cache: the
  * workspace_bytes of lla_decode_plan (0 when the call needs none).  bytes NULL -> LLA_ERR_NULL;
@@ -198,8 +209,11 @@ lla_status lla_decode_attn_rope(const lla_codec *codec, const lla_params *params
  * <q, mu_t^K>); c~ = sum_j softmax(s)_j c_v(j); out = c~ W_up,t^V + mu_t^V (plus the self term).
  * It is exact only while nothing acts between expansion and attention (no rotation); the per-token
  * work is r_k + r_v multiply-adds per head instead of the d x (r_k + r_v) of the expansion.
- * Arguments, layouts, plan and workspace (lla_decode_plan) are those of lla_decode_attn; bf16
- * codecs only (LLA_ERR_DTYPE otherwise), with the same supported (d_head, r_k, r_v).
+ * Arguments and layouts are those of lla_decode_attn; the plan and the workspace size are
+ * lla_decode_absorbed_plan's (the same as lla_decode_plan's except for LLA-2D codecs the
+ * all-heads kernel takes).  bf16 codecs only (LLA_ERR_DTYPE otherwise), with the same supported
+ * (d_head, r_k, r_v).  The all-heads kernel enqueues three kernels (q~; the latent stream; the
+ * merge of the splits with the expansion c~ W_up,t^V) and needs q 16-byte aligned.
  */
 lla_status lla_decode_attn_absorbed(const lla_codec *codec, const lla_params *params,
                                     const lla_cache *cache, int32_t t, const void *q,
@@ -208,8 +222,9 @@ lla_status lla_decode_attn_absorbed(const lla_codec *codec, const lla_params *pa
                                     size_t workspace_bytes, void *stream);
 
 /*
- * Encode and append (pith.science paper page, "What carries the argument": the T per-loop vectors
- * are stacked and centred, c = (x - mu) W_down).  For every sequence b, group g and axis:
+ * Encode and append (pith.science paper page, "What carries the argument": the loop-step vectors
+ * joined into one, mean removed, projected: c = (x - mu) W_down).  For every sequence b, group g
+ * and axis:
  *   c = (stack_g(x[b]) - mu[g]) W_down[g],  accumulated in fp32,
  *   written (rounded to the pool dtype, bf16 round-to-nearest-even) to the pool slot of logical
  *   position write_pos[b] (page block_table[b][pos/P], slot pos%P).
@@ -290,9 +305,9 @@ lla_status lla_prefill_attn(const lla_codec *codec, const lla_params *params,
                             void *stream);
 
 /*
- * Codec fit from the top right singular vectors of activations (pith.science paper page for
- * "Looped Latent Attention", "What carries the argument": the codec is initialised from the top
- * right singular vectors of teacher activations).  For every group g, with a_j the stacked
+ * Codec fit by truncated SVD (pith.science paper page for "Looped Latent Attention", "What
+ * carries the argument": the codec's starting point comes from an SVD of activation data, W_down
+ * spanning the leading right singular subspace).  For every group g, with a_j the stacked
  * vector of row j (the encode's stacking order) and n rows:
  *   mu[g] = mean_j a_j;   W_down[g] = the r leading right singular vectors of [a_j - mu], as
  *   columns in decreasing singular value, each column's entry of largest magnitude positive;

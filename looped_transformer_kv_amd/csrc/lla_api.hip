@@ -65,9 +65,10 @@ constexpr int kTargetBlocks = 512;
 
 // Context splits: enough workgroups to fill the chip, each covering a multiple of `unit`
 // tokens and at most `max_tps` tokens.
-void split_plan(int rows, int max_len, int unit, int max_tps, lla_plan *p) {
+void split_plan(int rows, int max_len, int unit, int max_tps, lla_plan *p,
+                int target = kTargetBlocks) {
     const int chunks = (max_len + unit - 1) / unit;
-    int S = (kTargetBlocks + rows - 1) / (rows > 0 ? rows : 1);
+    int S = (target + rows - 1) / (rows > 0 ? rows : 1);
     const int S_min = (max_len + max_tps - 1) / max_tps;
     if (S > chunks) S = chunks;
     if (S < S_min) S = S_min;
@@ -93,6 +94,24 @@ lla_status decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
     const bool direct = bf16 && p->splits == 1;
     p->workspace_bytes = direct ? 0 : (size_t)k->batch * c->n_heads * p->splits *
                                           (c->d_head + kPartialPad) * sizeof(float);
+    return LLA_OK;
+}
+
+// Workgroups the all-heads absorbed LLA-2D kernel aims for (two of four waves per compute unit).
+constexpr int kAbs2dTargetBlocks = 512;
+
+// lla_decode_attn_absorbed: LLA-2D codecs the all-heads kernel takes split each sequence's
+// context on its own (one workgroup per (sequence, split) serves every head); its workspace holds
+// q~, the per-split latent partials and their (max, sum).  Every other codec: lla_decode_plan.
+lla_status absorbed_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
+    if (!(c->dtype == LLA_BF16 && absorbed2d_supported(c->mode == LLA_2D ? 1 : 0, c->n_heads,
+                                                       c->d_head, c->r_k, c->r_v)))
+        return decode_plan(c, k, p);
+    p->kernel = 4;
+    p->waves_per_block = 4;
+    split_plan(k->batch, k->max_seq_len, 32 * 4, 32 * kMaxChunksPerSplit, p, kAbs2dTargetBlocks);
+    if (p->splits > kMaxAbs2dSplits) return LLA_ERR_UNSUPPORTED;
+    p->workspace_bytes = abs2d_layout(k->batch, p->splits, c->r_k, c->r_v).total * sizeof(float);
     return LLA_OK;
 }
 
@@ -141,6 +160,14 @@ lla_status lla_decode_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) 
     return decode_plan(c, k, p);
 }
 
+lla_status lla_decode_absorbed_plan(const lla_codec *c, const lla_cache *k, lla_plan *p) {
+    lla_status st = check_codec(c);
+    if (st != LLA_OK) return st;
+    if (!k || !p) return LLA_ERR_NULL;
+    if (k->batch < 0 || k->max_seq_len < 0) return LLA_ERR_SHAPE;
+    return absorbed_plan(c, k, p);
+}
+
 lla_status lla_decode_workspace_size(const lla_codec *c, const lla_cache *k, size_t *bytes) {
     if (!bytes) return LLA_ERR_NULL;
     lla_plan p;
@@ -160,7 +187,7 @@ lla_status prepare_decode(const lla_codec *c, const lla_params *prm, const lla_c
                           const void *q, const void *k_self, const void *v_self,
                           int64_t self_stride, float scale, void *out, void *workspace,
                           size_t workspace_bytes, bool bf16_only, DecodeArgs *args,
-                          lla_plan *plan) {
+                          lla_plan *plan, bool absorbed = false) {
     lla_status st = check_codec(c);
     if (st != LLA_OK) return st;
     if (!prm || !prm->W_up_k || !prm->W_up_v || !prm->mu_k || !prm->mu_v) return LLA_ERR_NULL;
@@ -180,7 +207,8 @@ lla_status prepare_decode(const lla_codec *c, const lla_params *prm, const lla_c
     } else if (decode_f32_lds_bytes(c->d_head, c->r_k, c->r_v) > kMaxDynLds) {
         return LLA_ERR_UNSUPPORTED;
     }
-    decode_plan(c, k, plan);
+    if ((st = absorbed ? absorbed_plan(c, k, plan) : decode_plan(c, k, plan)) != LLA_OK)
+        return st;
     if ((st = check_workspace(*plan, workspace, workspace_bytes)) != LLA_OK) return st;
 
     const Shape sh = shape_of(c);
@@ -327,10 +355,12 @@ lla_status lla_decode_attn_absorbed(const lla_codec *c, const lla_params *prm,
     DecodeArgs a;
     lla_plan plan;
     lla_status st = prepare_decode(c, prm, k, t, q, k_self, v_self, self_stride, scale, out,
-                                   workspace, workspace_bytes, true, &a, &plan);
+                                   workspace, workspace_bytes, true, &a, &plan, true);
     if (st != LLA_OK) return st;
     if (k->batch == 0) return LLA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan.kernel == 4)
+        return launch_decode_absorbed2d(a, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     if (launch_decode_absorbed(a, s) != hipSuccess) return LLA_ERR_HIP;
     if (plan.splits == 1) return LLA_OK;
     return launch_combine(a, c->d_head, true, true, false, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;

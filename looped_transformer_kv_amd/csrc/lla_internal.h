@@ -128,6 +128,33 @@ size_t fit_workspace_floats(int G, int X, int r, long n, int *S_out);
 int fit_block_cols(int r);
 int prefill_queries_per_block();
 
+// Absorbed LLA-2D decode (decode_absorbed2d.hip): heads are the 16 columns of its MFMA tiles.
+constexpr int kAbs2dHeads = 16;
+constexpr int kMaxAbs2dSplits = 1024;
+// Its workspace, in floats from the workspace base; every region starts 256-byte aligned.
+struct Abs2dLayout {
+    size_t qt;      // bf16 [B][2][16][r_k]: q~ (log2-scaled) as hi, lo
+    size_t qm;      // [B][16]: <q, mu_t^K>, log2-scaled
+    size_t self;    // [B][16]: the current token's own score (-inf without one)
+    size_t part;    // [B][S][16][r_v]: per split, sum_j p_j c_v(j) relative to the split max
+    size_t stat;    // [B][S][16][2]: split max, split sum of p
+    size_t total;
+};
+__host__ __device__ inline Abs2dLayout abs2d_layout(int B, int S, int r_k, int r_v) {
+    auto up = [](size_t n) { return (n + 63) & ~size_t(63); };
+    Abs2dLayout L;
+    L.qt = 0;
+    L.qm = L.qt + up((size_t)B * kAbs2dHeads * r_k);
+    L.self = L.qm + up((size_t)B * kAbs2dHeads);
+    L.part = L.self + up((size_t)B * kAbs2dHeads);
+    L.stat = L.part + up((size_t)B * S * kAbs2dHeads * r_v);
+    L.total = L.stat + up((size_t)B * S * kAbs2dHeads * 2);
+    return L;
+}
+bool absorbed2d_supported(int mode, int H, int d, int r_k, int r_v);
+// a.S / a.tokens_per_split are the splits per sequence of the absorbed plan
+hipError_t launch_decode_absorbed2d(const DecodeArgs &a, hipStream_t s);
+
 constexpr int kPartialPad = 4;   // partial record = d + 4 floats (16-byte aligned records)
 constexpr int kMaxChunksPerSplit = 512;   // 32-token chunks one latent-decode workgroup covers
 

@@ -74,6 +74,8 @@ def lib():
         L.lla_flat_bytes_per_token.argtypes = [P(lla_codec)]
         L.lla_decode_plan.restype = i32
         L.lla_decode_plan.argtypes = [P(lla_codec), P(lla_cache), P(lla_plan)]
+        L.lla_decode_absorbed_plan.restype = i32
+        L.lla_decode_absorbed_plan.argtypes = [P(lla_codec), P(lla_cache), P(lla_plan)]
         L.lla_decode_workspace_size.restype = i32
         L.lla_decode_workspace_size.argtypes = [P(lla_codec), P(lla_cache), P(sz)]
         L.lla_decode_attn.restype = i32
@@ -184,6 +186,14 @@ def lla_decode_plan(codec: lla_codec, cache: lla_cache) -> lla_plan:
     _check("lla_decode_plan",
            lib().lla_decode_plan(ctypes.byref(codec), ctypes.byref(cache), ctypes.byref(plan)),
            True)
+    return plan
+
+
+def lla_decode_absorbed_plan(codec: lla_codec, cache: lla_cache) -> lla_plan:
+    plan = lla_plan()
+    _check("lla_decode_absorbed_plan",
+           lib().lla_decode_absorbed_plan(ctypes.byref(codec), ctypes.byref(cache),
+                                          ctypes.byref(plan)), True)
     return plan
 
 

@@ -37,10 +37,13 @@ class LatentLayer:
         self.cache = lla.make_cache(t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                                     self.page_size, max_seq_len)
         self.plan = lla.lla_decode_plan(self.codec, self.cache)
+        self.absorbed_plan = lla.lla_decode_absorbed_plan(self.codec, self.cache)
 
     def workspace(self, device):
+        """One workspace for every decode entry point (the larger of the two plans)."""
         import torch
-        n = max(4, self.plan.workspace_bytes // 4)
+        need = max(self.plan.workspace_bytes, self.absorbed_plan.workspace_bytes)
+        n = max(4, (need + 3) // 4)
         return torch.empty(n, dtype=torch.float32, device=device)
 
     def decode(self, t, q, out, workspace, k_self=None, v_self=None, self_stride=0, scale=None,
@@ -61,7 +64,8 @@ class LatentLayer:
 
     def decode_absorbed(self, t, q, out, workspace, k_self=None, v_self=None, self_stride=0,
                         scale=None, stream=None, check=True):
-        """The same attention in the latent space (lla_decode_attn_absorbed); same workspace."""
+        """The same attention in the latent space (lla_decode_attn_absorbed); the workspace of
+        `workspace()` covers its plan."""
         if scale is None:
             scale = 1.0 / math.sqrt(self.codec.d_head)
         return lla.lla_decode_attn_absorbed(self.codec, self.params, self.cache, t, q, k_self,

@@ -99,6 +99,28 @@ def test_decode_workspace_size_matches_plan(B, N):
     assert L.lla_decode_workspace_size(ctypes.byref(_codec(c)), None,
                                        ctypes.byref(out)) == lla.LLA_ERR_NULL
 
+def test_absorbed_plan():
+    """lla_decode_absorbed_plan: kernel 4 (all heads per workgroup, splits per sequence) for LLA-2D
+    codecs with <= 16 heads, r_k % 32 == 0 and r_v % 16 == 0; the plain decode plan otherwise."""
+    c = synth.CONFIGS["ouro26_2d_64x"]
+    cache = lla.lla_cache(None, None, None, None, c.B, c.page, c.max_pages, c.B * c.max_pages, c.N)
+    plan = lla.lla_decode_absorbed_plan(_codec(c), cache)
+    assert (plan.kernel, plan.splits, plan.tokens_per_split) == (4, 32, 512)
+    rk, rv, B, S = c.r_k, c.r_v, c.B, 32
+    up = lambda n: (n + 63) // 64 * 64
+    floats = up(B * 16 * rk) + 2 * up(B * 16) + up(B * S * 16 * rv) + up(B * S * 16 * 2)
+    assert plan.workspace_bytes == 4 * floats
+    for mode, H, rk, rv in ((0, 16, 96, 160), (1, 32, 96, 160), (1, 16, 16, 32)):
+        codec = lla.make_codec(mode, 4, H, 128, rk, rv, lla.LLA_BF16)
+        a = lla.lla_decode_absorbed_plan(codec, cache)
+        b = lla.lla_decode_plan(codec, cache)
+        assert (a.kernel, a.splits, a.tokens_per_split, a.workspace_bytes) == \
+            (b.kernel, b.splits, b.tokens_per_split, b.workspace_bytes)
+    L = lla.lib()
+    assert L.lla_decode_absorbed_plan(ctypes.byref(_codec(c)), ctypes.byref(cache), None) == \
+        lla.LLA_ERR_NULL
+
+
 FAKE = 0x10000   # never dereferenced: every call below fails validation first
 
 

@@ -3,8 +3,8 @@
 * Out-of-range page ids.  A block-table entry outside [0, n_pages) inside a sequence's visible
   range makes that sequence's outputs NaN and never faults; every other sequence's outputs are
   bitwise those of a run with a valid table, and entries past a sequence's length are never read.
-  Covered for the reconstructing, absorbed and rotary decodes (bf16), the fp32 decode and the
-  chunked prefill.  An encode whose write position lands on such a page writes nothing for that
+  Covered for the reconstructing, absorbed (per head and the all-heads LLA-2D kernel) and rotary
+  decodes (bf16), the fp32 decode and the chunked prefill.  An encode whose write position lands on such a page writes nothing for that
   row and leaves every other write as it was.
 * HIP-graph replay.  Decode, encode-append (one layer or many) and prefill captured once and
   replayed several times, with eager work and synchronisations between the replays, give
@@ -36,7 +36,7 @@ def _same(a, b):
 
 # ------------------------------------------------------------------ out-of-range page ids
 DECODE_KINDS = {"decode": "ouro14_21x", "absorbed": "ouro14_21x", "rope": "ouro14_21x",
-                "decode_2d": "ouro26_2d_64x", "f32": "tiny_f32"}
+                "decode_2d": "ouro26_2d_64x", "absorbed_2d": "ouro26_2d_64x", "f32": "tiny_f32"}
 
 
 @pytest.mark.parametrize("kind", list(DECODE_KINDS))
@@ -51,7 +51,7 @@ def test_bad_page_ids_poison_only_their_sequence(gpu, kind):
     t = cfg.T - 1
 
     def run():
-        return dp.decode(t, True, absorbed=kind == "absorbed", rope=rope)
+        return dp.decode(t, True, absorbed=kind.startswith("absorbed"), rope=rope)
 
     say(f"bad pages {kind} ({cfg.name}): clean run")
     clean = run()
@@ -249,4 +249,41 @@ def test_graph_replay_of_multi_layer_encode(gpu):
         for i, (p, r) in enumerate(zip(pools, ref)):
             assert np.array_equal(synth.from_device(p), r), f"replay {rep}: pool {i} differs"
         _ = float(dps[0].x_k.float().abs().sum())     # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_of_absorbed_2d(gpu):
+    """The all-heads absorbed LLA-2D decode (three kernels) captured once gives bitwise its eager
+    result on every replay."""
+    cfg = synth.CONFIGS["ouro26_2d_64x"]
+    p = tinycase.make(cfg, B=3, N=700, ragged=True)
+    dp = gpucase.DeviceProblem(p)
+    assert dp.layer.absorbed_plan.kernel == 4 and dp.layer.absorbed_plan.splits > 1
+    t = 1
+    ws = dp.layer.workspace(gpu)
+    ks, vs, stride = dp.x_k[:, t], dp.x_v[:, t], cfg.T * cfg.H * cfg.d
+    out = torch.empty((3, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
+
+    def work():
+        dp.layer.decode_absorbed(t, dp.q[t], out, ws, ks, vs, stride)
+
+    say("absorbed 2D graph: eager reference")
+    out.fill_(float("nan"))
+    work()
+    torch.cuda.synchronize()
+    ref = synth.from_device(out)
+    assert np.all(np.isfinite(ref))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(float("nan"))                      # stale workspace must not leak into a replay
+        torch.cuda.synchronize()
+        say(f"absorbed 2D graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(synth.from_device(out), ref), f"replay {rep} differs from eager"
+        dp.layer.decode(0, dp.q[0], out, ws, dp.x_k[:, 0], dp.x_v[:, 0], stride)   # eager work
         torch.cuda.synchronize()
