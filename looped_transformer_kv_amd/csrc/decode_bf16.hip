@@ -79,9 +79,13 @@ struct Shape {
     // chunks; W_up operands live in registers.  Larger ranks: W_up operands from LDS, explicit
     // per-chunk V_hat tiles, query and output in VALU registers.
     static constexpr bool FUSED = !ROPE && KK <= 2 && KV <= 2;
+    // larger ranks without rotation: chunks go through the explicit path two at a time, so each
+    // W_up operand read from LDS feeds two MFMAs (one per chunk) and the LDS operand traffic per
+    // token halves (one operand per MFMA would keep LDS at its peak rate)
+    static constexpr bool PAIR = !FUSED && !ROPE && KK + KV > 4;
     static constexpr int WAVES = 4;
     static constexpr int DEPTH =
-        KK + KV <= 3 ? 3 : (KK + KV <= 4 ? 2 : 1);   // chunks in flight per wave
+        KK + KV <= 3 ? 3 : (KK + KV <= 4 || PAIR ? 2 : 1);   // chunks in flight per wave
 };
 
 template <int D, int RK, int RV, bool ROPE>
@@ -97,12 +101,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kThreads<D, RK, RV, ROP
 void decode_bf16_kernel(DecodeArgs a) {
     using SH = Shape<D, RK, RV, ROPE>;
     constexpr int MT = SH::MT, KK = SH::KK, KV = SH::KV, WAVES = SH::WAVES;
-    constexpr bool FUSED = SH::FUSED;
+    constexpr bool FUSED = SH::FUSED, PAIR = SH::PAIR;
     constexpr int RKP = RK + 8, RVP = RV + 8;   // padded LDS rows (keeps 16-byte alignment)
 
     __shared__ __align__(16) uint16_t sWk[D * RKP];   // W_up,t^K transposed: [i][k]
     __shared__ __align__(16) uint16_t sWv[D * RVP];   // W_up,t^V transposed: [i][k]
-    __shared__ __align__(16) float sP[WAVES][32];
+    __shared__ __align__(16) float sP[WAVES][64];   // p of one chunk (two in the paired path)
+    __shared__ __align__(16) float sQ[PAIR ? D : 4];   // paired path: q, log2-scaled
     __shared__ __align__(16) float sO[WAVES][D];
     __shared__ float sM[WAVES], sL[WAVES];
     __shared__ int sSlot[kMaxChunksPerSplit];         // chunk -> first token row in the pool
@@ -280,10 +285,11 @@ void decode_bf16_kernel(DecodeArgs a) {
         }
     }
 
-    // (3) the first latent chunks of this wave
+    // (3) the first latent chunks of this wave (paired path: the first one; the second follows
+    // once the W_up pieces are in LDS, so the two never hold registers at the same time)
     Chunk<KK, KV> buf[DEPTH];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
+    for (int i = 0; i < (PAIR ? 1 : DEPTH); ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
 
     // (4) page table (and, explicit path, W_up,t transposed: [column][rank]) into LDS;
     // <q, mu_t^K>, <q, k_self>
@@ -318,6 +324,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             }
         }
     }
+    if constexpr (PAIR) load_slot(wave + WAVES, first[1], buf[1]);
     // ROPE: revolutions per position of pair m, theta^(-2m/d) / (2 pi); the angle pos * f is
     // reduced to [0, 1) revolutions before the hardware sine / cosine
     // (pairs m >= R/2 stand for two unrotated dims: frequency 0)
@@ -351,10 +358,15 @@ void decode_bf16_kernel(DecodeArgs a) {
         qm = ROPE ? 0.f : wave_sum(am) * a.scale_log2;
         if (self_score) s_self = wave_sum(as) * a.scale_log2;
     }
-    float qs[(FUSED || ROPE) ? 1 : MT][16];
+    // explicit path: q rows in fp32, log2-scaled (the paired path reads them from LDS, to keep
+    // its registers for the second chunk)
+    if constexpr (PAIR) {
+        if (tid < D) sQ[tid] = bf2f(qp[tid]) * a.scale_log2;
+    }
+    float qs[(FUSED || ROPE || PAIR) ? 1 : MT][16];
     if constexpr (!FUSED) {
 #pragma unroll
-        for (int M = 0; M < ((FUSED || ROPE) ? 0 : MT); ++M)
+        for (int M = 0; M < ((FUSED || ROPE || PAIR) ? 0 : MT); ++M)
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const uint2 u = qrow[M][bb];
@@ -502,6 +514,26 @@ void decode_bf16_kernel(DecodeArgs a) {
         return p;
     };
 
+    // the same for two chunks at once (paired path): one running max over their 64 tokens; returns
+    // the weights of token l32 of each chunk
+    auto softmax_step2 = [&](float s0, float s1, float &p0, float &p1) {
+        const float sm = fmaxf(s0, s1);
+        if (__builtin_amdgcn_ballot_w64(sm > m_run) != 0) {
+            const float r = row16_max(sm);
+            const float cmax = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)),
+                                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16)));
+            const float m_new = fmaxf(m_run, cmax);
+            const float alpha = exp2_(m_run - m_new);
+            l_lane *= alpha;
+#pragma unroll
+            for (int N = 0; N < (FUSED ? 0 : MT); ++N) o[N] *= alpha;
+            m_run = m_new;
+        }
+        p0 = exp2_(s0 - m_run);
+        p1 = exp2_(s1 - m_run);
+        l_lane += (h2 == 0 ? p0 + p1 : 0.f);
+    };
+
     // ---- fused path, in two stages so that the matrix core can work on the next chunk's scores
     // while the vector ALUs finish the current one.
     // Scores: A = q-scaled W_up^K transposed (d x r_k), B = chunk latents (r_k x 32 tokens); the
@@ -628,6 +660,74 @@ void decode_bf16_kernel(DecodeArgs a) {
         }
     };
 
+    // paired explicit path: chunks c0 and c1 = c0 + WAVES (has1: c1 is one of this wave's chunks;
+    // otherwise x1 is ignored, its tokens get weight 0).  Every W_up operand read from LDS feeds
+    // one MFMA per chunk; the two chunks' scores share one softmax step, and the V_hat tiles are
+    // built one column tile at a time after it
+    auto compute2 = [&](int c0, const Chunk<KK, KV> &x0, const Chunk<KK, KV> &x1, bool has1) {
+        const int c1 = has1 ? c0 + WAVES : c0;
+        const int valid0 = j_end - (j_begin + 32 * c0);
+        const int valid1 = has1 ? j_end - (j_begin + 32 * c1) : 0;
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int M = 0; M < MT; ++M) {
+            f32x16 a0 = {}, a1 = {};
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) {
+                const uint4 w = wk_op(M, ks);
+                a0 = mfma32x32x16(w, x0.k[ks], a0);
+                a1 = mfma32x32x16(w, x1.k[ks], a1);
+            }
+            float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const float4 q4 = *reinterpret_cast<const float4 *>(&sQ[32 * M + 8 * bb + 4 * h2]);
+                u0 += q4.x * a0[4 * bb] + q4.y * a0[4 * bb + 1] + q4.z * a0[4 * bb + 2] + q4.w * a0[4 * bb + 3];
+                u1 += q4.x * a1[4 * bb] + q4.y * a1[4 * bb + 1] + q4.z * a1[4 * bb + 2] + q4.w * a1[4 * bb + 3];
+            }
+            t0 += u0;
+            t1 += u1;
+            __builtin_amdgcn_sched_barrier(0);   // one tile's accumulators live at a time
+        }
+        float sc0 = add_swap32(t0) + qm, sc1 = add_swap32(t1) + qm;
+        if (l32 >= valid0) sc0 = -INFINITY;
+        if (l32 >= valid1) sc1 = -INFINITY;
+        if (sSlot[c0] < 0) sc0 = __builtin_nanf("");
+        if (sSlot[c1] < 0) sc1 = __builtin_nanf("");
+        float p0, p1;
+        softmax_step2(sc0, sc1, p0, p1);
+        if (h2 == 0) {
+            sP[wave][l32] = p0;
+            sP[wave][32 + l32] = p1;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // V_hat tiles; the weights of the tile's token rows 8 bb + 4 h2 + 0..3 come from LDS
+#pragma unroll
+        for (int N = 0; N < MT; ++N) {
+            f32x16 v0 = {}, v1 = {};
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) {
+                const uint4 w = wv_op(N, ks);
+                v0 = mfma32x32x16(x0.v[ks], w, v0);
+                v1 = mfma32x32x16(x1.v[ks], w, v1);
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const float4 u = *reinterpret_cast<const float4 *>(&sP[wave][8 * bb + 4 * h2]);
+                acc += u.x * v0[4 * bb] + u.y * v0[4 * bb + 1] + u.z * v0[4 * bb + 2] + u.w * v0[4 * bb + 3];
+            }
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const float4 u = *reinterpret_cast<const float4 *>(&sP[wave][32 + 8 * bb + 4 * h2]);
+                acc += u.x * v1[4 * bb] + u.y * v1[4 * bb + 1] + u.z * v1[4 * bb + 2] + u.w * v1[4 * bb + 3];
+            }
+            o[(FUSED) ? 0 : N] += acc;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
     // ---- main loop: chunks wave, wave + WAVES, ...  DEPTH chunks per wave are in flight: a
     // buffer is refilled with the chunk DEPTH rounds ahead as soon as it has been consumed.
     // Prefetch indices are clamped to the last chunk, so no load sits behind a data-dependent
@@ -667,6 +767,16 @@ void decode_bf16_kernel(DecodeArgs a) {
                     c += WAVES;
                 }
             }
+        } else if constexpr (PAIR) {
+            // buf[0], buf[1] hold chunks c, c + WAVES; both are refilled two rounds ahead
+            for (; r + 2 <= rounds; r += 2) {
+                fair_prio(rounds - r);
+                compute2(c, buf[0], buf[1], true);
+                load(min(c + 2 * WAVES, nchunks - 1), buf[0]);
+                load(min(c + 3 * WAVES, nchunks - 1), buf[1]);
+                c += 2 * WAVES;
+            }
+            if (r < rounds) compute2(c, buf[0], buf[0], false);   // an odd last chunk
         } else {
             for (; r + DEPTH <= rounds; r += DEPTH) {
                 fair_prio(rounds - r);
