@@ -169,6 +169,22 @@ void decode_bf16_kernel(DecodeArgs a) {
             x.v[ks] = *reinterpret_cast<const uint4 *>(vb + dv + 16 * ks);
     };
     auto load = [&](int c, Chunk<KK, KV> &x) { load_slot(c, sSlot[c], x); };
+    // the key or the value half of load_slot, for refilling a buffer half as soon as it is consumed
+    auto load_half = [&](int c, Chunk<KK, KV> &x, bool keys) {
+        const int slot = sSlot[c];
+        const int row = __builtin_amdgcn_readfirstlane(slot < 0 ? -slot - 1 : slot);
+        const int valid = j_end - (j_begin + 32 * c);
+        const int tok = min(l32, max(valid - 1, 0));
+        if (keys) {
+            const uint16_t *kb = kpool + (size_t)row * RK + lane_k + (tok - l32) * RK;
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) x.k[ks] = *reinterpret_cast<const uint4 *>(kb + 16 * ks);
+        } else {
+            const uint16_t *vb = vpool + (size_t)row * RV + lane_v + (tok - l32) * RV;
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) x.v[ks] = *reinterpret_cast<const uint4 *>(vb + 16 * ks);
+        }
+    };
 
     // ---- prologue.  A wave's vector loads complete in order, so the order of issue matters:
     // (1) page-table entries of this wave's first chunks, (2) every small set-up operand, raw
@@ -570,7 +586,8 @@ void decode_bf16_kernel(DecodeArgs a) {
     };
 
     // explicit path (larger ranks): one chunk, start to end
-    auto compute = [&](int c, const Chunk<KK, KV> &x) {
+    // next >= 0: the chunk to refill x with, half by half as each half is consumed
+    auto compute = [&](int c, Chunk<KK, KV> &x, int next) {
         const int valid = j_end - (j_begin + 32 * c);   // >= 1, wave-uniform
         {
             // ---- scores: K_hat tiles (d rows x 32 token columns) dotted with q per lane
@@ -615,6 +632,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             float tot = sp[0];
 #pragma unroll
             for (int M = 1; M < MT; ++M) tot += sp[M];
+            if (next >= 0) load_half(next, x, true);   // the keys are consumed
             float sc = add_swap32(tot) + qm;        // token l32's score, in both lane halves
             if (l32 >= valid) sc = -INFINITY;
             if (sSlot[c] < 0) sc = __builtin_nanf("");
@@ -656,6 +674,7 @@ void decode_bf16_kernel(DecodeArgs a) {
                     for (int v = 0; v < 16; ++v) o[N] += pr[v] * vacc[N][v];
                 }
             }
+            if (next >= 0) load_half(next, x, false);   // the values are consumed
             __builtin_amdgcn_wave_barrier();
         }
     };
@@ -664,7 +683,10 @@ void decode_bf16_kernel(DecodeArgs a) {
     // otherwise x1 is ignored, its tokens get weight 0).  Every W_up operand read from LDS feeds
     // one MFMA per chunk; the two chunks' scores share one softmax step, and the V_hat tiles are
     // built one column tile at a time after it
-    auto compute2 = [&](int c0, const Chunk<KK, KV> &x0, const Chunk<KK, KV> &x1, bool has1) {
+    // n0, n1 >= 0: the chunks to refill x0 and x1 with; each half is refilled as soon as it has
+    // been consumed (keys after the scores, values after the V_hat tiles), so the next pair's loads
+    // overlap this pair's remaining work
+    auto compute2 = [&](int c0, Chunk<KK, KV> &x0, Chunk<KK, KV> &x1, bool has1, int n0, int n1) {
         const int c1 = has1 ? c0 + WAVES : c0;
         const int valid0 = j_end - (j_begin + 32 * c0);
         const int valid1 = has1 ? j_end - (j_begin + 32 * c1) : 0;
@@ -688,6 +710,10 @@ void decode_bf16_kernel(DecodeArgs a) {
             t0 += u0;
             t1 += u1;
             __builtin_amdgcn_sched_barrier(0);   // one tile's accumulators live at a time
+        }
+        if (n0 >= 0) {
+            load_half(n0, x0, true);
+            load_half(n1, x1, true);
         }
         float sc0 = add_swap32(t0) + qm, sc1 = add_swap32(t1) + qm;
         if (l32 >= valid0) sc0 = -INFINITY;
@@ -724,6 +750,10 @@ void decode_bf16_kernel(DecodeArgs a) {
             }
             o[(FUSED) ? 0 : N] += acc;
             __builtin_amdgcn_sched_barrier(0);
+        }
+        if (n0 >= 0) {
+            load_half(n0, x0, false);
+            load_half(n1, x1, false);
         }
         __builtin_amdgcn_wave_barrier();
     };
@@ -771,19 +801,25 @@ void decode_bf16_kernel(DecodeArgs a) {
             // buf[0], buf[1] hold chunks c, c + WAVES; both are refilled two rounds ahead
             for (; r + 2 <= rounds; r += 2) {
                 fair_prio(rounds - r);
-                compute2(c, buf[0], buf[1], true);
-                load(min(c + 2 * WAVES, nchunks - 1), buf[0]);
-                load(min(c + 3 * WAVES, nchunks - 1), buf[1]);
+                compute2(c, buf[0], buf[1], true, min(c + 2 * WAVES, nchunks - 1),
+                         min(c + 3 * WAVES, nchunks - 1));
                 c += 2 * WAVES;
             }
-            if (r < rounds) compute2(c, buf[0], buf[0], false);   // an odd last chunk
+            if (r < rounds) compute2(c, buf[0], buf[0], false, -1, -1);   // an odd last chunk
         } else {
             for (; r + DEPTH <= rounds; r += DEPTH) {
                 fair_prio(rounds - r);
 #pragma unroll
                 for (int i = 0; i < DEPTH; ++i) {
-                    compute(c, buf[i]);
-                    load(min(c + DEPTH * WAVES, nchunks - 1), buf[i]);
+                    // one chunk in flight: refill its buffer half by half inside compute (the
+                    // next chunk's keys then load during this chunk's values); with more chunks in
+                    // flight the whole buffer is refilled after it (measured faster there)
+                    if constexpr (DEPTH == 1) {
+                        compute(c, buf[i], min(c + DEPTH * WAVES, nchunks - 1));
+                    } else {
+                        compute(c, buf[i], -1);
+                        load(min(c + DEPTH * WAVES, nchunks - 1), buf[i]);
+                    }
                     c += WAVES;
                 }
             }
@@ -791,7 +827,7 @@ void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i + 1 < DEPTH; ++i) {
                 if (r + i < rounds) {
-                    compute(c, buf[i]);
+                    compute(c, buf[i], -1);
                     c += WAVES;
                 }
             }
