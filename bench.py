@@ -690,7 +690,7 @@ def main():
                                                                          (32, 32)):
         log("timing the chunked prefill")
         result["prefill"] = prefill_leg(cfg, layers, dev, launch, K, args.warmup)
-    if not args.no_fit and cfg.X % 128 == 0 and max(cfg.r_k, cfg.r_v) <= 64:
+    if not args.no_fit and cfg.X % 128 == 0 and cfg.X <= 8192 and max(cfg.r_k, cfg.r_v) <= 160:
         log("timing the codec fit")
         result["fit"] = fit_leg(cfg, dev, 3)
     log("timing the tiny fp32 configuration")

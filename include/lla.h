@@ -315,12 +315,13 @@ lla_status lla_prefill_attn(const lla_codec *codec, const lla_params *params,
  *   sigma[g] (optional, fp32 [G][r]) = the r leading singular values.
  * Computed on the GPU as the centred covariance A^T A - n mu^T mu (matrix cores, fp32
  * accumulation of the exact bf16 inputs), `iters` steps of subspace iteration with r + 8 columns
- * (CholeskyQR2), then a Rayleigh-Ritz step; the result converges to the exact one as
- * (lambda_{r+9} / lambda_r)^iters.  Outputs are rounded once to bf16.
+ * (CholeskyQR2), then a Rayleigh-Ritz step (Jacobi rotations, applied to the basis as they are
+ * logged); the result converges to the exact one as (lambda_{r+9} / lambda_r)^iters.  Outputs are
+ * rounded once to bf16.
  *   x          rows [n][T][H][d] bf16 (e.g. a layer's staged K or V trajectories), 16-byte aligned
  *   mu         [G][X], W_down [G][X][r], W_up [T][G][r][D_g], bf16, caller-owned
  *   workspace  device, >= lla_fit_plan bytes, 16-byte aligned
- * bf16 codecs only (LLA_ERR_DTYPE); r in [1, 64] and X = T*D_g a multiple of 128 (at most 8192)
+ * bf16 codecs only (LLA_ERR_DTYPE); r in [1, 160] and X = T*D_g a multiple of 128 (at most 8192)
  * else LLA_ERR_UNSUPPORTED (r > X: LLA_ERR_SHAPE); n >= r + 9 (+1 if r is odd), <= 2^30;
  * 0 <= iters <= 10000.
  */

@@ -20,7 +20,10 @@
 //   fit_init_kernel    the start block: a counter-based hash per (g, i, c) (splitmix64).
 //   fit_mul_kernel     W = C V (fp32), one workgroup per (g, 32 rows).
 //   fit_orth_kernel    V = orth(W) by CholeskyQR2, one workgroup per group.
-//   fit_ritz_kernel    Rayleigh-Ritz and the outputs, one workgroup per group.
+//   fit_ritz_kernel    Rayleigh-Ritz: H = V^T C V and its Jacobi rotations (logged), one
+//                      workgroup per group.
+//   fit_apply_kernel   the rotations applied to V's rows (W_down before signs), 32 rows each.
+//   fit_out_kernel     column signs and the outputs, one workgroup per group.
 #include "lla_internal.h"
 
 #include <cmath>
@@ -268,40 +271,40 @@ __global__ __launch_bounds__(FT) void fit_mul_kernel(FitArgs a) {
         if (u < nu) a.W[((size_t)g * a.X + 32 * q + il) * rb + c0 + 8 * u] = acc[u];
 }
 
-// 64-row chunks of an X x rb block (row-major, pitch rb) stream through sY (pitch kFitMaxCols + 1,
+// 32-row chunks of an X x rb block (row-major, pitch rb) stream through sY (pitch kFitMaxCols + 1,
 // odd, so rows read across lanes fall in different banks); slot m of thread tid is chunk element
-// tid + FT m, i.e. one fixed (row, column) per slot, and the next chunk's loads are in flight while
-// the current one is used.
-constexpr int CHE = (64 * kFitMaxCols + FT - 1) / FT;    // chunk elements per thread
+// tid + FT m (a chunk's rows are contiguous in memory), and the next chunk's loads are in flight
+// while the current one is used.
+constexpr int CR = 32;                                   // rows of a streamed chunk
+constexpr int CHE = (CR * kFitMaxCols + FT - 1) / FT;    // chunk elements per thread
 struct ChunkStream {
-    int row[CHE], col[CHE], n;
+    int n, rb;
     float pre[CHE];
-    __device__ void init(int rb) {
-        n = 64 * rb;
+    __device__ void init(int rb_) {
+        rb = rb_;
+        n = CR * rb;
+    }
+    __device__ void fetch(const float *Y, int k0) {
 #pragma unroll
         for (int m = 0; m < CHE; ++m) {
             const int e = min((int)threadIdx.x + FT * m, n - 1);
-            row[m] = e / rb;
-            col[m] = e - row[m] * rb;
+            pre[m] = Y[(size_t)k0 * rb + e];
         }
-    }
-    __device__ void fetch(const float *Y, int k0, int rb) {
-#pragma unroll
-        for (int m = 0; m < CHE; ++m)
-            pre[m] = Y[(size_t)k0 * rb + (size_t)row[m] * rb + col[m]];
     }
     __device__ void stage(float (*sY)[kFitMaxCols + 1]) {
 #pragma unroll
-        for (int m = 0; m < CHE; ++m)
-            if ((int)threadIdx.x + FT * m < n) sY[row[m]][col[m]] = pre[m];
+        for (int m = 0; m < CHE; ++m) {
+            const int e = (int)threadIdx.x + FT * m;
+            if (e < n) sY[e / rb][e % rb] = pre[m];
+        }
     }
 };
 
-// Cholesky factor L (lower, rb x rb, in LDS) of the Gram matrix of the X x rb block Y (global).
-// Thread (tp, tq) of a 16 x 16 grid accumulates entries (tp + 16u, tq + 16v) over the row chunks.
-// A pivot below a tiny fraction of the trace is clamped (rank-deficient blocks stay finite).
-// NB = ceil(rb / 16) (at most 5) is a template parameter so the inner loops carry no guards (a
-// guard per term would make every LDS read wait on its own).
+// Cholesky factor L (lower, rb x rb, in LDS; zero above the diagonal) of the Gram matrix of the
+// X x rb block Y (global).  Thread (tp, tq) of a 16 x 16 grid accumulates entries (tp + 16u,
+// tq + 16v) over the row chunks.  A pivot below a tiny fraction of the trace is clamped
+// (rank-deficient blocks stay finite).  NB = ceil(rb / 16) is a template parameter so the inner
+// loops carry no guards (a guard per term would make every LDS read wait on its own).
 template <int NB>
 __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
                                               float (*L)[kFitMaxCols + 1],
@@ -311,14 +314,14 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
     float acc[NB][NB] = {};
     ChunkStream cs;
     cs.init(rb);
-    cs.fetch(Y, 0, rb);
-    for (int k0 = 0; k0 < a.X; k0 += 64) {
+    cs.fetch(Y, 0);
+    for (int k0 = 0; k0 < a.X; k0 += CR) {
         __syncthreads();
         cs.stage(sY);
         __syncthreads();
-        if (k0 + 64 < a.X) cs.fetch(Y, k0 + 64, rb);
+        if (k0 + CR < a.X) cs.fetch(Y, k0 + CR);
 #pragma unroll 4
-        for (int k = 0; k < 64; ++k) {
+        for (int k = 0; k < CR; ++k) {
             float yp[NB], yq[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
@@ -337,7 +340,7 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
 #pragma unroll
         for (int v = 0; v < NB; ++v) {
             const int p = tp + 16 * u, q = tq + 16 * v;
-            if (p < rb && q <= p) L[p][q] = acc[u][v];
+            if (p < rb && q < rb) L[p][q] = q <= p ? acc[u][v] : 0.f;
         }
     __syncthreads();
     __shared__ float tr;
@@ -356,16 +359,16 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
         __syncthreads();
         if (tid > j && tid < rb) L[tid][j] /= L[j][j];
         __syncthreads();
-        // the trailing entries (p, q > j, below rb; the thread's whole block is visited) are
-        // updated branch-free: every visit stores, to a per-thread dummy slot when it is not a
-        // trailing entry, so no entry that another thread reads in this phase is written
+        // the trailing lower entries (p >= q > j, below rb) are updated branch-free: every
+        // visit stores, to a per-thread dummy slot when it is not such an entry, so no entry that
+        // another thread reads in this phase is written
 #pragma unroll
         for (int u = 0; u < NB; ++u)
 #pragma unroll
             for (int v = 0; v < NB; ++v) {
                 const int p = tp + 16 * u, q = tq + 16 * v;
-                if (NB == 5 && (p >= kFitMaxCols || q >= kFitMaxCols)) continue;
-                const bool upd = p > j && q > j && p < rb && q < rb;
+                if (16 * NB > kFitMaxCols && (p >= kFitMaxCols || q >= kFitMaxCols)) continue;
+                const bool upd = p > j && q > j && q <= p && p < rb;
                 const float val = L[p][q] - L[p][j] * L[q][j];
                 *(upd ? &L[p][q] : &sink[tid]) = val;
             }
@@ -373,65 +376,55 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
     }
 }
 
-// out = Y L^{-T}.  L^{-1} (lower triangular, zero above the diagonal) is formed in LDS by
-// elimination; then each 64-row chunk of Y is multiplied by it in full:
-// thread (row tid / 4, columns tid % 4 + 4v) sums over k < rb.  out may alias Y: a chunk is read
-// completely (and the next one fetched) before any of it is written.
+// out = Y L^{-T}.  L^{-1} overwrites L in LDS (lower triangular, zero above the diagonal), column
+// by column from the last: M[i][j] = -(sum_{k=j+1..i} M[i][k] L[k][j]) / L[j][j], where the
+// columns k > j of M are already in place and L's column j is kept in sX; then each 32-row chunk
+// of Y is multiplied by it in full: thread (row tid / 8, columns tid % 8 + 8v) sums over k < rb.
+// out may alias Y: a chunk is read completely (and the next one fetched) before any of it is
+// written.
 template <int NB>
 __device__ __forceinline__ void solve_rows(const FitArgs &a, const float *Y, float *out,
                                            float (*L)[kFitMaxCols + 1],
-                                           float (*Li)[kFitMaxCols + 1],
                                            float (*sY)[kFitMaxCols + 1]) {
-    constexpr int SV = 4 * NB;                           // output column slots per thread
+    constexpr int SV = 2 * NB;                           // output column slots per thread
     const int rb = a.rb, tid = threadIdx.x;
-    // L^{-1} by elimination on [L | I]: step j scales row j, then clears column j below it
-    const int tp = tid >> 4, tq = tid & 15;
-    __shared__ float sink[FT];                           // target of stores that must not land
-#pragma unroll
-    for (int u = 0; u < NB; ++u)
-#pragma unroll
-        for (int v = 0; v < NB; ++v) {
-            const int p = tp + 16 * u, q = tq + 16 * v;
-            if (p < rb && q < rb) Li[p][q] = p == q ? 1.f : 0.f;
-        }
-    __syncthreads();
-    for (int j = 0; j < rb; ++j) {
-        if (tid <= j) Li[j][tid] /= L[j][j];
+    __shared__ float sX[kFitMaxCols];
+    for (int j = rb - 1; j >= 0; --j) {
+        const float djj = 1.f / L[j][j];
+        if (tid > j && tid < rb) sX[tid] = L[tid][j];
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < NB; ++u)
-#pragma unroll
-            for (int v = 0; v < NB; ++v) {
-                const int p = tp + 16 * u, c = tq + 16 * v;
-                if (NB == 5 && (p >= kFitMaxCols || c >= kFitMaxCols)) continue;
-                const bool upd = p > j && p < rb && c <= j;
-                const float val = Li[p][c] - L[p][j] * Li[j][c];
-                *(upd ? &Li[p][c] : &sink[tid]) = val;   // dummy slot: see gram_cholesky
-            }
+        if (tid > j && tid < rb) {
+            float sum = 0.f;
+            for (int k = j + 1; k <= tid; ++k) sum += L[tid][k] * sX[k];
+            L[tid][j] = -djj * sum;
+        } else if (tid == j) {
+            L[j][j] = djj;
+        }
         __syncthreads();
     }
-    const int i = tid >> 2, jq = tid & 3;
-    const int nv = (rb - jq + 3) / 4;
+    const int i = tid >> 3, jq = tid & 7;
+    const int nv = (rb - jq + 7) / 8;
     ChunkStream cs;
     cs.init(rb);
-    cs.fetch(Y, 0, rb);
-    for (int k0 = 0; k0 < a.X; k0 += 64) {
+    cs.fetch(Y, 0);
+    for (int k0 = 0; k0 < a.X; k0 += CR) {
         __syncthreads();                                 // the previous chunk is used
         cs.stage(sY);
         __syncthreads();
-        if (k0 + 64 < a.X) cs.fetch(Y, k0 + 64, rb);
-        // all SV column slots are summed (rows of Li past rb hold whatever they hold and their
-        // sums are never stored), so the loop body has no guard
+        if (k0 + CR < a.X) cs.fetch(Y, k0 + CR);
+        // all SV column slots are summed over k < rb (rows of the inverse past rb read in-bounds
+        // LDS and their sums are never stored; its upper triangle is zero), so the loop body has
+        // no guard
         float acc[SV] = {};
 #pragma unroll 4
         for (int k = 0; k < rb; ++k) {
             const float y = sY[i][k];
 #pragma unroll
-            for (int v = 0; v < SV; ++v) acc[v] += y * Li[min(jq + 4 * v, kFitMaxCols - 1)][k];
+            for (int v = 0; v < SV; ++v) acc[v] += y * L[min(jq + 8 * v, kFitMaxCols - 1)][k];
         }
 #pragma unroll
         for (int v = 0; v < SV; ++v)
-            if (v < nv) out[(size_t)(k0 + i) * rb + jq + 4 * v] = acc[v];
+            if (v < nv) out[(size_t)(k0 + i) * rb + jq + 8 * v] = acc[v];
     }
 }
 
@@ -439,25 +432,25 @@ __device__ __forceinline__ void solve_rows(const FitArgs &a, const float *Y, flo
 template <int NB>
 __global__ __launch_bounds__(FT) void fit_orth_kernel(FitArgs a) {
     __shared__ float L[kFitMaxCols][kFitMaxCols + 1];
-    __shared__ float Li[kFitMaxCols][kFitMaxCols + 1];
-    __shared__ float sY[64][kFitMaxCols + 1];
+    __shared__ float sY[CR][kFitMaxCols + 1];
     const int g = blockIdx.x;
     float *W = a.W + (size_t)g * a.X * a.rb;
     float *V = a.V + (size_t)g * a.X * a.rb;
     gram_cholesky<NB>(a, W, L, sY);
-    solve_rows<NB>(a, W, V, L, Li, sY);
+    solve_rows<NB>(a, W, V, L, sY);
+    __syncthreads();
     gram_cholesky<NB>(a, V, L, sY);
-    solve_rows<NB>(a, V, V, L, Li, sY);
+    solve_rows<NB>(a, V, V, L, sY);
 }
 
-// Rayleigh-Ritz: H = V^T W (W = C V), Jacobi eigenvectors, sorted top r, outputs
+// Rayleigh-Ritz, first part: H = V^T W (W = C V), its eigenvectors by cyclic Jacobi sweeps.  Only
+// H lives in LDS: each round's rotations (cos, sin and the column pair) are logged to the
+// workspace, and fit_apply_kernel applies them to V's rows (V Q, Q never formed).  Also the order
+// of the Ritz values (decreasing, ties by index) and sigma.
 __global__ __launch_bounds__(FT) void fit_ritz_kernel(FitArgs a) {
     __shared__ float H[kFitMaxCols][kFitMaxCols + 1];
-    __shared__ float Q[kFitMaxCols][kFitMaxCols + 1];
     __shared__ float rc[kFitMaxCols / 2], rs[kFitMaxCols / 2];
     __shared__ int rp[kFitMaxCols / 2], rq[kFitMaxCols / 2];
-    __shared__ int order[kFitMaxCols];
-    __shared__ float colmax[kFitMaxCols];
     const int g = blockIdx.x, rb = a.rb, tid = threadIdx.x;
     const float *V = a.V + (size_t)g * a.X * rb;
     const float *W = a.W + (size_t)g * a.X * rb;
@@ -466,7 +459,6 @@ __global__ __launch_bounds__(FT) void fit_ritz_kernel(FitArgs a) {
         float s = 0.f;
         for (int k = 0; k < a.X; ++k) s += V[(size_t)k * rb + p] * W[(size_t)k * rb + q];
         H[p][q] = s;
-        Q[p][q] = p == q ? 1.f : 0.f;
     }
     __syncthreads();
     for (int e = tid; e < rb * rb; e += FT) {            // symmetrise
@@ -480,6 +472,7 @@ __global__ __launch_bounds__(FT) void fit_ritz_kernel(FitArgs a) {
     __syncthreads();
     // cyclic Jacobi in round-robin order: rb - 1 rounds of rb / 2 disjoint pairs per sweep
     const int half = rb / 2;
+    float4 *rot = a.rot + (size_t)g * kFitSweeps * (rb - 1) * half;
     for (int sweep = 0; sweep < kFitSweeps; ++sweep) {
         for (int round = 0; round < rb - 1; ++round) {
             if (tid < half) {
@@ -497,18 +490,17 @@ __global__ __launch_bounds__(FT) void fit_ritz_kernel(FitArgs a) {
                     sn = t * c;
                 }
                 rp[tid] = p; rq[tid] = q; rc[tid] = c; rs[tid] = sn;
+                rot[((size_t)sweep * (rb - 1) + round) * half + tid] =
+                    make_float4(c, sn, __int_as_float(p), __int_as_float(q));
             }
             __syncthreads();
-            for (int e = tid; e < half * rb; e += FT) {      // columns: H J, Q J
+            for (int e = tid; e < half * rb; e += FT) {      // columns: H J
                 const int k = e / rb, i = e % rb;
                 const int p = rp[k], q = rq[k];
                 const float c = rc[k], sn = rs[k];
                 const float hp = H[i][p], hq = H[i][q];
                 H[i][p] = c * hp - sn * hq;
                 H[i][q] = sn * hp + c * hq;
-                const float qp = Q[i][p], qq = Q[i][q];
-                Q[i][p] = c * qp - sn * qq;
-                Q[i][q] = sn * qp + c * qq;
             }
             __syncthreads();
             for (int e = tid; e < half * rb; e += FT) {      // rows: J^T H
@@ -530,22 +522,55 @@ __global__ __launch_bounds__(FT) void fit_ritz_kernel(FitArgs a) {
             const float lj = H[j][j];
             rank += (lj > li) || (lj == li && j < tid);
         }
-        order[rank] = tid;
+        a.order[(size_t)g * kFitMaxCols + rank] = tid;
+        if (a.sigma && rank < a.r) a.sigma[(size_t)g * a.r + rank] = sqrtf(fmaxf(li, 0.f));
     }
-    __syncthreads();
-    // W_down column c = V Q[:, order[c]]; written to the workspace W first for the sign pass
-    float *Y = a.W + (size_t)g * a.X * rb;
-    __syncthreads();                                     // every thread has read W for H
-    for (int e = tid; e < a.X * a.r; e += FT) {
-        const int i = e / a.r, c = e % a.r;
-        const int src = order[c];
-        float s = 0.f;
-        for (int k = 0; k < rb; ++k) s += V[(size_t)i * rb + k] * Q[k][src];
-        Y[(size_t)i * rb + c] = s;                       // W's rows are only read above
+}
+
+// Rayleigh-Ritz, second part: the logged rotations applied to 32 rows of V at a time (the rows of
+// V Q, Q = the product of the rotations in order); the first r columns of V Q in Ritz order go to
+// the workspace W (free once H is formed).  The next round's rotations load while this one is
+// applied.
+__global__ __launch_bounds__(FT) void fit_apply_kernel(FitArgs a) {
+    __shared__ float sR[CR][kFitMaxCols + 1];
+    __shared__ float4 sRot[2][kFitMaxCols / 2];
+    const int rb = a.rb, tid = threadIdx.x, half = rb / 2;
+    const int rows_per = a.X / CR;
+    const int g = blockIdx.x / rows_per, r0 = (blockIdx.x % rows_per) * CR;
+    const float *V = a.V + ((size_t)g * a.X + r0) * rb;
+    for (int e = tid; e < CR * rb; e += FT) sR[e / rb][e % rb] = V[e];
+    const int rounds = kFitSweeps * (rb - 1);
+    const float4 *rot = a.rot + (size_t)g * rounds * half;
+    float4 nxt = make_float4(1.f, 0.f, 0.f, 0.f);
+    if (tid < half) nxt = rot[tid];
+    for (int t = 0; t < rounds; ++t) {
+        if (tid < half) sRot[t & 1][tid] = nxt;
+        __syncthreads();                                 // this round's rotations and the rows
+        if (tid < half && t + 1 < rounds) nxt = rot[(size_t)(t + 1) * half + tid];
+        for (int e = tid; e < CR * half; e += FT) {
+            const int row = e / half, k = e % half;
+            const float4 r = sRot[t & 1][k];
+            const int p = __float_as_int(r.z), q = __float_as_int(r.w);
+            const float x = sR[row][p], y = sR[row][q];
+            sR[row][p] = r.x * x - r.y * y;
+            sR[row][q] = r.y * x + r.x * y;
+        }
+        __syncthreads();
     }
-    __threadfence_block();
-    __syncthreads();
-    // sign: the entry of largest magnitude (first on ties) of each column is positive
+    const int *order = a.order + (size_t)g * kFitMaxCols;
+    float *Y = a.W + ((size_t)g * a.X + r0) * rb;
+    for (int e = tid; e < CR * a.r; e += FT) {
+        const int row = e / a.r, c = e % a.r;
+        Y[(size_t)row * rb + c] = sR[row][order[c]];
+    }
+}
+
+// Outputs: each column's sign fixed so that its entry of largest magnitude (first on ties) is
+// positive, then W_down and the W_up,t blocks in the codec dtype.
+__global__ __launch_bounds__(FT) void fit_out_kernel(FitArgs a) {
+    __shared__ float colsign[kFitMaxCols];
+    const int g = blockIdx.x, rb = a.rb, tid = threadIdx.x;
+    const float *Y = a.W + (size_t)g * a.X * rb;
     if (tid < a.r) {
         float best = -1.f;
         int arg = 0;
@@ -553,14 +578,13 @@ __global__ __launch_bounds__(FT) void fit_ritz_kernel(FitArgs a) {
             const float v = fabsf(Y[(size_t)i * rb + tid]);
             if (v > best) { best = v; arg = i; }
         }
-        colmax[tid] = Y[(size_t)arg * rb + tid] < 0.f ? -1.f : 1.f;
-        if (a.sigma) a.sigma[(size_t)g * a.r + tid] = sqrtf(fmaxf(H[order[tid]][order[tid]], 0.f));
+        colsign[tid] = Y[(size_t)arg * rb + tid] < 0.f ? -1.f : 1.f;
     }
     __syncthreads();
     const int Dg = a.X / a.T;
     for (int e = tid; e < a.X * a.r; e += FT) {
         const int i = e / a.r, c = e % a.r;
-        const float v = colmax[c] * Y[(size_t)i * rb + c];
+        const float v = colsign[c] * Y[(size_t)i * rb + c];
         const size_t wd = ((size_t)g * a.X + i) * a.r + c;
         const int t = i / Dg, k = i - t * Dg;
         const size_t wu = (((size_t)t * a.G + g) * a.r + c) * Dg + k;
@@ -587,7 +611,11 @@ size_t fit_workspace_floats(int G, int X, int r, long n, int *S_out) {
     if (S_out) *S_out = S;
     const int rb = fit_block_cols(r);
     return (size_t)S * G * X * X + (size_t)S * G * X + (size_t)G * X * X + (size_t)G * X +
-           2 * (size_t)G * X * rb;
+           2 * (size_t)G * X * rb + fit_rotation_floats(G, rb) + (size_t)G * kFitMaxCols;
+}
+
+size_t fit_rotation_floats(int G, int rb) {
+    return (size_t)G * kFitSweeps * (rb - 1) * (rb / 2) * 4;
 }
 
 int fit_block_cols(int r) {
@@ -611,7 +639,13 @@ void launch_iter(const FitArgs &a, bool mul, hipStream_t st) {
     case 2: launch_step<2>(a, mul, st); break;
     case 3: launch_step<3>(a, mul, st); break;
     case 4: launch_step<4>(a, mul, st); break;
-    default: launch_step<5>(a, mul, st); break;
+    case 5: launch_step<5>(a, mul, st); break;
+    case 6: launch_step<6>(a, mul, st); break;
+    case 7: launch_step<7>(a, mul, st); break;
+    case 8: launch_step<8>(a, mul, st); break;
+    case 9: launch_step<9>(a, mul, st); break;
+    case 10: launch_step<10>(a, mul, st); break;
+    default: launch_step<11>(a, mul, st); break;
     }
 }
 
@@ -632,6 +666,8 @@ hipError_t launch_fit(FitArgs a, hipStream_t st) {
     }
     launch_iter(a, true, st);
     hipLaunchKernelGGL(fit_ritz_kernel, dim3(a.G), dim3(FT), 0, st, a);
+    hipLaunchKernelGGL(fit_apply_kernel, dim3(a.G * (a.X / CR)), dim3(FT), 0, st, a);
+    hipLaunchKernelGGL(fit_out_kernel, dim3(a.G), dim3(FT), 0, st, a);
     return hipGetLastError();
 }
 

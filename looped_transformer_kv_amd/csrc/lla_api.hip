@@ -621,7 +621,7 @@ lla_status fit_check(const lla_codec *c, int32_t r, int64_t n, int *S, size_t *b
     if (c->dtype != LLA_BF16) return LLA_ERR_DTYPE;
     const Shape sh = shape_of(c);
     if (r < 1 || r > sh.X) return LLA_ERR_SHAPE;
-    if (r > 64 || sh.X % 128 != 0 || sh.X > 8192) return LLA_ERR_UNSUPPORTED;
+    if (r > kFitMaxCols - 8 || sh.X % 128 != 0 || sh.X > 8192) return LLA_ERR_UNSUPPORTED;
     if (n < fit_block_cols(r) + 1 || n > (int64_t)1 << 30) return LLA_ERR_SHAPE;
     *bytes = fit_workspace_floats(sh.G, (int)sh.X, r, (long)n, S) * sizeof(float);
     return LLA_OK;
@@ -673,6 +673,10 @@ lla_status lla_fit_svd(const lla_codec *c, int32_t r, const void *x, int64_t n, 
     a.V = w;
     w += (size_t)a.G * a.X * a.rb;
     a.W = w;
+    w += (size_t)a.G * a.X * a.rb;
+    a.rot = reinterpret_cast<float4 *>(w);
+    w += fit_rotation_floats(a.G, a.rb);
+    a.order = reinterpret_cast<int *>(w);
     a.mu_out = mu;
     a.Wd_out = W_down;
     a.Wu_out = W_up;

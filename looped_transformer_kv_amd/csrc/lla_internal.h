@@ -65,7 +65,7 @@ struct PrefillArgs {
 };
 
 // One codec fit (bf16): workspace pointers are fp32 regions carved by the host.
-constexpr int kFitMaxCols = 72;      // columns of the iterated block (r + 8, r <= 64)
+constexpr int kFitMaxCols = 168;     // columns of the iterated block (r + 8, r <= 160)
 constexpr int kFitSweeps = 12;       // Jacobi sweeps of the Rayleigh-Ritz step
 struct FitArgs {
     const void *x;                   // trajectory rows [n][T][H][d]
@@ -78,6 +78,8 @@ struct FitArgs {
     float *V, *W;                    // [G][X][rb] iterate and product
     void *mu_out, *Wd_out, *Wu_out;  // [G][X], [G][X][r], [T][G][r][X/T] in the codec dtype
     float *sigma;                    // optional [G][r]
+    float4 *rot;                     // [G][sweeps][rb - 1][rb / 2] Jacobi rotations (c, s, p, q bits)
+    int *order;                      // [G][kFitMaxCols] Ritz columns by decreasing eigenvalue
 };
 
 // One encode+append call.
@@ -125,6 +127,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 bool prefill_supported(int d, int r_k, int r_v);
 hipError_t launch_fit(FitArgs a, hipStream_t s);
 size_t fit_workspace_floats(int G, int X, int r, long n, int *S_out);
+size_t fit_rotation_floats(int G, int rb);
 int fit_block_cols(int r);
 int prefill_queries_per_block();
 

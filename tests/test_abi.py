@@ -296,7 +296,7 @@ def test_fit_validation_without_launch():
     f32 = lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_F32)
     assert L.lla_fit_plan(ctypes.byref(f32), 16, 4096, ctypes.byref(sz)) == lla.LLA_ERR_DTYPE
     assert L.lla_fit_plan(ctypes.byref(bf), 0, 4096, ctypes.byref(sz)) == lla.LLA_ERR_SHAPE
-    assert L.lla_fit_plan(ctypes.byref(bf), 65, 4096, ctypes.byref(sz)) == \
+    assert L.lla_fit_plan(ctypes.byref(bf), 161, 4096, ctypes.byref(sz)) == \
         lla.LLA_ERR_UNSUPPORTED
     odd = lla.make_codec(0, 3, 16, 64, 16, 32, lla.LLA_BF16)          # X = 192
     assert L.lla_fit_plan(ctypes.byref(odd), 16, 4096, ctypes.byref(sz)) == \

@@ -42,7 +42,7 @@ def _planted(mode, T, H, d, r_true, n, seed, noise=0.02, decay=0.8):
     return synth.quantize(x, "bf16")
 
 
-CASES = {                                    # (mode, T, H, d, r, n[, factor decay])
+CASES = {                                    # (mode, T, H, d, r, n[, factor decay[, iters]])
     "per_head_X128_r16": (0, 2, 2, 64, 16, 3000),
     "lla2d_X256_r16": (1, 2, 2, 64, 16, 3000),
     "ouro14_X512_r16": (0, 4, 2, 128, 16, 4096),
@@ -53,6 +53,12 @@ CASES = {                                    # (mode, T, H, d, r, n[, factor dec
     "r8_block16": (0, 2, 2, 64, 8, 2000),
     "r48_block56": (0, 2, 2, 64, 48, 3000, 0.95),
     "r64_block72": (0, 2, 1, 128, 64, 3000, 0.95),
+    # the 4x codec's ranks: blocks of 104 and 168 columns (7 and 11 column tiles), per head and
+    # LLA-2D; a slow spectrum keeps all r + 12 planted directions above the noise, and the
+    # smaller gaps between them get more iterations
+    "r96_block104": (0, 4, 1, 128, 96, 4096, 0.985, 120),
+    "r160_block168": (0, 4, 1, 128, 160, 6000, 0.985, 150),
+    "lla2d_r96": (1, 4, 2, 64, 96, 4096, 0.985, 120),
 }
 
 
@@ -60,6 +66,7 @@ CASES = {                                    # (mode, T, H, d, r, n[, factor dec
 def test_fit_matches_oracle(gpu, name):
     mode, T, H, d, r, n, *rest = CASES[name]
     x = _planted(mode, T, H, d, r + 12, n, seed=len(name), decay=rest[0] if rest else 0.8)
+    iters = rest[1] if len(rest) > 1 else 40
     codec = lla.make_codec(mode, T, H, d, r, r, lla.LLA_BF16)
     G = 1 if mode == 1 else H
     X = T * (H * d if mode == 1 else d)
@@ -72,7 +79,7 @@ def test_fit_matches_oracle(gpu, name):
     Wu = torch.empty((T, G, r, Dg), dtype=torch.bfloat16, device=gpu)
     sig = torch.empty((G, r), dtype=torch.float32, device=gpu)
     say(f"fit {name}: n={n} X={X} r={r} workspace={ws_bytes >> 20} MiB")
-    lla.lla_fit_svd(codec, r, xd, n, 40, mu, Wd, Wu, sig, ws)
+    lla.lla_fit_svd(codec, r, xd, n, iters, mu, Wd, Wu, sig, ws)
     torch.cuda.synchronize()
     mu_o, Wd_o, Wu_o, sig_o = O.fit_svd(mode, T, H, d, r, x)
     mu_g, Wd_g, Wu_g = synth.from_device(mu), synth.from_device(Wd), synth.from_device(Wu)
