@@ -336,6 +336,9 @@ def tiny_leg(dev, reps=50):
 
 
 PREFILL_CHUNK = 512
+# (r_k, r_v) pairs lla_prefill_attn serves (d_head 64 or 128): two passes up to 32, one fused
+# kernel above
+PREFILL_RANKS = {(16, 16), (16, 32), (32, 32), (32, 64), (64, 64), (64, 128), (96, 160)}
 
 
 def prefill_leg(cfg, layers, dev, launch, steps, warmup):
@@ -402,6 +405,12 @@ def prefill_leg(cfg, layers, dev, launch, steps, warmup):
     # EXP_PEAK_PER_S is the chip's rate of those (transcendentals issue at half the fp32 rate).
     pairs = B * H * (Pn * N + Pn * (Pn + 1) // 2)
     exp_rate = pairs / (attn_us * 1e-6)
+    # matrix-core work of the latent-space formulation: q' = c W_up,t^K q and the expansion
+    # O_lat W_up,t^V once per query, 2 (r_k + r_v) per cached pair, 4d per causal chunk pair.
+    # At ranks above 32 this is what binds (the fused kernel: ~6x the flops per exponential).
+    flops = (B * H * Pn * 2 * d * (cfg.r_k + cfg.r_v) + B * H * Pn * N * 2 * (cfg.r_k + cfg.r_v) +
+             B * H * Pn * (Pn + 1) // 2 * 4 * d)
+    tflops = flops / (attn_us * 1e-6) / 1e12
     enc_bytes = sum(B * Pn * T * H * d * 2 + cfg.G * cfg.X * r * 2 + cfg.G * cfg.X * 2 +
                     B * Pn * cfg.G * r * 2 for r in (cfg.r_k, cfg.r_v))
     step_s = (attn_us * T * L + enc_us * L) * 1e-6
@@ -409,6 +418,9 @@ def prefill_leg(cfg, layers, dev, launch, steps, warmup):
             "attn_us_per_call": round(attn_us, 3), "pairs_per_call": pairs,
             "pairs_per_s": round(exp_rate, 1),
             "frac_of_exp_peak": round(exp_rate / EXP_PEAK_PER_S, 4),
+            "mfma_flops_per_call": flops, "TFLOPs": round(tflops, 1),
+            "frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bound": "mfma" if max(cfg.r_k, cfg.r_v) > 32 else "exp",
             "encode_chunk_us_per_call": round(enc_us, 3),
             "encode_chunk_bytes_per_call": enc_bytes,
             "encode_chunk_GBps": round(enc_bytes / (enc_us * 1e-6) / 1e9, 1),
@@ -686,8 +698,7 @@ def main():
                           "style": "half_split", **time_variant(
             lambda t, l: layers[l].decode_rope(t, rope, q[t][l], out, ws, xk[l][:, t],
                                                xv[l][:, t], stride))}
-    if not args.no_prefill and cfg.mode == 0 and (cfg.r_k, cfg.r_v) in ((16, 16), (16, 32),
-                                                                         (32, 32)):
+    if not args.no_prefill and (cfg.r_k, cfg.r_v) in PREFILL_RANKS:
         log("timing the chunked prefill")
         result["prefill"] = prefill_leg(cfg, layers, dev, launch, K, args.warmup)
     if not args.no_fit and cfg.X % 128 == 0 and cfg.X <= 8192 and max(cfg.r_k, cfg.r_v) <= 160:

@@ -43,6 +43,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -52,6 +55,11 @@ __device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
 // two fp32 -> two bf16 (round to nearest even), lo in the low half
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// two 16-bit values, lo in the low half
+__device__ __forceinline__ uint32_t pk16(short lo, short hi) {
+    return static_cast<uint32_t>(static_cast<uint16_t>(lo)) | (static_cast<uint32_t>(static_cast<uint16_t>(hi)) << 16);
 }
 
 // elements 8s .. 8s + 7 of an accumulator as one 8 x bf16 operand
@@ -96,6 +104,29 @@ __device__ __forceinline__ void load_query_operands(const PrefillArgs &a, int b,
         const uint2 hi = *reinterpret_cast<const uint2 *>(row + d0 + 8);
         qop[ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
+}
+
+// This lane's half of <q, mu_t^K> (the dims of its query operands); the partner lane h2 ^ 1
+// holds the other half.
+template <int D>
+__device__ __forceinline__ float query_dot_mu_k(const PrefillArgs &a, int g, int col0, int h2,
+                                                const uint4 (&qop)[D / 16]) {
+    const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
+                          (size_t)a.t * a.Dg + col0;
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(muk), 0, D * 2, kBufferWord3);
+    float qm = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t qv[4] = {qop[ks].x, qop[ks].y, qop[ks].z, qop[ks].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t m = __builtin_amdgcn_raw_buffer_load_b16(
+                mr, 8 * h2, (32 * (ks >> 1) + 16 * (ks & 1) + (e < 4 ? e : e + 4)) * 2, 0);
+            qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(m);
+        }
+    }
+    return qm;
 }
 
 // Partial softmax state of the cached pass, parked per query in that query's own out row until
@@ -188,8 +219,6 @@ void prefill_cached_kernel(PrefillArgs a) {
         // scalar one per element); the workgroup shares the slots
         const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
                              ((size_t)a.t * a.G + g) * RK * a.Dg + col0;
-        const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
-                              (size_t)a.t * a.Dg + col0;
         if (wave < KS) {
             const int ks = wave;
             const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -207,19 +236,7 @@ void prefill_cached_kernel(PrefillArgs a) {
         }
         uint4 qop[KS];
         load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
-        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(muk), 0, D * 2, kBufferWord3);
-        float qm = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const uint32_t qv[4] = {qop[ks].x, qop[ks].y, qop[ks].z, qop[ks].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t m = __builtin_amdgcn_raw_buffer_load_b16(
-                    mr, 8 * h2, (32 * (ks >> 1) + 16 * (ks & 1) + (e < 4 ? e : e + 4)) * 2, 0);
-                qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(m);
-            }
-        }
+        const float qm = query_dot_mu_k<D>(a, g, col0, h2, qop);
         __syncthreads();                                // the W_up,t^K slots
         f32x16 qa = {};
         const int rdw = srow(lane);
@@ -451,80 +468,21 @@ struct Stage {
     uint4 r[N];
 };
 
-// One workgroup of 8 waves (two per SIMD) per (sequence, head, block of 256 queries).  Starts from
-// the cached pass's state (O^T = W_up,t^V^T O_lat^T, weights and max) and runs flash attention
-// over the chunk's own tiles up to each query; normalises and stores.
+// W_up,t^V as the A operands of the expansion O^T = W_up,t^V^T O_lat^T: lane (dim, h2) of 32-dim
+// tile n, k-step ks (slot KV n + ks) holds the dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4,
+// the order of O_lat's B operand.  Wave w of nw builds slots w, w + nw, ..; buffer loads: a fixed
+// byte offset per lane plus a scalar one per element.
 template <int D, int RV>
-__global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs a) {
-    using SH = PShape<D>;
-    constexpr int MT = SH::MT, KS = SH::KS, KV = RV / 16;
-    constexpr int NEWP = SH::NEWP, NST = SH::NST;
-    using St = Stage<NST>;
-
-    // operand slots per buffer: [0, KS) for the keys (sK), [KS, KS + 2 MT) for the values (sV)
-    __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][kSlot];
-    // W_up,t^V operands (32-dim tile n, k-step ks at slot KV n + ks), built once per workgroup
-    __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
-
-    const int id = xcd_work_item(blockIdx.x, gridDim.x);
-    const int qb = id % a.QB;
-    const int h = (id / a.QB) % a.H;
-    const int b = id / (a.QB * a.H);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+__device__ __forceinline__ void build_wv_operands(const PrefillArgs &a, int g, int col0, int wave,
+                                                  int nw, int lane, uint4 (*sW)[kSlot]) {
+    constexpr int MT = D / 32, KV = RV / 16;
     const int l32 = lane & 31, h2 = lane >> 5;
-    const int g = a.mode ? 0 : h;
-    const int col0 = a.mode ? h * D : 0;
-
-    int nn = a.n_new[b];
-    nn = nn < 0 ? 0 : (nn > a.Pn ? a.Pn : nn);
-    const int q0 = qb * CQWG;
-    if (q0 >= nn) return;                               // the whole block is past the chunk
-    int len = a.seq_lens[b];
-    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-    const int qend = min(nn, q0 + CQWG);                 // this block's queries: [q0, qend)
-    const int tiles = (qend + 31) >> 5;                 // chunk tiles up to the last query
-    const int wq0 = q0 + 32 * wave;                     // this wave's first query
-    const bool wlive = wq0 < qend;
-    const int iq = wq0 + l32;
-    const float csc = a.scale_log2;
-
-    uint4 qop[KS];
-    load_query_operands<D>(a, b, h, min(iq, nn - 1), h2, qop);
-
-    // ---- state after the cached tokens.  The cached part back in model space:
-    // O^T = W_up,t^V^T O_lat^T (A: lane (dim, h2) of 32-dim tile n holds the dim's column at ranks
-    // 16 ks + 8 (e / 4) + 4 h2 + e % 4, the order O_lat's lanes are parked in); its weight sum
-    // l_lat later scales mu_t^V.  The sums live in the h2 = 0 lane (both lanes are added at the
-    // end); lanes of queries past the block start empty.
-    float m_run = -INFINITY, l_run = 0.f, l_lat = 0.f;
-    f32x16 oacc[MT];
-#pragma unroll
-    for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
-    uint4 lop[KV];
-#pragma unroll
-    for (int ks = 0; ks < KV; ++ks) lop[ks] = make_uint4(0u, 0u, 0u, 0u);
-    if (wlive && len > 0) {
-        float2 ml = make_float2(-INFINITY, 0.f);
-        if (iq < qend) {
-            const uint4 *st = state_row(a, b, iq, h, D);
-#pragma unroll
-            for (int ks = 0; ks < KV; ++ks) lop[ks] = st[KV * h2 + ks];
-            ml = *reinterpret_cast<const float2 *>(st + 2 * KV);
-        }
-        m_run = ml.x;
-        l_run = h2 ? 0.f : ml.y;
-        l_lat = l_run;
-    }
-    // wave w builds operand slots w, w + CWAVES, ..: lane (dim, h2) of 32-dim tile n, k-step ks
-    // holds the dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4.  Buffer loads: a fixed
-    // byte offset per lane plus a scalar one per element.
-    for (int slot = wave; len > 0 && slot < MT * KV; slot += CWAVES) {
+    const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
+                         ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(Wv), 0, ((RV - 1) * a.Dg + D) * 2, kBufferWord3);
+    for (int slot = wave; slot < MT * KV; slot += nw) {
         const int n = slot / KV, ks = slot % KV;
-        const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
-                             ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
-        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(Wv), 0, ((RV - 1) * a.Dg + D) * 2, kBufferWord3);
         const int wl = (4 * h2 * a.Dg + 32 * n + l32) * 2;
         uint16_t w[8];
 #pragma unroll
@@ -534,6 +492,32 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         sW[slot][srow(lane)] = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
                                           w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
     }
+}
+
+// Flash attention of a workgroup's queries [q0, qend) (8 waves, wave w owning 32 of them) over
+// the chunk's own tiles up to each query, from the state the cached context left (oacc = the
+// cached part in model space, unnormalised; m_run its reference in the log2 domain; l_run and
+// l_lat this lane's share of the cached weight sum).  Then + (sum of cached weights) mu_t^V,
+// normalise and store.  `expand` runs once, after the first chunk tile is in LDS: the two-pass
+// form forms the cached part's expansion there, while its loads are in flight.
+template <int D, typename Expand>
+__device__ __forceinline__ void chunk_phase(const PrefillArgs &a, int b, int h, int g, int col0,
+                                            int nn, int q0, int qend,
+                                            uint4 (&sbuf)[2][PShape<D>::SLOTS][kSlot],
+                                            const uint4 (&qop)[D / 16], f32x16 (&oacc)[D / 32],
+                                            float m_run, float l_run, float l_lat, Expand expand) {
+    using SH = PShape<D>;
+    constexpr int MT = SH::MT, KS = SH::KS;
+    constexpr int NEWP = SH::NEWP, NST = SH::NST;
+    using St = Stage<NST>;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int tiles = (qend + 31) >> 5;                 // chunk tiles up to the last query
+    const int wq0 = q0 + 32 * wave;                     // this wave's first query
+    const bool wlive = wq0 < qend;
+    const int iq = wq0 + l32;
+    const float csc = a.scale_log2;
 
     // ---- tile inputs.  Chunk tile n: piece p = tid + 512 x of each axis is row 32n + (p % 128) / 4
     // (clamped to the last valid row), dims 32 (p / 128) + 8 (p % 4) .. + 7: a wave covers 16 rows
@@ -605,7 +589,7 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
     };
 
     // ---- online softmax over the chunk's tiles (log2 domain; raw q . k scores need * c), lazy
-    // rescale as in the cached pass
+    // rescale
     const int wlast = min(wq0 + 31, qend - 1);          // this wave's last query
     const int rd = srow(lane);                          // this lane's operand row
     auto consume = [&](int tile, int buf) __attribute__((always_inline)) {
@@ -663,13 +647,7 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
     produce(0, S[0], 0);
     issue(CNS, S[0]);
     __syncthreads();
-    // the cached part back in model space, from the shared W_up,t^V operands
-    if (wlive && len > 0) {
-#pragma unroll
-        for (int n = 0; n < MT; ++n)
-#pragma unroll
-            for (int ks = 0; ks < KV; ++ks) oacc[n] = mfma(sW[n * KV + ks][rd], lop[ks], oacc[n]);
-    }
+    expand();
     // All CNS sub-steps run on every trip (a count that is not a multiple ends with empty ones):
     // a path that skips some of the loads would make the compiler wait on later loads too.
     for (int it = 0; it < tiles; it += CNS) {
@@ -704,6 +682,375 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         }
 }
 
+// One workgroup of 8 waves (two per SIMD) per (sequence, head, block of 256 queries).  Starts from
+// the cached pass's state (O^T = W_up,t^V^T O_lat^T, weights and max) and runs flash attention
+// over the chunk's own tiles up to each query; normalises and stores.
+template <int D, int RV>
+__global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs a) {
+    using SH = PShape<D>;
+    constexpr int MT = SH::MT, KS = SH::KS, KV = RV / 16;
+
+    // operand slots per buffer: [0, KS) for the keys (sK), [KS, KS + 2 MT) for the values (sV)
+    __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][kSlot];
+    // W_up,t^V operands (32-dim tile n, k-step ks at slot KV n + ks), built once per workgroup
+    __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
+
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
+    const int qb = id % a.QB;
+    const int h = (id / a.QB) % a.H;
+    const int b = id / (a.QB * a.H);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int g = a.mode ? 0 : h;
+    const int col0 = a.mode ? h * D : 0;
+
+    int nn = a.n_new[b];
+    nn = nn < 0 ? 0 : (nn > a.Pn ? a.Pn : nn);
+    const int q0 = qb * CQWG;
+    if (q0 >= nn) return;                               // the whole block is past the chunk
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    const int qend = min(nn, q0 + CQWG);                 // this block's queries: [q0, qend)
+    const int wq0 = q0 + 32 * wave;                     // this wave's first query
+    const bool wlive = wq0 < qend;
+    const int iq = wq0 + l32;
+
+    uint4 qop[KS];
+    load_query_operands<D>(a, b, h, min(iq, nn - 1), h2, qop);
+
+    // ---- state after the cached tokens, parked by the cached pass in lane order: the W_up,t^V
+    // expansion's B operand (O_lat), the max and the weight sum, which also scales mu_t^V later.
+    // The sums live in the h2 = 0 lane (both lanes are added at the end); lanes of queries past
+    // the block start empty.
+    float m_run = -INFINITY, l_run = 0.f, l_lat = 0.f;
+    f32x16 oacc[MT];
+#pragma unroll
+    for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
+    uint4 lop[KV];
+#pragma unroll
+    for (int ks = 0; ks < KV; ++ks) lop[ks] = make_uint4(0u, 0u, 0u, 0u);
+    if (wlive && len > 0) {
+        float2 ml = make_float2(-INFINITY, 0.f);
+        if (iq < qend) {
+            const uint4 *st = state_row(a, b, iq, h, D);
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) lop[ks] = st[KV * h2 + ks];
+            ml = *reinterpret_cast<const float2 *>(st + 2 * KV);
+        }
+        m_run = ml.x;
+        l_run = h2 ? 0.f : ml.y;
+        l_lat = l_run;
+    }
+    if (len > 0) build_wv_operands<D, RV>(a, g, col0, wave, CWAVES, lane, sW);
+    const int rd = srow(lane);
+    // the cached part back in model space, from the shared W_up,t^V operands
+    chunk_phase<D>(a, b, h, g, col0, nn, q0, qend, sbuf, qop, oacc, m_run, l_run, l_lat,
+                   [&]() __attribute__((always_inline)) {
+                       if (wlive && len > 0) {
+#pragma unroll
+                           for (int n = 0; n < MT; ++n)
+#pragma unroll
+                               for (int ks = 0; ks < KV; ++ks)
+                                   oacc[n] = mfma(sW[n * KV + ks][rd], lop[ks], oacc[n]);
+                       }
+                   });
+}
+
+// ================================================================ wide ranks: one fused kernel
+// Key and value ranks above 32 ((32, 64), (64, 64), (64, 128), (96, 160)): a query's latent state
+// (O_lat, r_v values) no longer fits its out row, so the cached part and the chunk part run in
+// one kernel and the state stays in registers.  Same grid and waves as the two passes (8 waves of
+// 32 queries per (sequence, head, block of 256 queries)), at two waves per SIMD.
+//  * cached part, per 32-token tile: r_k / 16 score MFMAs S^T = C_k q'^T (A: the key latents from
+//    LDS in the lane order of that operand, B: q' from registers) and 2 r_v / 32 value MFMAs into
+//    the rank x query accumulators O_lat^T += C_v^T P^T.  The value latents stay token-major in
+//    LDS, in blocks of 16 tokens x 32 ranks, and come back transposed through ds_read_b64_tr_b16
+//    (lane (rank, h2) gets four tokens of its rank per read); the tokens are taken in the order
+//    the score MFMA leaves the softmax weights in (k-step kj, element e: token
+//    16 kj + 8 (e / 4) + 4 h2 + e % 4), so P^T is packed in place.
+//  * then O^T = W_up,t^V^T O_lat^T (O_lat rounded once to bf16), and the chunk part as in the
+//    two-pass form.
+template <int RK, int RV>
+struct WShape {
+    static constexpr int KK = RK / 16;                 // score k-steps
+    static constexpr int RT = RV / 32;                 // 32-rank tiles of O_lat^T
+    static constexpr int KV = RV / 16;                 // k-steps of the expansion
+    // 16-byte pieces of a 32-token tile: keys (token p % 32, ranks 8 (p / 32) ..), then values
+    static constexpr int CPK = 4 * RK, CPV = 4 * RV, CP = CPK + CPV;
+    static constexpr int VOFF = KK * kSlot;            // value blocks of a staged tile (uint4)
+    static constexpr int TILE = VOFF + 2 * RT * 64;    // uint4 per staged tile
+    static_assert(RK % 32 == 0 && RV % 32 == 0, "whole 32-rank tiles");
+};
+
+template <int D, int RK, int RV, int TS>
+__global__ __launch_bounds__(64 * PWAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_wide_kernel(PrefillArgs a) {
+    using WS = WShape<RK, RV>;
+    using SH = PShape<D>;
+    constexpr int KS = D / 16, MT = D / 32, KK = WS::KK, RT = WS::RT, KV = WS::KV;
+    constexpr int CP = WS::CP, CPK = WS::CPK, TILE = WS::TILE, VOFF = WS::VOFF;
+    constexpr int NPS = (TS * CP + 64 * PWAVES - 1) / (64 * PWAVES);   // pieces per thread and step
+    constexpr int CBUF = 2 * TS * TILE, PBUF = 2 * SH::SLOTS * kSlot;
+    static_assert(CQWG == QWG, "the chunk part serves the same queries");
+
+    // cached staging (two steps of TS tiles), later the chunk part's two tile buffers
+    __shared__ __align__(16) uint4 pool[CBUF > PBUF ? CBUF : PBUF];
+    __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
+    __shared__ int sbad[PWAVES];
+
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
+    const int qb = id % a.QB;
+    const int h = (id / a.QB) % a.H;
+    const int b = id / (a.QB * a.H);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int g = a.mode ? 0 : h;
+    const int col0 = a.mode ? h * D : 0;
+
+    int nn = a.n_new[b];
+    nn = nn < 0 ? 0 : (nn > a.Pn ? a.Pn : nn);
+    const int q0 = qb * QWG;
+    if (q0 >= nn) return;                               // the whole block is past the chunk
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    const int qend = min(nn, q0 + QWG);
+    const int wq0 = q0 + 32 * wave;
+    const bool wlive = wq0 < qend;
+    const float csc = a.scale_log2;
+    const int rd = srow(lane);
+
+    float m_run = -INFINITY, l_run = 0.f, l_lat = 0.f;
+    f32x16 oacc[MT];
+#pragma unroll
+    for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
+
+    if (len > 0) {
+        build_wv_operands<D, RV>(a, g, col0, wave, PWAVES, lane, sW);
+
+        // ---- q' = c W_up,t^K q (rank x query tiles on the matrix cores; A = the W_up,t^K rows at
+        // the query operand's dims, straight from memory) and c <q, mu_t^K>.  Tile rt leaves lane
+        // (query, h2) ranks 32 rt + 8 (v / 4) + 4 h2 + v % 4, which packs into the score MFMA's B
+        // operand (k-step ks: ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4).
+        uint4 qlat[KK];
+        float qmu;
+        {
+            uint4 qop[KS];
+            load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
+            const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
+                                 ((size_t)a.t * a.G + g) * RK * a.Dg + col0 + 4 * h2;
+#pragma unroll
+            for (int rt = 0; rt < RK / 32; ++rt) {
+                const uint16_t *wrow = Wk + (size_t)(32 * rt + l32) * a.Dg;
+                f32x16 qa = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(wrow + 16 * ks);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(wrow + 16 * ks + 8);
+                    qa = mfma(make_uint4(lo.x, lo.y, hi.x, hi.y), qop[ks], qa);
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) qa[v] *= csc;
+                qlat[2 * rt] = pack8(qa, 0);
+                qlat[2 * rt + 1] = pack8(qa, 1);
+            }
+            const float qm = query_dot_mu_k<D>(a, g, col0, h2, qop);
+            qmu = (qm + __shfl_xor(qm, 32, 64)) * csc;
+        }
+
+        // ---- step inputs.  Piece p = 64 wave + 512 x + lane of step s lies in tile TS s + p / CP
+        // (clamped to the last cached tile); p' = p % CP < CPK is key piece (token p' % 32 (clamped
+        // to the last valid token), ranks 8 (p' / 32) .. + 7), else value piece u = p' - CPK of
+        // block u / 64 = (kj RT + rt): token 16 kj + (u % 64) / 4, ranks 32 rt + 8 (u % 4) .. + 7.
+        // CP and CPK are multiples of 64, so a wave's pieces of one slot are all keys or all
+        // values of one tile: the page lookup is scalar per wave and slot.
+        const int ctiles = (len + 31) >> 5;
+        const int steps = (ctiles + TS - 1) / TS;
+        const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
+        const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
+        const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+        const int tpp = a.P >> 5;                       // tiles per page
+        const uint32_t tmag = 0xFFFFFFFFu / (uint32_t)tpp;   // tile / tpp = mulhi or one more
+        struct St {
+            uint4 r[NPS];
+            bool bad;                                   // uniform: a page id was out of range
+        };
+        bool bad_w = false;
+        auto slot_base = [&](int x) { return 64 * wave + 64 * PWAVES * x; };
+        auto issue = [&](int s, St &st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int x = 0; x < NPS; ++x) {
+                const int sp = slot_base(x);
+                if ((TS * CP) % (64 * PWAVES) != 0 && sp >= TS * CP) break;
+                const int tile = min(TS * s + sp / CP, ctiles - 1);
+                uint32_t pidx = __umulhi((uint32_t)tile, tmag);
+                int toff = tile - (int)pidx * tpp;
+                if (toff >= tpp) {
+                    toff -= tpp;
+                    ++pidx;
+                }
+                int page = bt[pidx];
+                const bool ok = (unsigned)page < (unsigned)a.n_pages;
+                st.bad |= !ok;
+                page = ok ? page : 0;
+                const int row = (page * a.G + g) * a.P + 32 * toff;
+                const int lim = len - 1 - 32 * tile;
+                const int pc = sp % CP + lane;
+                const uint16_t *src;
+                if (sp % CP < CPK) {
+                    src = kp + (size_t)(row + min(pc & 31, lim)) * RK + 8 * (pc >> 5);
+                } else {
+                    const int u = pc - CPK, bi = u >> 6, w = u & 63;
+                    const int tok = 16 * (bi / RT) + (w >> 2), c8 = 4 * (bi % RT) + (w & 3);
+                    src = vp + (size_t)(row + min(tok, lim)) * RV + 8 * c8;
+                }
+                st.r[x] = *reinterpret_cast<const uint4 *>(src);
+            }
+        };
+        // ---- step s's pieces into LDS buffer `buf`.  Key piece (token j, ranks 8c .. 8c + 7):
+        // ranks 8c + 4 hh + {0..3} are elements 4 (c % 2) .. + 3 of lane (j, hh) in k-step c / 2
+        // (padded operand slots); value pieces keep their place in the 1 KB block.
+        auto produce = [&](int s, St &st, int buf) __attribute__((always_inline)) {
+            if (s >= steps) return;
+            bad_w |= st.bad;
+            st.bad = false;
+#pragma unroll
+            for (int x = 0; x < NPS; ++x) {
+                const int sp = slot_base(x);
+                if ((TS * CP) % (64 * PWAVES) != 0 && sp >= TS * CP) break;
+                uint4 *T = pool + (buf * TS + sp / CP) * TILE;
+                const int pc = sp % CP + lane;
+                const uint4 w = st.r[x];
+                if (sp % CP < CPK) {
+                    const int j = pc & 31, c8 = pc >> 5;
+                    uint2 *d0 = reinterpret_cast<uint2 *>(&T[(c8 >> 1) * kSlot + srow(j)]) + (c8 & 1);
+                    uint2 *d1 =
+                        reinterpret_cast<uint2 *>(&T[(c8 >> 1) * kSlot + srow(32 + j)]) + (c8 & 1);
+                    *d0 = make_uint2(w.x, w.y);
+                    *d1 = make_uint2(w.z, w.w);
+                } else {
+                    T[VOFF + pc - CPK] = w;
+                }
+            }
+        };
+
+        // ---- online softmax over the cached tiles (log2 domain, scores relative to c <q, mu_t^K>,
+        // which is the same for every cached token and joins the reference at the end), lazy
+        // rescale
+        f32x16 olat[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) olat[rt] = f32x16{};
+        float m_lat = -INFINITY, l_sum = 0.f;
+        // transposed reads: lane (4 e' + m) of each 16-lane group addresses token 4 h2 + e' (+ 8
+        // for the second read) of the block at ranks 16 ((lane / 16) % 2) + 4 m .. + 3, and lane
+        // l gets rank l % 32 of those four tokens
+        const uint32_t vrd =
+            (uint32_t)(((4 * h2 + ((lane & 15) >> 2)) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+        auto consume = [&](int s, int buf) __attribute__((always_inline)) {
+            if (!wlive || s >= steps) return;
+            const int nt = min(TS, ctiles - TS * s);
+            for (int j = 0; j < nt; ++j) {
+                const uint4 *T = pool + (buf * TS + j) * TILE;
+                const int j0 = 32 * (TS * s + j);
+                f32x16 sc = {};
+#pragma unroll
+                for (int ks = 0; ks < KK; ++ks) sc = mfma(T[ks * kSlot + rd], qlat[ks], sc);
+                // the last tile masks tokens past len.  Lane (query, h2), element v: token
+                // 8 (v / 4) + 4 h2 + v % 4.
+                if (j0 + 32 > len) {
+                    const int lm = len - 1 - j0 - 4 * h2;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (8 * (v >> 2) + (v & 3) > lm) sc[v] = -INFINITY;
+                }
+                float mx = sc[0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+                mx = max_swap32(mx);
+                const float m_cand = fmaxf(m_lat, mx);
+                if (__builtin_amdgcn_ballot_w64(m_cand > m_lat + kSlack) != 0) {
+                    const float alpha = m_cand == -INFINITY ? 1.f : exp2_(m_lat - m_cand);
+                    l_sum *= alpha;
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) olat[rt][v] *= alpha;
+                    m_lat = m_cand;
+                }
+                f32x16 pr;
+                float ls = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    pr[v] = exp2_(sc[v] - m_lat);
+                    ls += pr[v];
+                }
+                l_sum += ls;
+                const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
+                lds_char *vb = (lds_char *)(T + VOFF) + vrd;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int kj = 0; kj < 2; ++kj) {
+                        lds_char *blk = vb + 1024 * (kj * RT + rt);
+                        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)blk);
+                        const s16x4 r1 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(blk + 512));
+                        const uint4 va = make_uint4(pk16(r0[0], r0[1]), pk16(r0[2], r0[3]),
+                                                    pk16(r1[0], r1[1]), pk16(r1[2], r1[3]));
+                        olat[rt] = mfma(va, kj ? p1 : p0, olat[rt]);
+                    }
+            }
+        };
+
+        // ---- pipeline: step i + 1 produced while step i is consumed; step i + 2's inputs in
+        // flight
+        St s0, s1;
+        s0.bad = s1.bad = false;
+        issue(0, s0);
+        issue(1, s1);
+        produce(0, s0, 0);
+        issue(2, s0);
+        __syncthreads();
+        for (int it = 0; it < steps; it += 2) {
+            produce(it + 1, s1, 1);
+            issue(it + 3, s1);
+            consume(it, 0);
+            __syncthreads();
+            produce(it + 2, s0, 0);
+            issue(it + 4, s0);
+            consume(it + 1, 1);
+            __syncthreads();
+        }
+        // an out-of-range page id anywhere in the cached context makes the outputs NaN
+        if (lane == 0) sbad[wave] = bad_w;
+        __syncthreads();
+        bool bad_any = false;
+#pragma unroll
+        for (int w = 0; w < PWAVES; ++w) bad_any |= sbad[w] != 0;
+
+        // ---- the cached part in model space: O^T = W_up,t^V^T O_lat^T
+        if (wlive) {
+            uint4 lop[KV];
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) lop[ks] = pack8(olat[ks >> 1], ks & 1);
+#pragma unroll
+            for (int n = 0; n < MT; ++n)
+#pragma unroll
+                for (int ks = 0; ks < KV; ++ks) oacc[n] = mfma(sW[n * KV + ks][rd], lop[ks], oacc[n]);
+        }
+        m_run = m_lat + qmu;
+        l_run = bad_any ? __builtin_nanf("") : l_sum;
+        l_lat = l_run;
+    }
+
+    uint4 qop[KS];
+    load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
+    auto &sbuf = *reinterpret_cast<uint4 (*)[2][SH::SLOTS][kSlot]>(pool);
+    chunk_phase<D>(a, b, h, g, col0, nn, q0, qend, sbuf, qop, oacc, m_run, l_run, l_lat,
+                   []() {});
+}
+
 template <int D, int RK, int RV>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.QB;
@@ -717,11 +1064,27 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+#ifndef PREFILL_WIDE_TS
+#define PREFILL_WIDE_TS 1
+#endif
+
+template <int D, int RK, int RV>
+hipError_t launch_wide(const PrefillArgs &a, hipStream_t st) {
+    const unsigned blocks = (unsigned)a.B * a.H * a.QB;
+    hipLaunchKernelGGL((prefill_wide_kernel<D, RK, RV, PREFILL_WIDE_TS>), dim3(blocks),
+                       dim3(64 * PWAVES), 0, st, a);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
     if (a.r_k == 16 && a.r_v == 16) return launch_t<D, 16, 16>(a, st);
     if (a.r_k == 16 && a.r_v == 32) return launch_t<D, 16, 32>(a, st);
     if (a.r_k == 32 && a.r_v == 32) return launch_t<D, 32, 32>(a, st);
+    if (a.r_k == 32 && a.r_v == 64) return launch_wide<D, 32, 64>(a, st);
+    if (a.r_k == 64 && a.r_v == 64) return launch_wide<D, 64, 64>(a, st);
+    if (a.r_k == 64 && a.r_v == 128) return launch_wide<D, 64, 128>(a, st);
+    if (a.r_k == 96 && a.r_v == 160) return launch_wide<D, 96, 160>(a, st);
     return hipErrorInvalidValue;
 }
 
@@ -731,7 +1094,8 @@ int prefill_queries_per_block() { return QWG; }
 
 bool prefill_supported(int d, int r_k, int r_v) {
     if (d != 64 && d != 128) return false;
-    return (r_k == 16 && (r_v == 16 || r_v == 32)) || (r_k == 32 && r_v == 32);
+    return (r_k == 16 && (r_v == 16 || r_v == 32)) || (r_k == 32 && (r_v == 32 || r_v == 64)) ||
+           (r_k == 64 && (r_v == 64 || r_v == 128)) || (r_k == 96 && r_v == 160);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {

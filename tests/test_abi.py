@@ -247,7 +247,8 @@ def test_prefill_validation_without_launch():
                                   ctypes.byref(cache_ or cache), t, chunk, n_new, q, FAKE, FAKE,
                                   stride, 0.1, FAKE, None)
     assert call(lla.make_codec(0, 4, 16, 128, 16, 32, lla.LLA_F32)) == lla.LLA_ERR_DTYPE
-    assert call(lla.make_codec(0, 4, 16, 128, 96, 160, lla.LLA_BF16)) == lla.LLA_ERR_UNSUPPORTED
+    assert call(lla.make_codec(0, 4, 16, 128, 96, 128, lla.LLA_BF16)) == lla.LLA_ERR_UNSUPPORTED
+    assert call(lla.make_codec(0, 4, 16, 128, 32, 128, lla.LLA_BF16)) == lla.LLA_ERR_UNSUPPORTED
     assert call(n_new=None) == lla.LLA_ERR_NULL
     assert call(t=4) == lla.LLA_ERR_SHAPE
     assert call(chunk=-1) == lla.LLA_ERR_SHAPE

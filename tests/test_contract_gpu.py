@@ -67,18 +67,20 @@ def test_bad_page_ids_poison_only_their_sequence(gpu, kind):
     assert _same(got[[0, 2]], clean[[0, 2]]), "other sequences changed"
 
 
-def test_bad_page_ids_in_prefill(gpu):
-    cfg = synth.CONFIGS["ouro14_21x"]
+@pytest.mark.parametrize("codec", ["ouro14_21x", "ouro14_4x"])
+def test_bad_page_ids_in_prefill(gpu, codec):
+    """Two passes (ranks up to 32) and the fused kernel (96 / 160)."""
+    cfg = synth.CONFIGS[codec]
     lens, n_new = [200, 150, 90, 64], [70, 50, 0, 33]
     ch = Chunk(cfg, B=4, N=200, Pn=70, lens=lens, n_new=n_new, gpu=gpu)
     P, t = ch.cfg.page, 1
-    say("bad pages prefill: clean run")
+    say(f"bad pages prefill {codec}: clean run")
     clean = ch.run(t)
     bt0 = ch.dp.block_table.clone()
     ch.dp.block_table[1, 1] = ch.p.n_pages                  # inside the cached context
     ch.dp.block_table[2, 0] = -1                            # a sequence with an empty chunk
     ch.dp.block_table[3, (lens[3] + n_new[3]) // P + 1] = -3   # past the chunk's positions
-    say("bad pages prefill: poisoned table")
+    say(f"bad pages prefill {codec}: poisoned table")
     got = ch.run(t)
     ch.dp.block_table.copy_(bt0)
     assert np.all(np.isnan(got[1, :n_new[1]])), "bad page did not poison"
@@ -286,4 +288,37 @@ def test_graph_replay_of_absorbed_2d(gpu):
         torch.cuda.synchronize()
         assert _same(synth.from_device(out), ref), f"replay {rep} differs from eager"
         dp.layer.decode(0, dp.q[0], out, ws, dp.x_k[:, 0], dp.x_v[:, 0], stride)   # eager work
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_of_wide_prefill(gpu):
+    """The fused prefill kernel of the wide ranks (LLA-2D, 96 / 160) captured once gives bitwise
+    its eager result on every replay."""
+    cfg = synth.CONFIGS["ouro26_2d_64x"]
+    ch = Chunk(cfg, B=3, N=300, Pn=90, lens=[300, 45, 0], n_new=[90, 33, 60], gpu=gpu)
+    t = 2
+    out = torch.empty((3, ch.Pn, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
+    kn, vn, stride = ch.xkd[:, :, t], ch.xvd[:, :, t], cfg.T * cfg.H * cfg.d
+
+    def work():
+        ch.dp.layer.prefill(t, ch.Pn, ch.nd, ch.qd[t], kn, vn, out, new_stride=stride)
+
+    say("wide prefill graph: eager reference")
+    out.fill_(float("nan"))
+    work()
+    torch.cuda.synchronize()
+    ref = synth.from_device(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"wide prefill graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(synth.from_device(out), ref), f"replay {rep} differs from eager"
+        ch.dp.layer.prefill(0, ch.Pn, ch.nd, ch.qd[0], ch.xkd[:, :, 0], ch.xvd[:, :, 0], out,
+                            new_stride=stride)               # eager work between replays
         torch.cuda.synchronize()

@@ -151,36 +151,43 @@ class NeedleChunk(Chunk):
         torch.cuda.synchronize()
 
 
-def test_prefill_needles_cached_pass(gpu):
+PREFILL_CODECS = ["ouro14_21x", "ouro14_4x"]    # two passes (r <= 32); fused kernel (96 / 160)
+
+
+@pytest.mark.parametrize("codec", PREFILL_CODECS)
+def test_prefill_needles_cached_pass(gpu, codec):
     """Needles in the cached context (latents) at tile edges 31/32, 256-token step edges 255/256,
     the first and the last cached token; each aimed at one query row of the chunk."""
+    cfg = synth.CONFIGS[codec]
     t = 2
     lens = [300, 300, 300, 300, 257, 300]
     pos = [0, 31, 32, 255, 256, 299]
     aim = [0, 5, 63, 64, 1, 100]                       # query row each needle is aimed at
-    ch = NeedleChunk(CFG, len(lens), 300, 128, lens, [128] * len(lens), gpu, q_gain=8.0)
+    ch = NeedleChunk(cfg, len(lens), 300, 128, lens, [128] * len(lens), gpu, q_gain=8.0)
     ch.saved = (ch.p.k_pool.copy(), ch.xk.copy())
     for b in range(len(lens)):
         _plant(ch.p, t, b, pos[b], ch.q[t][b, aim[b]])
     ch.upload()
-    say(f"prefill cached-pass needles at {pos}")
+    say(f"prefill {codec} cached-pass needles at {pos}")
     ref = ch.oracle(t)
     _prefill_power(ch, t, list(enumerate(aim)), ref, "cached pass")
     ch.check(ch.run(t), ref, "prefill cached-pass needles")
 
 
-def test_prefill_needles_chunk_pass(gpu):
+@pytest.mark.parametrize("codec", PREFILL_CODECS)
+def test_prefill_needles_chunk_pass(gpu, codec):
     """Needles among the chunk's own keys at chunk positions 0, 31, 32, 255, 256 and the last live
     row, each aimed at the query on the causal diagonal (it must be seen) and, in a second
     sequence, at the query just before it (it must not be)."""
+    cfg = synth.CONFIGS[codec]
     t = 1
     Pn = 300
     pos = [0, 31, 32, 255, 256, 299]
     B = 2 * len(pos)
     lens = [200] * B
-    ch = NeedleChunk(CFG, B, 200, Pn, lens, [Pn] * B, gpu, q_gain=8.0)
+    ch = NeedleChunk(cfg, B, 200, Pn, lens, [Pn] * B, gpu, q_gain=8.0)
     ch.saved = (ch.p.k_pool.copy(), ch.xk.copy())
-    scale = 1.0 / np.sqrt(CFG.d)
+    scale = 1.0 / np.sqrt(cfg.d)
     seen = []
     for k, i0 in enumerate(pos):
         for b, i1 in ((2 * k, i0), (2 * k + 1, max(i0 - 1, 0))):
@@ -189,13 +196,13 @@ def test_prefill_needles_chunk_pass(gpu):
             qa = ch.q[t][b, i1]                           # [H][d]
             n = np.linalg.norm(qa, axis=-1, keepdims=True)
             # every other score of row i1 is at most scale |q| |k|; beat it by MARGIN
-            kmax = np.abs(ch.xk[b, :, t]).max() * np.sqrt(CFG.d)
+            kmax = np.abs(ch.xk[b, :, t]).max() * np.sqrt(cfg.d)
             alpha = (MARGIN + scale * n * kmax + 50.0) / (scale * n)
             ch.xk[b, i0, t] = synth.quantize(alpha * qa / n, "bf16")
             if b == 2 * k:
                 seen.append((b, i1))
     ch.upload()
-    say(f"prefill chunk-pass needles at {pos}")
+    say(f"prefill {codec} chunk-pass needles at {pos}")
     ref = ch.oracle(t)
     _prefill_power(ch, t, seen, ref, "chunk pass")
     ch.check(ch.run(t), ref, "prefill chunk-pass needles")

@@ -4,8 +4,9 @@ through the C ABI, against the fp64 oracle on seeded inputs.
 Bar (as for decode): bf16 max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3 over the live rows; rows
 past a sequence's chunk size must stay untouched.  Small cases span two query blocks of 256,
 several 32-token tiles of cached context and of chunk, ragged tails, empty contexts and empty
-chunks; the full-size case runs the benchmark's launch (32 sequences x 4096 cached tokens, a
-chunk of 512) and checks sampled sequences.
+chunks, for every (d, r_k, r_v) the library accepts: the two-pass kernels of ranks up to 32 and
+the fused kernel of the wider pairs, per-head and LLA-2D.  The full-size cases run the benchmark's
+launch (the codec's batch x 4096 cached tokens, a chunk of 512) and check sampled sequences.
 """
 import sys
 
@@ -40,6 +41,25 @@ SHAPES = {
                                    cid=143),
     "h2_d64_r32_32": synth.Config("pf_d64_r32", L=1, H=2, d=64, T=4, r_k=32, r_v=32, B=1, N=1,
                                   cid=144),
+    # the fused kernel of the wider rank pairs
+    "h2_d128_r96_160": synth.Config("pf_d128_r96", L=1, H=2, d=128, T=4, r_k=96, r_v=160, B=1,
+                                    N=1, cid=145),
+    "h4_d128_2d_r96_160": synth.Config("pf_2d_r96", L=1, H=4, d=128, T=2, r_k=96, r_v=160, B=1,
+                                       N=1, mode=1, cid=146),
+    "h2_d64_r96_160": synth.Config("pf_d64_r96", L=1, H=2, d=64, T=3, r_k=96, r_v=160, B=1, N=1,
+                                   cid=147),
+    "h2_d128_r32_64": synth.Config("pf_d128_r32_64", L=1, H=2, d=128, T=4, r_k=32, r_v=64, B=1,
+                                   N=1, cid=148),
+    "h3_d64_2d_r32_64": synth.Config("pf_d64_2d_r32_64", L=1, H=3, d=64, T=2, r_k=32, r_v=64,
+                                     B=1, N=1, mode=1, cid=149),
+    "h2_d128_2d_r64_64": synth.Config("pf_d128_2d_r64", L=1, H=2, d=128, T=4, r_k=64, r_v=64,
+                                      B=1, N=1, mode=1, cid=150),
+    "h2_d64_r64_64": synth.Config("pf_d64_r64", L=1, H=2, d=64, T=4, r_k=64, r_v=64, B=1, N=1,
+                                  cid=151),
+    "h2_d128_r64_128": synth.Config("pf_d128_r64_128", L=1, H=2, d=128, T=3, r_k=64, r_v=128,
+                                    B=1, N=1, cid=152),
+    "h2_d64_r64_128": synth.Config("pf_d64_r64_128", L=1, H=2, d=64, T=4, r_k=64, r_v=128, B=1,
+                                   N=1, cid=153),
 }
 
 
@@ -57,9 +77,11 @@ def test_prefill_small(gpu, shape):
             ch.check(ch.run(t, strided), ch.oracle(t), f"{shape} t={t}")
 
 
+@pytest.mark.parametrize("codec", ["ouro14_21x", "ouro14_4x"])
 @pytest.mark.parametrize("variant", ["peaked", "long_context", "tiny_chunks"])
-def test_prefill_variants(gpu, variant):
-    cfg = SHAPES["ouro14_21x"]
+def test_prefill_variants(gpu, variant, codec):
+    """The headline codec (two passes) and the 4x codec (ranks 96 / 160: the fused kernel)."""
+    cfg = synth.CONFIGS[codec]
     if variant == "peaked":            # sharp softmax: q x 8
         ch = Chunk(cfg, 2, 500, 64, [500, 31], [64, 33], gpu, q_gain=8.0)
     elif variant == "long_context":    # context much longer than the chunk
@@ -67,8 +89,8 @@ def test_prefill_variants(gpu, variant):
     else:                              # one-token and two-token chunks, empty context
         ch = Chunk(cfg, 4, 70, 2, [0, 70, 1, 33], [1, 2, 2, 1], gpu)
     t = cfg.T - 1
-    say(f"prefill {variant}")
-    ch.check(ch.run(t), ch.oracle(t), variant)
+    say(f"prefill {codec} {variant}")
+    ch.check(ch.run(t), ch.oracle(t), f"{codec} {variant}")
 
 
 def test_prefill_single_token_chunk_matches_decode(gpu):
@@ -138,10 +160,12 @@ def test_encode_chunk_row_streaming(gpu):
                         [512, 0, 512, 300, 7, 511, 512, 64])
 
 
-def test_prefill_bench_shape_sampled(gpu):
-    """The benchmark's launch: 32 sequences x 4096 cached tokens, a chunk of 512, all 16 heads;
-    the oracle checks three sampled sequences."""
-    cfg = synth.CONFIGS["ouro14_21x"]
+@pytest.mark.parametrize("codec", ["ouro14_21x", "ouro14_4x", "ouro26_2d_64x"])
+def test_prefill_bench_shape_sampled(gpu, codec):
+    """The benchmark's launch on each codec it times prefill for: the codec's batch x 4096 cached
+    tokens, a chunk of 512, all 16 heads (per-head codecs at ranks 16 / 32 and 96 / 160, and the
+    LLA-2D codec); the oracle checks three sampled sequences."""
+    cfg = synth.CONFIGS[codec]
     B, N, Pn = cfg.B, cfg.N, 512
     cfgp = synth.scaled(cfg, N=N + Pn)
     max_pages = cfgp.max_pages
@@ -153,8 +177,8 @@ def test_prefill_bench_shape_sampled(gpu):
     bt = synth.block_table(cfgp, B, max_pages)
     lens = synth.seq_lens(cfg, B, N)
     up = lambda a: synth.to_device(a, "bf16", gpu)
-    codec = lla.make_codec(0, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
-    layer = LatentLayer(codec, up(Wdk), up(Wdv), up(Wuk), up(Wuv), up(muk), up(muv), kpool, vpool,
+    cd = lla.make_codec(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
+    layer = LatentLayer(cd, up(Wdk), up(Wdv), up(Wuk), up(Wuv), up(muk), up(muv), kpool, vpool,
                         torch.from_numpy(bt).to(gpu), torch.from_numpy(lens).to(gpu), cfg.page, N)
     t = cfg.T - 1
     q = synth.chunk_queries(cfg, 0, t, B, Pn)
@@ -163,7 +187,7 @@ def test_prefill_bench_shape_sampled(gpu):
     n_new = np.full(B, Pn, dtype=np.int32)
     xkd, xvd = up(xk), up(xv)
     out = torch.empty((B, Pn, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
-    say(f"prefill full size B={B} N={N} Pn={Pn}")
+    say(f"prefill full size {codec} B={B} N={N} Pn={Pn}")
     layer.prefill(t, Pn, torch.from_numpy(n_new).to(gpu), up(q), xkd[:, :, t], xvd[:, :, t], out,
                   new_stride=cfg.T * cfg.H * cfg.d)
     torch.cuda.synchronize()
@@ -177,6 +201,6 @@ def test_prefill_bench_shape_sampled(gpu):
     kp = synth.from_device(kpool.index_select(0, idx))
     vp = synth.from_device(vpool.index_select(0, idx))
     say(f"prefill full size: oracle on sequences {sel}")
-    ref = O.prefill(0, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, Wuk, Wuv, muk, muv, kp, vp, bt2,
+    ref = O.prefill(cfg.mode, cfg.T, cfg.H, cfg.d, cfg.r_k, cfg.r_v, t, Wuk, Wuv, muk, muv, kp, vp, bt2,
                     lens[sel], cfg.page, q[sel], xk[sel][:, :, t], xv[sel][:, :, t], n_new[sel])
-    assert_close(got[sel], ref, "bf16", "prefill full size")
+    assert_close(got[sel], ref, "bf16", f"prefill full size {codec}")
