@@ -783,21 +783,25 @@ struct WShape {
     static_assert(RK % 32 == 0 && RV % 32 == 0, "whole 32-rank tiles");
 };
 
-template <int D, int RK, int RV, int TS>
+template <int D, int RK, int RV>
 __global__ __launch_bounds__(64 * PWAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_wide_kernel(PrefillArgs a) {
     using WS = WShape<RK, RV>;
     using SH = PShape<D>;
     constexpr int KS = D / 16, MT = D / 32, KK = WS::KK, RT = WS::RT, KV = WS::KV;
     constexpr int CP = WS::CP, CPK = WS::CPK, TILE = WS::TILE, VOFF = WS::VOFF;
-    constexpr int NPS = (TS * CP + 64 * PWAVES - 1) / (64 * PWAVES);   // pieces per thread and step
-    constexpr int CBUF = 2 * TS * TILE, PBUF = 2 * SH::SLOTS * kSlot;
+    constexpr int NPS = (CP + 64 * PWAVES - 1) / (64 * PWAVES);   // pieces per thread and tile
+    constexpr int CBUF = 3 * TILE, PBUF = 2 * SH::SLOTS * kSlot;
     static_assert(CQWG == QWG, "the chunk part serves the same queries");
 
-    // cached staging (two steps of TS tiles), later the chunk part's two tile buffers
-    __shared__ __align__(16) uint4 pool[CBUF > PBUF ? CBUF : PBUF];
-    __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
+    // one LDS array: at its start the cached staging (three tile buffers), later the chunk
+    // part's two tile buffers (the cached part's reads then take immediate offsets), then the
+    // W_up,t^V operands
+    constexpr int CB = CBUF > PBUF ? CBUF : PBUF;
+    __shared__ __align__(16) uint4 lds[CB + MT * KV * kSlot];
     __shared__ int sbad[PWAVES];
+    uint4 *const pool = lds;
+    uint4 (*const sW)[kSlot] = reinterpret_cast<uint4 (*)[kSlot]>(lds + CB);
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -859,14 +863,12 @@ void prefill_wide_kernel(PrefillArgs a) {
             qmu = (qm + __shfl_xor(qm, 32, 64)) * csc;
         }
 
-        // ---- step inputs.  Piece p = 64 wave + 512 x + lane of step s lies in tile TS s + p / CP
-        // (clamped to the last cached tile); p' = p % CP < CPK is key piece (token p' % 32 (clamped
-        // to the last valid token), ranks 8 (p' / 32) .. + 7), else value piece u = p' - CPK of
-        // block u / 64 = (kj RT + rt): token 16 kj + (u % 64) / 4, ranks 32 rt + 8 (u % 4) .. + 7.
-        // CP and CPK are multiples of 64, so a wave's pieces of one slot are all keys or all
-        // values of one tile: the page lookup is scalar per wave and slot.
+        // ---- tile inputs.  Piece p = 64 wave + 512 x + lane of tile n (clamped to the last cached
+        // tile): p < CPK is key piece (token p % 32 (clamped to the last valid token), ranks
+        // 8 (p / 32) .. + 7), else value piece u = p - CPK of block u / 64 = (kj RT + rt): token
+        // 16 kj + (u % 64) / 4, ranks 32 rt + 8 (u % 4) .. + 7.  CPK is a multiple of 64, so a
+        // wave's pieces of one slot are all keys or all values; the page lookup is scalar.
         const int ctiles = (len + 31) >> 5;
-        const int steps = (ctiles + TS - 1) / TS;
         const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
         const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
         const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
@@ -878,27 +880,27 @@ void prefill_wide_kernel(PrefillArgs a) {
         };
         bool bad_w = false;
         auto slot_base = [&](int x) { return 64 * wave + 64 * PWAVES * x; };
-        auto issue = [&](int s, St &st) __attribute__((always_inline)) {
+        auto issue = [&](int n, St &st) __attribute__((always_inline)) {
+            const int tile = min(n, ctiles - 1);
+            uint32_t pidx = __umulhi((uint32_t)tile, tmag);
+            int toff = tile - (int)pidx * tpp;
+            if (toff >= tpp) {
+                toff -= tpp;
+                ++pidx;
+            }
+            int page = bt[pidx];
+            const bool ok = (unsigned)page < (unsigned)a.n_pages;
+            st.bad |= !ok;
+            page = ok ? page : 0;
+            const int row = (page * a.G + g) * a.P + 32 * toff;
+            const int lim = len - 1 - 32 * tile;
 #pragma unroll
             for (int x = 0; x < NPS; ++x) {
                 const int sp = slot_base(x);
-                if ((TS * CP) % (64 * PWAVES) != 0 && sp >= TS * CP) break;
-                const int tile = min(TS * s + sp / CP, ctiles - 1);
-                uint32_t pidx = __umulhi((uint32_t)tile, tmag);
-                int toff = tile - (int)pidx * tpp;
-                if (toff >= tpp) {
-                    toff -= tpp;
-                    ++pidx;
-                }
-                int page = bt[pidx];
-                const bool ok = (unsigned)page < (unsigned)a.n_pages;
-                st.bad |= !ok;
-                page = ok ? page : 0;
-                const int row = (page * a.G + g) * a.P + 32 * toff;
-                const int lim = len - 1 - 32 * tile;
-                const int pc = sp % CP + lane;
+                if (CP % (64 * PWAVES) != 0 && sp >= CP) break;
+                const int pc = sp + lane;
                 const uint16_t *src;
-                if (sp % CP < CPK) {
+                if (sp < CPK) {
                     src = kp + (size_t)(row + min(pc & 31, lim)) * RK + 8 * (pc >> 5);
                 } else {
                     const int u = pc - CPK, bi = u >> 6, w = u & 63;
@@ -908,21 +910,21 @@ void prefill_wide_kernel(PrefillArgs a) {
                 st.r[x] = *reinterpret_cast<const uint4 *>(src);
             }
         };
-        // ---- step s's pieces into LDS buffer `buf`.  Key piece (token j, ranks 8c .. 8c + 7):
+        // ---- tile n's pieces into LDS tile buffer `buf` (past the last tile: a copy of it, unused).
+        // Key piece (token j, ranks 8c .. 8c + 7):
         // ranks 8c + 4 hh + {0..3} are elements 4 (c % 2) .. + 3 of lane (j, hh) in k-step c / 2
         // (padded operand slots); value pieces keep their place in the 1 KB block.
-        auto produce = [&](int s, St &st, int buf) __attribute__((always_inline)) {
-            if (s >= steps) return;
+        auto produce = [&](int n, St &st, int buf) __attribute__((always_inline)) {
             bad_w |= st.bad;
             st.bad = false;
+            uint4 *T = pool + buf * TILE;
 #pragma unroll
             for (int x = 0; x < NPS; ++x) {
                 const int sp = slot_base(x);
-                if ((TS * CP) % (64 * PWAVES) != 0 && sp >= TS * CP) break;
-                uint4 *T = pool + (buf * TS + sp / CP) * TILE;
-                const int pc = sp % CP + lane;
+                if (CP % (64 * PWAVES) != 0 && sp >= CP) break;
+                const int pc = sp + lane;
                 const uint4 w = st.r[x];
-                if (sp % CP < CPK) {
+                if (sp < CPK) {
                     const int j = pc & 31, c8 = pc >> 5;
                     uint2 *d0 = reinterpret_cast<uint2 *>(&T[(c8 >> 1) * kSlot + srow(j)]) + (c8 & 1);
                     uint2 *d1 =
@@ -935,92 +937,167 @@ void prefill_wide_kernel(PrefillArgs a) {
             }
         };
 
-        // ---- online softmax over the cached tiles (log2 domain, scores relative to c <q, mu_t^K>,
-        // which is the same for every cached token and joins the reference at the end), lazy
-        // rescale
+        // ---- online softmax over the cached tiles (log2 domain; scores relative to c <q, mu_t^K>,
+        // which is the same for every cached token and joins the reference at the end).  Lazy
+        // rescale guarded by the weight sums: m_lat is the first tile's max and moves (to a tile's
+        // max) only when a lane's weights of one tile sum past 2^32 (an overflowed weight
+        // included); that tile's weights are then recomputed, so no weight the accumulators take
+        // exceeds 2^32 and the result is exact after the final normalisation.  The sums are taken
+        // from the rounded bf16 weights the value MFMAs use.
+        constexpr float kSumMax = 4294967296.f;         // 2^32
         f32x16 olat[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) olat[rt] = f32x16{};
-        float m_lat = -INFINITY, l_sum = 0.f;
+        float m_lat = 0.f, l_sum = 0.f;
+        bool started = false;                           // uniform: m_lat has been set
         // transposed reads: lane (4 e' + m) of each 16-lane group addresses token 4 h2 + e' (+ 8
         // for the second read) of the block at ranks 16 ((lane / 16) % 2) + 4 m .. + 3, and lane
         // l gets rank l % 32 of those four tokens
         const uint32_t vrd =
             (uint32_t)(((4 * h2 + ((lane & 15) >> 2)) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
-        auto consume = [&](int s, int buf) __attribute__((always_inline)) {
-            if (!wlive || s >= steps) return;
-            const int nt = min(TS, ctiles - TS * s);
-            for (int j = 0; j < nt; ++j) {
-                const uint4 *T = pool + (buf * TS + j) * TILE;
-                const int j0 = 32 * (TS * s + j);
-                f32x16 sc = {};
+        // move the reference to the tile's max (both lanes of a query agree); first: no history
+        auto rebase = [&](const f32x16 &sc, bool first) __attribute__((always_inline)) {
+            float mx = sc[0];
 #pragma unroll
-                for (int ks = 0; ks < KK; ++ks) sc = mfma(T[ks * kSlot + rd], qlat[ks], sc);
-                // the last tile masks tokens past len.  Lane (query, h2), element v: token
-                // 8 (v / 4) + 4 h2 + v % 4.
-                if (j0 + 32 > len) {
-                    const int lm = len - 1 - j0 - 4 * h2;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (8 * (v >> 2) + (v & 3) > lm) sc[v] = -INFINITY;
-                }
-                float mx = sc[0];
-#pragma unroll
-                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-                mx = max_swap32(mx);
-                const float m_cand = fmaxf(m_lat, mx);
-                if (__builtin_amdgcn_ballot_w64(m_cand > m_lat + kSlack) != 0) {
-                    const float alpha = m_cand == -INFINITY ? 1.f : exp2_(m_lat - m_cand);
-                    l_sum *= alpha;
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) olat[rt][v] *= alpha;
-                    m_lat = m_cand;
-                }
-                f32x16 pr;
-                float ls = 0.f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    pr[v] = exp2_(sc[v] - m_lat);
-                    ls += pr[v];
-                }
-                l_sum += ls;
-                const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
-                lds_char *vb = (lds_char *)(T + VOFF) + vrd;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int kj = 0; kj < 2; ++kj) {
-                        lds_char *blk = vb + 1024 * (kj * RT + rt);
-                        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)blk);
-                        const s16x4 r1 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(blk + 512));
-                        const uint4 va = make_uint4(pk16(r0[0], r0[1]), pk16(r0[2], r0[3]),
-                                                    pk16(r1[0], r1[1]), pk16(r1[2], r1[3]));
-                        olat[rt] = mfma(va, kj ? p1 : p0, olat[rt]);
-                    }
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+            mx = max_swap32(mx);
+            if (!(mx > -INFINITY)) return;              // all masked (or NaN): keep m_lat
+            if (first) {
+                m_lat = mx;
+                return;
             }
+            if (!(mx > m_lat)) return;
+            const float alpha = exp2_(m_lat - mx);
+            l_sum *= alpha;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) olat[rt][v] *= alpha;
+            m_lat = mx;
+        };
+        const uint32_t one2 = 0x3F803F80u;              // two bf16 ones
+        auto wsum = [&](const uint4 &p0, const uint4 &p1) __attribute__((always_inline)) {
+            const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]),
+                                                      __builtin_bit_cast(bf16x2, one2), acc, false);
+            return acc;
+        };
+        // score MFMAs of the tile in buffer `buf` (raw latent scores S^T, lane (query, h2))
+        auto score = [&](int buf) __attribute__((always_inline)) {
+            const uint4 *T = pool + buf * TILE;
+            uint4 ka[KK];
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) ka[ks] = T[ks * kSlot + rd];
+            f32x16 sc = {};
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) sc = mfma(ka[ks], qlat[ks], sc);
+            return sc;
+        };
+        // Tile n (buffer `buf`), whose scores `scn` holds, then the inputs of tile n + 2 (into
+        // buffer `pbuf`, from stage set `st`) and the loads of tile n + 4 (into `st`).  After two
+        // rare uniform branches (the last tile's mask, the first tile's reference) the step is two
+        // branch-free scheduling regions whose MFMAs are fenced between the other instructions:
+        //  1. tile n + 1's key operands and tile n's value operands from LDS, tile n + 1's score
+        //     MFMAs, each followed by its share of tile n's softmax;
+        //  2. tile n's value MFMAs in pairs (block kj RT + rt holds tokens 16 kj .. + 15 of ranks
+        //     32 rt .. + 31), tile n + 2's LDS writes and tile n + 4's loads between them.
+        // (The interleave measures the same as clumped MFMAs: what bounds a tile is the burst of
+        // LDS reads all eight waves issue after the barrier, not issue order.)
+        // Every wave runs every step (a wave whose queries are all past the chunk computes on
+        // the chunk's last query and discards the result); the score MFMAs past the last tile
+        // read a stale buffer and go unused.
+        f32x16 scn = {};
+        auto step = [&](int n, int buf, int nbuf, int pbuf, St &st) __attribute__((always_inline)) {
+            f32x16 sc = scn;
+            // the last tile masks tokens past len.  Lane (query, h2), element v: token
+            // 8 (v / 4) + 4 h2 + v % 4.
+            const int j0 = 32 * n;
+            if (j0 + 32 > len) {
+                const int lm = len - 1 - j0 - 4 * h2;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (8 * (v >> 2) + (v & 3) > lm) sc[v] = -INFINITY;
+            }
+            if (!started) {
+                rebase(sc, true);
+                started = true;
+            }
+            // ---- region 1: tile n + 1's key operands, then tile n's value operands from LDS
+            const uint4 *Tn = pool + nbuf * TILE;
+            uint4 ka[KK];
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) ka[ks] = Tn[ks * kSlot + rd];
+            uint4 va[2 * RT];
+            lds_char *vb = (lds_char *)(pool + buf * TILE + VOFF) + vrd;
+#pragma unroll
+            for (int i = 0; i < 2 * RT; ++i) {
+                lds_char *blk = vb + 1024 * i;
+                const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)blk);
+                const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(blk + 512));
+                va[i] = make_uint4(pk16(r0[0], r0[1]), pk16(r0[2], r0[3]), pk16(r1[0], r1[1]),
+                                   pk16(r1[2], r1[3]));
+            }
+            // tile n + 1's score MFMAs, each followed by its share of tile n's softmax (fenced,
+            // so that the scheduler keeps the interleave)
+            f32x16 s2 = {}, pr;
+#pragma unroll
+            for (int i = 0; i < KK; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
+                s2 = mfma(ka[i], qlat[i], s2);
+#pragma unroll
+                for (int v = 16 * i / KK; v < 16 * (i + 1) / KK; ++v) pr[v] = exp2_(sc[v] - m_lat);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            scn = s2;
+            uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
+            float ls = wsum(p0, p1);
+            if (__builtin_amdgcn_ballot_w64(ls > kSumMax) != 0) {
+                rebase(sc, false);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) pr[v] = exp2_(sc[v] - m_lat);
+                p0 = pack8(pr, 0);
+                p1 = pack8(pr, 1);
+                ls = wsum(p0, p1);
+            }
+            l_sum += ls;
+            // ---- region 2: the value MFMAs in fenced pairs, with tile n + 2's LDS writes and tile
+            // n + 4's loads between them
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                __builtin_amdgcn_sched_barrier(0);
+                olat[rt] = mfma(va[rt], p0, olat[rt]);
+                olat[rt] = mfma(va[RT + rt], p1, olat[rt]);
+                if (rt == 0) produce(n + 2, st, pbuf);
+                if (rt == (RT > 2 ? 2 : RT - 1)) issue(n + 4, st);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         };
 
-        // ---- pipeline: step i + 1 produced while step i is consumed; step i + 2's inputs in
-        // flight
+        // ---- pipeline over a ring of three LDS tile buffers (tile n in buffer n % 3): tile n's
+        // step writes tile n + 2 into the buffer tile n - 1 has left (one barrier per tile) and
+        // loads tile n + 4 (stage set n % 2)
         St s0, s1;
         s0.bad = s1.bad = false;
         issue(0, s0);
         issue(1, s1);
         produce(0, s0, 0);
         issue(2, s0);
+        produce(1, s1, 1);
+        issue(3, s1);
         __syncthreads();
-        for (int it = 0; it < steps; it += 2) {
-            produce(it + 1, s1, 1);
-            issue(it + 3, s1);
-            consume(it, 0);
+        scn = score(0);
+        int bj = 0;                                     // j % 3
+        auto nx3 = [](int x) { return x == 2 ? 0 : x + 1; };
+        for (int j = 0; j < ctiles; j += 2) {
+            const int b1 = nx3(bj), b2 = nx3(b1);
+            step(j, bj, b1, b2, s0);
             __syncthreads();
-            produce(it + 2, s0, 0);
-            issue(it + 4, s0);
-            consume(it + 1, 1);
+            if (j + 1 < ctiles) step(j + 1, b1, b2, nx3(b2), s1);
             __syncthreads();
+            bj = b2;
         }
         // an out-of-range page id anywhere in the cached context makes the outputs NaN
         if (lane == 0) sbad[wave] = bad_w;
@@ -1064,14 +1141,10 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-#ifndef PREFILL_WIDE_TS
-#define PREFILL_WIDE_TS 1
-#endif
-
 template <int D, int RK, int RV>
 hipError_t launch_wide(const PrefillArgs &a, hipStream_t st) {
     const unsigned blocks = (unsigned)a.B * a.H * a.QB;
-    hipLaunchKernelGGL((prefill_wide_kernel<D, RK, RV, PREFILL_WIDE_TS>), dim3(blocks),
+    hipLaunchKernelGGL((prefill_wide_kernel<D, RK, RV>), dim3(blocks),
                        dim3(64 * PWAVES), 0, st, a);
     return hipGetLastError();
 }
