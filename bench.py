@@ -428,23 +428,31 @@ def prefill_leg(cfg, layers, dev, launch, steps, warmup):
 
 
 FIT_ITERS = 40
+FIT_MAX_BYTES = 8 << 30        # staged rows per axis: B x N rows, capped at 8 GiB of bf16
 
 
 def fit_leg(cfg, dev, steps):
-    """Codec fit of one layer (both axes) from n = B x N rows of staged trajectories
+    """Codec fit of one layer (both axes) from n = B x N rows of staged trajectories, at most
+    FIT_MAX_BYTES per axis (Huginn's 32 loops x 32 heads make a row 256 KB: 32768 rows there)
     (lla_fit_svd, FIT_ITERS steps of subspace iteration).  The rows are i.i.d. draws with the
     staging spread: the work per call does not depend on the data."""
     import torch
     from looped_transformer_kv_amd import lla, synth
 
     T, H, d = cfg.T, cfg.H, cfg.d
-    n = cfg.B * cfg.N
+    n = min(cfg.B * cfg.N, FIT_MAX_BYTES // (T * H * d * 2))
     codec = lla.make_codec(cfg.mode, T, H, d, cfg.r_k, cfg.r_v, lla.LLA_BF16)
     gen = torch.Generator(device=dev)
     gen.manual_seed(synth.ROOT_SEED + 11)
     xs = math.sqrt(sum(cfg.decay ** i for i in range(cfg.r_k)) / cfg.X + 0.01)
-    x = [(xs * torch.randn((n, T, H, d), generator=gen, device=dev)).to(torch.bfloat16)
-         for _ in range(2)]
+    x = []
+    for _ in range(2):
+        xa = torch.empty((n, T, H, d), dtype=torch.bfloat16, device=dev)
+        for i in range(0, n, 8192):                 # fp32 draws a slice at a time
+            j = min(n, i + 8192)
+            xa[i:j] = (xs * torch.randn((j - i, T, H, d), generator=gen, device=dev)).to(
+                torch.bfloat16)
+        x.append(xa)
     G, X, Dg = cfg.G, cfg.X, cfg.Dg
     outs, wss = [], []
     for r in (cfg.r_k, cfg.r_v):
