@@ -515,6 +515,237 @@ __global__ __launch_bounds__(64 * RWAVES) void encode_rows_kernel(EncodePair pr)
     }
 }
 
+// ---------------------------------------------------------------- bf16, many rows, wide ranks
+// The bulk encode of a prefill chunk when both latent ranks are multiples of 32 (at least one 64
+// or more): C^T = W_down^T (X - 1 mu)^T per (axis, group) as one GEMM on v_mfma_f32_32x32x16_bf16.
+// A workgroup of GWAVES waves owns (axis, group, a block of `rows` rows) and every latent column of
+// its axis; wave w owns the 32-row tile [32 w, 32 w + 32) of the block (waves past the block only
+// help stage).  The stacked axis is walked in chunks of 128 (64 at r = 160):
+//  * the chunk's W_down rows (chunk x r, row-major as stored) and mu values are staged in LDS by the
+//    whole workgroup, double-buffered with one barrier per chunk, and W comes back through
+//    ds_read_b64_tr_b16 as the A operand (lane (rank, h2) of k-step ks: stacked 16 ks + 8 h2 ..
+//    + 7 of its rank; the four rows a 16-lane group reads fall in distinct banks, padding the LDS
+//    row where r is a multiple of 64);
+//  * the B operand, 8 consecutive stacked elements of one row, comes straight from the staging
+//    row (16 bytes per lane, one chunk ahead) and is centred on the way: x - mu is formed in fp32
+//    and rounded to bf16 (relative 2^-9 per element, the class of the latent's own bf16
+//    rounding), so the rows need no separate mu W chain.
+// A lane's result is one row at 16 latent columns per 32-column tile, so its append slot is one
+// lookup, fetched before the stream.
+constexpr int GWAVES = 8;            // waves per workgroup
+constexpr int GKMIN = 64;            // the stacked axis is a multiple of this
+
+template <int CT>
+struct GShape {
+    static constexpr int R = 32 * CT;                                    // latent columns
+    // stacked elements per chunk: 128 (more bytes in flight per wave), 64 at r = 160, where the
+    // larger chunk's registers spill
+    static constexpr int GKC = CT >= 5 ? 64 : 128;
+    static constexpr int GKS = GKC / 16;                                 // k-steps per chunk
+    // LDS row of a staged W_down row (elements): padded when 2R bytes would map the four rows a
+    // transposed read touches onto the same banks
+    static constexpr int WST = R % 64 == 0 ? (R == 64 ? 72 : R + 16) : R;
+    static constexpr int WP = GKC * R / 8;                               // 16-byte W pieces
+    static constexpr int NPW = (WP + 64 * GWAVES - 1) / (64 * GWAVES);   // per thread
+    static constexpr int BUF = GKC * WST + GKC;                          // W rows, then mu
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> two bf16 (round to nearest even), lo in the low half
+__device__ __forceinline__ uint32_t pk2bf(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// 8 bf16 of x minus 8 bf16 of mu, in fp32, rounded once to 8 bf16
+__device__ __forceinline__ uint4 centre8(const uint4 xv, const uint4 mv) {
+    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ms[4] = {mv.x, mv.y, mv.z, mv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pk2bf(__uint_as_float(xs[i] << 16) - __uint_as_float(ms[i] << 16),
+                     __uint_as_float(xs[i] & 0xFFFF0000u) - __uint_as_float(ms[i] & 0xFFFF0000u));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int CT>
+__device__ __forceinline__ void encode_gemm_tile(const EncodeArgs a, int blk, int rows,
+                                                 uint16_t *lds) {
+    using GS = GShape<CT>;
+    constexpr int R = GS::R, WST = GS::WST, NPW = GS::NPW, WP = GS::WP, BUF = GS::BUF;
+    constexpr int GKC = GS::GKC, GKS = GS::GKS;
+    const int X = a.T * a.Dg;
+    const int rblocks = (a.B + rows - 1) / rows;
+    const int rb = blk % rblocks, g = blk / rblocks;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const bool wlive = 32 * wave < rows;                  // uniform
+    const int rr = rb * rows + 32 * wave + l32;           // this lane's row
+    const int row = min(rr, a.B - 1);                     // (clamped for the loads)
+    const int nch = X / GKC;
+
+    // ---- append slot of this lane's row, fetched first
+    uint16_t *dst = nullptr;
+    bool live = false;
+    if (wlive && rr < a.B) {
+        int seq, pos;
+        live = encode_row(a, rr, seq, pos);
+        if (live && pos >= 0 && pos < a.max_pages * a.P) {
+            const int page = a.block_table[(size_t)seq * a.max_pages + pos / a.P];
+            if ((unsigned)page < (unsigned)a.n_pages)
+                dst = static_cast<uint16_t *>(a.pool) + (((size_t)page * a.G + g) * a.P + pos % a.P) * R;
+        }
+    }
+
+    const uint16_t *W = static_cast<const uint16_t *>(a.W_down) + (size_t)g * X * R;
+    const uint16_t *mu = static_cast<const uint16_t *>(a.mu) + (size_t)g * X;
+    // staging offset of stacked index k: k + t (H d - d) with t = k / d per head ((t, i) of head
+    // g), plain k for LLA-2D ((t, h, i) order); d is a power of two
+    const int dsh = 31 - __builtin_clz(a.d);
+    const int tjump = a.mode ? 0 : (a.H - 1) * a.d;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x) +
+                         (a.mode ? (size_t)row * X : ((size_t)row * a.T * a.H + g) * a.d);
+
+    // ---- chunk c's W_down rows and mu into registers, then into LDS buffer `buf`
+    struct WV {
+        uint4 w[NPW];
+        uint4 m;
+    };
+    auto wload = [&](int c) __attribute__((always_inline)) {
+        WV v;
+        const uint16_t *src = W + (size_t)c * GKC * R;
+#pragma unroll
+        for (int x = 0; x < NPW; ++x) {
+            // the last slot clamps its piece (WP is a multiple of 64, so per wave)
+            const int p = min(tid + 64 * GWAVES * x, WP - 1);
+            v.w[x] = *reinterpret_cast<const uint4 *>(src + 8 * p);
+        }
+        v.m = *reinterpret_cast<const uint4 *>(mu + (size_t)c * GKC + 8 * (tid & (GKC / 8 - 1)));
+        return v;
+    };
+    auto wstore = [&](int buf, const WV v) __attribute__((always_inline)) {
+        uint16_t *b = lds + buf * BUF;
+#pragma unroll
+        for (int x = 0; x < NPW; ++x) {
+            const int p = tid + 64 * GWAVES * x;
+            if (WP % (64 * GWAVES) == 0 || 64 * wave + 64 * GWAVES * x < WP)
+                *reinterpret_cast<uint4 *>(b + (p / (R / 8)) * WST + 8 * (p % (R / 8))) = v.w[x];
+        }
+        if (tid < GKC / 8) *reinterpret_cast<uint4 *>(b + GKC * WST + 8 * tid) = v.m;
+    };
+    // ---- chunk c's rows of this lane: stacked 64 c + 16 ks + 8 h2 .. + 7
+    struct XV {
+        uint4 v[GKS];
+    };
+    auto xload = [&](int c) __attribute__((always_inline)) {
+        XV xv;
+#pragma unroll
+        for (int ks = 0; ks < GKS; ++ks) {
+            const int k = GKC * c + 16 * ks + 8 * h2;
+            xv.v[ks] = *reinterpret_cast<const uint4 *>(xr + k + (k >> dsh) * tjump);
+        }
+        return xv;
+    };
+    // transposed reads: lane (4 e' + m) of each 16-lane group addresses stacked row 8 h2 + e'
+    // (+ 4 for the second read) at ranks 16 ((lane / 16) % 2) + 4 m .. + 3, and lane l gets rank
+    // l % 32 of those four rows
+    const uint32_t vrd =
+        (uint32_t)(((8 * h2 + ((lane & 15) >> 2)) * WST + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+    f32x16 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
+    auto compute = [&](int buf, const XV xv) __attribute__((always_inline)) {
+        uint16_t *b = lds + buf * BUF;
+        lds_char *wb = (lds_char *)b + vrd;
+#pragma unroll
+        for (int ks = 0; ks < GKS; ++ks) {
+            // one k-step's operand reads at a time (hoisting them all would spill)
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 mv = *reinterpret_cast<const uint4 *>(b + GKC * WST + 16 * ks + 8 * h2);
+            const uint4 bx = centre8(xv.v[ks], mv);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                lds_char *p0 = wb + (16 * ks * WST + 32 * ct) * 2;
+                const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+                const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 8 * WST));
+                const uint4 av = make_uint4(
+                    (uint32_t)(uint16_t)r0[0] | (uint32_t)(uint16_t)r0[1] << 16,
+                    (uint32_t)(uint16_t)r0[2] | (uint32_t)(uint16_t)r0[3] << 16,
+                    (uint32_t)(uint16_t)r1[0] | (uint32_t)(uint16_t)r1[1] << 16,
+                    (uint32_t)(uint16_t)r1[2] | (uint32_t)(uint16_t)r1[3] << 16);
+                acc[ct] = mfma32(av, bx, acc[ct]);
+            }
+        }
+    };
+
+    // ---- pipeline: chunk c + 1's W_down and rows in flight while chunk c is multiplied
+    XV xa, xb;
+    WV wv = wload(0);
+    xa = xload(0);
+    wstore(0, wv);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+        const bool n1 = c + 1 < nch, n2 = c + 2 < nch;
+        if (n1) {
+            wv = wload(c + 1);
+            xb = xload(c + 1);
+        }
+        if (wlive) compute(0, xa);
+        if (n1) wstore(1, wv);
+        __syncthreads();
+        if (!n1) break;
+        if (n2) {
+            wv = wload(c + 2);
+            xa = xload(c + 2);
+        }
+        if (wlive) compute(1, xb);
+        if (n2) wstore(0, wv);
+        __syncthreads();
+    }
+
+    // ---- result: lane (row, h2), element v of tile ct: latent column 32 ct + 8 (v / 4) + 4 h2 + v % 4
+    if (!live) return;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = 32 * ct + 8 * q + 4 * h2;
+            const float c0 = acc[ct][4 * q], c1 = acc[ct][4 * q + 1], c2 = acc[ct][4 * q + 2],
+                        c3 = acc[ct][4 * q + 3];
+            if (a.c_out)
+                *reinterpret_cast<float4 *>(a.c_out + ((size_t)rr * a.G + g) * R + col) =
+                    make_float4(c0, c1, c2, c3);
+            if (dst) *reinterpret_cast<uint2 *>(dst + col) = make_uint2(pk2bf(c0, c1), pk2bf(c2, c3));
+        }
+}
+
+struct EncodeGemm {
+    EncodeArgs ax[2];
+    int blocks_k;         // workgroups of the K axis (the V axis follows)
+    int rows;             // rows per workgroup (32-row tiles: 256, 128 or 64)
+};
+
+template <int CTK, int CTV>
+__global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void encode_gemm_kernel(EncodeGemm eg) {
+    constexpr int BUF = GShape<CTK>::BUF > GShape<CTV>::BUF ? GShape<CTK>::BUF : GShape<CTV>::BUF;
+    __shared__ __align__(16) uint16_t lds[2 * BUF];
+    int blk = blockIdx.x;
+    if (blk < eg.blocks_k) {
+        encode_gemm_tile<CTK>(eg.ax[0], blk, eg.rows, lds);
+    } else {
+        blk -= eg.blocks_k;
+        encode_gemm_tile<CTV>(eg.ax[1], blk, eg.rows, lds);
+    }
+}
+
+int gemm_blocks_of(const EncodeArgs &a, int rows) { return a.G * ((a.B + rows - 1) / rows); }
+
 int rows_blocks_of(const EncodeArgs &a) {
     return a.G * ((a.r + 31) / 32) * ((a.B + 32 * RTILES - 1) / (32 * RTILES));
 }
@@ -538,6 +769,47 @@ int rows_per_block(const EncodeArgs &k_axis, const EncodeArgs &v_axis, int layer
     return 4;
 }
 
+// The wide-rank GEMM serves bf16 bulk encodes of many rows when both ranks are multiples of 32
+// with one of them 64 or more (the rank pairs (32,64), (64,64), (64,128), (96,160)), the stacked
+// axis is a multiple of 64 and the operands are 16-byte aligned.
+bool gemm_kernel_fits(const EncodeArgs &k, const EncodeArgs &v) {
+    auto ok = [](const EncodeArgs &a) {
+        return a.B >= 1024 && (a.T * a.Dg) % (a.r >= 160 ? GKMIN : 2 * GKMIN) == 0 &&
+               a.r % 32 == 0 && a.r <= 160 &&
+               (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 &&
+               (reinterpret_cast<uintptr_t>(a.W_down) & 15) == 0 &&
+               (reinterpret_cast<uintptr_t>(a.mu) & 15) == 0 &&
+               (reinterpret_cast<uintptr_t>(a.c_out) & 15) == 0;
+    };
+    const int pk = k.r / 32, pv = v.r / 32;
+    const bool pair = (pk == 1 && pv == 2) || (pk == 2 && pv == 2) || (pk == 2 && pv == 4) ||
+                      (pk == 3 && pv == 5);
+    return pair && ok(k) && ok(v) && k.B == v.B;
+}
+
+template <int CTK, int CTV>
+hipError_t launch_gemm_t(const EncodeGemm &eg, unsigned blocks, hipStream_t st) {
+    hipLaunchKernelGGL((encode_gemm_kernel<CTK, CTV>), dim3(blocks), dim3(64 * GWAVES), 0, st, eg);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const EncodeArgs &k_axis, const EncodeArgs &v_axis, hipStream_t st) {
+    EncodeGemm eg;
+    eg.ax[0] = k_axis;
+    eg.ax[1] = v_axis;
+    // 256-row blocks unless that leaves the grid short of two workgroups per CU (LLA-2D: one group)
+    eg.rows = 256;
+    while (eg.rows > 64 && gemm_blocks_of(k_axis, eg.rows) + gemm_blocks_of(v_axis, eg.rows) < 512)
+        eg.rows /= 2;
+    eg.blocks_k = gemm_blocks_of(k_axis, eg.rows);
+    const unsigned blocks = (unsigned)(eg.blocks_k + gemm_blocks_of(v_axis, eg.rows));
+    const int pk = k_axis.r / 32, pv = v_axis.r / 32;
+    if (pk == 1 && pv == 2) return launch_gemm_t<1, 2>(eg, blocks, st);
+    if (pk == 2 && pv == 2) return launch_gemm_t<2, 2>(eg, blocks, st);
+    if (pk == 2 && pv == 4) return launch_gemm_t<2, 4>(eg, blocks, st);
+    return launch_gemm_t<3, 5>(eg, blocks, st);
+}
+
 }  // namespace
 
 hipError_t launch_encode_layers(const EncodeArgs *k_axes, const EncodeArgs *v_axes, int n,
@@ -547,8 +819,9 @@ hipError_t launch_encode_layers(const EncodeArgs *k_axes, const EncodeArgs *v_ax
     // the single-call launcher, so each pool is written exactly as a single call writes it
     bool per_layer = !bf16;
     for (int i = 0; i < n && !per_layer; ++i)
-        per_layer = rows_kernel_fits(k_axes[i]) && rows_kernel_fits(v_axes[i]) &&
-                    rows_blocks_of(k_axes[i]) + rows_blocks_of(v_axes[i]) >= 256;
+        per_layer = (rows_kernel_fits(k_axes[i]) && rows_kernel_fits(v_axes[i]) &&
+                     rows_blocks_of(k_axes[i]) + rows_blocks_of(v_axes[i]) >= 256) ||
+                    gemm_kernel_fits(k_axes[i], v_axes[i]);
     if (per_layer) {
         for (int i = 0; i < n; ++i) {
             const hipError_t e = launch_encode(k_axes[i], v_axes[i], bf16, st);
@@ -586,6 +859,7 @@ hipError_t launch_encode_layers(const EncodeArgs *k_axes, const EncodeArgs *v_ax
 
 hipError_t launch_encode(const EncodeArgs &k_axis, const EncodeArgs &v_axis, bool bf16,
                          hipStream_t st) {
+    if (bf16 && gemm_kernel_fits(k_axis, v_axis)) return launch_gemm(k_axis, v_axis, st);
     EncodePair pr;
     pr.ax[0] = k_axis;
     pr.ax[1] = v_axis;

@@ -112,10 +112,10 @@ def test_prefill_single_token_chunk_matches_decode(gpu):
     assert_close(synth.from_device(out), ref, "bf16", "decode with the chunk token as self")
 
 
-def _check_encode_chunk(gpu, shape, B, N, Pn, lens, n_new):
+def _check_encode_chunk(gpu, shape, B, N, Pn, lens, n_new, shapes=None):
     """lla_encode_chunk: c against the oracle; the pool holds c rounded once at write_pos + i for
     live rows only; every other slot keeps its bytes."""
-    cfg = SHAPES[shape]
+    cfg = (shapes or SHAPES)[shape]
     ch = Chunk(cfg, B, N, Pn, lens, n_new, gpu)
     c, p = ch.cfg, ch.p
     wpos_h = p.seq_lens.copy()
@@ -151,6 +151,35 @@ def _check_encode_chunk(gpu, shape, B, N, Pn, lens, n_new):
 def test_encode_chunk(gpu, shape, Pn):
     """A few hundred rows: the split-axis kernel."""
     _check_encode_chunk(gpu, shape, 3, 90, Pn, [90, 0, 33], [Pn, 0, 41])
+
+
+# codecs whose bulk encode takes the wide-rank GEMM (both ranks multiples of 32, one >= 64, at
+# least 1024 rows): per head and LLA-2D, stacked axes from 128 (2 chunks of 64) to 4096
+# (32 loops, the Huginn shape per head)
+WIDE_ENCODE = {
+    "ouro14_4x": (synth.CONFIGS["ouro14_4x"], 4, 70, 512, [70, 0, 33, 64], [512, 300, 0, 511]),
+    "2d_h4_r96_160": (synth.Config("enc_2d", L=1, H=4, d=128, T=4, r_k=96, r_v=160, B=1, N=1,
+                                   mode=1, cid=160), 4, 40, 300, [40, 7, 0, 31], [300, 299, 1, 0]),
+    "t32_h2_r96_160": (synth.Config("enc_t32", L=1, H=2, d=128, T=32, r_k=96, r_v=160, B=1,
+                                    N=1, cid=161), 2, 64, 512, [64, 5], [512, 480]),
+    "d64_r32_64": (synth.Config("enc_d64", L=1, H=2, d=64, T=2, r_k=32, r_v=64, B=1, N=1,
+                                cid=162), 8, 20, 128, [20, 0, 3, 19, 17, 1, 7, 8],
+                   [128, 127, 0, 64, 128, 1, 99, 128]),
+    "2d_d128_r64_64": (synth.Config("enc_2d64", L=1, H=2, d=128, T=2, r_k=64, r_v=64, B=1, N=1,
+                                    mode=1, cid=163), 4, 10, 256, [10, 0, 5, 9], [256, 200, 256, 3]),
+    "d128_r64_128": (synth.Config("enc_r128", L=1, H=2, d=128, T=3, r_k=64, r_v=128, B=1, N=1,
+                                  cid=164), 4, 10, 256, [10, 1, 0, 9], [256, 255, 100, 256]),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_ENCODE))
+def test_encode_chunk_wide_ranks(gpu, name):
+    """Thousands of rows of the wider rank pairs: the GEMM kernel (W_down staged per 64-element
+    chunk, rows centred on the way), with empty, full and ragged chunks, writes starting
+    mid-page and rows past a chunk left alone."""
+    cfg, B, N, Pn, lens, n_new = WIDE_ENCODE[name]
+    assert B * Pn >= 1024 and max(lens) <= N
+    _check_encode_chunk(gpu, name, B, N, Pn, lens, n_new, shapes={name: cfg})
 
 
 def test_encode_chunk_row_streaming(gpu):
