@@ -250,6 +250,9 @@ lla_status lla_encode_append(const lla_codec *codec, const lla_params *params,
  *                   (< 0 or >= max_pages*P) are skipped
  *   c_k_out/c_v_out optional device fp32 [B][chunk][G][r] copies of c before rounding, written
  *                   for live rows only (NULL = none)
+ * Precision (bf16 codecs): fp32 accumulation of exact bf16 products; at 1024 rows or more with
+ * both ranks multiples of 32 and one of them 64 or more, x - mu is formed in fp32 and rounded once
+ * to bf16 before the product (relative 2^-9 per element, the class of the output's rounding).
  * chunk = 0 (or batch 0) enqueues nothing.  chunk < 0 or batch*chunk > 2^30 -> LLA_ERR_SHAPE;
  * n_new NULL -> LLA_ERR_NULL; otherwise validated like lla_encode_append.
  */
