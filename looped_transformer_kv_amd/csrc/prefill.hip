@@ -106,24 +106,24 @@ __device__ __forceinline__ void load_query_operands(const PrefillArgs &a, int b,
     }
 }
 
-// This lane's half of <q, mu_t^K> (the dims of its query operands); the partner lane h2 ^ 1
-// holds the other half.
+// This lane's half of <q, mu_t^K> (the dims of its query operands: k-step ks covers dims
+// 16 ks + 4 h2 + {0..3} and 16 ks + 8 + 4 h2 + {0..3}); the partner lane h2 ^ 1 holds the other half.
 template <int D>
 __device__ __forceinline__ float query_dot_mu_k(const PrefillArgs &a, int g, int col0, int h2,
                                                 const uint4 (&qop)[D / 16]) {
     const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
-                          (size_t)a.t * a.Dg + col0;
-    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(muk), 0, D * 2, kBufferWord3);
+                          (size_t)a.t * a.Dg + col0 + 4 * h2;
     float qm = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
+        const uint2 lo = *reinterpret_cast<const uint2 *>(muk + 16 * ks);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(muk + 16 * ks + 8);
+        const uint32_t mv[4] = {lo.x, lo.y, hi.x, hi.y};
         const uint32_t qv[4] = {qop[ks].x, qop[ks].y, qop[ks].z, qop[ks].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint16_t m = __builtin_amdgcn_raw_buffer_load_b16(
-                mr, 8 * h2, (32 * (ks >> 1) + 16 * (ks & 1) + (e < 4 ? e : e + 4)) * 2, 0);
-            qm += bf2f(static_cast<uint16_t>(qv[e >> 1] >> (16 * (e & 1)))) * bf2f(m);
+        for (int i = 0; i < 4; ++i) {
+            qm += __uint_as_float(qv[i] << 16) * __uint_as_float(mv[i] << 16);
+            qm += __uint_as_float(qv[i] & 0xFFFF0000u) * __uint_as_float(mv[i] & 0xFFFF0000u);
         }
     }
     return qm;
@@ -468,30 +468,39 @@ struct Stage {
     uint4 r[N];
 };
 
-// W_up,t^V as the A operands of the expansion O^T = W_up,t^V^T O_lat^T: lane (dim, h2) of 32-dim
-// tile n, k-step ks (slot KV n + ks) holds the dim's column at ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4,
-// the order of O_lat's B operand.  Wave w of nw builds slots w, w + nw, ..; buffer loads: a fixed
-// byte offset per lane plus a scalar one per element.
+// W_up,t^V, the A operand of the expansion O^T = W_up,t^V^T O_lat^T, staged once per workgroup in
+// LDS as stored (rank-major rows of the head's D dims, each row padded to D + 16 elements so that
+// the four rows a transposed read touches fall in distinct banks), with 16-byte loads by every
+// thread.  Lane (dim, h2) of 32-dim tile n, k-step ks takes the dim's column at ranks
+// 16 ks + 8 (e / 4) + 4 h2 + e % 4 (the order of O_lat's B operand) through two ds_read_b64_tr_b16.
+template <int D>
+constexpr int wv_stride() { return D + 16; }
+
 template <int D, int RV>
-__device__ __forceinline__ void build_wv_operands(const PrefillArgs &a, int g, int col0, int wave,
-                                                  int nw, int lane, uint4 (*sW)[kSlot]) {
-    constexpr int MT = D / 32, KV = RV / 16;
-    const int l32 = lane & 31, h2 = lane >> 5;
+__device__ __forceinline__ void stage_wv(const PrefillArgs &a, int g, int col0, int tid, int nthr,
+                                         uint16_t *sWv) {
+    constexpr int ST = wv_stride<D>(), PR = D / 8;            // 16-byte pieces per row
     const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) +
                          ((size_t)a.t * a.G + g) * RV * a.Dg + col0;
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(Wv), 0, ((RV - 1) * a.Dg + D) * 2, kBufferWord3);
-    for (int slot = wave; slot < MT * KV; slot += nw) {
-        const int n = slot / KV, ks = slot % KV;
-        const int wl = (4 * h2 * a.Dg + 32 * n + l32) * 2;
-        uint16_t w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            w[e] = __builtin_amdgcn_raw_buffer_load_b16(
-                wr, wl, (16 * ks + 8 * (e >> 2) + (e & 3)) * a.Dg * 2, 0);
-        sW[slot][srow(lane)] = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16,
-                                          w[4] | (uint32_t)w[5] << 16, w[6] | (uint32_t)w[7] << 16);
+    for (int p = tid; p < RV * PR; p += nthr) {
+        const int row = p / PR, c8 = p - row * PR;
+        *reinterpret_cast<uint4 *>(sWv + row * ST + 8 * c8) =
+            *reinterpret_cast<const uint4 *>(Wv + (size_t)row * a.Dg + 8 * c8);
     }
+}
+
+// the A operand of 32-dim tile n, k-step ks: lane (4 e' + m) of each 16-lane group addresses rank
+// 16 ks + 4 h2 + e' (+ 8 for the second read) at dims 32 n + 16 ((lane / 16) % 2) + 4 m .. + 3
+template <int D>
+__device__ __forceinline__ uint4 wv_operand(const uint16_t *sWv, int n, int ks, int lane) {
+    constexpr int ST = wv_stride<D>();
+    const int h2 = lane >> 5;
+    lds_char *p = (lds_char *)(sWv) +
+                  ((16 * ks + 4 * h2 + ((lane & 15) >> 2)) * ST + 32 * n + 16 * ((lane >> 4) & 1) +
+                   4 * (lane & 3)) * 2;
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * ST));
+    return make_uint4(pk16(r0[0], r0[1]), pk16(r0[2], r0[3]), pk16(r1[0], r1[1]), pk16(r1[2], r1[3]));
 }
 
 // Flash attention of a workgroup's queries [q0, qend) (8 waves, wave w owning 32 of them) over
@@ -692,8 +701,8 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
 
     // operand slots per buffer: [0, KS) for the keys (sK), [KS, KS + 2 MT) for the values (sV)
     __shared__ __align__(16) uint4 sbuf[2][SH::SLOTS][kSlot];
-    // W_up,t^V operands (32-dim tile n, k-step ks at slot KV n + ks), built once per workgroup
-    __shared__ __align__(16) uint4 sW[MT * KV][kSlot];
+    // W_up,t^V, staged once per workgroup
+    __shared__ __align__(16) uint16_t sWv[RV * wv_stride<D>()];
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -742,7 +751,7 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         l_run = h2 ? 0.f : ml.y;
         l_lat = l_run;
     }
-    if (len > 0) build_wv_operands<D, RV>(a, g, col0, wave, CWAVES, lane, sW);
+    if (len > 0) stage_wv<D, RV>(a, g, col0, tid, 64 * CWAVES, sWv);
     const int rd = srow(lane);
     // the cached part back in model space, from the shared W_up,t^V operands
     chunk_phase<D>(a, b, h, g, col0, nn, q0, qend, sbuf, qop, oacc, m_run, l_run, l_lat,
@@ -752,7 +761,7 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
                            for (int n = 0; n < MT; ++n)
 #pragma unroll
                                for (int ks = 0; ks < KV; ++ks)
-                                   oacc[n] = mfma(sW[n * KV + ks][rd], lop[ks], oacc[n]);
+                                   oacc[n] = mfma(wv_operand<D>(sWv, n, ks, lane), lop[ks], oacc[n]);
                        }
                    });
 }
@@ -798,10 +807,11 @@ void prefill_wide_kernel(PrefillArgs a) {
     // part's two tile buffers (the cached part's reads then take immediate offsets), then the
     // W_up,t^V operands
     constexpr int CB = CBUF > PBUF ? CBUF : PBUF;
-    __shared__ __align__(16) uint4 lds[CB + MT * KV * kSlot];
+    static_assert(RV * wv_stride<D>() % 8 == 0, "whole uint4 of staged W_up,t^V");
+    __shared__ __align__(16) uint4 lds[CB + RV * wv_stride<D>() / 8];
     __shared__ int sbad[PWAVES];
     uint4 *const pool = lds;
-    uint4 (*const sW)[kSlot] = reinterpret_cast<uint4 (*)[kSlot]>(lds + CB);
+    uint16_t *const sWv = reinterpret_cast<uint16_t *>(lds + CB);
 
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
     const int qb = id % a.QB;
@@ -831,38 +841,6 @@ void prefill_wide_kernel(PrefillArgs a) {
     for (int n = 0; n < MT; ++n) oacc[n] = f32x16{};
 
     if (len > 0) {
-        build_wv_operands<D, RV>(a, g, col0, wave, PWAVES, lane, sW);
-
-        // ---- q' = c W_up,t^K q (rank x query tiles on the matrix cores; A = the W_up,t^K rows at
-        // the query operand's dims, straight from memory) and c <q, mu_t^K>.  Tile rt leaves lane
-        // (query, h2) ranks 32 rt + 8 (v / 4) + 4 h2 + v % 4, which packs into the score MFMA's B
-        // operand (k-step ks: ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4).
-        uint4 qlat[KK];
-        float qmu;
-        {
-            uint4 qop[KS];
-            load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
-            const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
-                                 ((size_t)a.t * a.G + g) * RK * a.Dg + col0 + 4 * h2;
-#pragma unroll
-            for (int rt = 0; rt < RK / 32; ++rt) {
-                const uint16_t *wrow = Wk + (size_t)(32 * rt + l32) * a.Dg;
-                f32x16 qa = {};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(wrow + 16 * ks);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(wrow + 16 * ks + 8);
-                    qa = mfma(make_uint4(lo.x, lo.y, hi.x, hi.y), qop[ks], qa);
-                }
-#pragma unroll
-                for (int v = 0; v < 16; ++v) qa[v] *= csc;
-                qlat[2 * rt] = pack8(qa, 0);
-                qlat[2 * rt + 1] = pack8(qa, 1);
-            }
-            const float qm = query_dot_mu_k<D>(a, g, col0, h2, qop);
-            qmu = (qm + __shfl_xor(qm, 32, 64)) * csc;
-        }
-
         // ---- tile inputs.  Piece p = 64 wave + 512 x + lane of tile n (clamped to the last cached
         // tile): p < CPK is key piece (token p % 32 (clamped to the last valid token), ranks
         // 8 (p / 32) .. + 7), else value piece u = p - CPK of block u / 64 = (kj RT + rt): token
@@ -936,6 +914,43 @@ void prefill_wide_kernel(PrefillArgs a) {
                 }
             }
         };
+
+        // the first two tiles' loads go out before the set-up below
+        St s0, s1;
+        s0.bad = s1.bad = false;
+        issue(0, s0);
+        issue(1, s1);
+        stage_wv<D, RV>(a, g, col0, tid, 64 * PWAVES, sWv);
+
+        // ---- q' = c W_up,t^K q (rank x query tiles on the matrix cores; A = the W_up,t^K rows at
+        // the query operand's dims, straight from memory) and c <q, mu_t^K>.  Tile rt leaves lane
+        // (query, h2) ranks 32 rt + 8 (v / 4) + 4 h2 + v % 4, which packs into the score MFMA's B
+        // operand (k-step ks: ranks 16 ks + 8 (e / 4) + 4 h2 + e % 4).
+        uint4 qlat[KK];
+        float qmu;
+        {
+            uint4 qop[KS];
+            load_query_operands<D>(a, b, h, min(wq0 + l32, nn - 1), h2, qop);
+            const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) +
+                                 ((size_t)a.t * a.G + g) * RK * a.Dg + col0 + 4 * h2;
+#pragma unroll
+            for (int rt = 0; rt < RK / 32; ++rt) {
+                const uint16_t *wrow = Wk + (size_t)(32 * rt + l32) * a.Dg;
+                f32x16 qa = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(wrow + 16 * ks);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(wrow + 16 * ks + 8);
+                    qa = mfma(make_uint4(lo.x, lo.y, hi.x, hi.y), qop[ks], qa);
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) qa[v] *= csc;
+                qlat[2 * rt] = pack8(qa, 0);
+                qlat[2 * rt + 1] = pack8(qa, 1);
+            }
+            const float qm = query_dot_mu_k<D>(a, g, col0, h2, qop);
+            qmu = (qm + __shfl_xor(qm, 32, 64)) * csc;
+        }
 
         // ---- online softmax over the cached tiles (log2 domain; scores relative to c <q, mu_t^K>,
         // which is the same for every cached token and joins the reference at the end).  Lazy
@@ -1079,10 +1094,6 @@ void prefill_wide_kernel(PrefillArgs a) {
         // ---- pipeline over a ring of three LDS tile buffers (tile n in buffer n % 3): tile n's
         // step writes tile n + 2 into the buffer tile n - 1 has left (one barrier per tile) and
         // loads tile n + 4 (stage set n % 2)
-        St s0, s1;
-        s0.bad = s1.bad = false;
-        issue(0, s0);
-        issue(1, s1);
         produce(0, s0, 0);
         issue(2, s0);
         produce(1, s1, 1);
@@ -1114,7 +1125,8 @@ void prefill_wide_kernel(PrefillArgs a) {
 #pragma unroll
             for (int n = 0; n < MT; ++n)
 #pragma unroll
-                for (int ks = 0; ks < KV; ++ks) oacc[n] = mfma(sW[n * KV + ks][rd], lop[ks], oacc[n]);
+                for (int ks = 0; ks < KV; ++ks)
+                    oacc[n] = mfma(wv_operand<D>(sWv, n, ks, lane), lop[ks], oacc[n]);
         }
         m_run = m_lat + qmu;
         l_run = bad_any ? __builtin_nanf("") : l_sum;
