@@ -133,6 +133,54 @@ def test_encode_append(gpu, name):
         assert np.array_equal(after, expect), f"{name} axis {axis}: pool differs"
 
 
+@pytest.mark.parametrize("name", ["ouro14_4x", "ouro26_2d_64x"])
+def test_encode_append_wide_ranks_many_sequences(gpu, name):
+    """A decode-step encode over 1024 sequences at ranks 96 / 160 takes the bulk-encode GEMM (one
+    row per sequence): c against the oracle, the pool against O.append of c rounded once; then
+    lla_encode_append_layers over two layers (each layer through the same single-call path)
+    writes bitwise what one call per layer writes."""
+    cfg = synth.CONFIGS[name]
+    B, N = 1024, 8
+    dps = [gpucase.DeviceProblem(tinycase.make(cfg, layer=l, B=B, N=N, salt=l)) for l in range(2)]
+    p, dp = dps[0].p, dps[0]
+    pos_h = np.full(B, N, dtype=np.int32)
+    pos_h[1] = 3                       # overwrite an existing slot
+    pos_h[2] = -1                      # skipped
+    pos_h[5] = 1 << 20                 # past the block table: skipped
+    pos = torch.from_numpy(pos_h).to(gpu)
+    ck = torch.zeros((B, cfg.G, cfg.r_k), dtype=torch.float32, device=gpu)
+    cv = torch.zeros((B, cfg.G, cfg.r_v), dtype=torch.float32, device=gpu)
+    before = [(synth.from_device(d.k_pool), synth.from_device(d.v_pool)) for d in dps]
+    say(f"{name} encode_append B={B} (bulk-encode GEMM)")
+    dp.layer.encode_append(dp.x_k, dp.x_v, pos, ck, cv)
+    torch.cuda.synchronize()
+    keep = (pos_h >= 0) & (pos_h < p.block_table.shape[1] * cfg.page)
+    for axis, cgpu, W, mu, r, kb, pool in (
+            (0, ck, p.W_down_k, p.mu_k, cfg.r_k, before[0][0], dp.k_pool),
+            (1, cv, p.W_down_v, p.mu_v, cfg.r_v, before[0][1], dp.v_pool)):
+        ref = O.encode(cfg.mode, cfg.T, cfg.H, cfg.d, r, W, mu, p.x_v if axis else p.x_k)
+        c = cgpu.double().cpu().numpy()
+        assert_close(c, ref, "bf16", f"{name} c axis {axis}")
+        stored = synth.quantize(c, "bf16")
+        expect = O.append(stored[keep], pos_h[keep], p.block_table[keep], cfg.page, kb)
+        assert np.array_equal(synth.from_device(pool), expect), f"{name} axis {axis}: pool differs"
+    single = [(synth.from_device(d.k_pool), synth.from_device(d.v_pool)) for d in dps[:1]]
+    dps[1].layer.encode_append(dps[1].x_k, dps[1].x_v, pos)
+    torch.cuda.synchronize()
+    single.append((synth.from_device(dps[1].k_pool), synth.from_device(dps[1].v_pool)))
+    for d, (kb, vb) in zip(dps, before):
+        d.k_pool.copy_(synth.to_device(kb, "bf16", gpu))
+        d.v_pool.copy_(synth.to_device(vb, "bf16", gpu))
+    torch.cuda.synchronize()
+    say(f"{name}: encode_append_layers over 2 layers, B={B}")
+    LatentLayer.encode_append_layers([d.layer for d in dps], [d.x_k for d in dps],
+                                     [d.x_v for d in dps], pos)
+    torch.cuda.synchronize()
+    for l, d in enumerate(dps):
+        assert np.array_equal(synth.from_device(d.k_pool), single[l][0]), f"layer {l} K pool"
+        assert np.array_equal(synth.from_device(d.v_pool), single[l][1]), f"layer {l} V pool"
+
+
 @pytest.mark.parametrize("name,n_layers", [("ouro14_21x", 3), ("ouro14_21x", 35),
                                            ("ouro26_2d_64x", 2), ("tiny_f32", 2)])
 def test_encode_append_layers_matches_single_calls(gpu, name, n_layers):
