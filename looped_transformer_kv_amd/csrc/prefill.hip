@@ -457,7 +457,11 @@ struct PShape {
     static constexpr int PIECES = 32 * D / 8;
     static constexpr int NEWP = (PIECES + 64 * CWAVES - 1) / (64 * CWAVES);
     static constexpr int NST = 2 * NEWP;               // stage registers per thread
-    static constexpr int SLOTS = KS + 2 * MT;          // 1 KB operand slots per LDS buffer
+    // value rows are kept as stored (token-major, each row padded to D + 16 elements so that the
+    // four rows a transposed read touches fall in distinct banks) after the KS key slots
+    static constexpr int VST = D + 16;
+    static constexpr int VSLOTS = (32 * VST * 2 + 16 * kSlot - 1) / (16 * kSlot);
+    static constexpr int SLOTS = KS + VSLOTS;          // 1 KB operand slots per LDS buffer
     static_assert(MT == 2 || MT == 4, "head dim 64 or 128");
 };
 
@@ -575,26 +579,28 @@ __device__ __forceinline__ void chunk_phase(const PrefillArgs &a, int b, int h, 
             *d0 = make_uint2(w.x, w.y);
             *d1 = make_uint2(w.z, w.w);
         }
-        // value piece (row jr, dims 8p .. 8p + 7) -> the V^T operand of each dim: lane
-        // (dim % 32, h2) of slot KS + 2 (dim / 32) + jr / 16 holds tokens 16 kj + 8 (e / 4) +
-        // 4 h2 + e % 4 at element e
+        // value piece (row jr, dims 8p .. 8p + 7) -> its place in the token-major value rows
+        uint16_t *vrow = reinterpret_cast<uint16_t *>(&sbuf[buf][KS][0]);
 #pragma unroll
         for (int x = 0; x < NEWP; ++x) {
             const int pc = tid + 64 * CWAVES * x;
             if (SH::PIECES % (64 * CWAVES) != 0 && pc >= SH::PIECES) break;
-            const int jr = piece_row(pc), p8 = piece_dim(pc);
-            const int kj = jr >> 4, rem = jr & 15;
-            const int hh = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
-            const uint4 w = st.r[NEWP + x];
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int y = 0; y < 8; ++y) {
-                const int dim = p8 + y;
-                uint16_t *dst = reinterpret_cast<uint16_t *>(
-                    &sbuf[buf][KS + 2 * (dim >> 5) + kj][srow(32 * hh + (dim & 31))]);
-                dst[e] = static_cast<uint16_t>(wd[y >> 1] >> (16 * (y & 1)));
-            }
+            *reinterpret_cast<uint4 *>(vrow + piece_row(pc) * SH::VST + piece_dim(pc)) =
+                st.r[NEWP + x];
         }
+    };
+    // the V^T operand of 32-dim tile n, token k-step kj: lane (dim, h2) holds tokens
+    // 16 kj + 8 (e / 4) + 4 h2 + e % 4 at element e (the order of P^T), through two transposed
+    // reads: lane (4 e' + m) of each 16-lane group addresses token 16 kj + 4 h2 + e' (+ 8) at dims
+    // 32 n + 16 ((lane / 16) % 2) + 4 m .. + 3, and lane l gets dim 32 n + l % 32
+    const uint32_t vtr = (uint32_t)(((4 * h2 + ((lane & 15) >> 2)) * SH::VST +
+                                     16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+    auto vt_operand = [&](int buf, int n, int kj) __attribute__((always_inline)) {
+        lds_char *p = (lds_char *)(&sbuf[buf][KS][0]) + vtr + (16 * kj * SH::VST + 32 * n) * 2;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * SH::VST));
+        return make_uint4(pk16(r0[0], r0[1]), pk16(r0[2], r0[3]), pk16(r1[0], r1[1]),
+                          pk16(r1[2], r1[3]));
     };
 
     // ---- online softmax over the chunk's tiles (log2 domain; raw q . k scores need * c), lazy
@@ -643,8 +649,8 @@ __device__ __forceinline__ void chunk_phase(const PrefillArgs &a, int b, int h, 
         const uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
 #pragma unroll
         for (int n = 0; n < MT; ++n) {
-            oacc[n] = mfma(sbuf[buf][KS + 2 * n][rd], p0, oacc[n]);
-            oacc[n] = mfma(sbuf[buf][KS + 2 * n + 1][rd], p1, oacc[n]);
+            oacc[n] = mfma(vt_operand(buf, n, 0), p0, oacc[n]);
+            oacc[n] = mfma(vt_operand(buf, n, 1), p1, oacc[n]);
         }
     };
 
