@@ -797,9 +797,11 @@ hipError_t launch_gemm(const EncodeArgs &k_axis, const EncodeArgs &v_axis, hipSt
     EncodeGemm eg;
     eg.ax[0] = k_axis;
     eg.ax[1] = v_axis;
-    // 256-row blocks unless that leaves the grid short of two workgroups per CU (LLA-2D: one group)
-    eg.rows = 256;
-    while (eg.rows > 64 && gemm_blocks_of(k_axis, eg.rows) + gemm_blocks_of(v_axis, eg.rows) < 512)
+    // a 32-row tile per wave unless that leaves the grid short of two workgroups per CU (LLA-2D:
+    // one group)
+    eg.rows = 32 * GWAVES;
+    while (eg.rows > 32 * GWAVES / 4 &&
+           gemm_blocks_of(k_axis, eg.rows) + gemm_blocks_of(v_axis, eg.rows) < 512)
         eg.rows /= 2;
     eg.blocks_k = gemm_blocks_of(k_axis, eg.rows);
     const unsigned blocks = (unsigned)(eg.blocks_k + gemm_blocks_of(v_axis, eg.rows));
