@@ -1,0 +1,503 @@
+// decode_rope.hip -- rotary latent decode for key rank 16: two heads of one sequence per wave, each
+// chunk's rotation sines and cosines computed once for both, scores on the matrix core.
+//
+// Computes what the rotary form of decode_bf16.hip computes (the rotation follows reconstruction:
+// "Axiom & Free-Parameter Ledger" page, a token keeps its position at every recurrence step, so
+// RoPE can be applied after reconstruction; pith.science "Looped Latent Attention", section "What
+// carries the argument": x_hat_t = c W_up,t + mu_t):
+//   s_j = scale <q, R_j K_hat(j)>,  K_hat(j) = c_k(j) W_up,t^K + mu_t^K
+//   out = sum_j softmax(s)_j V_hat(j) (plus the current token's own key and value)
+//
+// Scores.  With pair m = (i, i') of the head dims and phi_jm token j's angle for it,
+//   <q, R_j x> = sum_m cos(phi_jm) (q_i x_i + q_i' x_i') + sin(phi_jm) (q_i' x_i - q_i x_i'),
+// and x = c_k W_up,t^K + mu_t^K is linear in the latent.  Per head, the coefficients of both
+// brackets over the ranks (q_i W[k][i] + q_i' W[k][i'] and q_i' W[k][i] - q_i W[k][i'], and the
+// same with mu_t^K in place of a W row) form a matrix A of (r_k + 1) rows over d pair-space
+// columns (d/2 cosine columns, then d/2 sine columns).  For a chunk of 32 tokens the pair-space
+// matrix Phi = [cos phi; sin phi] (d x 32) depends on the positions only, so it is built once per
+// chunk for every head the wave serves, and one MFMA contraction per head, A Phi, gives each token
+// its query over the latent ranks (and its mu term): the score is then a 16-term dot product with
+// the token's latent.  Both operands are bf16 (A rounded once from fp32; Phi from the hardware
+// sine and cosine), accumulation fp32.
+// Values.  The rotation leaves values alone, so sum_j p_j V_hat(j) = (sum_j p_j c_v(j)) W_up,t^V +
+// (sum_j p_j) mu_t^V: the p-weighted value latents accumulate in fp32 and are expanded once, at
+// the end.
+//
+// Work decomposition: one workgroup of 8 waves per (sequence b, pair of heads, context split s),
+// the same splits as the latent decode plan (B * H / 2 * S workgroups of 8 waves = the plan's
+// B * H * S workgroups of 4).  Waves take 32-token chunks round-robin with three chunks of both
+// heads' latents in flight; a single-split plan finishes the output here (self term and
+// (sum p) mu_t^V included), otherwise one (o, m, l) partial per (head, split) goes to combine.hip,
+// with the rotated self score in the first split's record.
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int D, int RK, int RV>
+struct RopeShape {
+    static_assert(RK == 16, "the score tile holds the 16 ranks and the mu row");
+    static_assert(RV % 16 == 0 && RV <= 32, "value ranks");
+    static constexpr int HG = 2;          // heads per wave
+    static constexpr int WAVES = 8;
+    static constexpr int KS = D / 16;     // MFMA k-steps over pair space: cosine half, sine half
+    static constexpr int KC = KS / 2;     // k-steps of the cosine half
+    static constexpr int NF = 8 * KC;     // pairs whose angle a lane computes (d/4)
+    static constexpr int KV = RV / 16;    // 16-byte value latent slices per lane and head
+    static constexpr int DEPTH = 3;       // chunks in flight per wave
+};
+
+// this lane's latent slices of one 32-token chunk, for both heads: keys (ranks 8 h2 .. +7),
+// values (ranks 16 ks + 8 h2 .. +7)
+template <int HG, int KV>
+struct RopeChunk {
+    uint4 k[HG];
+    uint4 v[HG][KV];
+};
+
+template <int D, int RK, int RV>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_rope_kernel(DecodeArgs a) {
+    using SH = RopeShape<D, RK, RV>;
+    constexpr int HG = SH::HG, WAVES = SH::WAVES, KS = SH::KS, KC = SH::KC, NF = SH::NF;
+    constexpr int KV = SH::KV, DEPTH = SH::DEPTH;
+    constexpr int NT = 64 * WAVES;
+    static_assert(kMaxChunksPerSplit <= 64 * WAVES, "one page-table entry per lane and wave");
+    static_assert(HG * D <= NT, "one output element per thread");
+
+    __shared__ __align__(16) uint4 sA[HG][KS][64];          // A operands (bf16), per k-step and lane
+    __shared__ __align__(16) uint16_t sWk[HG][RK + 1][D];   // W_up,t^K rows, then mu_t^K
+    __shared__ __align__(16) uint16_t sWv[HG][RV][D];       // W_up,t^V
+    __shared__ __align__(16) uint16_t sQ[HG][D];
+    __shared__ __align__(16) float sC[WAVES][HG][RV];       // each wave's p-weighted latent sums
+    __shared__ __align__(16) float sCbar[HG][RV];
+    __shared__ float sM[WAVES][HG], sL[WAVES][HG], sSelf[HG];
+    __shared__ int sSlot[kMaxChunksPerSplit];               // chunk -> head h0's first pool row
+
+    const int S = a.S, HP = a.H / HG;
+    const int id = xcd_work_item(blockIdx.x, gridDim.x);
+    const int s = id % S;
+    const int hp = (id / S) % HP;
+    const int b = id / (S * HP);
+    const int h0 = HG * hp;                                  // heads h0 .. h0 + HG - 1
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h2 = lane >> 5;
+
+    // ---- this split's token range and its chunk -> pool row table
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    const int j_begin = s * a.tokens_per_split;
+    const int j_end = min(j_begin + a.tokens_per_split, len);
+    const int nchunks = j_end > j_begin ? (j_end - j_begin + 31) >> 5 : 0;
+    const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+    // chunk c -> head h0's row of its first token (head h0 + e: e * P rows on, the next group of
+    // the same page); negative marks an invalid page id.  The table read is clamped.
+    auto slot_of = [&](int c) {
+        const int j = j_begin + 32 * c;
+        const int page = bt[min(j / a.P, a.max_pages - 1)];
+        const bool bad = (unsigned)page >= (unsigned)a.n_pages;
+        const int row = ((bad ? 0 : page) * a.G + h0) * a.P + j % a.P;
+        return bad ? -row - 1 : row;
+    };
+    const uint16_t *kpool = static_cast<const uint16_t *>(a.k_pool);
+    const uint16_t *vpool = static_cast<const uint16_t *>(a.v_pool);
+    // chunk c at row `slot`: lanes past the sequence end read the chunk's last valid token (its
+    // weight is zero); a chunk past the end (only ever prefetched) reads its page slot's first row
+    auto load_slot = [&](int c, int slot, RopeChunk<HG, KV> &x) {
+        const int row = __builtin_amdgcn_readfirstlane(slot < 0 ? -slot - 1 : slot);
+        const int valid = j_end - (j_begin + 32 * c);
+        const int tok = min(l32, max(valid - 1, 0));
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const size_t r = (size_t)(row + e * a.P + tok);
+            x.k[e] = *reinterpret_cast<const uint4 *>(kpool + r * RK + 8 * h2);
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks)
+                x.v[e][ks] = *reinterpret_cast<const uint4 *>(vpool + r * RV + 16 * ks + 8 * h2);
+        }
+    };
+    auto load = [&](int c, RopeChunk<HG, KV> &x) { load_slot(c, sSlot[c], x); };
+
+    // ---- prologue, in issue order: (1) the page-table entries of this wave's first chunks,
+    // (2) every set-up operand raw into registers, (3) the first latent chunks, (4) LDS stores and
+    // the work that waits on (2).  All loads are unconditional at clamped in-bounds indices.
+    const int c_last = max(nchunks - 1, 0);
+    int first[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) first[i] = slot_of(wave + i * WAVES);
+
+    // W_up,t^K and W_up,t^V of heads h0 .. h0 + HG - 1: consecutive groups, one contiguous block
+    // of HG * r * d elements each, in 16-byte pieces
+    const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) + ((size_t)a.t * a.G + h0) * RK * D;
+    const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) + ((size_t)a.t * a.G + h0) * RV * D;
+    constexpr int PWK = HG * RK * D / 8, PWV = HG * RV * D / 8;
+    constexpr int UWK = (PWK + NT - 1) / NT, UWV = (PWV + NT - 1) / NT;
+    uint4 wkp[UWK], wvp[UWV];
+#pragma unroll
+    for (int u = 0; u < UWK; ++u)
+        wkp[u] = reinterpret_cast<const uint4 *>(Wk)[min(tid + u * NT, PWK - 1)];
+#pragma unroll
+    for (int u = 0; u < UWV; ++u)
+        wvp[u] = reinterpret_cast<const uint4 *>(Wv)[min(tid + u * NT, PWV - 1)];
+    // element (e, i) = (tid / D, tid % D) of the heads' q, mu_t^K, mu_t^V and own value
+    const int oe = (tid % (HG * D)) / D, oi = tid % D;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h0) * D;
+    const size_t mu_off = (size_t)(h0 + oe) * a.T * a.Dg + (size_t)a.t * a.Dg + oi;
+    const uint16_t q_raw = qp[oe * D + oi];
+    const uint16_t mk_raw = static_cast<const uint16_t *>(a.mu_k)[mu_off];
+    const uint16_t mv_raw = static_cast<const uint16_t *>(a.mu_v)[mu_off];
+    const bool has_self = a.k_self != nullptr;
+    const bool self_here = S == 1 && has_self;
+    // (without a self term this reads mu_t^V instead and the value is dropped)
+    const uint16_t *vsp = self_here ? static_cast<const uint16_t *>(a.v_self) + (size_t)b * a.self_stride +
+                                          (size_t)(h0 + oe) * D + oi
+                                    : static_cast<const uint16_t *>(a.mu_v) + mu_off;
+    const uint16_t vs_raw = *vsp;
+    // the current token's own key for head h0 + (wave % HG), lanes over d (rotation partners too)
+    const int R = a.rope_rot;
+    auto partner = [&](int i) {
+        if (i >= R) return i;
+        return a.rope_style ? (i ^ 1) : (i < R / 2 ? i + R / 2 : i - R / 2);
+    };
+    constexpr int UD = D / 64;
+    const int se = wave % HG;
+    const uint16_t *ksp = has_self ? static_cast<const uint16_t *>(a.k_self) +
+                                         (size_t)b * a.self_stride + (size_t)(h0 + se) * D
+                                   : qp + se * D;
+    uint16_t sq_raw[UD], sk_raw[UD], skp_raw[UD];
+#pragma unroll
+    for (int u = 0; u < UD; ++u) {
+        const int i = lane + 64 * u;
+        sq_raw[u] = qp[se * D + i];
+        sk_raw[u] = ksp[i];
+        skp_raw[u] = ksp[partner(i)];
+    }
+    const int slot_reg = slot_of(min(wave + WAVES * lane, c_last));
+
+    // (3) the first latent chunks of this wave
+    RopeChunk<HG, KV> buf[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
+
+    // (4) LDS: page table, W_up,t, q and mu_t^K
+    if (wave + WAVES * lane < nchunks) sSlot[wave + WAVES * lane] = slot_reg;
+#pragma unroll
+    for (int u = 0; u < UWK; ++u) {
+        const int e = tid + u * NT;   // element 8e of the [HG][RK][D] block
+        if (e < PWK)
+            *reinterpret_cast<uint4 *>(&sWk[(8 * e) / (RK * D)][((8 * e) / D) % RK][(8 * e) % D]) = wkp[u];
+    }
+#pragma unroll
+    for (int u = 0; u < UWV; ++u) {
+        const int e = tid + u * NT;
+        if (e < PWV)
+            *reinterpret_cast<uint4 *>(&sWv[(8 * e) / (RV * D)][((8 * e) / D) % RV][(8 * e) % D]) = wvp[u];
+    }
+    if (tid < HG * D) {
+        sQ[oe][oi] = q_raw;
+        sWk[oe][RK][oi] = mk_raw;
+    }
+    // revolutions per position of pair m, theta^(-2m/R) / (2 pi); pairs m >= R/2 stand for two
+    // unrotated dims (frequency 0)
+    auto rope_rev = [&](int m) {
+        return m < R / 2
+                   ? exp2_(-2.0f * (float)m / (float)R * a.rope_log2_theta) * 0.15915494309189535f
+                   : 0.f;
+    };
+    // this lane's pairs: 16 kc + 8 h2 + e, kc < KC, e < 8 (the Phi rows it holds)
+    float fr[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fr[f] = rope_rev(16 * (f / 8) + 8 * h2 + f % 8);
+    // the rotated self score of head h0 + se: the current token's key turns to position len
+    {
+        float as = 0.f;
+#pragma unroll
+        for (int u = 0; u < UD; ++u) {
+            const int i = lane + 64 * u;
+            float kk = bf2f(sk_raw[u]);
+            if (i < R) {
+                const bool first_el = a.rope_style ? !(i & 1) : i < R / 2;
+                const int m = a.rope_style ? i >> 1 : (first_el ? i : i - R / 2);
+                const float rev = __builtin_amdgcn_fractf((float)len * rope_rev(m));
+                const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                const float kp = bf2f(skp_raw[u]);
+                kk = first_el ? kk * cs - kp * sn : kp * sn + kk * cs;
+            }
+            as += bf2f(sq_raw[u]) * kk;
+        }
+        const float ss = wave_sum(as) * a.scale_log2;
+        if (wave < HG && lane == 0) sSelf[wave] = has_self ? ss : -INFINITY;
+    }
+    __syncthreads();
+
+    // ---- A operands.  Row rho of the 32-row score tile: the MFMA result element v of lane
+    // (l32, h2) is row 8 (v / 4) + 4 h2 + v % 4, so rank 8 h2 + v (v < 8) goes to that row, the
+    // lane's key latent slice lines up with its elements 0..7, and mu_t^K takes element 8 of the
+    // h2 = 0 lanes (row 16); the other rows are zero.  Column k of k-step ks: pair
+    // m = 16 (ks % KC) + 8 h2 + e, cosine bracket for ks < KC, sine bracket after; log2-scaled.
+    auto pair_elems = [&](int m, int &i, int &ip) {
+        if (m >= R / 2) {
+            i = R + 2 * (m - R / 2);
+            ip = i + 1;
+        } else if (a.rope_style) {
+            i = 2 * m;
+            ip = 2 * m + 1;
+        } else {
+            i = m;
+            ip = m + R / 2;
+        }
+    };
+    for (int it = wave; it < HG * KS; it += WAVES) {         // each wave builds whole k-steps
+        const int e = it / KS, ks = it % KS;
+        const bool sine = ks >= KC;
+        const int v = 4 * (l32 / 8) + l32 % 4, vh = (l32 / 4) % 2;   // row l32 = element v of half vh
+        const int kap = v < 8 ? 8 * vh + v : (v == 8 && vh == 0 ? RK : -1);
+        const int kr = max(kap, 0);
+        uint32_t w[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            float c2[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                int i, ip;
+                pair_elems(16 * (ks % KC) + 8 * h2 + 2 * x + y, i, ip);
+                const float qi = bf2f(sQ[e][i]), qip = bf2f(sQ[e][ip]);
+                const float wi = bf2f(sWk[e][kr][i]), wip = bf2f(sWk[e][kr][ip]);
+                const float cf = sine ? qip * wi - qi * wip : qi * wi + qip * wip;
+                c2[y] = kap >= 0 ? cf * a.scale_log2 : 0.f;
+            }
+            w[x] = pk_bf16(c2[0], c2[1]);
+        }
+        sA[e][ks][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __syncthreads();
+
+    // ---- per-head running state: max (log2 domain), this lane's share of the weight sum, and
+    // the p-weighted value latents of ranks 16 ks + 8 h2 + x (fp32)
+    float m_run[HG], l_lane[HG], cb[HG][8 * KV];
+#pragma unroll
+    for (int e = 0; e < HG; ++e) {
+        m_run[e] = -INFINITY;
+        l_lane[e] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8 * KV; ++x) cb[e][x] = 0.f;
+    }
+
+    // one chunk, both heads
+    auto compute = [&](int c, const RopeChunk<HG, KV> &x) {
+        const int valid = j_end - (j_begin + 32 * c);   // >= 1, wave-uniform
+        const bool bad = sSlot[c] < 0;
+        // Phi for token l32 (position j_begin + 32c + l32): cosines of this lane's pairs in
+        // k-steps 0..KC-1, sines in KC..KS-1 (element e of k-step kc: pair 16 kc + 8 h2 + e)
+        const float pos = (float)(j_begin + 32 * c + l32);
+        uint4 phi[KS];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint32_t cw[4], sw[4];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const float r0 = __builtin_amdgcn_fractf(pos * fr[8 * kc + 2 * y]);
+                const float r1 = __builtin_amdgcn_fractf(pos * fr[8 * kc + 2 * y + 1]);
+                cw[y] = pk_bf16(__builtin_amdgcn_cosf(r0), __builtin_amdgcn_cosf(r1));
+                sw[y] = pk_bf16(__builtin_amdgcn_sinf(r0), __builtin_amdgcn_sinf(r1));
+            }
+            phi[kc] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            phi[KC + kc] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+        }
+        // the A operands are read from LDS at every chunk: an index the compiler cannot see
+        // through keeps it from holding all of them in registers across the loop
+        int la = lane;
+        asm volatile("" : "+v"(la));
+        f32x16 acc[HG];
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            acc[e] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc[e] = mfma32x32x16(sA[e][ks][la], phi[ks], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const uint4 kx = x.k[e];
+            float sp = (h2 == 0 ? acc[e][8] : 0.f);
+            sp = fmaf(lo_bf(kx.x), acc[e][0], sp);
+            sp = fmaf(hi_bf(kx.x), acc[e][1], sp);
+            sp = fmaf(lo_bf(kx.y), acc[e][2], sp);
+            sp = fmaf(hi_bf(kx.y), acc[e][3], sp);
+            sp = fmaf(lo_bf(kx.z), acc[e][4], sp);
+            sp = fmaf(hi_bf(kx.z), acc[e][5], sp);
+            sp = fmaf(lo_bf(kx.w), acc[e][6], sp);
+            sp = fmaf(hi_bf(kx.w), acc[e][7], sp);
+            float sc = add_swap32(sp);                  // token l32's score, in both lane halves
+            if (l32 >= valid) sc = -INFINITY;
+            if (bad) sc = __builtin_nanf("");
+            // online softmax (log2 domain); the running max only moves when a score exceeds it,
+            // so the rescale is skipped otherwise (a wave-uniform branch)
+            if (__builtin_amdgcn_ballot_w64(sc > m_run[e]) != 0) {
+                const float r = row16_max(sc);
+                const float cmax =
+                    fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16)));
+                const float m_new = fmaxf(m_run[e], cmax);
+                const float alpha = exp2_(m_run[e] - m_new);
+                l_lane[e] *= alpha;
+#pragma unroll
+                for (int y = 0; y < 8 * KV; ++y) cb[e][y] *= alpha;
+                m_run[e] = m_new;
+            }
+            const float p = exp2_(sc - m_run[e]);
+            l_lane[e] += (h2 == 0 ? p : 0.f);
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks) {
+                const uint4 vx = x.v[e][ks];
+                cb[e][8 * ks + 0] = fmaf(p, lo_bf(vx.x), cb[e][8 * ks + 0]);
+                cb[e][8 * ks + 1] = fmaf(p, hi_bf(vx.x), cb[e][8 * ks + 1]);
+                cb[e][8 * ks + 2] = fmaf(p, lo_bf(vx.y), cb[e][8 * ks + 2]);
+                cb[e][8 * ks + 3] = fmaf(p, hi_bf(vx.y), cb[e][8 * ks + 3]);
+                cb[e][8 * ks + 4] = fmaf(p, lo_bf(vx.z), cb[e][8 * ks + 4]);
+                cb[e][8 * ks + 5] = fmaf(p, hi_bf(vx.z), cb[e][8 * ks + 5]);
+                cb[e][8 * ks + 6] = fmaf(p, lo_bf(vx.w), cb[e][8 * ks + 6]);
+                cb[e][8 * ks + 7] = fmaf(p, hi_bf(vx.w), cb[e][8 * ks + 7]);
+            }
+        }
+    };
+
+    // ---- main loop: chunks wave, wave + WAVES, ...; a buffer is refilled with the chunk DEPTH
+    // rounds ahead as soon as it has been consumed (prefetch indices clamped to the last chunk).
+    // Waves w and w + 4 share a SIMD, whose arbiter issues from the older wave first; a wave's
+    // issue priority rises with the chunks it has left, which keeps the two in step.
+    auto fair_prio = [](int left) {
+        if (left > 12) __builtin_amdgcn_s_setprio(3);
+        else if (left > 6) __builtin_amdgcn_s_setprio(2);
+        else if (left > 3) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+    };
+    if (wave < nchunks) {
+        const int rounds = (nchunks - wave + WAVES - 1) / WAVES;   // >= 1
+        int c = wave, r = 0;
+        for (; r + DEPTH <= rounds; r += DEPTH) {
+            fair_prio(rounds - r);
+#pragma unroll
+            for (int i = 0; i < DEPTH; ++i) {
+                compute(c, buf[i]);
+                load(min(c + DEPTH * WAVES, nchunks - 1), buf[i]);
+                c += WAVES;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i + 1 < DEPTH; ++i) {
+            if (r + i < rounds) {
+                compute(c, buf[i]);
+                c += WAVES;
+            }
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    // ---- merge: lanes (the 32 tokens of each half), then waves, then expand the latent sums
+#pragma unroll
+    for (int e = 0; e < HG; ++e) {
+        const float lw = wave_sum(l_lane[e]);
+#pragma unroll
+        for (int y = 0; y < 8 * KV; ++y) cb[e][y] = group_sum<32>(cb[e][y]);
+        if (l32 == 0) {
+#pragma unroll
+            for (int ks = 0; ks < KV; ++ks)
+#pragma unroll
+                for (int y = 0; y < 8; ++y) sC[wave][e][16 * ks + 8 * h2 + y] = cb[e][8 * ks + y];
+        }
+        if (lane == 0) {
+            sM[wave][e] = m_run[e];
+            sL[wave][e] = lw;
+        }
+    }
+    __syncthreads();
+    // the heads' maxima over the waves (and, single split, the self score)
+    auto head_max = [&](int e) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sM[w][e]);
+        if (S == 1) M = fmaxf(M, sSelf[e]);
+        return M;
+    };
+    if (tid < HG * RV) {
+        const int e = tid / RV, k = tid % RV;
+        const float M = head_max(e);
+        float C = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) C += sC[w][e][k] * exp2_(sM[w][e] - M);
+        }
+        sCbar[e][k] = C;
+    }
+    __syncthreads();
+    if (tid < HG * D) {
+        const float M = head_max(oe);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) L += sL[w][oe] * exp2_(sM[w][oe] - M);
+#pragma unroll
+            for (int k = 0; k < RV; ++k) O = fmaf(sCbar[oe][k], bf2f(sWv[oe][k][oi]), O);
+        }
+        const int h = h0 + oe;
+        if (S == 1) {
+            float res = 0.f;
+            if (M != -INFINITY) {
+                const float w_self = self_here ? exp2_(sSelf[oe] - M) : 0.f;
+                const float v_self = self_here ? bf2f(vs_raw) : 0.f;
+                res = (O + L * bf2f(mv_raw) + w_self * v_self) / (L + w_self);
+            }
+            static_cast<uint16_t *>(a.out)[((size_t)b * a.H + h) * D + oi] = f2bf(res);
+        } else {
+            float *rec = a.ws + (((size_t)b * a.H + h) * S + s) * (D + kPartialPad);
+            rec[oi] = O;
+            if (oi == 0) {
+                rec[D] = M;
+                rec[D + 1] = L;
+                if (s == 0) rec[D + 2] = sSelf[oe];   // the rotated self score, for combine
+            }
+        }
+    }
+}
+
+template <int D, int RK, int RV>
+hipError_t launch_rope_t(const DecodeArgs &a, hipStream_t st) {
+    using SH = RopeShape<D, RK, RV>;
+    const unsigned blocks = (unsigned)a.B * (a.H / SH::HG) * a.S;
+    hipLaunchKernelGGL((decode_rope_kernel<D, RK, RV>), dim3(blocks), dim3(64 * SH::WAVES), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_rope_heads_supported(int mode, int H, int d, int r_k, int r_v) {
+    return mode == 0 && H % 2 == 0 && (d == 64 || d == 128) && r_k == 16 &&
+           (r_v == 16 || r_v == 32);
+}
+
+hipError_t launch_decode_rope_heads(const DecodeArgs &a, hipStream_t st) {
+    const int d = a.Dg;
+    if (!decode_rope_heads_supported(a.mode, a.H, d, a.r_k, a.r_v)) return hipErrorInvalidValue;
+    if (d == 128) return a.r_v == 16 ? launch_rope_t<128, 16, 16>(a, st) : launch_rope_t<128, 16, 32>(a, st);
+    return a.r_v == 16 ? launch_rope_t<64, 16, 16>(a, st) : launch_rope_t<64, 16, 32>(a, st);
+}
+
+}  // namespace lla

@@ -342,7 +342,10 @@ lla_status lla_decode_attn_rope(const lla_codec *c, const lla_params *prm, const
     a.rope_style = rope->style;
     a.rope_rot = rope->rot_dims;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_decode_bf16(a, true, s) != hipSuccess) return LLA_ERR_HIP;
+    const hipError_t e = decode_rope_heads_supported(a.mode, a.H, c->d_head, a.r_k, a.r_v)
+                             ? launch_decode_rope_heads(a, s)
+                             : launch_decode_bf16(a, true, s);
+    if (e != hipSuccess) return LLA_ERR_HIP;
     if (plan.splits == 1) return LLA_OK;
     return launch_combine(a, c->d_head, true, true, true, s) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
 }

@@ -109,6 +109,11 @@ __device__ __forceinline__ bool encode_row(const EncodeArgs &a, int row, int &se
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
 hipError_t launch_decode_bf16(const DecodeArgs &a, bool rope, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
+// rotary decode, two heads per wave, scores on the matrix core (per-head codecs, even head count,
+// r_k = 16, r_v 16 or 32, d 64 or 128); same plan, workspace and partial records as
+// launch_decode_bf16(a, true, s)
+bool decode_rope_heads_supported(int mode, int H, int d, int r_k, int r_v);
+hipError_t launch_decode_rope_heads(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_absorbed(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_flat(const DecodeArgs &a, int d, bool bf16, hipStream_t s);
 constexpr int kStreamReadSlots = 512;   // sink entries of lla_stream_read (= its largest grid)

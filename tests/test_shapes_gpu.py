@@ -94,6 +94,24 @@ def test_decode_every_shape(gpu, d, pair, form):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("style", [0, 1])
+@pytest.mark.parametrize("pair", [(16, 16), (16, 32)], ids=["r16_16", "r16_32"])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_rope_odd_head_count(gpu, d, pair, style):
+    """Rotary decode of a rank-16 key codec with an odd head count: the kernel that serves two
+    heads per wave needs an even count, so these calls take the one-head-per-workgroup kernel."""
+    cfg = synth.Config(f"rope_odd_d{d}_{pair[0]}_{pair[1]}", L=1, H=3, d=d, T=4, r_k=pair[0],
+                       r_v=pair[1], B=3, N=1, mode=0,
+                       cid=500 + 10 * HEAD_DIMS.index(d) + DECODE_PAIRS.index(pair))
+    p, dp = _problem(cfg)
+    rope = lla.lla_rope(10000.0, d, style)
+    for t in (0, cfg.T - 1):
+        say(f"rope odd heads d={d} r={pair} style={style} lens={list(p.seq_lens)} t={t}")
+        assert_close(dp.decode(t, True, rope=rope), dp.oracle_decode_rope(t, rope, True), "bf16",
+                     f"odd heads d={d} r={pair} style={style} t={t}")
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("form", ["plain", "absorbed", "rope_half"])
 @pytest.mark.parametrize("pair", [(16, 32), (32, 64), (96, 160)],
                          ids=["r16_32", "r32_64", "r96_160"])
