@@ -25,7 +25,7 @@
 //
 // Work decomposition: one workgroup of 8 waves per (sequence b, pair of heads, context split s),
 // the same splits as the latent decode plan (B * H / 2 * S workgroups of 8 waves = the plan's
-// B * H * S workgroups of 4).  Waves take 32-token chunks round-robin with three chunks of both
+// B * H * S workgroups of 4).  Waves take 32-token chunks round-robin with two chunks of both
 // heads' latents in flight; a single-split plan finishes the output here (self term and
 // (sum p) mu_t^V included), otherwise one (o, m, l) partial per (head, split) goes to combine.hip,
 // with the rotated self score in the first split's record.
@@ -61,7 +61,7 @@ struct RopeShape {
     static constexpr int KC = KS / 2;     // k-steps of the cosine half
     static constexpr int NF = 8 * KC;     // pairs whose angle a lane computes (d/4)
     static constexpr int KV = RV / 16;    // 16-byte value latent slices per lane and head
-    static constexpr int DEPTH = 3;       // chunks in flight per wave
+    static constexpr int DEPTH = 2;       // chunks in flight per wave
 };
 
 // this lane's latent slices of one 32-token chunk, for both heads: keys (ranks 8 h2 .. +7),
@@ -83,13 +83,13 @@ void decode_rope_kernel(DecodeArgs a) {
     static_assert(HG * D <= NT, "one output element per thread");
 
     __shared__ __align__(16) uint4 sA[HG][KS][64];          // A operands (bf16), per k-step and lane
-    __shared__ __align__(16) uint16_t sWk[HG][RK + 1][D];   // W_up,t^K rows, then mu_t^K
-    __shared__ __align__(16) uint16_t sWv[HG][RV][D];       // W_up,t^V
+    constexpr int DP = D + 8;   // padded W_up^K rows: the A build's row-varying reads spread over banks
+    __shared__ __align__(16) uint16_t sWk[HG][RK + 1][DP];  // W_up,t^K rows, then mu_t^K
     __shared__ __align__(16) uint16_t sQ[HG][D];
     __shared__ __align__(16) float sC[WAVES][HG][RV];       // each wave's p-weighted latent sums
     __shared__ __align__(16) float sCbar[HG][RV];
     __shared__ float sM[WAVES][HG], sL[WAVES][HG], sSelf[HG];
-    __shared__ int sSlot[kMaxChunksPerSplit];               // chunk -> head h0's first pool row
+    __shared__ int sSlot[64 * WAVES];                       // chunk -> head h0's first pool row
 
     const int S = a.S, HP = a.H / HG;
     const int id = xcd_work_item(blockIdx.x, gridDim.x);
@@ -143,20 +143,20 @@ void decode_rope_kernel(DecodeArgs a) {
     int first[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) first[i] = slot_of(wave + i * WAVES);
+    // this wave's chunks c = wave + WAVES * lane (entries past the split repeat its last chunk)
+    const int slot_reg = slot_of(min(wave + WAVES * lane, c_last));
 
-    // W_up,t^K and W_up,t^V of heads h0 .. h0 + HG - 1: consecutive groups, one contiguous block
-    // of HG * r * d elements each, in 16-byte pieces
+    // W_up,t^K of heads h0 .. h0 + HG - 1: consecutive groups, one contiguous block of
+    // HG * r_k * d elements, in 16-byte pieces (W_up,t^V is read at the end, by the threads that
+    // expand the value sums)
     const uint16_t *Wk = static_cast<const uint16_t *>(a.W_up_k) + ((size_t)a.t * a.G + h0) * RK * D;
     const uint16_t *Wv = static_cast<const uint16_t *>(a.W_up_v) + ((size_t)a.t * a.G + h0) * RV * D;
-    constexpr int PWK = HG * RK * D / 8, PWV = HG * RV * D / 8;
-    constexpr int UWK = (PWK + NT - 1) / NT, UWV = (PWV + NT - 1) / NT;
-    uint4 wkp[UWK], wvp[UWV];
+    constexpr int PWK = HG * RK * D / 8;
+    constexpr int UWK = (PWK + NT - 1) / NT;
+    uint4 wkp[UWK];
 #pragma unroll
     for (int u = 0; u < UWK; ++u)
         wkp[u] = reinterpret_cast<const uint4 *>(Wk)[min(tid + u * NT, PWK - 1)];
-#pragma unroll
-    for (int u = 0; u < UWV; ++u)
-        wvp[u] = reinterpret_cast<const uint4 *>(Wv)[min(tid + u * NT, PWV - 1)];
     // element (e, i) = (tid / D, tid % D) of the heads' q, mu_t^K, mu_t^V and own value
     const int oe = (tid % (HG * D)) / D, oi = tid % D;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h0) * D;
@@ -190,37 +190,31 @@ void decode_rope_kernel(DecodeArgs a) {
         sk_raw[u] = ksp[i];
         skp_raw[u] = ksp[partner(i)];
     }
-    const int slot_reg = slot_of(min(wave + WAVES * lane, c_last));
 
-    // (3) the first latent chunks of this wave
+    // (3) the first latent chunks of this wave.  The set-up loads above stay ahead of them: a
+    // wave's loads complete in order, and the LDS stores below wait only for those.
+    __builtin_amdgcn_sched_barrier(0);
     RopeChunk<HG, KV> buf[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
 
-    // (4) LDS: page table, W_up,t, q and mu_t^K
-    if (wave + WAVES * lane < nchunks) sSlot[wave + WAVES * lane] = slot_reg;
+    // (4) LDS: page table, W_up,t, q and mu_t^K.  Every store is unconditional (threads past a
+    // table's end write a copy of its last entry, the same value), so no load is moved into a
+    // branch behind the latent burst.
+    sSlot[wave + WAVES * lane] = slot_reg;
 #pragma unroll
     for (int u = 0; u < UWK; ++u) {
-        const int e = tid + u * NT;   // element 8e of the [HG][RK][D] block
-        if (e < PWK)
-            *reinterpret_cast<uint4 *>(&sWk[(8 * e) / (RK * D)][((8 * e) / D) % RK][(8 * e) % D]) = wkp[u];
+        const int e = min(tid + u * NT, PWK - 1);   // element 8e of the [HG][RK][D] block
+        *reinterpret_cast<uint4 *>(&sWk[(8 * e) / (RK * D)][((8 * e) / D) % RK][(8 * e) % D]) = wkp[u];
     }
-#pragma unroll
-    for (int u = 0; u < UWV; ++u) {
-        const int e = tid + u * NT;
-        if (e < PWV)
-            *reinterpret_cast<uint4 *>(&sWv[(8 * e) / (RV * D)][((8 * e) / D) % RV][(8 * e) % D]) = wvp[u];
-    }
-    if (tid < HG * D) {
-        sQ[oe][oi] = q_raw;
-        sWk[oe][RK][oi] = mk_raw;
-    }
+    sQ[oe][oi] = q_raw;          // threads from HG * D on repeat (oe, oi) of thread tid - HG * D
+    sWk[oe][RK][oi] = mk_raw;
     // revolutions per position of pair m, theta^(-2m/R) / (2 pi); pairs m >= R/2 stand for two
     // unrotated dims (frequency 0)
+    const float kexp = R > 0 ? -2.0f * a.rope_log2_theta / (float)R : 0.f;
     auto rope_rev = [&](int m) {
-        return m < R / 2
-                   ? exp2_(-2.0f * (float)m / (float)R * a.rope_log2_theta) * 0.15915494309189535f
-                   : 0.f;
+        const float f = exp2_((float)m * kexp) * 0.15915494309189535f;
+        return m < R / 2 ? f : 0.f;
     };
     // this lane's pairs: 16 kc + 8 h2 + e, kc < KC, e < 8 (the Phi rows it holds)
     float fr[NF];
@@ -254,16 +248,12 @@ void decode_rope_kernel(DecodeArgs a) {
     // h2 = 0 lanes (row 16); the other rows are zero.  Column k of k-step ks: pair
     // m = 16 (ks % KC) + 8 h2 + e, cosine bracket for ks < KC, sine bracket after; log2-scaled.
     auto pair_elems = [&](int m, int &i, int &ip) {
-        if (m >= R / 2) {
-            i = R + 2 * (m - R / 2);
-            ip = i + 1;
-        } else if (a.rope_style) {
-            i = 2 * m;
-            ip = 2 * m + 1;
-        } else {
-            i = m;
-            ip = m + R / 2;
-        }
+        const bool rot = m < R / 2;
+        const int i_rot = a.rope_style ? 2 * m : m;
+        const int ip_rot = a.rope_style ? 2 * m + 1 : m + R / 2;
+        const int i_flat = R + 2 * (m - R / 2);
+        i = rot ? i_rot : i_flat;
+        ip = rot ? ip_rot : i_flat + 1;
     };
     for (int it = wave; it < HG * KS; it += WAVES) {         // each wave builds whole k-steps
         const int e = it / KS, ks = it % KS;
@@ -301,14 +291,24 @@ void decode_rope_kernel(DecodeArgs a) {
         for (int x = 0; x < 8 * KV; ++x) cb[e][x] = 0.f;
     }
 
+    // the A operands of both heads stay in registers
+    uint4 areg[HG][KS];
+#pragma unroll
+    for (int e = 0; e < HG; ++e)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) areg[e][ks] = sA[e][ks][lane];
+
     // one chunk, both heads
     auto compute = [&](int c, const RopeChunk<HG, KV> &x) {
         const int valid = j_end - (j_begin + 32 * c);   // >= 1, wave-uniform
         const bool bad = sSlot[c] < 0;
-        // Phi for token l32 (position j_begin + 32c + l32): cosines of this lane's pairs in
-        // k-steps 0..KC-1, sines in KC..KS-1 (element e of k-step kc: pair 16 kc + 8 h2 + e)
+        // Phi for token l32 (position j_begin + 32c + l32), one cosine k-step and its sine
+        // k-step at a time (element e of k-step kc: pair 16 kc + 8 h2 + e), each pair of k-steps
+        // feeding both heads' MFMAs as soon as it is built
         const float pos = (float)(j_begin + 32 * c + l32);
-        uint4 phi[KS];
+        f32x16 acc[HG];
+#pragma unroll
+        for (int e = 0; e < HG; ++e) acc[e] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             uint32_t cw[4], sw[4];
@@ -319,19 +319,12 @@ void decode_rope_kernel(DecodeArgs a) {
                 cw[y] = pk_bf16(__builtin_amdgcn_cosf(r0), __builtin_amdgcn_cosf(r1));
                 sw[y] = pk_bf16(__builtin_amdgcn_sinf(r0), __builtin_amdgcn_sinf(r1));
             }
-            phi[kc] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-            phi[KC + kc] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
-        }
-        // the A operands are read from LDS at every chunk: an index the compiler cannot see
-        // through keeps it from holding all of them in registers across the loop
-        int la = lane;
-        asm volatile("" : "+v"(la));
-        f32x16 acc[HG];
+            const uint4 pc = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            const uint4 ps = make_uint4(sw[0], sw[1], sw[2], sw[3]);
 #pragma unroll
-        for (int e = 0; e < HG; ++e) {
-            acc[e] = f32x16{};
+            for (int e = 0; e < HG; ++e) acc[e] = mfma32x32x16(areg[e][kc], pc, acc[e]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc[e] = mfma32x32x16(sA[e][ks][la], phi[ks], acc[e]);
+            for (int e = 0; e < HG; ++e) acc[e] = mfma32x32x16(areg[e][KC + kc], ps, acc[e]);
         }
 #pragma unroll
         for (int e = 0; e < HG; ++e) {
@@ -410,6 +403,11 @@ void decode_rope_kernel(DecodeArgs a) {
         }
     }
     __builtin_amdgcn_s_setprio(0);
+    // this thread's output column of W_up,t^V (head h0 + oe, element oi): in flight during the
+    // merge below
+    uint16_t wv_raw[RV];
+#pragma unroll
+    for (int k = 0; k < RV; ++k) wv_raw[k] = Wv[((size_t)oe * RV + k) * D + oi];
 
     // ---- merge: lanes (the 32 tokens of each half), then waves, then expand the latent sums
 #pragma unroll
@@ -455,7 +453,7 @@ void decode_rope_kernel(DecodeArgs a) {
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) L += sL[w][oe] * exp2_(sM[w][oe] - M);
 #pragma unroll
-            for (int k = 0; k < RV; ++k) O = fmaf(sCbar[oe][k], bf2f(sWv[oe][k][oi]), O);
+            for (int k = 0; k < RV; ++k) O = fmaf(sCbar[oe][k], bf2f(wv_raw[k]), O);
         }
         const int h = h0 + oe;
         if (S == 1) {
