@@ -157,39 +157,14 @@ void decode_rope_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < UWK; ++u)
         wkp[u] = reinterpret_cast<const uint4 *>(Wk)[min(tid + u * NT, PWK - 1)];
-    // element (e, i) = (tid / D, tid % D) of the heads' q, mu_t^K, mu_t^V and own value
+    // element (e, i) = (tid / D, tid % D) of the heads' q and mu_t^K (the operands of the output
+    // step, mu_t^V, the own key and value and W_up,t^V, are read after the chunk loop)
     const int oe = (tid % (HG * D)) / D, oi = tid % D;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h0) * D;
     const size_t mu_off = (size_t)(h0 + oe) * a.T * a.Dg + (size_t)a.t * a.Dg + oi;
     const uint16_t q_raw = qp[oe * D + oi];
     const uint16_t mk_raw = static_cast<const uint16_t *>(a.mu_k)[mu_off];
-    const uint16_t mv_raw = static_cast<const uint16_t *>(a.mu_v)[mu_off];
-    const bool has_self = a.k_self != nullptr;
-    const bool self_here = S == 1 && has_self;
-    // (without a self term this reads mu_t^V instead and the value is dropped)
-    const uint16_t *vsp = self_here ? static_cast<const uint16_t *>(a.v_self) + (size_t)b * a.self_stride +
-                                          (size_t)(h0 + oe) * D + oi
-                                    : static_cast<const uint16_t *>(a.mu_v) + mu_off;
-    const uint16_t vs_raw = *vsp;
-    // the current token's own key for head h0 + (wave % HG), lanes over d (rotation partners too)
     const int R = a.rope_rot;
-    auto partner = [&](int i) {
-        if (i >= R) return i;
-        return a.rope_style ? (i ^ 1) : (i < R / 2 ? i + R / 2 : i - R / 2);
-    };
-    constexpr int UD = D / 64;
-    const int se = wave % HG;
-    const uint16_t *ksp = has_self ? static_cast<const uint16_t *>(a.k_self) +
-                                         (size_t)b * a.self_stride + (size_t)(h0 + se) * D
-                                   : qp + se * D;
-    uint16_t sq_raw[UD], sk_raw[UD], skp_raw[UD];
-#pragma unroll
-    for (int u = 0; u < UD; ++u) {
-        const int i = lane + 64 * u;
-        sq_raw[u] = qp[se * D + i];
-        sk_raw[u] = ksp[i];
-        skp_raw[u] = ksp[partner(i)];
-    }
 
     // (3) the first latent chunks of this wave.  The set-up loads above stay ahead of them: a
     // wave's loads complete in order, and the LDS stores below wait only for those.
@@ -220,26 +195,6 @@ void decode_rope_kernel(DecodeArgs a) {
     float fr[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) fr[f] = rope_rev(16 * (f / 8) + 8 * h2 + f % 8);
-    // the rotated self score of head h0 + se: the current token's key turns to position len
-    {
-        float as = 0.f;
-#pragma unroll
-        for (int u = 0; u < UD; ++u) {
-            const int i = lane + 64 * u;
-            float kk = bf2f(sk_raw[u]);
-            if (i < R) {
-                const bool first_el = a.rope_style ? !(i & 1) : i < R / 2;
-                const int m = a.rope_style ? i >> 1 : (first_el ? i : i - R / 2);
-                const float rev = __builtin_amdgcn_fractf((float)len * rope_rev(m));
-                const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-                const float kp = bf2f(skp_raw[u]);
-                kk = first_el ? kk * cs - kp * sn : kp * sn + kk * cs;
-            }
-            as += bf2f(sq_raw[u]) * kk;
-        }
-        const float ss = wave_sum(as) * a.scale_log2;
-        if (wave < HG && lane == 0) sSelf[wave] = has_self ? ss : -INFINITY;
-    }
     __syncthreads();
 
     // ---- A operands.  Row rho of the 32-row score tile: the MFMA result element v of lane
@@ -261,21 +216,43 @@ void decode_rope_kernel(DecodeArgs a) {
         const int v = 4 * (l32 / 8) + l32 % 4, vh = (l32 / 4) % 2;   // row l32 = element v of half vh
         const int kap = v < 8 ? 8 * vh + v : (v == 8 && vh == 0 ? RK : -1);
         const int kr = max(kap, 0);
-        uint32_t w[4];
+        const int m0 = 16 * (ks % KC) + 8 * h2;   // this lane's pairs m0 .. m0 + 7
+        float cf[8];
+        if ((R & 15) == 0) {
+            // each group of 8 pairs is wholly rotated or wholly unrotated: 16-byte reads.  Half
+            // split: elements m0.. and m0 + R/2..; interleaved (and unrotated): 2 m0 .. 2 m0 + 15
+            const bool half = m0 < R / 2 && !a.rope_style;
+            const int o0 = half ? m0 : 2 * m0, o1 = half ? m0 + R / 2 : 2 * m0 + 8;
+            const uint4 w0 = *reinterpret_cast<const uint4 *>(&sWk[e][kr][o0]);
+            const uint4 w1 = *reinterpret_cast<const uint4 *>(&sWk[e][kr][o1]);
+            const uint4 q0 = *reinterpret_cast<const uint4 *>(&sQ[e][o0]);
+            const uint4 q1 = *reinterpret_cast<const uint4 *>(&sQ[e][o1]);
+            const uint32_t W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            const uint32_t Q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            float c2[2];
+            for (int y = 0; y < 8; ++y) {
+                const uint32_t wa = W[y / 2], wb = W[4 + y / 2], qa = Q[y / 2], qb = Q[4 + y / 2];
+                const float wi = half ? ((y & 1) ? hi_bf(wa) : lo_bf(wa)) : lo_bf(W[y]);
+                const float wip = half ? ((y & 1) ? hi_bf(wb) : lo_bf(wb)) : hi_bf(W[y]);
+                const float qi = half ? ((y & 1) ? hi_bf(qa) : lo_bf(qa)) : lo_bf(Q[y]);
+                const float qip = half ? ((y & 1) ? hi_bf(qb) : lo_bf(qb)) : hi_bf(Q[y]);
+                cf[y] = sine ? qip * wi - qi * wip : qi * wi + qip * wip;
+            }
+        } else {
 #pragma unroll
-            for (int y = 0; y < 2; ++y) {
+            for (int y = 0; y < 8; ++y) {
                 int i, ip;
-                pair_elems(16 * (ks % KC) + 8 * h2 + 2 * x + y, i, ip);
+                pair_elems(m0 + y, i, ip);
                 const float qi = bf2f(sQ[e][i]), qip = bf2f(sQ[e][ip]);
                 const float wi = bf2f(sWk[e][kr][i]), wip = bf2f(sWk[e][kr][ip]);
-                const float cf = sine ? qip * wi - qi * wip : qi * wi + qip * wip;
-                c2[y] = kap >= 0 ? cf * a.scale_log2 : 0.f;
+                cf[y] = sine ? qip * wi - qi * wip : qi * wi + qip * wip;
             }
-            w[x] = pk_bf16(c2[0], c2[1]);
         }
+        uint32_t w[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            w[x] = pk_bf16(kap >= 0 ? cf[2 * x] * a.scale_log2 : 0.f,
+                           kap >= 0 ? cf[2 * x + 1] * a.scale_log2 : 0.f);
         sA[e][ks][lane] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __syncthreads();
@@ -403,11 +380,52 @@ void decode_rope_kernel(DecodeArgs a) {
         }
     }
     __builtin_amdgcn_s_setprio(0);
-    // this thread's output column of W_up,t^V (head h0 + oe, element oi): in flight during the
-    // merge below
-    uint16_t wv_raw[RV];
+    // operands of the output step, read only by the waves that use them (threads below HG * D
+    // form the output, waves below HG the self scores), in flight during the merge below: this
+    // thread's column of W_up,t^V, mu_t^V and own value (head h0 + oe, element oi), and the
+    // current token's own key for head h0 + wave (lanes over d, rotation partners too).  The
+    // waves past them, which the SIMDs' oldest-first issue usually leaves last, go straight to
+    // the merge.
+    const bool has_self = a.k_self != nullptr;
+    const bool self_here = S == 1 && has_self;
+    uint16_t wv_raw[RV], mv_raw = 0, vs_raw = 0;
+    if (tid < HG * D) {
 #pragma unroll
-    for (int k = 0; k < RV; ++k) wv_raw[k] = Wv[((size_t)oe * RV + k) * D + oi];
+        for (int k = 0; k < RV; ++k) wv_raw[k] = Wv[((size_t)oe * RV + k) * D + oi];
+        mv_raw = static_cast<const uint16_t *>(a.mu_v)[mu_off];
+        if (self_here)
+            vs_raw = static_cast<const uint16_t *>(a.v_self)[(size_t)b * a.self_stride +
+                                                             (size_t)(h0 + oe) * D + oi];
+    }
+    // the rotated self score of head h0 + wave: the current token's key turns to position len
+    if (wave < HG) {
+        const int se = wave;
+        auto partner = [&](int i) {
+            if (i >= R) return i;
+            return a.rope_style ? (i ^ 1) : (i < R / 2 ? i + R / 2 : i - R / 2);
+        };
+        float as = 0.f;
+        if (has_self) {
+            const uint16_t *ksp = static_cast<const uint16_t *>(a.k_self) +
+                                  (size_t)b * a.self_stride + (size_t)(h0 + se) * D;
+#pragma unroll
+            for (int u = 0; u < D / 64; ++u) {
+                const int i = lane + 64 * u;
+                float kk = bf2f(ksp[i]);
+                if (i < R) {
+                    const bool first_el = a.rope_style ? !(i & 1) : i < R / 2;
+                    const int m = a.rope_style ? i >> 1 : (first_el ? i : i - R / 2);
+                    const float rev = __builtin_amdgcn_fractf((float)len * rope_rev(m));
+                    const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                    const float kp = bf2f(ksp[partner(i)]);
+                    kk = first_el ? kk * cs - kp * sn : kp * sn + kk * cs;
+                }
+                as += bf2f(qp[se * D + i]) * kk;
+            }
+        }
+        const float ss = wave_sum(as) * a.scale_log2;
+        if (lane == 0) sSelf[wave] = has_self ? ss : -INFINITY;
+    }
 
     // ---- merge: lanes (the 32 tokens of each half), then waves, then expand the latent sums
 #pragma unroll
