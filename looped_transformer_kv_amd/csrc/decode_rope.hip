@@ -29,6 +29,8 @@
 // heads' latents in flight; a single-split plan finishes the output here (self term and
 // (sum p) mu_t^V included), otherwise one (o, m, l) partial per (head, split) goes to combine.hip,
 // with the rotated self score in the first split's record.
+#include <cmath>
+
 #include "lla_internal.h"
 
 namespace lla {
@@ -50,6 +52,11 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+// c + a.lo * b.lo + a.hi * b.hi over bf16 pairs, fp32 result (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                           c, false);
+}
 
 template <int D, int RK, int RV>
 struct RopeShape {
@@ -72,7 +79,12 @@ struct RopeChunk {
     uint4 v[HG][KV];
 };
 
-template <int D, int RK, int RV>
+// KF: the number of leading pair groups kc (pairs 16 kc .. 16 kc + 15) whose angles the chunk loop
+// reduces to [0, 1) before the hardware sine and cosine, which take revolutions and are accurate
+// for |x| <= 256.  Frequencies fall with m, so the groups that can pass 256 revolutions come
+// first; the launcher picks KF = 1 when no position of the cache takes a pair m >= 16 that far,
+// else KF = d / 32 (every group).
+template <int D, int RK, int RV, int KF>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_rope_kernel(DecodeArgs a) {
     using SH = RopeShape<D, RK, RV>;
@@ -210,7 +222,10 @@ void decode_rope_kernel(DecodeArgs a) {
         i = rot ? i_rot : i_flat;
         ip = rot ? ip_rot : i_flat + 1;
     };
-    for (int it = wave; it < HG * KS; it += WAVES) {         // each wave builds whole k-steps
+    static_assert((HG * KS) % WAVES == 0, "whole k-steps per wave");
+#pragma unroll
+    for (int j = 0; j < HG * KS / WAVES; ++j) {              // each wave builds whole k-steps
+        const int it = wave + WAVES * j;
         const int e = it / KS, ks = it % KS;
         const bool sine = ks >= KC;
         const int v = 4 * (l32 / 8) + l32 % 4, vh = (l32 / 4) % 2;   // row l32 = element v of half vh
@@ -291,8 +306,11 @@ void decode_rope_kernel(DecodeArgs a) {
             uint32_t cw[4], sw[4];
 #pragma unroll
             for (int y = 0; y < 4; ++y) {
-                const float r0 = __builtin_amdgcn_fractf(pos * fr[8 * kc + 2 * y]);
-                const float r1 = __builtin_amdgcn_fractf(pos * fr[8 * kc + 2 * y + 1]);
+                float r0 = pos * fr[8 * kc + 2 * y], r1 = pos * fr[8 * kc + 2 * y + 1];
+                if (kc < KF) {
+                    r0 = __builtin_amdgcn_fractf(r0);
+                    r1 = __builtin_amdgcn_fractf(r1);
+                }
                 cw[y] = pk_bf16(__builtin_amdgcn_cosf(r0), __builtin_amdgcn_cosf(r1));
                 sw[y] = pk_bf16(__builtin_amdgcn_sinf(r0), __builtin_amdgcn_sinf(r1));
             }
@@ -305,16 +323,14 @@ void decode_rope_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < HG; ++e) {
+            // the token's query over ranks 8 h2 .. + 7, rounded to bf16, against its latent slice
+            // (bf16 pairs, v_dot2_f32_bf16); the mu term stays fp32
             const uint4 kx = x.k[e];
             float sp = (h2 == 0 ? acc[e][8] : 0.f);
-            sp = fmaf(lo_bf(kx.x), acc[e][0], sp);
-            sp = fmaf(hi_bf(kx.x), acc[e][1], sp);
-            sp = fmaf(lo_bf(kx.y), acc[e][2], sp);
-            sp = fmaf(hi_bf(kx.y), acc[e][3], sp);
-            sp = fmaf(lo_bf(kx.z), acc[e][4], sp);
-            sp = fmaf(hi_bf(kx.z), acc[e][5], sp);
-            sp = fmaf(lo_bf(kx.w), acc[e][6], sp);
-            sp = fmaf(hi_bf(kx.w), acc[e][7], sp);
+            sp = dot2bf(pk_bf16(acc[e][0], acc[e][1]), kx.x, sp);
+            sp = dot2bf(pk_bf16(acc[e][2], acc[e][3]), kx.y, sp);
+            sp = dot2bf(pk_bf16(acc[e][4], acc[e][5]), kx.z, sp);
+            sp = dot2bf(pk_bf16(acc[e][6], acc[e][7]), kx.w, sp);
             float sc = add_swap32(sp);                  // token l32's score, in both lane halves
             if (l32 >= valid) sc = -INFINITY;
             if (bad) sc = __builtin_nanf("");
@@ -334,17 +350,20 @@ void decode_rope_kernel(DecodeArgs a) {
             }
             const float p = exp2_(sc - m_run[e]);
             l_lane[e] += (h2 == 0 ? p : 0.f);
+            // p (rounded to bf16) times each bf16 value latent, added in fp32: (p, 0) and (0, p)
+            // against a latent pair pick its low and its high element (v_dot2_f32_bf16)
+            const uint32_t plo = pk_bf16(p, 0.f), phi = pk_bf16(0.f, p);
 #pragma unroll
             for (int ks = 0; ks < KV; ++ks) {
                 const uint4 vx = x.v[e][ks];
-                cb[e][8 * ks + 0] = fmaf(p, lo_bf(vx.x), cb[e][8 * ks + 0]);
-                cb[e][8 * ks + 1] = fmaf(p, hi_bf(vx.x), cb[e][8 * ks + 1]);
-                cb[e][8 * ks + 2] = fmaf(p, lo_bf(vx.y), cb[e][8 * ks + 2]);
-                cb[e][8 * ks + 3] = fmaf(p, hi_bf(vx.y), cb[e][8 * ks + 3]);
-                cb[e][8 * ks + 4] = fmaf(p, lo_bf(vx.z), cb[e][8 * ks + 4]);
-                cb[e][8 * ks + 5] = fmaf(p, hi_bf(vx.z), cb[e][8 * ks + 5]);
-                cb[e][8 * ks + 6] = fmaf(p, lo_bf(vx.w), cb[e][8 * ks + 6]);
-                cb[e][8 * ks + 7] = fmaf(p, hi_bf(vx.w), cb[e][8 * ks + 7]);
+                cb[e][8 * ks + 0] = dot2bf(plo, vx.x, cb[e][8 * ks + 0]);
+                cb[e][8 * ks + 1] = dot2bf(phi, vx.x, cb[e][8 * ks + 1]);
+                cb[e][8 * ks + 2] = dot2bf(plo, vx.y, cb[e][8 * ks + 2]);
+                cb[e][8 * ks + 3] = dot2bf(phi, vx.y, cb[e][8 * ks + 3]);
+                cb[e][8 * ks + 4] = dot2bf(plo, vx.z, cb[e][8 * ks + 4]);
+                cb[e][8 * ks + 5] = dot2bf(phi, vx.z, cb[e][8 * ks + 5]);
+                cb[e][8 * ks + 6] = dot2bf(plo, vx.w, cb[e][8 * ks + 6]);
+                cb[e][8 * ks + 7] = dot2bf(phi, vx.w, cb[e][8 * ks + 7]);
             }
         }
     };
@@ -498,7 +517,17 @@ template <int D, int RK, int RV>
 hipError_t launch_rope_t(const DecodeArgs &a, hipStream_t st) {
     using SH = RopeShape<D, RK, RV>;
     const unsigned blocks = (unsigned)a.B * (a.H / SH::HG) * a.S;
-    hipLaunchKernelGGL((decode_rope_kernel<D, RK, RV>), dim3(blocks), dim3(64 * SH::WAVES), 0, st, a);
+    // the fastest pair past group 0, m = 16: theta^(-32 / rot) / (2 pi) revolutions per position
+    // (frequency 0 when it is not rotated); cached positions are below max_seq_len
+    const int R = a.rope_rot;
+    const double f16 = 16 < R / 2 ? std::exp2(-32.0 / R * a.rope_log2_theta) / (2.0 * M_PI) : 0.0;
+    const bool first_only = (double)a.max_seq_len * f16 < 250.0;
+    if (first_only)
+        hipLaunchKernelGGL((decode_rope_kernel<D, RK, RV, 1>), dim3(blocks), dim3(64 * SH::WAVES), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((decode_rope_kernel<D, RK, RV, SH::KC>), dim3(blocks),
+                           dim3(64 * SH::WAVES), 0, st, a);
     return hipGetLastError();
 }
 

@@ -485,6 +485,20 @@ def test_rope_decode_small(gpu, name, variant, style):
                      f"rope {name}/{variant}/{style} t={t}")
 
 
+def test_rope_fast_rotation(gpu):
+    """theta = 10 over 4000 positions: the pairs past the first 16 turn up to ~356 revolutions,
+    beyond the range the hardware sine and cosine take unreduced, so the rotary decode reduces
+    every pair group's angle (the instantiation the 10^4-theta workloads never launch)."""
+    cfg = synth.CONFIGS["ouro14_21x"]
+    p = tinycase.make(cfg, B=2, N=4000, lens=np.array([4000, 2345], dtype=np.int32))
+    dp = gpucase.DeviceProblem(p)
+    for style in (0, 1):
+        rope = lla.lla_rope(10.0, cfg.d, style)
+        say(f"rope theta 10 style={style} splits={dp.layer.plan.splits}")
+        assert_close(dp.decode(1, True, rope=rope), dp.oracle_decode_rope(1, rope, True), "bf16",
+                     f"rope theta 10 style {style}")
+
+
 def test_rope_split_context_long_positions(gpu):
     """One sequence of 4000 tokens (positions up to 4000, split context: the rotated self score
     reaches combine through the partial record), with a self term."""
