@@ -195,6 +195,12 @@ typedef struct {
  * workspace).  The ledger fixes neither the rotated width nor the pairing, so rot_dims and style
  * are arguments.  bf16 codecs only (LLA_ERR_DTYPE); rope NULL -> LLA_ERR_NULL; theta <= 1, a
  * style other than 0/1, or rot_dims odd, negative or above d_head -> LLA_ERR_SHAPE.
+ * Per-head codecs with r_k = 16, r_v 16 or 32 and an even head count run two heads per wave: the
+ * rotated scores come from the per-position cosines and sines contracted with each head's pair
+ * coefficients on the matrix core (bf16 operands, fp32 accumulation; each token's query over the
+ * ranks rounded to bf16), and values are summed in latent space (bf16 weights, fp32 sums) and
+ * expanded through W_up,t^V once, which equals the reconstruct-then-rotate attention up to
+ * rounding.  Other codecs rotate in the same pair space one head per workgroup.
  */
 lla_status lla_decode_attn_rope(const lla_codec *codec, const lla_params *params,
                                 const lla_cache *cache, int32_t t, const lla_rope *rope,
