@@ -17,11 +17,12 @@
 // matrix Phi = [cos phi; sin phi] (d x 32) depends on the positions only, so it is built once per
 // chunk for every head the wave serves, and one MFMA contraction per head, A Phi, gives each token
 // its query over the latent ranks (and its mu term): the score is then a 16-term dot product with
-// the token's latent.  Both operands are bf16 (A rounded once from fp32; Phi from the hardware
-// sine and cosine), accumulation fp32.
+// the token's latent.  Both MFMA operands are bf16 (A rounded once from fp32; Phi from the
+// hardware sine and cosine), accumulation fp32; the token's query is rounded to bf16 for the dot
+// (bf16 pairs, v_dot2_f32_bf16), the mu term stays fp32.
 // Values.  The rotation leaves values alone, so sum_j p_j V_hat(j) = (sum_j p_j c_v(j)) W_up,t^V +
-// (sum_j p_j) mu_t^V: the p-weighted value latents accumulate in fp32 and are expanded once, at
-// the end.
+// (sum_j p_j) mu_t^V: the value latents, weighted by p rounded to bf16, accumulate in fp32 and
+// are expanded once, at the end.
 //
 // Work decomposition: one workgroup of 8 waves per (sequence b, pair of heads, context split s),
 // the same splits as the latent decode plan (B * H / 2 * S workgroups of 8 waves = the plan's
