@@ -6,9 +6,10 @@
   Covered for the reconstructing, absorbed (per head and the all-heads LLA-2D kernel) and rotary
   decodes (bf16), the fp32 decode and the chunked prefill.  An encode whose write position lands on such a page writes nothing for that
   row and leaves every other write as it was.
-* HIP-graph replay.  Decode, encode-append (one layer or many) and prefill captured once and
-  replayed several times, with eager work and synchronisations between the replays, give
-  bitwise the eager results on every replay (the benchmark times graph launches).
+* HIP-graph replay.  Decode (plain, absorbed, rotary), encode-append (one layer or many) and
+  prefill captured once and replayed several times, with eager work and synchronisations between
+  the replays, give bitwise the eager results on every replay (the benchmark times graph
+  launches).
 """
 import sys
 
@@ -164,6 +165,8 @@ def test_graph_replay_matches_eager(gpu):
     pos = torch.full((3,), 300, dtype=torch.int32, device=gpu)
     out_d = torch.empty((3, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
     out_a = torch.empty_like(out_d)
+    out_r = torch.empty_like(out_d)
+    rope = lla.lla_rope(10000.0, cfg.d, 0)
     ck = torch.empty((3, cfg.G, cfg.r_k), dtype=torch.float32, device=gpu)
     cv = torch.empty((3, cfg.G, cfg.r_v), dtype=torch.float32, device=gpu)
     out_p = torch.empty((3, ch.Pn, cfg.H, cfg.d), dtype=torch.bfloat16, device=gpu)
@@ -172,10 +175,11 @@ def test_graph_replay_matches_eager(gpu):
     def work():
         dp.layer.decode(t, q, out_d, ws, ks, vs, stride)
         dp.layer.decode_absorbed(t, q, out_a, ws, ks, vs, stride)
+        dp.layer.decode_rope(t, rope, q, out_r, ws, ks, vs, stride)
         dp.layer.encode_append(dp.x_k, dp.x_v, pos, ck, cv)
         ch.dp.layer.prefill(t, ch.Pn, ch.nd, ch.qd[t], kn, vn, out_p, new_stride=stride)
 
-    outs = (out_d, out_a, ck, cv, out_p)
+    outs = (out_d, out_a, out_r, ck, cv, out_p)
 
     def snap():
         return [synth.from_device(o) for o in outs]
