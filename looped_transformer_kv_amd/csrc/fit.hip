@@ -271,29 +271,44 @@ __global__ __launch_bounds__(FT) void fit_mul_kernel(FitArgs a) {
         if (u < nu) a.W[((size_t)g * a.X + 32 * q + il) * rb + c0 + 8 * u] = acc[u];
 }
 
-// 32-row chunks of an X x rb block (row-major, pitch rb) stream through sY (pitch kFitMaxCols + 1,
-// odd, so rows read across lanes fall in different banks); slot m of thread tid is chunk element
-// tid + FT m (a chunk's rows are contiguous in memory), and the next chunk's loads are in flight
-// while the current one is used.
-constexpr int CR = 32;                                   // rows of a streamed chunk
-constexpr int CHE = (CR * kFitMaxCols + FT - 1) / FT;    // chunk elements per thread
+constexpr int CR = 32;                                   // rows of a fit_apply_kernel block
+
+// The orthonormalisation's LDS layout for NB 16-column tiles.  Blocks of up to 3 tiles (48
+// columns, the small ranks) hold 16 NB columns per matrix row, form L^-1 in a second matrix (every
+// column at once) and stream 64-row chunks; wider blocks hold kFitMaxCols columns, form the
+// inverse in place (one matrix: 137 KB of LDS at 168 columns) and stream 32-row chunks.
+template <int NB>
+struct OrthCfg {
+    static constexpr bool SMALL = NB <= 3;
+    static constexpr int C = SMALL ? 16 * NB : kFitMaxCols;   // columns a matrix row holds
+    static constexpr int P = C + 1;                           // LDS pitch (odd: rows read across
+                                                              // lanes fall in different banks)
+    static constexpr int OR = SMALL ? 64 : 32;                // rows of a streamed chunk
+    static constexpr int CHE = (OR * C + FT - 1) / FT;        // chunk elements per thread
+};
+
+// OR-row chunks of an X x rb block (row-major, pitch rb) stream through sY; slot m of thread tid
+// is chunk element tid + FT m (a chunk's rows are contiguous in memory), and the next chunk's
+// loads are in flight while the current one is used.  X is a multiple of 64.
+template <int NB>
 struct ChunkStream {
+    using CF = OrthCfg<NB>;
     int n, rb;
-    float pre[CHE];
+    float pre[CF::CHE];
     __device__ void init(int rb_) {
         rb = rb_;
-        n = CR * rb;
+        n = CF::OR * rb;
     }
     __device__ void fetch(const float *Y, int k0) {
 #pragma unroll
-        for (int m = 0; m < CHE; ++m) {
+        for (int m = 0; m < CF::CHE; ++m) {
             const int e = min((int)threadIdx.x + FT * m, n - 1);
             pre[m] = Y[(size_t)k0 * rb + e];
         }
     }
-    __device__ void stage(float (*sY)[kFitMaxCols + 1]) {
+    __device__ void stage(float (*sY)[CF::P]) {
 #pragma unroll
-        for (int m = 0; m < CHE; ++m) {
+        for (int m = 0; m < CF::CHE; ++m) {
             const int e = (int)threadIdx.x + FT * m;
             if (e < n) sY[e / rb][e % rb] = pre[m];
         }
@@ -307,26 +322,27 @@ struct ChunkStream {
 // loops carry no guards (a guard per term would make every LDS read wait on its own).
 template <int NB>
 __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
-                                              float (*L)[kFitMaxCols + 1],
-                                              float (*sY)[kFitMaxCols + 1]) {
+                                              float (*L)[OrthCfg<NB>::P],
+                                              float (*sY)[OrthCfg<NB>::P]) {
+    using CF = OrthCfg<NB>;
     const int rb = a.rb, tid = threadIdx.x;
     const int tp = tid >> 4, tq = tid & 15;
     float acc[NB][NB] = {};
-    ChunkStream cs;
+    ChunkStream<NB> cs;
     cs.init(rb);
     cs.fetch(Y, 0);
-    for (int k0 = 0; k0 < a.X; k0 += CR) {
+    for (int k0 = 0; k0 < a.X; k0 += CF::OR) {
         __syncthreads();
         cs.stage(sY);
         __syncthreads();
-        if (k0 + CR < a.X) cs.fetch(Y, k0 + CR);
+        if (k0 + CF::OR < a.X) cs.fetch(Y, k0 + CF::OR);
 #pragma unroll 4
-        for (int k = 0; k < CR; ++k) {
+        for (int k = 0; k < CF::OR; ++k) {
             float yp[NB], yq[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-                yp[u] = sY[k][min(tp + 16 * u, kFitMaxCols)];
-                yq[u] = sY[k][min(tq + 16 * u, kFitMaxCols)];
+                yp[u] = sY[k][min(tp + 16 * u, CF::C)];
+                yq[u] = sY[k][min(tq + 16 * u, CF::C)];
             }
 #pragma unroll
             for (int u = 0; u < NB; ++u)
@@ -367,7 +383,7 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
 #pragma unroll
             for (int v = 0; v < NB; ++v) {
                 const int p = tp + 16 * u, q = tq + 16 * v;
-                if (16 * NB > kFitMaxCols && (p >= kFitMaxCols || q >= kFitMaxCols)) continue;
+                if (16 * NB > CF::C && (p >= CF::C || q >= CF::C)) continue;
                 const bool upd = p > j && q > j && q <= p && p < rb;
                 const float val = L[p][q] - L[p][j] * L[q][j];
                 *(upd ? &L[p][q] : &sink[tid]) = val;
@@ -376,71 +392,106 @@ __device__ __forceinline__ void gram_cholesky(const FitArgs &a, const float *Y,
     }
 }
 
-// out = Y L^{-T}.  L^{-1} overwrites L in LDS (lower triangular, zero above the diagonal), column
-// by column from the last: M[i][j] = -(sum_{k=j+1..i} M[i][k] L[k][j]) / L[j][j], where the
-// columns k > j of M are already in place and L's column j is kept in sX; then each 32-row chunk
-// of Y is multiplied by it in full: thread (row tid / 8, columns tid % 8 + 8v) sums over k < rb.
-// out may alias Y: a chunk is read completely (and the next one fetched) before any of it is
-// written.
+// out = Y L^{-T}; then each chunk of Y is multiplied by L^{-1} in full.  out may alias Y: a chunk
+// is read completely (and the next one fetched) before any of it is written.
+// Small blocks: L^{-1} in Li by elimination on [L | I] (step j scales row j, then clears column j
+// below it for every column at once, O(1) work per thread and step); 64-row chunks, thread
+// (row tid / 4, columns tid % 4 + 4v).
+// Wide blocks: L^{-1} overwrites L, column by column from the last:
+// M[i][j] = -(sum_{k=j+1..i} M[i][k] L[k][j]) / L[j][j], where the columns k > j of M are already
+// in place and L's column j is kept in sX; 32-row chunks, thread (row tid / 8, columns
+// tid % 8 + 8v).  In both, all column slots are summed over k < rb (rows of the inverse past rb
+// read in-bounds LDS and their sums are never stored; its upper triangle is zero), so the loop
+// body has no guard.
 template <int NB>
 __device__ __forceinline__ void solve_rows(const FitArgs &a, const float *Y, float *out,
-                                           float (*L)[kFitMaxCols + 1],
-                                           float (*sY)[kFitMaxCols + 1]) {
-    constexpr int SV = 2 * NB;                           // output column slots per thread
+                                           float (*L)[OrthCfg<NB>::P],
+                                           float (*Li)[OrthCfg<NB>::P],
+                                           float (*sY)[OrthCfg<NB>::P]) {
+    using CF = OrthCfg<NB>;
+    constexpr int LN = CF::SMALL ? 4 : 8;                // lanes per chunk row
+    constexpr int SV = 16 * NB / LN;                     // output column slots per thread
     const int rb = a.rb, tid = threadIdx.x;
-    __shared__ float sX[kFitMaxCols];
-    for (int j = rb - 1; j >= 0; --j) {
-        const float djj = 1.f / L[j][j];
-        if (tid > j && tid < rb) sX[tid] = L[tid][j];
+    float (*M)[CF::P] = CF::SMALL ? Li : L;              // where L^{-1} ends up
+    if constexpr (CF::SMALL) {
+        const int tp = tid >> 4, tq = tid & 15;
+        __shared__ float sink[FT];                       // target of stores that must not land
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+#pragma unroll
+            for (int v = 0; v < NB; ++v) {
+                const int p = tp + 16 * u, q = tq + 16 * v;
+                if (p < rb && q < rb) Li[p][q] = p == q ? 1.f : 0.f;
+            }
         __syncthreads();
-        if (tid > j && tid < rb) {
-            float sum = 0.f;
-            for (int k = j + 1; k <= tid; ++k) sum += L[tid][k] * sX[k];
-            L[tid][j] = -djj * sum;
-        } else if (tid == j) {
-            L[j][j] = djj;
+        for (int j = 0; j < rb; ++j) {
+            if (tid <= j) Li[j][tid] /= L[j][j];
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+#pragma unroll
+                for (int v = 0; v < NB; ++v) {
+                    const int p = tp + 16 * u, c = tq + 16 * v;
+                    const bool upd = p > j && p < rb && c <= j;
+                    const float val = Li[p][c] - L[p][j] * Li[j][c];
+                    *(upd ? &Li[p][c] : &sink[tid]) = val;   // dummy slot: see gram_cholesky
+                }
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        __shared__ float sX[kFitMaxCols];
+        for (int j = rb - 1; j >= 0; --j) {
+            const float djj = 1.f / L[j][j];
+            if (tid > j && tid < rb) sX[tid] = L[tid][j];
+            __syncthreads();
+            if (tid > j && tid < rb) {
+                float sum = 0.f;
+                for (int k = j + 1; k <= tid; ++k) sum += L[tid][k] * sX[k];
+                L[tid][j] = -djj * sum;
+            } else if (tid == j) {
+                L[j][j] = djj;
+            }
+            __syncthreads();
+        }
     }
-    const int i = tid >> 3, jq = tid & 7;
-    const int nv = (rb - jq + 7) / 8;
-    ChunkStream cs;
+    const int i = tid / LN, jq = tid % LN;
+    const int nv = (rb - jq + LN - 1) / LN;
+    ChunkStream<NB> cs;
     cs.init(rb);
     cs.fetch(Y, 0);
-    for (int k0 = 0; k0 < a.X; k0 += CR) {
+    for (int k0 = 0; k0 < a.X; k0 += CF::OR) {
         __syncthreads();                                 // the previous chunk is used
         cs.stage(sY);
         __syncthreads();
-        if (k0 + CR < a.X) cs.fetch(Y, k0 + CR);
-        // all SV column slots are summed over k < rb (rows of the inverse past rb read in-bounds
-        // LDS and their sums are never stored; its upper triangle is zero), so the loop body has
-        // no guard
+        if (k0 + CF::OR < a.X) cs.fetch(Y, k0 + CF::OR);
         float acc[SV] = {};
 #pragma unroll 4
         for (int k = 0; k < rb; ++k) {
             const float y = sY[i][k];
 #pragma unroll
-            for (int v = 0; v < SV; ++v) acc[v] += y * L[min(jq + 8 * v, kFitMaxCols - 1)][k];
+            for (int v = 0; v < SV; ++v) acc[v] += y * M[min(jq + LN * v, CF::C - 1)][k];
         }
 #pragma unroll
         for (int v = 0; v < SV; ++v)
-            if (v < nv) out[(size_t)(k0 + i) * rb + jq + 8 * v] = acc[v];
+            if (v < nv) out[(size_t)(k0 + i) * rb + jq + LN * v] = acc[v];
     }
 }
 
 // V = orth(W) by CholeskyQR2 (W L1^-T, then once more)
 template <int NB>
 __global__ __launch_bounds__(FT) void fit_orth_kernel(FitArgs a) {
-    __shared__ float L[kFitMaxCols][kFitMaxCols + 1];
-    __shared__ float sY[CR][kFitMaxCols + 1];
+    using CF = OrthCfg<NB>;
+    __shared__ float L[CF::C][CF::P];
+    __shared__ float Li[CF::SMALL ? CF::C : 1][CF::P];
+    __shared__ float sY[CF::OR][CF::P];
     const int g = blockIdx.x;
     float *W = a.W + (size_t)g * a.X * a.rb;
     float *V = a.V + (size_t)g * a.X * a.rb;
     gram_cholesky<NB>(a, W, L, sY);
-    solve_rows<NB>(a, W, V, L, sY);
+    solve_rows<NB>(a, W, V, L, Li, sY);
     __syncthreads();
     gram_cholesky<NB>(a, V, L, sY);
-    solve_rows<NB>(a, V, V, L, sY);
+    solve_rows<NB>(a, V, V, L, Li, sY);
 }
 
 // Rayleigh-Ritz, first part: H = V^T W (W = C V), its eigenvectors by cyclic Jacobi sweeps.  Only
