@@ -189,7 +189,7 @@ int blocks_of(const EncodeArgs &a) {
 // Every lane loads its own operands straight from memory: A = staging rows (16 bytes per lane
 // per k-step) and the mean mu (the same in every row), B = W_down rows 16ks + 8h2 + 0..7 of
 // column c0 + l32 (eight 2-byte loads; a wave's loads cover whole 64-byte row segments).  Groups
-// of EGRP k-steps are double-buffered.  Inputs stay exact bf16; x W and mu W accumulate in
+// of EG k-steps are double-buffered.  Inputs stay exact bf16; x W and mu W accumulate in
 // separate fp32 chains and are subtracted at the end; the waves' partial tiles are summed in a
 // fixed order through LDS.  The append slots (write_pos, then the page table) are fetched at the
 // start so that the stores at the end wait on nothing.
@@ -199,19 +199,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int EWAVES = 8;            // waves per workgroup
 // word 3 of a raw (untyped, unswizzled) buffer resource
 constexpr int kBufferWord3 = 0x00020000;
-constexpr int EGRP = 4;              // k-steps per load group
+// k-steps per load group: four in the single-call kernel; one in the many-layer kernel, whose
+// tiles leave each wave a few k-steps, so that its registers fit two workgroups per CU
+constexpr int EGRP = 4, EGRP_LAYERS = 1;
 
 __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+template <int EG>
 struct EncOps {
-    uint4 x[EGRP], m[EGRP];
-    uint16_t w[EGRP][8];
+    uint4 x[EG], m[EG];
+    uint16_t w[EG][8];
 };
 
 // One workgroup's tile `blk` of axis `a` (RS rows per workgroup).
+template <int EG>
 __device__ __forceinline__ void encode_mfma_tile(const EncodeArgs a, int blk, const int RS) {
     __shared__ float sAcc[EWAVES][32][33];
 
@@ -265,10 +269,10 @@ __device__ __forceinline__ void encode_mfma_tile(const EncodeArgs a, int blk, co
     const int ml = 16 * h2;
     const int dsh = a.d == 128 ? 7 : 6;
 
-    // k-steps kg .. kg + EGRP - 1 of this wave; steps past its range load in bounds and are zeroed
-    auto load_grp = [&](int kg, EncOps &op) {
+    // k-steps kg .. kg + EG - 1 of this wave; steps past its range load in bounds and are zeroed
+    auto load_grp = [&](int kg, EncOps<EG> &op) {
 #pragma unroll
-        for (int j = 0; j < EGRP; ++j) {
+        for (int j = 0; j < EG; ++j) {
             const int ks = min(kg + j, max(ks1 - 1, 0));
             int xo;                                             // the k-step's row offset
             if (a.mode) {
@@ -285,9 +289,9 @@ __device__ __forceinline__ void encode_mfma_tile(const EncodeArgs a, int blk, co
         }
     };
     f32x16 acc = {}, accmu = {};
-    auto compute = [&](int kg, const EncOps &op) {
+    auto compute = [&](int kg, const EncOps<EG> &op) {
 #pragma unroll
-        for (int j = 0; j < EGRP; ++j) {
+        for (int j = 0; j < EG; ++j) {
             const bool live = kg + j < ks1;
             const uint4 ax = live ? op.x[j] : make_uint4(0, 0, 0, 0);
             const uint4 am = live ? op.m[j] : make_uint4(0, 0, 0, 0);
@@ -299,7 +303,7 @@ __device__ __forceinline__ void encode_mfma_tile(const EncodeArgs a, int blk, co
         }
     };
 
-    EncOps A, Bq;
+    EncOps<EG> A, Bq;
     load_grp(ks0, A);
 #pragma unroll
     for (int o = 0; o < OUTS; ++o) {
@@ -307,12 +311,12 @@ __device__ __forceinline__ void encode_mfma_tile(const EncodeArgs a, int blk, co
         const int pi = min(max(pos, 0) / a.P, a.max_pages - 1);
         page[o] = a.block_table[(size_t)wseq[o] * a.max_pages + pi];
     }
-    for (int kg = ks0; kg < ks1; kg += 2 * EGRP) {
-        load_grp(kg + EGRP, Bq);
+    for (int kg = ks0; kg < ks1; kg += 2 * EG) {
+        load_grp(kg + EG, Bq);
         compute(kg, A);
-        if (kg + EGRP >= ks1) break;
-        load_grp(kg + 2 * EGRP, A);
-        compute(kg + EGRP, Bq);
+        if (kg + EG >= ks1) break;
+        load_grp(kg + 2 * EG, A);
+        compute(kg + EG, Bq);
     }
 
     // ---- partial tile (rows 8(v/4) + 4h2 + v%4, column l32) -> fixed-order sum over waves
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_mfma_kernel(EncodePair pr)
     int blk = blockIdx.x;
     const int axis = blk < pr.blocks_k ? 0 : 1;
     if (axis) blk -= pr.blocks_k;
-    encode_mfma_tile(axis ? pr.ax[1] : pr.ax[0], blk, pr.rows);
+    encode_mfma_tile<EGRP>(axis ? pr.ax[1] : pr.ax[0], blk, pr.rows);
 }
 
 // Several layers' encodes in one launch (the same tiles as encode_mfma_kernel, layer after
@@ -356,7 +360,8 @@ struct EncodeLayers {
     int blocks_k, blocks_layer, rows;
 };
 
-__global__ __launch_bounds__(64 * EWAVES) void encode_layers_kernel(EncodeLayers el) {
+__global__ __launch_bounds__(64 * EWAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void encode_layers_kernel(EncodeLayers el) {
     const int layer = blockIdx.x / el.blocks_layer;
     int blk = blockIdx.x - layer * el.blocks_layer;
     const int axis = blk < el.blocks_k ? 0 : 1;
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(64 * EWAVES) void encode_layers_kernel(EncodeLayers
     a.mu = el.src[layer][axis][2];
     a.pool = el.pool[layer][axis];
     a.block_table = el.block_table[layer];
-    encode_mfma_tile(a, blk, el.rows);
+    encode_mfma_tile<EGRP_LAYERS>(a, blk, el.rows);
 }
 
 int mfma_blocks_of(const EncodeArgs &a, int rows) {
