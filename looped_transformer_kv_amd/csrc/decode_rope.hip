@@ -371,19 +371,13 @@ void decode_rope_kernel(DecodeArgs a) {
 
     // ---- main loop: chunks wave, wave + WAVES, ...; a buffer is refilled with the chunk DEPTH
     // rounds ahead as soon as it has been consumed (prefetch indices clamped to the last chunk).
-    // Waves w and w + 4 share a SIMD, whose arbiter issues from the older wave first; a wave's
-    // issue priority rises with the chunks it has left, which keeps the two in step.
-    auto fair_prio = [](int left) {
-        if (left > 12) __builtin_amdgcn_s_setprio(3);
-        else if (left > 6) __builtin_amdgcn_s_setprio(2);
-        else if (left > 3) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
-    };
+    // Waves w and w + 4 share a SIMD; both serve the same two heads and keep the default issue
+    // priority (raising it by the work left, as the one-head kernel does, measured ~0.2 us slower
+    // here, and skewing the split towards the older wave ~4 us slower).
     if (wave < nchunks) {
         const int rounds = (nchunks - wave + WAVES - 1) / WAVES;   // >= 1
         int c = wave, r = 0;
         for (; r + DEPTH <= rounds; r += DEPTH) {
-            fair_prio(rounds - r);
 #pragma unroll
             for (int i = 0; i < DEPTH; ++i) {
                 compute(c, buf[i]);
@@ -399,7 +393,6 @@ void decode_rope_kernel(DecodeArgs a) {
             }
         }
     }
-    __builtin_amdgcn_s_setprio(0);
     // operands of the output step, read only by the waves that use them (threads below HG * D
     // form the output, waves below HG the self scores), in flight during the merge below: this
     // thread's column of W_up,t^V, mu_t^V and own value (head h0 + oe, element oi), and the

@@ -758,7 +758,6 @@ __global__ __launch_bounds__(64 * CWAVES) void prefill_chunk_kernel(PrefillArgs 
         l_lat = l_run;
     }
     if (len > 0) stage_wv<D, RV>(a, g, col0, tid, 64 * CWAVES, sWv);
-    const int rd = srow(lane);
     // the cached part back in model space, from the shared W_up,t^V operands
     chunk_phase<D>(a, b, h, g, col0, nn, q0, qend, sbuf, qop, oacc, m_run, l_run, l_lat,
                    [&]() __attribute__((always_inline)) {
