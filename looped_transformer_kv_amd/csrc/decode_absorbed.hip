@@ -106,47 +106,87 @@ __global__ __launch_bounds__(256) void absorbed_kernel(DecodeArgs a) {
         }
     };
 
-    // ---- prologue: the first chunks go out first (rows straight from the page table)
+    // ---- prologue.  A wave's vector loads complete in order, so the set-up loads go out before
+    // the latent burst and the arithmetic on them waits only for them: (1) the page-table entries
+    // of this wave's first chunks, (2) the set-up operands raw into registers, (3) the first
+    // latent chunks, (4) q~, <q, mu_t^K>, the self score and the LDS stores.  Every load is
+    // unconditional at a clamped in-bounds index (a load under a branch waits at the join).
+    const int c_last = max(nchunks - 1, 0);
+    int first[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) first[i] = slot_of(wave + i * WAVES);
+    // (2) q~[k] = <W_up,t^K row k (this head's columns), q>: thread t takes the 16-byte piece
+    // pc = t % NPC of rows k = t / NPC + RPP p; the NPC pieces of a row sit in one aligned lane
+    // group and are summed there.  <q, mu_t^K> and the self score: elements lane + 64 u per wave.
+    constexpr int NPC = D / 8, RPP = 64 * WAVES / NPC, QPASS = (RK + RPP - 1) / RPP;
+    constexpr int UD = D / 64;
+    const int pc = tid % NPC, kr0 = tid / NPC;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h) * D;
+    const uint16_t *wk0 = static_cast<const uint16_t *>(a.W_up_k) +
+                          ((size_t)a.t * a.G + g) * RK * a.Dg + col0 + 8 * pc;
+    uint4 wq[QPASS];
+#pragma unroll
+    for (int p = 0; p < QPASS; ++p)
+        wq[p] = *reinterpret_cast<const uint4 *>(wk0 + (size_t)min(kr0 + RPP * p, RK - 1) * a.Dg);
+    const uint4 qpc = *reinterpret_cast<const uint4 *>(qp + 8 * pc);
+    const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) + (size_t)g * a.T * a.Dg +
+                          (size_t)a.t * a.Dg + col0;
+    const bool self_here = S == 1 && a.k_self != nullptr;
+    // without a self term this reads q again and the value is dropped
+    const uint16_t *ksp = self_here ? static_cast<const uint16_t *>(a.k_self) +
+                                          (size_t)b * a.self_stride + (size_t)h * D
+                                    : qp;
+    uint16_t qv[UD], mkv[UD], ksv[UD];
+#pragma unroll
+    for (int u = 0; u < UD; ++u) {
+        qv[u] = qp[lane + 64 * u];
+        mkv[u] = muk[lane + 64 * u];
+        ksv[u] = ksp[lane + 64 * u];
+    }
+    constexpr int US = (kMaxChunksPerSplit + 64 * WAVES - 1) / (64 * WAVES);
+    int slot_reg[US];
+#pragma unroll
+    for (int u = 0; u < US; ++u) slot_reg[u] = slot_of(min(tid + 64 * WAVES * u, c_last));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (3) the first latent chunks of this wave
     AbsChunk<PK, PV> buf[DEPTH];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, slot_of(wave + i * WAVES), buf[i]);
-    for (int c = tid; c < nchunks; c += 64 * WAVES) sSlot[c] = slot_of(c);
+    for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * WAVES, first[i], buf[i]);
 
-    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + ((size_t)b * a.H + h) * D;
-    // q~[k] = <W_up,t^K row k (this head's columns), q>
-    if (tid < RK) {
-        const uint16_t *wrow = static_cast<const uint16_t *>(a.W_up_k) +
-                               (((size_t)a.t * a.G + g) * RK + tid) * a.Dg + col0;
+    // (4) the arithmetic on the set-up operands, and the LDS stores
+    auto dot8 = [](const uint4 &x, const uint4 &y) {
+        const uint32_t xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
         float acc = 0.f;
-#pragma unroll 4
-        for (int i0 = 0; i0 < D; i0 += 8) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(wrow + i0);
-            const uint4 qq = *reinterpret_cast<const uint4 *>(qp + i0);
-            const uint32_t wv[4] = {w.x, w.y, w.z, w.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
-                acc += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
-            }
+        for (int e = 0; e < 4; ++e) {
+            acc += __uint_as_float(xv[e] << 16) * __uint_as_float(yv[e] << 16);
+            acc += __uint_as_float(xv[e] & 0xffff0000u) * __uint_as_float(yv[e] & 0xffff0000u);
         }
-        sQt[tid] = acc * a.scale_log2;
+        return acc;
+    };
+#pragma unroll
+    for (int p = 0; p < QPASS; ++p) {
+        const float v = group_sum<NPC>(dot8(wq[p], qpc));
+        const int k = kr0 + RPP * p;
+        if (pc == 0 && k < RK) sQt[k] = v * a.scale_log2;
     }
-    float qm;   // <q, mu_t^K>, log2-scaled
+    float qm, s_self = -INFINITY;   // <q, mu_t^K> and the self score, log2-scaled
     {
-        const uint16_t *muk = static_cast<const uint16_t *>(a.mu_k) +
-                              (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0;
-        float acc = 0.f;
-        for (int i = lane; i < D; i += 64) acc += bf2f(qp[i]) * bf2f(muk[i]);
-        qm = wave_sum(acc) * a.scale_log2;
+        float am = 0.f, as = 0.f;
+#pragma unroll
+        for (int u = 0; u < UD; ++u) {
+            am += bf2f(qv[u]) * bf2f(mkv[u]);
+            as += bf2f(qv[u]) * bf2f(ksv[u]);
+        }
+        qm = wave_sum(am) * a.scale_log2;
+        const float ss = wave_sum(as) * a.scale_log2;
+        if (self_here) s_self = ss;
     }
-    const bool self_here = S == 1 && a.k_self != nullptr;
-    float s_self = -INFINITY;
-    if (self_here) {
-        const uint16_t *ksp = static_cast<const uint16_t *>(a.k_self) + (size_t)b * a.self_stride +
-                              (size_t)h * D;
-        float acc = 0.f;
-        for (int i = lane; i < D; i += 64) acc += bf2f(qp[i]) * bf2f(ksp[i]);
-        s_self = wave_sum(acc) * a.scale_log2;
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+        const int c = tid + 64 * WAVES * u;
+        if (c < nchunks) sSlot[c] = slot_reg[u];
     }
     __syncthreads();
     float qt[8];
@@ -231,6 +271,26 @@ __global__ __launch_bounds__(256) void absorbed_kernel(DecodeArgs a) {
         }
     }
 
+    // ---- operands of the output step, which the threads below D form: column tid % D of
+    // W_up,t^V, mu_t^V and the own value, issued now so that they arrive during the merge below
+    // (value ranks up to 64; wider ones read the column during the expansion)
+    constexpr bool EARLY_W = RV <= 64;
+    const uint16_t *wv = static_cast<const uint16_t *>(a.W_up_v) +
+                         ((size_t)a.t * a.G + g) * RV * a.Dg + col0 + tid % D;
+    // every thread loads (column tid % D, no branch: a load under one would wait at the join);
+    // without a self term the own-value read repeats mu_t^V and is dropped
+    const uint16_t *muvp = static_cast<const uint16_t *>(a.mu_v) + (size_t)g * a.T * a.Dg +
+                           (size_t)a.t * a.Dg + col0 + tid % D;
+    const uint16_t *vsp = self_here ? static_cast<const uint16_t *>(a.v_self) +
+                                          (size_t)b * a.self_stride + (size_t)h * D + tid % D
+                                    : muvp;
+    uint16_t wcol[EARLY_W ? RV : 1];
+    if constexpr (EARLY_W) {
+#pragma unroll
+        for (int k = 0; k < RV; ++k) wcol[k] = wv[(size_t)k * a.Dg];
+    }
+    const uint16_t muv_raw = *muvp, vs_raw = *vsp;
+
     // ---- this wave's c~: sum the lanes of each rank group (tokens tv0 = 0, 1, ...), fixed order
 #pragma unroll
     for (int e = 0; e < 8; ++e) sRed[wave][lane][e] = cacc[e];
@@ -267,22 +327,21 @@ __global__ __launch_bounds__(256) void absorbed_kernel(DecodeArgs a) {
             for (int w = 0; w < WAVES; ++w) L += sL[w] * exp2_(sM[w] - M);
         }
         // O = c~ W_up,t^V (this head's column tid)
-        const uint16_t *wv = static_cast<const uint16_t *>(a.W_up_v) +
-                             ((size_t)a.t * a.G + g) * RV * a.Dg + col0 + tid;
         float O = 0.f;
-        for (int k = 0; k < RV; ++k) O += sCbar[k] * bf2f(wv[(size_t)k * a.Dg]);
+        if constexpr (EARLY_W) {
+#pragma unroll
+            for (int k = 0; k < RV; ++k) O += sCbar[k] * bf2f(wcol[k]);
+        } else {
+            for (int k = 0; k < RV; ++k) O += sCbar[k] * bf2f(wv[(size_t)k * a.Dg]);
+        }
         if (S == 1) {
             const float Mf = fmaxf(M, s_self);
             float res = 0.f;
             if (Mf != -INFINITY) {
                 const float e = M != -INFINITY ? exp2_(M - Mf) : 0.f;
                 const float w_self = self_here ? exp2_(s_self - Mf) : 0.f;
-                const float v_self = self_here ? bf2f(static_cast<const uint16_t *>(a.v_self)[
-                                                     (size_t)b * a.self_stride + (size_t)h * D + tid])
-                                               : 0.f;
-                const float mu = bf2f(static_cast<const uint16_t *>(a.mu_v)[
-                    (size_t)g * a.T * a.Dg + (size_t)a.t * a.Dg + col0 + tid]);
-                res = ((O + L * mu) * e + w_self * v_self) / (L * e + w_self);
+                const float v_self = self_here ? bf2f(vs_raw) : 0.f;
+                res = ((O + L * bf2f(muv_raw)) * e + w_self * v_self) / (L * e + w_self);
             }
             static_cast<uint16_t *>(a.out)[((size_t)b * a.H + h) * D + tid] = f2bf(res);
         } else {
