@@ -207,12 +207,15 @@ __global__ __launch_bounds__(64 * kWaves, OCC) void absorbed2d_kernel(DecodeArgs
         }
     };
 
-    // ---- prologue: first chunks in flight, then the chunk -> row table
-    Abs2dChunk<RK, RV> buf[DEPTH];
+    // ---- prologue.  A wave's vector loads complete in order, so the small loads go out before
+    // the latent burst: (1) the page-table entries of this wave's first chunks, (2) the q~ operands,
+    // <q, mu^K> and the table entries of this wave's own chunks (c = wave + kWaves * (lane + 64 u);
+    // only this wave reads them, so no barrier is needed), (3) the first latent chunks.  Every
+    // load is unconditional at a clamped in-bounds index (a load under a branch waits at the join).
+    const int c_last = max(nchunks - 1, 0);
+    int first[DEPTH];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-        if (wave + i * kWaves < nchunks) load_slot(wave + i * kWaves, slot_of(wave + i * kWaves), buf[i]);
-    for (int c = tid; c < nchunks; c += 64 * kWaves) sSlot[c] = slot_of(c);
+    for (int i = 0; i < DEPTH; ++i) first[i] = slot_of(wave + i * kWaves);
 
     // B operands of the score MFMA: lane l holds head l % 16, ranks 32 kk + 8 g .. + 7
     bf16x8 qhi[NKK], qlo[NKK];
@@ -226,7 +229,20 @@ __global__ __launch_bounds__(64 * kWaves, OCC) void absorbed2d_kernel(DecodeArgs
         }
     }
     const float qm = a.ws[lay.qm + (size_t)b * kAbs2dHeads + c16];
-    __syncthreads();
+    constexpr int US = (kMaxChunksPerSplit / kWaves + 63) / 64;
+    int slot_reg[US];
+#pragma unroll
+    for (int u = 0; u < US; ++u) slot_reg[u] = slot_of(min(wave + kWaves * (lane + 64 * u), c_last));
+    __builtin_amdgcn_sched_barrier(0);
+
+    Abs2dChunk<RK, RV> buf[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) load_slot(wave + i * kWaves, first[i], buf[i]);
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+        const int c = wave + kWaves * (lane + 64 * u);
+        if (c < nchunks) sSlot[c] = slot_reg[u];
+    }
 
     float m_run = -INFINITY, l_lane = 0.f;
     f32x4 acc[NVB];
