@@ -21,51 +21,98 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a, int has_mu, in
     const int b = bh / a.H, h = bh % a.H;
     const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
     const float *rec0 = a.ws + (size_t)bh * a.S * (D + kPartialPad);
+    const int S = a.S;
+    auto rec = [&](int s) { return rec0 + (size_t)min(s, S - 1) * (D + kPartialPad); };
+
+    // Every load goes out before the first use: the first UB splits' (m, l, o[i]), the self
+    // operands and mu; later splits (S > UB) follow in blocks of UB.  The sums run over the
+    // splits in order, as two passes (the common max, then the weighted sums).
+    constexpr int UB = 8;
+    float m0[UB], l0[UB], o0[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+        const float *r = rec(u);
+        m0[u] = r[D];
+        l0[u] = r[D + 1];
+        o0[u] = r[i];
+    }
+    const bool has_self = a.k_self != nullptr;
+    const bool self_dot = has_self && !self_in_record;   // the self score is formed here
+    const TS *qp = static_cast<const TS *>(a.q) + ((size_t)b * a.H + h) * D;
+    // without a self term these read q and the values are dropped
+    const TS *ks = has_self ? static_cast<const TS *>(a.k_self) + (size_t)b * a.self_stride +
+                                  (size_t)h * D
+                            : qp;
+    const TS *vs = has_self ? static_cast<const TS *>(a.v_self) + (size_t)b * a.self_stride +
+                                  (size_t)h * D
+                            : qp;
+    const float q_i = ld_elt<TS>(qp + i), k_i = ld_elt<TS>(ks + i), v_i = ld_elt<TS>(vs + i);
+    const int g = a.mode ? 0 : h;
+    const int col0 = a.mode ? h * D : 0;
+    const float mu_i = has_mu ? ld_elt<TS>(static_cast<const TS *>(a.mu_v) + (size_t)g * a.T * a.Dg +
+                                           (size_t)a.t * a.Dg + col0 + i)
+                              : 0.f;
 
     float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, rec0[(size_t)s * (D + kPartialPad) + D]);
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+        if (u < S) M = fmaxf(M, m0[u]);
+    for (int s0 = UB; s0 < S; s0 += UB) {
+        float mv[UB];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) mv[u] = rec(s0 + u)[D];
+#pragma unroll
+        for (int u = 0; u < UB; ++u)
+            if (s0 + u < S) M = fmaxf(M, mv[u]);
+    }
 
-    const bool has_self = a.k_self != nullptr;
     float s_self = -INFINITY, v_self = 0.f;
     if (has_self && self_in_record) {
         s_self = rec0[D + 2];
-        v_self = ld_elt<TS>(static_cast<const TS *>(a.v_self) + (size_t)b * a.self_stride +
-                            (size_t)h * D + i);
+        v_self = v_i;
         M = fmaxf(M, s_self);
-    } else if (has_self) {
-        const TS *qp = static_cast<const TS *>(a.q) + ((size_t)b * a.H + h) * D;
-        const TS *ks = static_cast<const TS *>(a.k_self) + (size_t)b * a.self_stride +
-                       (size_t)h * D;
-        const TS *vs = static_cast<const TS *>(a.v_self) + (size_t)b * a.self_stride +
-                       (size_t)h * D;
-        float prod = wave_sum(ld_elt<TS>(qp + i) * ld_elt<TS>(ks + i));
+    } else if (self_dot) {
+        float prod = wave_sum(q_i * k_i);
         if (lane == 0) red[wave] = prod;
         __syncthreads();
         float dot = 0.f;
         for (int w = 0; w < D / 64; ++w) dot += red[w];
         s_self = dot * a.scale_log2;
-        v_self = ld_elt<TS>(vs + i);
+        v_self = v_i;
         M = fmaxf(M, s_self);
     }
 
     float res = 0.f;
     if (M != -INFINITY) {
         float L = 0.f, O = 0.f;
-        for (int s = 0; s < a.S; ++s) {
-            const float *rec = rec0 + (size_t)s * (D + kPartialPad);
-            const float e = exp2_(rec[D] - M);
-            L += rec[D + 1] * e;
-            O += rec[i] * e;
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            if (u < S) {
+                const float e = exp2_(m0[u] - M);
+                L += l0[u] * e;
+                O += o0[u] * e;
+            }
         }
-        float mu = 0.f;
-        if (has_mu) {
-            const int g = a.mode ? 0 : h;
-            const int col0 = a.mode ? h * D : 0;
-            mu = ld_elt<TS>(static_cast<const TS *>(a.mu_v) + (size_t)g * a.T * a.Dg +
-                            (size_t)a.t * a.Dg + col0 + i);
+        for (int s0 = UB; s0 < S; s0 += UB) {
+            float mv[UB], lv[UB], ov[UB];
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const float *r = rec(s0 + u);
+                mv[u] = r[D];
+                lv[u] = r[D + 1];
+                ov[u] = r[i];
+            }
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                if (s0 + u < S) {
+                    const float e = exp2_(mv[u] - M);
+                    L += lv[u] * e;
+                    O += ov[u] * e;
+                }
+            }
         }
         const float w_self = has_self ? exp2_(s_self - M) : 0.f;
-        res = (O + L * mu + w_self * v_self) / (L + w_self);
+        res = (O + L * mu_i + w_self * v_self) / (L + w_self);
     }
     st_elt<TS>(static_cast<TS *>(a.out) + (size_t)bh * D + i, res);
 }
