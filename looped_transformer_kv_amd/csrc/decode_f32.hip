@@ -27,10 +27,13 @@ __device__ float block_reduce(float v, float *red, bool is_max) {
     return r;
 }
 
-template <int D>
+// RKC, RVC: the latent ranks when known at compile time (0: read from the arguments).  Known ranks
+// let the rank loops unroll, so a token's latent row is read once into registers instead of once
+// per head-dim element; the arithmetic and its order are the same either way.
+template <int D, int RKC, int RVC>
 __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
     extern __shared__ float smem[];
-    const int RK = a.r_k, RV = a.r_v;
+    const int RK = RKC ? RKC : a.r_k, RV = RVC ? RVC : a.r_v;
     float *sWk = smem;               // [RK][D]
     float *sWv = sWk + RK * D;       // [RV][D]
     float *sQ = sWv + RV * D;        // [D]  q * scale * log2(e)
@@ -136,10 +139,12 @@ hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t st) {
     const int d = a.mode ? a.Dg / a.H : a.Dg;
     const unsigned blocks = (unsigned)a.B * a.H * a.S;
     const size_t lds = decode_f32_lds_bytes(d, a.r_k, a.r_v);
-    if (d == 128)
-        hipLaunchKernelGGL(decode_f32_kernel<128>, dim3(blocks), dim3(kThreads), lds, st, a);
+    if (d == 64 && a.r_k == 8 && a.r_v == 16)   // the small fp32 codec of the tiny configuration
+        hipLaunchKernelGGL((decode_f32_kernel<64, 8, 16>), dim3(blocks), dim3(kThreads), lds, st, a);
+    else if (d == 128)
+        hipLaunchKernelGGL((decode_f32_kernel<128, 0, 0>), dim3(blocks), dim3(kThreads), lds, st, a);
     else if (d == 64)
-        hipLaunchKernelGGL(decode_f32_kernel<64>, dim3(blocks), dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL((decode_f32_kernel<64, 0, 0>), dim3(blocks), dim3(kThreads), lds, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -229,3 +229,24 @@ def test_bench_flat_launch_sampled(gpu):
     vp = synth.from_device(vf.index_select(0, idx))
     ref = O.flat_attn(H, d, kp, vp, bt2, lens[sel], P, q[sel])
     assert_close(got[sel], ref, "bf16", "flat comparator, benchmark launch")
+
+
+F32_SHAPES = [(64, 8, 16), (64, 12, 20), (128, 16, 32), (128, 24, 8)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=[f"d{d}_r{a}_{b}" for d, a, b in F32_SHAPES])
+def test_decode_f32_shapes(gpu, shape):
+    """fp32 codecs: the kernel built for the 8/16 codec at d = 64 and the one with runtime ranks
+    (any other pair), with ragged lengths including 0 and 1, a self term, loops 0 and T - 1, and
+    several context splits."""
+    d, r_k, r_v = shape
+    cfg = synth.Config(f"f32_d{d}_{r_k}_{r_v}", L=1, H=2, d=d, T=4, r_k=r_k, r_v=r_v, B=3, N=1,
+                       mode=0, dtype="f32", cid=700 + F32_SHAPES.index(shape))
+    p, dp = _problem(cfg)
+    assert dp.layer.plan.splits > 1
+    for t in (0, cfg.T - 1):
+        say(f"f32 decode d={d} r=({r_k},{r_v}) lens={list(p.seq_lens)} t={t} "
+            f"splits={dp.layer.plan.splits}")
+        assert_close(dp.decode(t, True), dp.oracle_decode(t, True), "f32",
+                     f"f32 d={d} r=({r_k},{r_v}) t={t}")
