@@ -709,7 +709,6 @@ void decode_bf16_kernel(DecodeArgs a) {
             }
             t0 += u0;
             t1 += u1;
-            __builtin_amdgcn_sched_barrier(0);   // one tile's accumulators live at a time
         }
         if (n0 >= 0) {
             load_half(n0, x0, true);
@@ -749,7 +748,6 @@ void decode_bf16_kernel(DecodeArgs a) {
                 acc += u.x * v1[4 * bb] + u.y * v1[4 * bb + 1] + u.z * v1[4 * bb + 2] + u.w * v1[4 * bb + 3];
             }
             o[(FUSED) ? 0 : N] += acc;
-            __builtin_amdgcn_sched_barrier(0);
         }
         if (n0 >= 0) {
             load_half(n0, x0, false);
