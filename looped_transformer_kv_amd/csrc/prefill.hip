@@ -1018,14 +1018,14 @@ void prefill_wide_kernel(PrefillArgs a) {
         };
         // Tile n (buffer `buf`), whose scores `scn` holds, then the inputs of tile n + 2 (into
         // buffer `pbuf`, from stage set `st`) and the loads of tile n + 4 (into `st`).  After two
-        // rare uniform branches (the last tile's mask, the first tile's reference) the step is two
-        // branch-free scheduling regions whose MFMAs are fenced between the other instructions:
+        // rare uniform branches (the last tile's mask, the first tile's reference) the step is
+        // branch-free code in two parts, which the compiler schedules together (fencing each MFMA
+        // between the other instructions measured 3.5 % slower at 96/160, and fencing only the
+        // second part 17 % slower):
         //  1. tile n + 1's key operands and tile n's value operands from LDS, tile n + 1's score
         //     MFMAs, each followed by its share of tile n's softmax;
         //  2. tile n's value MFMAs in pairs (block kj RT + rt holds tokens 16 kj .. + 15 of ranks
         //     32 rt .. + 31), tile n + 2's LDS writes and tile n + 4's loads between them.
-        // (The interleave measures the same as clumped MFMAs: what bounds a tile is the burst of
-        // LDS reads all eight waves issue after the barrier, not issue order.)
         // Every wave runs every step (a wave whose queries are all past the chunk computes on
         // the chunk's last query and discards the result); the score MFMAs past the last tile
         // read a stale buffer and go unused.
@@ -1060,17 +1060,15 @@ void prefill_wide_kernel(PrefillArgs a) {
                 va[i] = make_uint4(pk16(r0[0], r0[1]), pk16(r0[2], r0[3]), pk16(r1[0], r1[1]),
                                    pk16(r1[2], r1[3]));
             }
-            // tile n + 1's score MFMAs, each followed by its share of tile n's softmax (fenced,
-            // so that the scheduler keeps the interleave)
+            // tile n + 1's score MFMAs, each followed by its share of tile n's softmax (the
+            // scheduler interleaves them with the value step below: no fences)
             f32x16 s2 = {}, pr;
 #pragma unroll
             for (int i = 0; i < KK; ++i) {
-                __builtin_amdgcn_sched_barrier(0);
                 s2 = mfma(ka[i], qlat[i], s2);
 #pragma unroll
                 for (int v = 16 * i / KK; v < 16 * (i + 1) / KK; ++v) pr[v] = exp2_(sc[v] - m_lat);
             }
-            __builtin_amdgcn_sched_barrier(0);
             scn = s2;
             uint4 p0 = pack8(pr, 0), p1 = pack8(pr, 1);
             float ls = wsum(p0, p1);
@@ -1083,17 +1081,15 @@ void prefill_wide_kernel(PrefillArgs a) {
                 ls = wsum(p0, p1);
             }
             l_sum += ls;
-            // ---- region 2: the value MFMAs in fenced pairs, with tile n + 2's LDS writes and tile
-            // n + 4's loads between them
+            // ---- region 2: the value MFMAs in pairs, with tile n + 2's LDS writes and tile n + 4's
+            // loads between them
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                __builtin_amdgcn_sched_barrier(0);
                 olat[rt] = mfma(va[rt], p0, olat[rt]);
                 olat[rt] = mfma(va[RT + rt], p1, olat[rt]);
                 if (rt == 0) produce(n + 2, st, pbuf);
                 if (rt == (RT > 2 ? 2 : RT - 1)) issue(n + 4, st);
             }
-            __builtin_amdgcn_sched_barrier(0);
         };
 
         // ---- pipeline over a ring of three LDS tile buffers (tile n in buffer n % 3): tile n's
